@@ -1,0 +1,236 @@
+/*
+ * fg — 4-bit zig-zag block decode of an OPT-style decoder on MI355X (gfx950).
+ *
+ * C ABI of libfg.so.  Every entry point takes plain device pointers and sizes;
+ * fp16 tensors are raw binary16 arrays, row-major unless stated.  `stream` is
+ * a hipStream_t passed as void* (NULL = the null stream).
+ *
+ * Pages the operations come from (cited by title and section):
+ *   [P2] "FlexGen 完全拆解:用线性规划编排 GPU、CPU 与 SSD 上的大模型推理"
+ *        (pinghaoyang.com.cn)
+ *   [P1] bjbfmj.com FlexGen walkthrough (sections 一…八 cited as §1…§8)
+ *
+ * Conventions shared by every call:
+ *   - Ownership: the caller allocates and owns every buffer.  Calls keep no
+ *     pointer after they return.  Buffers must stay valid until the work
+ *     enqueued on `stream` has finished.
+ *   - Asynchrony: calls only validate on the host and enqueue kernels; the
+ *     results are ready once the stream is synchronised.
+ *   - Errors: arguments are checked on the host before anything is launched;
+ *     a failed check returns a negative status, launches nothing and leaves
+ *     every buffer untouched.  A failing HIP runtime call returns
+ *     FG_ERR_HIP.  fg_last_error() gives the detail of the calling thread's
+ *     last failure.  No C++ exception crosses this interface.
+ *   - Threading: calls are stateless and may be issued from several threads.
+ */
+#ifndef FG_H
+#define FG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status */
+enum {
+    FG_OK = 0,
+    FG_ERR_INVALID = -1,      /* null pointer, bad size, inconsistent shapes */
+    FG_ERR_UNSUPPORTED = -2,  /* valid but not implemented (e.g. head_dim 96) */
+    FG_ERR_CAPACITY = -3,     /* workspace or cache too small for the request */
+    FG_ERR_HIP = -4           /* a HIP runtime call failed */
+};
+
+const char* fg_status_str(int status);
+/* Detail of the calling thread's last failing call ("" if none). */
+const char* fg_last_error(void);
+/* ABI version, bumped on any incompatible change of this header. */
+int fg_abi_version(void);
+
+/* ----------------------------------------------------------------- formats */
+enum {
+    FG_FMT_F16 = 0,     /* fp16 tensor */
+    FG_FMT_Q4G64 = 1    /* 4-bit codes + fp16 (min, scale) per group of 64 */
+};
+
+/* Decoder dimensions: hidden h1, MLP h2, heads n_heads of head_dim each.
+ * Requires h1 = n_heads * head_dim, h1 % 64 == 0, h2 % 64 == 0,
+ * head_dim in {64, 128}. */
+typedef struct {
+    int32_t h1, h2, n_heads, head_dim;
+} fg_dims;
+
+/* ------------------------------------------------------------------- codec */
+/*
+ * Group-wise asymmetric 4-bit min-max quantization ([P2] "权重压缩与 KV Cache
+ * 压缩", quantize equation; [P1] §6.3 CompressionConfig num_bits 4,
+ * group_size 64, asymmetric, two 4-bit values per uint8, fp16 scale tensor).
+ *
+ * x: fp16 viewed as [outer, axis, inner]; each run of `group` consecutive
+ * elements along `axis` (fixed outer, inner) is one group.  Per group, in
+ * binary32 with one rounding per operation:
+ *   mn, mx = min, max (-0 canonicalised to +0); range = mx - mn;
+ *   q = range > 0 ? clamp(rint((x - mn) * (15 / range)), 0, 15) : 0
+ *   (rint: nearest, ties to even; 15/range computed once per group).
+ * codes: uint8 [outer, axis/2, inner]; byte j of a group holds element 2j in
+ *   its low nibble and element 2j+1 in its high nibble.
+ * meta:  fp16  [outer, axis/group, 2, inner] = (fp16(mn), fp16(range / 15)).
+ * Weights [N, K] are quantized with outer = 1, axis = N, inner = K (groups
+ * along output channels); the KV cache with inner = 1 along head_dim.
+ * Requirements: group == 64, axis % 64 == 0, outer, inner >= 1.
+ * Results are bit-identical to the CPU definition for identical inputs.
+ */
+int fg_quant_group4(const void* x, int64_t outer, int64_t axis, int64_t inner,
+                    int32_t group, void* codes, void* meta, void* stream);
+
+/* Inverse ([P2] dequantize equation): y = fp16(mn + q * scale), a binary32
+ * multiply then add.  Same layouts and requirements as fg_quant_group4. */
+int fg_dequant_group4(const void* codes, const void* meta, int64_t outer, int64_t axis,
+                      int64_t inner, int32_t group, void* y, void* stream);
+
+/* ------------------------------------------------------------ layer weights */
+/*
+ * One decoder layer ([P2] "从 Transformer 推理的数据流重新定义卸载": four
+ * h1 x h1 attention matrices and two MLP matrices; pre-LN, ReLU MLP).
+ * Matrices are [N = out, K = in]: w_qkv [3*h1, h1] stacks W_Q, W_K, W_V rows;
+ * w_o [h1, h1]; w_1 [h2, h1]; w_2 [h1, h2].
+ *   fmt FG_FMT_F16:   w_* fp16; m_* unused (NULL).
+ *   fmt FG_FMT_Q4G64: w_* = codes [N/2, K], m_* = meta [N/64, 2, K]
+ *                     (fg_quant_group4 with outer 1, axis N, inner K).
+ * Biases b_* [N] and LayerNorm gamma/beta [h1] are fp16 in both formats.
+ */
+typedef struct {
+    int32_t fmt;
+    const void *w_qkv, *m_qkv, *b_qkv;
+    const void *w_o, *m_o, *b_o;
+    const void *w_1, *m_1, *b_1;
+    const void *w_2, *m_2, *b_2;
+    const void *ln1_g, *ln1_b, *ln2_g, *ln2_b;
+} fg_layer_w;
+
+/*
+ * One layer's KV cache for n_seq sequences and max_len positions
+ * ([P2] KV append: K_{1:s+t} = Concat(K_{1:s+t-1}, X_t W_K), same for V).
+ *   fmt FG_FMT_Q4G64: k, v = codes [n_seq, n_heads, max_len, head_dim/2];
+ *                     k_meta, v_meta = fp16 [n_seq, n_heads, max_len, head_dim/64, 2]
+ *                     (groups of 64 along head_dim, [P1] §6.3 group_dim 2).
+ *   fmt FG_FMT_F16:   k, v = fp16 [n_seq, n_heads, max_len, head_dim]; metas NULL.
+ */
+typedef struct {
+    int32_t fmt;
+    void *k, *k_meta, *v, *v_meta;
+    int32_t max_len;
+    int32_t n_seq;
+} fg_kv;
+
+/* ---------------------------------------------------------- KV append / attn */
+/*
+ * Append one position: quantize (or copy, for fp16 caches) k_new, v_new of
+ * each of the first bls sequences into position `pos` of the cache.
+ * k_new, v_new: fp16 rows of stride ld elements (ld >= h1), head h at
+ * columns [h*head_dim, (h+1)*head_dim).  Requires 0 <= pos < max_len,
+ * 1 <= bls <= n_seq, kv->fmt matching the function.
+ */
+int fg_kv_append_q4(const void* k_new, const void* v_new, int64_t ld, const fg_kv* kv,
+                    int32_t bls, const fg_dims* d, int32_t pos, void* stream);
+int fg_kv_append_f16(const void* k_new, const void* v_new, int64_t ld, const fg_kv* kv,
+                     int32_t bls, const fg_dims* d, int32_t pos, void* stream);
+
+/*
+ * Decode attention for one new token per sequence at position `pos`
+ * ([P2] decode: the single query attends to all s+t cached keys).
+ * out[b, h*hd + c] = sum_p softmax_p(q.k_p / sqrt(hd)) v_p[c] over p = 0..pos:
+ * positions < pos come from the cache (dequantized in registers for 4-bit
+ * caches); position pos uses the fresh fp16 k_new, v_new.  With fuse_append
+ * != 0 the same launch also appends k_new, v_new at pos (as fg_kv_append_*).
+ * q, k_new, v_new: fp16 rows of stride ld; out: fp16 [bls, h1] (stride h1).
+ */
+int fg_attn_decode_q4(const void* q, const void* k_new, const void* v_new, int64_t ld,
+                      const fg_kv* kv, int32_t bls, const fg_dims* d, int32_t pos,
+                      int32_t fuse_append, void* out, void* stream);
+int fg_attn_decode_f16(const void* q, const void* k_new, const void* v_new, int64_t ld,
+                       const fg_kv* kv, int32_t bls, const fg_dims* d, int32_t pos,
+                       int32_t fuse_append, void* out, void* stream);
+
+/*
+ * Causal prompt attention ([P2] prefill over all s prompt tokens):
+ * qkv fp16 [b*s, 3*h1] rows (q | k | v); out fp16 [b*s, h1];
+ * row t of a sequence attends to its rows 0..t.
+ */
+int fg_attn_prefill(const void* qkv, int32_t b, int32_t s, const fg_dims* d, void* out,
+                    void* stream);
+
+/* --------------------------------------------------------- decoder pieces */
+/*
+ * y = act(x W^T + bias) + residual, fp32 accumulation on fp16 MFMA, one
+ * rounding to fp16.  x fp16 [M, K]; W [N, K] in `fmt` (q4: codes w, meta m,
+ * dequantized on the fly); bias fp16 [N] or NULL; act: 0 none, 1 ReLU
+ * (applied before the residual); residual fp16 [M, N] or NULL and may equal y.
+ * ws: device scratch of ws_bytes >= fg_linear_workspace_bytes(M, N, K) (may
+ * be NULL when that is 0).  Requires K % 64 == 0, N % 64 == 0 for q4 and
+ * N % 8 == 0 for fp16.
+ */
+int fg_linear(const void* x, int64_t M, int64_t K, int32_t fmt, const void* w, const void* m,
+              int64_t N, const void* bias, int32_t act, const void* residual, void* y,
+              void* ws, size_t ws_bytes, void* stream);
+size_t fg_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Row LayerNorm over the last dim h (biased variance, eps 1e-5):
+ * y = (x - mean) / sqrt(var + eps) * gamma + beta.  x, y fp16 [rows, h]. */
+int fg_layernorm(const void* x, int64_t rows, int64_t h, const void* gamma, const void* beta,
+                 void* y, void* stream);
+
+/* x[r] = fp16(E[tok[r]] + P[pos[r]]): tok, pos int32 [rows] (device),
+ * E fp16 [vocab, h1], P fp16 [max_pos, h1].  Ids are clamped to the tables'
+ * ranges on the device (the host cannot see device-resident ids). */
+int fg_embed(const int32_t* tok, const int32_t* pos, int64_t rows, const void* E, int64_t vocab,
+             const void* P, int64_t max_pos, int64_t h1, void* x, void* stream);
+
+/* out[r] = index of the largest fp16 value of row r of logits [rows, n]
+ * (lowest index on ties). */
+int fg_argmax(const void* logits, int64_t rows, int64_t n, int32_t* out, void* stream);
+
+/* ---------------------------------------------------------------- layers */
+/*
+ * Prefill one layer for a block of nb GPU batches of gbs sequences each
+ * (bls = gbs * nb), prompt length s ([P2] "FlexGen 的核心:计算图分块…":
+ * inside one layer every GPU batch of the block runs before the next layer).
+ * x: fp16 [bls*s, h1], in/out (row b*s + t = token t of sequence b).
+ * Per GPU batch: LN1 -> QKV -> causal attention -> append K, V of positions
+ * 0..s-1 to kv -> out-proj + residual -> LN2 -> FC1 + ReLU -> FC2 + residual.
+ * ws: ws_bytes >= fg_workspace_bytes(d, gbs * s, w->fmt).
+ */
+int fg_layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, int32_t nb,
+                     int32_t s, const fg_kv* kv, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One decode step of one layer for the whole block (bls = gbs * nb new
+ * tokens, one per sequence, all at position pos) — the zig-zag block's inner
+ * loop ([P2] block schedule; pipeline pseudocode in "一个层级流水的伪代码").
+ * The layer's weights are read once for all bls rows: every projection is one
+ * contraction over bls rows; attention runs per (sequence, head) with the
+ * fused K, V append at pos.
+ * x: fp16 [bls, h1], in/out.  ws: ws_bytes >= fg_workspace_bytes(d, bls, w->fmt).
+ */
+int fg_layer_decode_block(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs,
+                          int32_t nb, int32_t pos, const fg_kv* kv, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* Device scratch needed by one layer pass over `rows` token rows
+ * (decode: rows = bls; prefill: rows = gbs * s). */
+size_t fg_workspace_bytes(const fg_dims* d, int64_t rows, int32_t fmt_w);
+
+/* --------------------------------------------------------------- sizes */
+/* Bytes of the six layer matrices of n_layers layers ([P2]: M_W =
+ * l (8 h1^2 + 4 h1 h2) in fp16; 4-bit: codes + 4 bytes of meta per 64). */
+int64_t fg_weight_bytes(const fg_dims* d, int32_t n_layers, int32_t fmt);
+/* Bytes of the KV cache ([P2]: M_KV = 4 b l h1 (s + n) in fp16; 4-bit:
+ * 9/32 of that). */
+int64_t fg_kv_bytes(const fg_dims* d, int32_t n_layers, int32_t bls, int32_t s, int32_t n,
+                    int32_t fmt);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FG_H */

@@ -40,6 +40,8 @@ def _gen(device, s):
 def normal_f16(shape, seed: int, device="cpu", std: float = STD, chunk_rows: int = 4096):
     """fp16 tensor ~ N(0, std^2); drawn in fp32 in row chunks (bounded scratch)."""
     out = torch.empty(shape, dtype=torch.float16, device=device)
+    if out.numel() == 0:
+        return out
     g = _gen(device, seed)
     flat = out.view(shape[0], -1) if len(shape) > 1 else out.view(1, -1)
     for r0 in range(0, flat.shape[0], chunk_rows):

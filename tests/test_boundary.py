@@ -1,0 +1,141 @@
+"""Host-side checks of the C ABI (no GPU work): the library loads and exports
+every function include/fg.h declares; the closed-form sizes equal the pages'
+formulas; bad arguments are rejected on the host before any launch."""
+import ctypes
+
+import pytest
+
+import oracle
+
+
+@pytest.fixture(scope="module")
+def L():
+    from throughput_oriented_offloaded_amd import _lib
+    return _lib
+
+
+def test_exports_every_declared_symbol(L):
+    declared = L.header_symbols()
+    assert len(declared) >= 20
+    missing = [n for n in declared if n not in L.exported_symbols()]
+    assert not missing, missing
+    for name in ("fg_quant_group4", "fg_dequant_group4", "fg_layer_prefill",
+                 "fg_layer_decode_block", "fg_kv_append_q4", "fg_attn_decode_q4"):
+        assert name in declared
+    assert L.raw("fg_abi_version")() == 1
+
+
+def test_status_strings(L):
+    assert L.status_str(0) == "ok"
+    assert L.status_str(-1) == "invalid argument"
+    assert L.status_str(-3) == "capacity exceeded"
+    assert L.status_str(99) == "unknown status"
+
+
+@pytest.mark.parametrize("h1,h2,nh,hd,l", [(768, 3072, 12, 64, 2), (2048, 8192, 32, 64, 24),
+                                           (7168, 28672, 56, 128, 48), (9216, 36864, 72, 128, 64),
+                                           (12288, 49152, 96, 128, 96)])
+def test_size_closed_forms(L, h1, h2, nh, hd, l):
+    d = L.dims(h1, h2, nh, hd)
+    f16 = L.fg_weight_bytes(d, l, L.FG_FMT_F16)
+    assert f16 == oracle.weight_bytes_f16(h1, h2, l)
+    assert L.fg_weight_bytes(d, l, L.FG_FMT_Q4G64) * 32 == f16 * 9
+    for bls, s, n in ((144, 512, 32), (512, 512, 32), (4, 32, 8)):
+        kv = L.fg_kv_bytes(d, l, bls, s, n, L.FG_FMT_F16)
+        assert kv == oracle.kv_bytes_f16(h1, l, bls, s, n)
+        assert L.fg_kv_bytes(d, l, bls, s, n, L.FG_FMT_Q4G64) * 32 == kv * 9
+
+
+def test_175b_q4_weights_fit_in_hbm(L):
+    """The 4-bit OPT-175B weights (~98 GB) and the 4-bit KV of bls = 144 at
+    s + n = 544 (~104 GB) fit together in 288 GB of HBM."""
+    d = L.dims(12288, 49152, 96, 128)
+    w = L.fg_weight_bytes(d, 96, L.FG_FMT_Q4G64)
+    kv = L.fg_kv_bytes(d, 96, 144, 512, 32, L.FG_FMT_Q4G64)
+    codes_only = 96 * (4 * 12288 ** 2 + 2 * 12288 * 49152) // 2
+    assert abs(codes_only / 1e9 - 88) < 1.5          # "~88 GB" of codes (86.97)
+    assert w + kv < 288e9 * 0.75
+
+
+def _bad(L, name, *args):
+    st = L.raw(name)(*args)
+    return st, L.last_error()
+
+
+def test_codec_rejects_bad_arguments(L):
+    st, msg = _bad(L, "fg_quant_group4", None, 1, 64, 1, 64, None, None, None)
+    assert st == L.FG_ERR_INVALID and "null" in msg
+    p = ctypes.c_void_p(1 << 20)    # never dereferenced: validation fails first
+    st, msg = _bad(L, "fg_quant_group4", p, 1, 96, 1, 64, p, p, None)
+    assert st == L.FG_ERR_INVALID and "multiple" in msg
+    st, msg = _bad(L, "fg_quant_group4", p, 1, 128, 1, 32, p, p, None)
+    assert st == L.FG_ERR_UNSUPPORTED
+    st, msg = _bad(L, "fg_dequant_group4", p, p, 0, 64, 1, 64, p, None)
+    assert st == L.FG_ERR_INVALID
+
+
+def test_linear_rejects_bad_arguments(L):
+    p = ctypes.c_void_p(1 << 20)
+    st, _ = _bad(L, "fg_linear", p, 4, 100, 0, p, None, 64, None, 0, None, p, None, 0, None)
+    assert st == L.FG_ERR_UNSUPPORTED                  # K % 64
+    st, _ = _bad(L, "fg_linear", p, 4, 64, 1, p, None, 64, None, 0, None, p, None, 0, None)
+    assert st == L.FG_ERR_INVALID                      # q4 without meta
+    st, _ = _bad(L, "fg_linear", p, 4, 64, 1, p, p, 100, None, 0, None, p, None, 0, None)
+    assert st == L.FG_ERR_UNSUPPORTED                  # q4 N % 64
+    st, _ = _bad(L, "fg_linear", p, 4, 64, 0, p, None, 64, None, 7, None, p, None, 0, None)
+    assert st == L.FG_ERR_INVALID                      # unknown activation
+
+
+def _kv(L, fmt=1, max_len=16, n_seq=4):
+    p = 1 << 20
+    return L.KV(fmt, p, p, p, p, max_len, n_seq)
+
+
+def test_attention_rejects_bad_arguments(L):
+    p = ctypes.c_void_p(1 << 20)
+    d = L.dims(256, 1024, 2, 128)
+    kv = _kv(L)
+    f = L.raw("fg_attn_decode_q4")
+    assert f(p, p, p, 768, ctypes.byref(kv), 4, ctypes.byref(d), 16, 1, p, None) == L.FG_ERR_INVALID
+    assert "pos" in L.last_error()
+    assert f(p, p, p, 768, ctypes.byref(kv), 5, ctypes.byref(d), 3, 1, p, None) == L.FG_ERR_INVALID
+    assert f(p, p, p, 100, ctypes.byref(kv), 4, ctypes.byref(d), 3, 1, p, None) == L.FG_ERR_INVALID
+    kv16 = _kv(L, fmt=0)
+    assert f(p, p, p, 768, ctypes.byref(kv16), 4, ctypes.byref(d), 3, 1, p, None) == L.FG_ERR_INVALID
+    bad = L.dims(256, 1024, 4, 64 + 32)
+    assert f(p, p, p, 768, ctypes.byref(kv), 4, ctypes.byref(bad), 3, 1, p, None) == L.FG_ERR_INVALID
+    d96 = L.dims(192, 768, 2, 96)
+    assert f(p, p, p, 768, ctypes.byref(kv), 4, ctypes.byref(d96), 3, 1, p, None) == L.FG_ERR_UNSUPPORTED
+
+
+def test_layer_rejects_bad_arguments(L):
+    p = 1 << 20
+    d = L.dims(256, 1024, 2, 128)
+    w = L.LayerW(1, *([p] * 16))
+    kv = _kv(L, max_len=16, n_seq=4)
+    f = L.raw("fg_layer_decode_block")
+    need = L.fg_workspace_bytes(d, 4, 1)
+    assert need > 0
+    st = f(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(p), 2, 2, 3, ctypes.byref(kv),
+           ctypes.c_void_p(p), need - 1, None)
+    assert st == L.FG_ERR_CAPACITY
+    st = f(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(p), 3, 2, 3, ctypes.byref(kv),
+           ctypes.c_void_p(p), need, None)
+    assert st == L.FG_ERR_INVALID                     # 6 sequences > n_seq
+    w.m_o = None
+    st = f(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(p), 2, 2, 3, ctypes.byref(kv),
+           ctypes.c_void_p(p), need, None)
+    assert st == L.FG_ERR_INVALID
+    g = L.raw("fg_layer_prefill")
+    w.m_o = p
+    st = g(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(p), 2, 2, 17, ctypes.byref(kv),
+           ctypes.c_void_p(p), 1 << 40, None)
+    assert st == L.FG_ERR_INVALID                     # s > max_len
+
+
+def test_workspace_grows_with_rows(L):
+    d = L.dims(12288, 49152, 96, 128)
+    a = L.fg_workspace_bytes(d, 144, 1)
+    b = L.fg_workspace_bytes(d, 48 * 512, 1)
+    assert 0 < a < b
+    assert L.fg_linear_workspace_bytes(144, 12288, 49152) % 4 == 0

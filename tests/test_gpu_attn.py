@@ -1,0 +1,136 @@
+"""GPU parity of the KV append and decode / prefill attention against the oracle.
+
+Cache contents are bit-exact (same fp16 rows quantized by both sides); the
+attention outputs meet max|err| <= 1e-2 max|ref| + 1e-3."""
+import numpy as np
+import pytest
+
+import oracle
+from helpers import assert_close, dev16, np16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    from throughput_oriented_offloaded_amd import _lib
+    return _lib
+
+
+def _setup(L, fmt, bls, nh, hd, P, lmax, seed):
+    """Fill positions 0..P-1 of a device cache and of an oracle cache from the
+    same seeded fp16 rows; return both and a fresh (q | k_new | v_new) block."""
+    import torch
+    from throughput_oriented_offloaded_amd.model import DeviceKV
+    rng = np.random.default_rng(seed)
+    h1 = nh * hd
+    d = L.dims(h1, 4 * h1, nh, hd)
+    fmt_id = L.FG_FMT_Q4G64 if fmt == "q4" else L.FG_FMT_F16
+    kv = DeviceKV(fmt_id, bls, nh, hd, lmax, "cuda")
+    kx = (rng.standard_normal((bls, P, h1)) * 2).astype(np.float16)
+    vx = (rng.standard_normal((bls, P, h1)) * 2).astype(np.float16)
+    append = L.fg_kv_append_q4 if fmt == "q4" else L.fg_kv_append_f16
+    kd, vd = dev16(kx), dev16(vx)
+    for p in range(P):
+        append(kd[:, p].contiguous(), vd[:, p].contiguous(), h1, kv.struct, bls, d, p)
+    oc = oracle.KVCache(fmt, bls, nh, hd, lmax)
+    if P:
+        oc.store(kx, vx, 0)
+    qkv = (rng.standard_normal((bls, 3 * h1)) * 2).astype(np.float16)
+    return d, kv, oc, qkv
+
+
+def _cache_equal(kv, oc, upto):
+    assert np.array_equal(kv.k.cpu().numpy().view(oc.k.dtype)[:, :, :upto], oc.k[:, :, :upto])
+    assert np.array_equal(kv.v.cpu().numpy().view(oc.v.dtype)[:, :, :upto], oc.v[:, :, :upto])
+    if oc.km is not None:
+        assert np.array_equal(np16(kv.km)[:, :, :upto], oc.km[:, :, :upto])
+        assert np.array_equal(np16(kv.vm)[:, :, :upto], oc.vm[:, :, :upto])
+
+
+CASES = [  # fmt, bls, nh, hd, pos
+    ("q4", 1, 1, 128, 0), ("q4", 3, 5, 128, 1), ("q4", 2, 3, 128, 15), ("q4", 2, 2, 128, 16),
+    ("q4", 2, 2, 128, 17), ("q4", 1, 3, 128, 64), ("q4", 2, 2, 128, 65), ("q4", 1, 2, 128, 200),
+    ("q4", 2, 1, 128, 527), ("q4", 3, 5, 64, 33), ("q4", 2, 12, 64, 39), ("q4", 1, 1, 64, 0),
+    ("f16", 2, 3, 128, 0), ("f16", 3, 5, 128, 40), ("f16", 2, 2, 64, 77), ("f16", 1, 32, 64, 130),
+]
+
+
+@pytest.mark.parametrize("fmt,bls,nh,hd,pos", CASES)
+def test_decode_attention_and_append(L, fmt, bls, nh, hd, pos):
+    import torch
+    lmax = pos + 3
+    d, kv, oc, qkv = _setup(L, fmt, bls, nh, hd, pos, lmax, seed=pos * 31 + nh)
+    _cache_equal(kv, oc, pos)
+    h1 = nh * hd
+    buf = dev16(qkv)
+    out = torch.empty((bls, h1), dtype=torch.float16, device="cuda")
+    fn = L.fg_attn_decode_q4 if fmt == "q4" else L.fg_attn_decode_f16
+    fn(buf, buf[:, h1:], buf[:, 2 * h1:], 3 * h1, kv.struct, bls, d, pos, 1, out)
+    torch.cuda.synchronize()
+    kh, vh = oc.history()
+    ref = oracle.attn_decode(qkv, bls, nh, hd, kh, vh, lmax, pos)
+    assert_close(np16(out), ref, f"{fmt} attention pos {pos}")
+    # the fused append wrote position pos exactly as the codec would
+    q3 = qkv.reshape(bls, 1, 3, h1)
+    oc.store(q3[:, :, 1], q3[:, :, 2], pos)
+    _cache_equal(kv, oc, pos + 1)
+    # unfused launch: identical output, cache row pos + 1 left untouched
+    out2 = torch.empty_like(out)
+    if pos + 1 < lmax:
+        before = kv.k[:, :, pos + 1].clone()
+        fn(buf, buf[:, h1:], buf[:, 2 * h1:], 3 * h1, kv.struct, bls, d, pos + 1, 0, out2)
+        torch.cuda.synchronize()
+        assert torch.equal(before, kv.k[:, :, pos + 1])
+        kh, vh = oc.history()
+        ref2 = oracle.attn_decode(qkv, bls, nh, hd, kh, vh, lmax, pos + 1)
+        assert_close(np16(out2), ref2, f"{fmt} attention pos {pos + 1} (unfused)")
+
+
+def test_decode_attention_full_shape_sampled(L):
+    """OPT-175B shape (96 heads x 128) at bls = 144, context 528 (s + n/2): the
+    launch the benchmark times; sampled (sequence, head) pairs against the oracle."""
+    import torch
+    from throughput_oriented_offloaded_amd.model import DeviceKV
+    import synth
+    bls, nh, hd, pos, lmax = 144, 96, 128, 528, 544
+    h1 = nh * hd
+    d = L.dims(h1, 4 * h1, nh, hd)
+    kv = DeviceKV(L.FG_FMT_Q4G64, bls, nh, hd, lmax, "cuda")
+    kh, vh = synth.kv_history(bls, nh, pos, hd, seed=5, device="cuda")
+    for p in range(pos):   # append every history position (one launch each)
+        L.fg_kv_append_q4(kh[:, p].contiguous(), vh[:, p].contiguous(), h1, kv.struct, bls, d, p)
+    qkv = synth.activations(bls, 3 * h1, seed=6, device="cuda", std=2.0)
+    out = torch.empty((bls, h1), dtype=torch.float16, device="cuda")
+    L.fg_attn_decode_q4(qkv, qkv[:, h1:], qkv[:, 2 * h1:], 3 * h1, kv.struct, bls, d, pos, 1, out)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    seqs = sorted(set([0, bls - 1] + list(rng.integers(0, bls, 3))))
+    for b in seqs:
+        heads = sorted(set([0, nh - 1] + list(rng.integers(0, nh, 3))))
+        khb = np16(kh[b]).reshape(pos, nh, hd)[:, heads]          # [pos, H, hd]
+        vhb = np16(vh[b]).reshape(pos, nh, hd)[:, heads]
+        oc = oracle.KVCache("q4", 1, len(heads), hd, lmax)
+        oc.store(khb.reshape(1, pos, -1), vhb.reshape(1, pos, -1), 0)
+        # device cache rows of these heads equal the oracle's codes
+        assert np.array_equal(kv.k[b, heads, :pos].cpu().numpy(), oc.k[0, :, :pos])
+        assert np.array_equal(np16(kv.vm[b, heads, :pos]), oc.vm[0, :, :pos])
+        q3 = np16(qkv[b]).reshape(3, nh, hd)[:, heads].reshape(1, -1)
+        hist = oc.history()
+        ref = oracle.attn_decode(q3, 1, len(heads), hd, hist[0], hist[1], lmax, pos)
+        got = np16(out[b]).reshape(nh, hd)[heads].reshape(1, -1)
+        assert_close(got, ref, f"seq {b} heads {heads}")
+
+
+@pytest.mark.parametrize("b,s,nh,hd", [(1, 1, 1, 128), (2, 5, 3, 128), (1, 64, 2, 128),
+                                       (2, 65, 2, 128), (1, 130, 1, 64), (3, 32, 12, 64),
+                                       (1, 300, 2, 128)])
+def test_prefill_attention(L, b, s, nh, hd):
+    import torch
+    rng = np.random.default_rng(b * 100 + s)
+    h1 = nh * hd
+    qkv = (rng.standard_normal((b * s, 3 * h1)) * 2).astype(np.float16)
+    out = torch.empty((b * s, h1), dtype=torch.float16, device="cuda")
+    L.fg_attn_prefill(dev16(qkv), b, s, L.dims(h1, 4 * h1, nh, hd), out)
+    torch.cuda.synchronize()
+    assert_close(np16(out), oracle.attn_prefill(qkv, b, s, nh, hd), f"prefill b{b} s{s}")

@@ -1,0 +1,101 @@
+"""GPU parity of fg_linear (fp16 and dequant-fused 4-bit MFMA GEMM) against the
+oracle's fp64 linear on the oracle's own dequantized weights."""
+import numpy as np
+import pytest
+
+import oracle
+from helpers import assert_close, dev16, np16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    from throughput_oriented_offloaded_amd import _lib
+    return _lib
+
+
+def _run(L, fmt, M, N, K, bias=True, act=0, residual=False, inplace=False, seed=0):
+    import torch
+    rng = np.random.default_rng(seed + M * 7 + N * 3 + K)
+    x = (rng.standard_normal((M, K))).astype(np.float16)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    b = (rng.standard_normal(N) * 0.02).astype(np.float16) if bias else None
+    r = (rng.standard_normal((M, N))).astype(np.float16) if residual else None
+    xd, wd = dev16(x), dev16(w)
+    if fmt == "q4":
+        codes = torch.empty((N // 2, K), dtype=torch.uint8, device="cuda")
+        meta = torch.empty((N // 64, 2, K), dtype=torch.float16, device="cuda")
+        L.fg_quant_group4(wd, 1, N, K, codes, meta)
+        wc, wm, f = codes, meta, L.FG_FMT_Q4G64
+        rc, rm = oracle.quant_weight(w)
+        torch.cuda.synchronize()
+        assert np.array_equal(codes.cpu().numpy(), rc) and np.array_equal(np16(meta), rm)
+        w_ref = oracle.dequant_weight(rc, rm, N, K)
+    else:
+        wc, wm, f = wd, None, L.FG_FMT_F16
+        w_ref = w
+    bd = dev16(b) if bias else None
+    rd = dev16(r) if residual else None
+    y = rd if inplace else torch.empty((M, N), dtype=torch.float16, device="cuda")
+    wsb = L.fg_linear_workspace_bytes(M, N, K)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    L.fg_linear(xd, M, K, f, wc, wm, N, bd, act, rd, y, ws, wsb)
+    torch.cuda.synchronize()
+    ref = oracle.linear(x, w_ref, b, relu=bool(act), residual=r)
+    return np16(y), ref
+
+
+SHAPES = [  # M, N, K
+    (1, 64, 64), (4, 2304, 768), (4, 768, 3072), (16, 256, 128), (17, 320, 192),
+    (100, 192, 256), (128, 512, 256), (144, 768, 768), (144, 3072, 768), (144, 768, 3072),
+    (145, 256, 128), (300, 512, 192), (700, 384, 128), (1000, 128, 64), (2048, 256, 256),
+]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_linear_q4(L, M, N, K):
+    got, ref = _run(L, "q4", M, N, K)
+    assert_close(got, ref, f"q4 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES + [(5, 200, 64), (144, 1000, 128), (3, 50272, 64)])
+def test_linear_f16(L, M, N, K):
+    got, ref = _run(L, "f16", M, N, K)
+    assert_close(got, ref, f"f16 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("fmt", ["q4", "f16"])
+def test_linear_epilogues(L, fmt):
+    got, ref = _run(L, fmt, 144, 512, 1024, act=1)
+    assert_close(got, ref, "relu")
+    assert np.all(got.view(np.float16) >= 0)
+    got, ref = _run(L, fmt, 144, 512, 2048, residual=True)
+    assert_close(got, ref, "residual")
+    got, ref = _run(L, fmt, 144, 512, 2048, residual=True, inplace=True)
+    assert_close(got, ref, "residual in place")
+    got, ref = _run(L, fmt, 37, 256, 192, bias=False)
+    assert_close(got, ref, "no bias")
+
+
+def test_linear_rows_independent_of_batch_split(L):
+    """Same M, any split of the rows into GPU batches: a row's result depends
+    only on that row (bitwise), which is what lets the block be one GEMM."""
+    import torch
+    rng = np.random.default_rng(9)
+    M, N, K = 144, 512, 1024
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    wd = dev16(w)
+    codes = torch.empty((N // 2, K), dtype=torch.uint8, device="cuda")
+    meta = torch.empty((N // 64, 2, K), dtype=torch.float16, device="cuda")
+    L.fg_quant_group4(wd, 1, N, K, codes, meta)
+    wsb = L.fg_linear_workspace_bytes(M, N, K)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    y1 = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    L.fg_linear(dev16(x), M, K, L.FG_FMT_Q4G64, codes, meta, N, None, 0, None, y1, ws, wsb)
+    perm = rng.permutation(M)
+    y2 = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    L.fg_linear(dev16(x[perm]), M, K, L.FG_FMT_Q4G64, codes, meta, N, None, 0, None, y2, ws, wsb)
+    torch.cuda.synchronize()
+    assert torch.equal(y1[torch.from_numpy(perm).cuda()], y2)

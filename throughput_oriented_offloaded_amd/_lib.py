@@ -1,0 +1,216 @@
+"""ctypes binding of libfg.so (include/fg.h).  Argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU (or plain
+ints for sizes), passes their data pointers and the current HIP stream to the
+C ABI, and raises FgError on a non-zero status.  Nothing here computes: when
+the library is missing, importing this module raises, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfg.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "fg.h")
+
+FG_OK, FG_ERR_INVALID, FG_ERR_UNSUPPORTED, FG_ERR_CAPACITY, FG_ERR_HIP = 0, -1, -2, -3, -4
+FG_FMT_F16, FG_FMT_Q4G64 = 0, 1
+
+
+class FgError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn}: {status_str(status)} ({status}): {detail}")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                      "(or python -m throughput_oriented_offloaded_amd._build)")
+_L = ctypes.CDLL(LIB_PATH)
+
+P = ctypes.c_void_p
+I32, I64, SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("h1", I32), ("h2", I32), ("n_heads", I32), ("head_dim", I32)]
+
+
+class LayerW(ctypes.Structure):
+    _fields_ = [("fmt", I32)] + [(n, P) for n in (
+        "w_qkv", "m_qkv", "b_qkv", "w_o", "m_o", "b_o", "w_1", "m_1", "b_1",
+        "w_2", "m_2", "b_2", "ln1_g", "ln1_b", "ln2_g", "ln2_b")]
+
+
+class KV(ctypes.Structure):
+    _fields_ = [("fmt", I32), ("k", P), ("k_meta", P), ("v", P), ("v_meta", P),
+                ("max_len", I32), ("n_seq", I32)]
+
+
+_PROTOS = {
+    "fg_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "fg_last_error": (ctypes.c_char_p, []),
+    "fg_abi_version": (ctypes.c_int, []),
+    "fg_quant_group4": (ctypes.c_int, [P, I64, I64, I64, I32, P, P, P]),
+    "fg_dequant_group4": (ctypes.c_int, [P, P, I64, I64, I64, I32, P, P]),
+    "fg_kv_append_q4": (ctypes.c_int, [P, P, I64, ctypes.POINTER(KV), I32, ctypes.POINTER(Dims), I32, P]),
+    "fg_kv_append_f16": (ctypes.c_int, [P, P, I64, ctypes.POINTER(KV), I32, ctypes.POINTER(Dims), I32, P]),
+    "fg_attn_decode_q4": (ctypes.c_int, [P, P, P, I64, ctypes.POINTER(KV), I32, ctypes.POINTER(Dims),
+                                         I32, I32, P, P]),
+    "fg_attn_decode_f16": (ctypes.c_int, [P, P, P, I64, ctypes.POINTER(KV), I32, ctypes.POINTER(Dims),
+                                          I32, I32, P, P]),
+    "fg_attn_prefill": (ctypes.c_int, [P, I32, I32, ctypes.POINTER(Dims), P, P]),
+    "fg_linear": (ctypes.c_int, [P, I64, I64, I32, P, P, I64, P, I32, P, P, P, SZ, P]),
+    "fg_linear_workspace_bytes": (SZ, [I64, I64, I64]),
+    "fg_layernorm": (ctypes.c_int, [P, I64, I64, P, P, P, P]),
+    "fg_embed": (ctypes.c_int, [P, P, I64, P, I64, P, I64, I64, P, P]),
+    "fg_argmax": (ctypes.c_int, [P, I64, I64, P, P]),
+    "fg_layer_prefill": (ctypes.c_int, [ctypes.POINTER(Dims), ctypes.POINTER(LayerW), P, I32, I32, I32,
+                                        ctypes.POINTER(KV), P, SZ, P]),
+    "fg_layer_decode_block": (ctypes.c_int, [ctypes.POINTER(Dims), ctypes.POINTER(LayerW), P, I32, I32,
+                                             I32, ctypes.POINTER(KV), P, SZ, P]),
+    "fg_workspace_bytes": (SZ, [ctypes.POINTER(Dims), I64, I32]),
+    "fg_weight_bytes": (I64, [ctypes.POINTER(Dims), I32, I32]),
+    "fg_kv_bytes": (I64, [ctypes.POINTER(Dims), I32, I32, I32, I32, I32]),
+}
+for _name, (_res, _args) in _PROTOS.items():
+    _f = getattr(_L, _name)
+    _f.restype, _f.argtypes = _res, _args
+
+
+def header_symbols() -> list[str]:
+    """Names of the functions include/fg.h declares."""
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(fg_[a-z0-9_]+)\s*\(", txt)))
+
+
+def exported_symbols() -> list[str]:
+    return [n for n in header_symbols() if hasattr(_L, n)]
+
+
+def status_str(st: int) -> str:
+    return _L.fg_status_str(st).decode()
+
+
+def last_error() -> str:
+    return _L.fg_last_error().decode()
+
+
+def _check(fn: str, st: int):
+    if st != FG_OK:
+        raise FgError(fn, st, last_error())
+
+
+def ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def stream_ptr(stream=None) -> int | None:
+    if stream is None:
+        if not torch.cuda.is_available():
+            return None
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def dims(h1: int, h2: int, n_heads: int, head_dim: int) -> Dims:
+    return Dims(h1, h2, n_heads, head_dim)
+
+
+# --------------------------------------------------------------- entry points
+def fg_quant_group4(x, outer, axis, inner, codes, meta, group=64, stream=None):
+    _check("fg_quant_group4", _L.fg_quant_group4(ptr(x), outer, axis, inner, group, ptr(codes),
+                                                 ptr(meta), stream_ptr(stream)))
+
+
+def fg_dequant_group4(codes, meta, outer, axis, inner, y, group=64, stream=None):
+    _check("fg_dequant_group4", _L.fg_dequant_group4(ptr(codes), ptr(meta), outer, axis, inner,
+                                                     group, ptr(y), stream_ptr(stream)))
+
+
+def fg_kv_append_q4(k_new, v_new, ld, kv: KV, bls, d: Dims, pos, stream=None):
+    _check("fg_kv_append_q4", _L.fg_kv_append_q4(ptr(k_new), ptr(v_new), ld, ctypes.byref(kv), bls,
+                                                 ctypes.byref(d), pos, stream_ptr(stream)))
+
+
+def fg_kv_append_f16(k_new, v_new, ld, kv: KV, bls, d: Dims, pos, stream=None):
+    _check("fg_kv_append_f16", _L.fg_kv_append_f16(ptr(k_new), ptr(v_new), ld, ctypes.byref(kv), bls,
+                                                   ctypes.byref(d), pos, stream_ptr(stream)))
+
+
+def fg_attn_decode_q4(q, k_new, v_new, ld, kv: KV, bls, d: Dims, pos, fuse_append, out, stream=None):
+    _check("fg_attn_decode_q4", _L.fg_attn_decode_q4(ptr(q), ptr(k_new), ptr(v_new), ld, ctypes.byref(kv),
+                                                     bls, ctypes.byref(d), pos, int(fuse_append),
+                                                     ptr(out), stream_ptr(stream)))
+
+
+def fg_attn_decode_f16(q, k_new, v_new, ld, kv: KV, bls, d: Dims, pos, fuse_append, out, stream=None):
+    _check("fg_attn_decode_f16", _L.fg_attn_decode_f16(ptr(q), ptr(k_new), ptr(v_new), ld,
+                                                       ctypes.byref(kv), bls, ctypes.byref(d), pos,
+                                                       int(fuse_append), ptr(out), stream_ptr(stream)))
+
+
+def fg_attn_prefill(qkv, b, s, d: Dims, out, stream=None):
+    _check("fg_attn_prefill", _L.fg_attn_prefill(ptr(qkv), b, s, ctypes.byref(d), ptr(out),
+                                                 stream_ptr(stream)))
+
+
+def fg_linear_workspace_bytes(M, N, K) -> int:
+    return _L.fg_linear_workspace_bytes(M, N, K)
+
+
+def fg_linear(x, M, K, fmt, w, m, N, bias, act, residual, y, ws=None, ws_bytes=0, stream=None):
+    _check("fg_linear", _L.fg_linear(ptr(x), M, K, fmt, ptr(w), ptr(m), N, ptr(bias), act,
+                                     ptr(residual), ptr(y), ptr(ws), ws_bytes, stream_ptr(stream)))
+
+
+def fg_layernorm(x, rows, h, gamma, beta, y, stream=None):
+    _check("fg_layernorm", _L.fg_layernorm(ptr(x), rows, h, ptr(gamma), ptr(beta), ptr(y),
+                                           stream_ptr(stream)))
+
+
+def fg_embed(tok, pos, rows, E, vocab, Pt, max_pos, h1, x, stream=None):
+    _check("fg_embed", _L.fg_embed(ptr(tok), ptr(pos), rows, ptr(E), vocab, ptr(Pt), max_pos, h1,
+                                   ptr(x), stream_ptr(stream)))
+
+
+def fg_argmax(logits, rows, n, out, stream=None):
+    _check("fg_argmax", _L.fg_argmax(ptr(logits), rows, n, ptr(out), stream_ptr(stream)))
+
+
+def fg_layer_prefill(d: Dims, w: LayerW, x, gbs, nb, s, kv: KV, ws, ws_bytes, stream=None):
+    _check("fg_layer_prefill", _L.fg_layer_prefill(ctypes.byref(d), ctypes.byref(w), ptr(x), gbs, nb, s,
+                                                   ctypes.byref(kv), ptr(ws), ws_bytes,
+                                                   stream_ptr(stream)))
+
+
+def fg_layer_decode_block(d: Dims, w: LayerW, x, gbs, nb, pos, kv: KV, ws, ws_bytes, stream=None):
+    _check("fg_layer_decode_block", _L.fg_layer_decode_block(ctypes.byref(d), ctypes.byref(w), ptr(x),
+                                                             gbs, nb, pos, ctypes.byref(kv), ptr(ws),
+                                                             ws_bytes, stream_ptr(stream)))
+
+
+def fg_workspace_bytes(d: Dims, rows, fmt_w) -> int:
+    return _L.fg_workspace_bytes(ctypes.byref(d), rows, fmt_w)
+
+
+def fg_weight_bytes(d: Dims, n_layers, fmt) -> int:
+    return _L.fg_weight_bytes(ctypes.byref(d), n_layers, fmt)
+
+
+def fg_kv_bytes(d: Dims, n_layers, bls, s, n, fmt) -> int:
+    return _L.fg_kv_bytes(ctypes.byref(d), n_layers, bls, s, n, fmt)
+
+
+def raw(name: str):
+    """The raw ctypes function (tests use it to pass deliberately bad arguments)."""
+    return getattr(_L, name)

@@ -1,0 +1,109 @@
+// Internal declarations shared by the translation units of libfg.so.
+// Not part of the C ABI (see include/fg.h for that).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <cstdarg>
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/fg.h"
+
+namespace fg {
+
+// ------------------------------------------------------------------ errors
+// Records a formatted detail for fg_last_error() and returns `status`.
+int set_error(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+#define FG_CHECK_ARG(cond, ...)                                      \
+    do {                                                             \
+        if (!(cond)) return ::fg::set_error(FG_ERR_INVALID, __VA_ARGS__); \
+    } while (0)
+
+#define FG_CHECK_SUP(cond, ...)                                          \
+    do {                                                                 \
+        if (!(cond)) return ::fg::set_error(FG_ERR_UNSUPPORTED, __VA_ARGS__); \
+    } while (0)
+
+#define FG_HIP(call)                                                              \
+    do {                                                                          \
+        hipError_t e_ = (call);                                                   \
+        if (e_ != hipSuccess)                                                     \
+            return ::fg::set_error(FG_ERR_HIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+    } while (0)
+
+// After a kernel launch: reports a launch failure as FG_ERR_HIP.
+#define FG_LAUNCHED(name)                                                         \
+    do {                                                                          \
+        hipError_t e_ = hipGetLastError();                                        \
+        if (e_ != hipSuccess)                                                     \
+            return ::fg::set_error(FG_ERR_HIP, "launch of %s failed: %s", name,   \
+                                   hipGetErrorString(e_));                        \
+    } while (0)
+
+#define FG_TRY(expr)                  \
+    do {                              \
+        int st_ = (expr);             \
+        if (st_ != FG_OK) return st_; \
+    } while (0)
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Compute units of the current device (cached per device).
+int num_cus();
+
+// Validates an fg_dims (h1 = heads * head_dim, multiples of 64, head_dim 64/128).
+int check_dims(const fg_dims* d);
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ------------------------------------------------------------ launch helpers
+// All take device pointers that the public entry points validated.
+
+// Codec over [outer, axis, inner], group 64.
+int launch_quant_g4(const __half* x, int64_t outer, int64_t axis, int64_t inner, uint8_t* codes,
+                    __half* meta, hipStream_t st);
+int launch_dequant_g4(const uint8_t* codes, const __half* meta, int64_t outer, int64_t axis,
+                      int64_t inner, __half* y, hipStream_t st);
+
+// GEMM y = act(x W^T + bias) + residual.  ldx / ldy are row strides (elements).
+struct LinearArgs {
+    const __half* x;
+    int64_t M, K, ldx;
+    int32_t fmt;
+    const void* w;       // fp16 [N, K] or q4 codes [N/2, K]
+    const __half* meta;  // q4 meta [N/64, 2, K]
+    int64_t N;
+    const __half* bias;
+    int32_t act;         // 0 none, 1 relu
+    const __half* residual;
+    __half* y;
+    int64_t ldy;
+    void* ws;
+    size_t ws_bytes;
+};
+int launch_linear(const LinearArgs& a, hipStream_t st);
+size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t fmt);
+
+int launch_layernorm(const __half* x, int64_t rows, int64_t h, const __half* g, const __half* b,
+                     __half* y, hipStream_t st);
+int launch_embed(const int32_t* tok, const int32_t* pos, int32_t pos_const, int64_t pos_period,
+                 int64_t rows, const __half* E, int64_t vocab, const __half* P, int64_t max_pos,
+                 int64_t h1, __half* x, hipStream_t st);
+int launch_argmax(const __half* logits, int64_t rows, int64_t n, int32_t* out, hipStream_t st);
+
+// KV cache: store nt consecutive positions t0.. of nseq sequences starting at
+// sequence seq0.  Row (b, t) of k/v is at k + ((b * nt) + t) * ld.
+int launch_kv_store(const __half* k, const __half* v, int64_t ld, const fg_kv* kv, int32_t seq0,
+                    int32_t nseq, int32_t t0, int32_t nt, const fg_dims* d, hipStream_t st);
+int launch_attn_decode(const __half* q, const __half* k_new, const __half* v_new, int64_t ld,
+                       const fg_kv* kv, int32_t bls, const fg_dims* d, int32_t pos, int fuse,
+                       __half* out, hipStream_t st);
+int launch_attn_prefill(const __half* qkv, int32_t b, int32_t s, const fg_dims* d, __half* out,
+                        hipStream_t st);
+
+}  // namespace fg

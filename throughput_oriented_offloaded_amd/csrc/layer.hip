@@ -1,0 +1,168 @@
+// One decoder layer, prefill and decode-block forms.
+//
+// Pre-LN OPT-style layer: x += Attn(LN1(x)) W_O^T + b_O; x += ReLU(LN2(x)
+// W_1^T + b_1) W_2^T + b_2, with K, V kept in the per-layer cache ("FlexGen
+// 完全拆解", section "从 Transformer 推理的数据流重新定义卸载").
+//
+// Block schedule (section "FlexGen 的核心:计算图分块与张量生命周期" and the
+// pipeline pseudocode of section "一个层级流水的伪代码"): while one layer's
+// weights are resident, every GPU batch of the block passes through it.  Here
+// the weights live in HBM; the decode block issues each projection once over
+// all bls = gbs * nb rows, so every weight byte is read once per layer per
+// step for the whole block.  The prefill walks the block's GPU batches one at
+// a time (workspace bounded by one GPU batch of gbs * s rows).
+#include "fg_internal.h"
+
+namespace fg {
+namespace {
+
+struct WsLayout {
+    size_t a, qkv, o, f, part, total;
+};
+
+size_t part_bytes(const fg_dims* d, int64_t rows, int32_t fmt) {
+    const int64_t h1 = d->h1, h2 = d->h2;
+    size_t m = 0;
+    m = std::max(m, linear_ws_bytes(rows, 3 * h1, h1, fmt));
+    m = std::max(m, linear_ws_bytes(rows, h1, h1, fmt));
+    m = std::max(m, linear_ws_bytes(rows, h2, h1, fmt));
+    m = std::max(m, linear_ws_bytes(rows, h1, h2, fmt));
+    return m;
+}
+
+WsLayout layout(const fg_dims* d, int64_t rows, int32_t fmt) {
+    WsLayout L{};
+    const size_t A = 256;
+    size_t off = 0;
+    L.a = off;   off = align_up(off + (size_t)rows * d->h1 * 2, A);
+    L.qkv = off; off = align_up(off + (size_t)rows * 3 * d->h1 * 2, A);
+    L.o = off;   off = align_up(off + (size_t)rows * d->h1 * 2, A);
+    L.f = off;   off = align_up(off + (size_t)rows * d->h2 * 2, A);
+    L.part = off;
+    off = align_up(off + part_bytes(d, rows, fmt), A);
+    L.total = off;
+    return L;
+}
+
+int check_layer(const fg_dims* d, const fg_layer_w* w, const void* x, const fg_kv* kv,
+                const void* ws) {
+    FG_TRY(check_dims(d));
+    FG_CHECK_ARG(w && x && kv && ws, "null pointer argument");
+    FG_CHECK_ARG(w->fmt == FG_FMT_F16 || w->fmt == FG_FMT_Q4G64, "unknown weight format %d",
+                 w->fmt);
+    FG_CHECK_ARG(w->w_qkv && w->b_qkv && w->w_o && w->b_o && w->w_1 && w->b_1 && w->w_2 &&
+                     w->b_2 && w->ln1_g && w->ln1_b && w->ln2_g && w->ln2_b,
+                 "null weight pointer");
+    FG_CHECK_ARG(w->fmt != FG_FMT_Q4G64 || (w->m_qkv && w->m_o && w->m_1 && w->m_2),
+                 "null 4-bit weight metadata");
+    FG_CHECK_ARG(kv->fmt == FG_FMT_F16 || kv->fmt == FG_FMT_Q4G64, "unknown cache format %d",
+                 kv->fmt);
+    FG_CHECK_ARG(kv->k && kv->v && (kv->fmt != FG_FMT_Q4G64 || (kv->k_meta && kv->v_meta)),
+                 "null cache tensors");
+    const uintptr_t al = (uintptr_t)x | (uintptr_t)ws | (uintptr_t)w->w_qkv | (uintptr_t)w->w_o |
+                         (uintptr_t)w->w_1 | (uintptr_t)w->w_2 | (uintptr_t)w->ln1_g |
+                         (uintptr_t)w->ln1_b | (uintptr_t)w->ln2_g | (uintptr_t)w->ln2_b |
+                         (uintptr_t)kv->k | (uintptr_t)kv->v | (uintptr_t)w->m_qkv |
+                         (uintptr_t)w->m_o | (uintptr_t)w->m_1 | (uintptr_t)w->m_2;
+    FG_CHECK_ARG(al % 16 == 0, "tensors must be 16-byte aligned");
+    FG_CHECK_ARG(((uintptr_t)w->b_qkv | (uintptr_t)w->b_o | (uintptr_t)w->b_1 |
+                  (uintptr_t)w->b_2) % 8 == 0, "biases must be 8-byte aligned");
+    FG_CHECK_ARG(((uintptr_t)kv->k_meta | (uintptr_t)kv->v_meta) % 4 == 0,
+                 "cache metadata must be 4-byte aligned");
+    return FG_OK;
+}
+
+int lin(const fg_layer_w* w, int which, const __half* x, int64_t M, int64_t K, int64_t N,
+        int32_t act, const __half* res, __half* y, void* part, size_t part_bytes, hipStream_t st) {
+    LinearArgs a{};
+    a.x = x; a.M = M; a.K = K; a.ldx = K; a.fmt = w->fmt; a.N = N; a.act = act;
+    a.residual = res; a.y = y; a.ldy = N; a.ws = part; a.ws_bytes = part_bytes;
+    switch (which) {
+        case 0: a.w = w->w_qkv; a.meta = (const __half*)w->m_qkv; a.bias = (const __half*)w->b_qkv; break;
+        case 1: a.w = w->w_o; a.meta = (const __half*)w->m_o; a.bias = (const __half*)w->b_o; break;
+        case 2: a.w = w->w_1; a.meta = (const __half*)w->m_1; a.bias = (const __half*)w->b_1; break;
+        default: a.w = w->w_2; a.meta = (const __half*)w->m_2; a.bias = (const __half*)w->b_2; break;
+    }
+    return launch_linear(a, st);
+}
+
+}  // namespace
+}  // namespace fg
+
+extern "C" size_t fg_workspace_bytes(const fg_dims* d, int64_t rows, int32_t fmt_w) {
+    if (!d || rows < 0 || d->h1 <= 0 || d->h2 <= 0) return 0;
+    return fg::layout(d, rows, fmt_w).total;
+}
+
+extern "C" int fg_layer_decode_block(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs,
+                                     int32_t nb, int32_t pos, const fg_kv* kv, void* ws,
+                                     size_t ws_bytes, void* stream) {
+    using namespace fg;
+    clear_error();
+    FG_TRY(check_layer(d, w, x, kv, ws));
+    FG_CHECK_ARG(gbs >= 1 && nb >= 1 && (int64_t)gbs * nb <= kv->n_seq,
+                 "block %d x %d exceeds the cache's %d sequences", gbs, nb, kv->n_seq);
+    FG_CHECK_ARG(pos >= 0 && pos < kv->max_len, "pos %d outside [0, max_len %d)", pos,
+                 kv->max_len);
+    const int64_t bls = (int64_t)gbs * nb;
+    const WsLayout L = layout(d, bls, w->fmt);
+    if (ws_bytes < L.total)
+        return set_error(FG_ERR_CAPACITY, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+    hipStream_t st = as_stream(stream);
+    unsigned char* base = static_cast<unsigned char*>(ws);
+    __half* a = (__half*)(base + L.a);
+    __half* qkv = (__half*)(base + L.qkv);
+    __half* o = (__half*)(base + L.o);
+    __half* f = (__half*)(base + L.f);
+    void* part = base + L.part;
+    const size_t pb = L.total - L.part;
+    __half* xh = (__half*)x;
+    const int64_t h1 = d->h1, h2 = d->h2;
+
+    FG_TRY(launch_layernorm(xh, bls, h1, (const __half*)w->ln1_g, (const __half*)w->ln1_b, a, st));
+    FG_TRY(lin(w, 0, a, bls, h1, 3 * h1, 0, nullptr, qkv, part, pb, st));
+    FG_TRY(launch_attn_decode(qkv, qkv + h1, qkv + 2 * h1, 3 * h1, kv, (int32_t)bls, d, pos, 1, o, st));
+    FG_TRY(lin(w, 1, o, bls, h1, h1, 0, xh, xh, part, pb, st));
+    FG_TRY(launch_layernorm(xh, bls, h1, (const __half*)w->ln2_g, (const __half*)w->ln2_b, a, st));
+    FG_TRY(lin(w, 2, a, bls, h1, h2, 1, nullptr, f, part, pb, st));
+    FG_TRY(lin(w, 3, f, bls, h2, h1, 0, xh, xh, part, pb, st));
+    return FG_OK;
+}
+
+extern "C" int fg_layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs,
+                                int32_t nb, int32_t s, const fg_kv* kv, void* ws, size_t ws_bytes,
+                                void* stream) {
+    using namespace fg;
+    clear_error();
+    FG_TRY(check_layer(d, w, x, kv, ws));
+    FG_CHECK_ARG(gbs >= 1 && nb >= 1 && (int64_t)gbs * nb <= kv->n_seq,
+                 "block %d x %d exceeds the cache's %d sequences", gbs, nb, kv->n_seq);
+    FG_CHECK_ARG(s >= 1 && s <= kv->max_len, "prompt length %d outside [1, max_len %d]", s,
+                 kv->max_len);
+    const int64_t rows = (int64_t)gbs * s;
+    const WsLayout L = layout(d, rows, w->fmt);
+    if (ws_bytes < L.total)
+        return set_error(FG_ERR_CAPACITY, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+    hipStream_t st = as_stream(stream);
+    unsigned char* base = static_cast<unsigned char*>(ws);
+    __half* a = (__half*)(base + L.a);
+    __half* qkv = (__half*)(base + L.qkv);
+    __half* o = (__half*)(base + L.o);
+    __half* f = (__half*)(base + L.f);
+    void* part = base + L.part;
+    const size_t pb = L.total - L.part;
+    const int64_t h1 = d->h1, h2 = d->h2;
+
+    for (int32_t k = 0; k < nb; ++k) {     // GPU batches of the block, one layer resident
+        __half* xh = (__half*)x + (int64_t)k * rows * h1;
+        FG_TRY(launch_layernorm(xh, rows, h1, (const __half*)w->ln1_g, (const __half*)w->ln1_b, a, st));
+        FG_TRY(lin(w, 0, a, rows, h1, 3 * h1, 0, nullptr, qkv, part, pb, st));
+        FG_TRY(launch_attn_prefill(qkv, gbs, s, d, o, st));
+        FG_TRY(launch_kv_store(qkv + h1, qkv + 2 * h1, 3 * h1, kv, k * gbs, gbs, 0, s, d, st));
+        FG_TRY(lin(w, 1, o, rows, h1, h1, 0, xh, xh, part, pb, st));
+        FG_TRY(launch_layernorm(xh, rows, h1, (const __half*)w->ln2_g, (const __half*)w->ln2_b, a, st));
+        FG_TRY(lin(w, 2, a, rows, h1, h2, 1, nullptr, f, part, pb, st));
+        FG_TRY(lin(w, 3, f, rows, h2, h1, 0, xh, xh, part, pb, st));
+    }
+    return FG_OK;
+}

@@ -1,0 +1,187 @@
+"""OPT-style decoder driven through the C ABI: device-resident weights (fp16
+or group-wise 4-bit), per-layer KV caches, prefill and zig-zag block decode.
+
+Every step runs in libfg.so's kernels; this module owns the device buffers
+(allocated with torch) and issues the per-layer calls in the block order of
+"FlexGen 完全拆解" (pinghaoyang.com.cn), section "一个层级流水的伪代码": token
+step outermost, then layers, with the block's GPU batches innermost (inside
+fg_layer_decode_block / fg_layer_prefill).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib as L
+
+MATS = ("qkv", "o", "1", "2")
+
+
+@dataclass(frozen=True)
+class Shape:
+    n_layers: int
+    h1: int
+    h2: int
+    n_heads: int
+    head_dim: int
+    vocab: int = 50272
+
+    @property
+    def dims(self) -> L.Dims:
+        return L.dims(self.h1, self.h2, self.n_heads, self.head_dim)
+
+    def mat_shape(self, name):
+        return {"qkv": (3 * self.h1, self.h1), "o": (self.h1, self.h1),
+                "1": (self.h2, self.h1), "2": (self.h1, self.h2)}[name]
+
+
+def quantize_weight(w: torch.Tensor, stream=None):
+    """[N, K] fp16 -> (codes [N/2, K] uint8, meta [N/64, 2, K] fp16), groups along N."""
+    N, K = w.shape
+    codes = torch.empty((N // 2, K), dtype=torch.uint8, device=w.device)
+    meta = torch.empty((N // 64, 2, K), dtype=torch.float16, device=w.device)
+    L.fg_quant_group4(w, 1, N, K, codes, meta, stream=stream)
+    return codes, meta
+
+
+class DeviceLayer:
+    """One layer's weights on the device plus the fg_layer_w that points at them."""
+
+    def __init__(self, fmt: int, t: dict):
+        self.fmt, self.t = fmt, t
+        s = L.LayerW()
+        s.fmt = fmt
+        for name in MATS:
+            setattr(s, "w_" + name, L.ptr(t["w_" + name]))
+            setattr(s, "m_" + name, L.ptr(t.get("m_" + name)))
+            setattr(s, "b_" + name, L.ptr(t["b_" + name]))
+        for k in ("ln1_g", "ln1_b", "ln2_g", "ln2_b"):
+            setattr(s, k, L.ptr(t[k]))
+        self.struct = s
+
+    @classmethod
+    def from_fp16(cls, W: dict, fmt: int, stream=None) -> "DeviceLayer":
+        """W: fp16 device tensors (w_*, b_*, ln*).  For 4-bit, the matrices are
+        quantized on the device and the fp16 copies are not kept."""
+        t = {k: v for k, v in W.items() if not k.startswith("w_")}
+        for name in MATS:
+            w = W["w_" + name]
+            if fmt == L.FG_FMT_Q4G64:
+                t["w_" + name], t["m_" + name] = quantize_weight(w, stream)
+            else:
+                t["w_" + name] = w
+        return cls(fmt, t)
+
+
+class DeviceKV:
+    """One layer's cache: q4 codes [n_seq, nh, max_len, hd/2] + meta
+    [n_seq, nh, max_len, hd/64, 2], or fp16 [n_seq, nh, max_len, hd]."""
+
+    def __init__(self, fmt: int, n_seq: int, n_heads: int, head_dim: int, max_len: int, device):
+        self.fmt = fmt
+        shp = (n_seq, n_heads, max_len)
+        if fmt == L.FG_FMT_Q4G64:
+            self.k = torch.zeros(shp + (head_dim // 2,), dtype=torch.uint8, device=device)
+            self.v = torch.zeros_like(self.k)
+            self.km = torch.zeros(shp + (head_dim // 64, 2), dtype=torch.float16, device=device)
+            self.vm = torch.zeros_like(self.km)
+        else:
+            self.k = torch.zeros(shp + (head_dim,), dtype=torch.float16, device=device)
+            self.v = torch.zeros_like(self.k)
+            self.km = self.vm = None
+        s = L.KV()
+        s.fmt, s.k, s.v = fmt, L.ptr(self.k), L.ptr(self.v)
+        s.k_meta, s.v_meta = L.ptr(self.km), L.ptr(self.vm)
+        s.max_len, s.n_seq = max_len, n_seq
+        self.struct = s
+
+
+class Model:
+    """A decoder of `shape` on one GPU.  layers: list of DeviceLayer; emb: dict
+    with embed [vocab, h1], pos [max_pos, h1], lnf_g, lnf_b (fp16, device)."""
+
+    def __init__(self, shape: Shape, layers, emb: dict, kv_fmt: int, n_seq: int, max_len: int,
+                 device="cuda"):
+        self.shape, self.layers, self.emb = shape, layers, emb
+        self.d = shape.dims
+        self.n_seq, self.max_len = n_seq, max_len
+        self.kv = [DeviceKV(kv_fmt, n_seq, shape.n_heads, shape.head_dim, max_len, device)
+                   for _ in layers]
+        self.device = device
+        self._ws = None
+
+    def workspace(self, rows: int) -> torch.Tensor:
+        fmt = self.layers[0].fmt
+        need = max(L.fg_workspace_bytes(self.d, rows, fmt),
+                   L.fg_linear_workspace_bytes(self.n_seq, self.shape.vocab, self.shape.h1), 256)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def _head(self, x_last: torch.Tensor, stream=None):
+        """Final LayerNorm, tied LM head (fp16 GEMM on MFMA), greedy pick."""
+        sh = self.shape
+        rows = x_last.shape[0]
+        a = torch.empty_like(x_last)
+        L.fg_layernorm(x_last, rows, sh.h1, self.emb["lnf_g"], self.emb["lnf_b"], a, stream=stream)
+        logits = torch.empty((rows, sh.vocab), dtype=torch.float16, device=self.device)
+        ws = self.workspace(rows)
+        L.fg_linear(a, rows, sh.h1, L.FG_FMT_F16, self.emb["embed"], None, sh.vocab, None, 0, None,
+                    logits, ws, ws.numel(), stream=stream)
+        tok = torch.empty(rows, dtype=torch.int32, device=self.device)
+        L.fg_argmax(logits, rows, sh.vocab, tok, stream=stream)
+        return logits, tok
+
+    def prefill(self, tokens: torch.Tensor, gbs: int, nb: int, stream=None):
+        """tokens int32 [bls, s] (device).  Returns (logits [bls, vocab], next token [bls])."""
+        sh = self.shape
+        bls, s = tokens.shape
+        assert bls == gbs * nb <= self.n_seq and s <= self.max_len
+        pos = torch.arange(s, dtype=torch.int32, device=self.device).repeat(bls)
+        x = torch.empty((bls * s, sh.h1), dtype=torch.float16, device=self.device)
+        L.fg_embed(tokens.reshape(-1), pos, bls * s, self.emb["embed"], sh.vocab, self.emb["pos"],
+                   self.emb["pos"].shape[0], sh.h1, x, stream=stream)
+        ws = self.workspace(gbs * s)
+        for lay, kv in zip(self.layers, self.kv):
+            L.fg_layer_prefill(self.d, lay.struct, x, gbs, nb, s, kv.struct, ws, ws.numel(),
+                               stream=stream)
+        last = x.view(bls, s, sh.h1)[:, s - 1, :].contiguous()
+        return self._head(last, stream)
+
+    def decode_step(self, tok: torch.Tensor, pos: int, gbs: int, nb: int, stream=None):
+        """One new token per sequence at position pos.  Returns (logits, next token)."""
+        sh = self.shape
+        bls = gbs * nb
+        x = self.embed_step(tok, pos, stream)
+        ws = self.workspace(bls)
+        for lay, kv in zip(self.layers, self.kv):
+            L.fg_layer_decode_block(self.d, lay.struct, x, gbs, nb, pos, kv.struct, ws, ws.numel(),
+                                    stream=stream)
+        return self._head(x, stream)
+
+    def embed_step(self, tok: torch.Tensor, pos: int, stream=None) -> torch.Tensor:
+        sh = self.shape
+        bls = tok.numel()
+        posv = torch.full((bls,), pos, dtype=torch.int32, device=self.device)
+        x = torch.empty((bls, sh.h1), dtype=torch.float16, device=self.device)
+        L.fg_embed(tok, posv, bls, self.emb["embed"], sh.vocab, self.emb["pos"],
+                   self.emb["pos"].shape[0], sh.h1, x, stream=stream)
+        return x
+
+    def generate(self, tokens: torch.Tensor, n: int, gbs: int, nb: int, stream=None,
+                 forced=None):
+        """Greedy generation of n tokens: one from the prefill, n-1 decode steps
+        ("FlexGen 完全拆解", section "从硬件画像得到每层时间": T = l T_pre +
+        l (n-1) T_gen).  forced: optional [bls, n] tokens fed instead of the
+        model's own picks (teacher forcing).  Returns (tokens [bls, n], logits list)."""
+        bls, s = tokens.shape
+        assert s + n - 1 <= self.max_len
+        logits, tok = self.prefill(tokens, gbs, nb, stream)
+        out, lg = [tok], [logits]
+        for t in range(1, n):
+            feed = forced[:, t - 1].contiguous() if forced is not None else out[-1]
+            logits, tok = self.decode_step(feed, s + t - 1, gbs, nb, stream)
+            out.append(tok)
+            lg.append(logits)
+        return torch.stack(out, 1), lg
