@@ -1,0 +1,227 @@
+"""Benchmark: zig-zag block decode of an OPT-shape decoder with 4-bit weights and
+4-bit KV cache on one MI355X.
+
+A step is one decode step of the whole model for the whole block: embed, every
+layer (LN1, QKV dequant-GEMM, decode attention over the 4-bit cache with the
+fused append, out-proj, LN2, FC1, FC2), final LN, LM head and greedy pick, for
+bls = gbs x nb sequences at once.  Before the timed region the prompt (s
+tokens per sequence) is prefilled and W warm-up steps run; the K timed steps
+then generate positions s .. s+K-1 again from the prefill's first token, so
+the timed steps are exactly the decode phase of an n = K+1 token generation.
+
+Printed: one JSON line (stdout) with decode tokens/s, the per-kernel roofline
+of the dominant kernel (measured live with HIP events on the launch stream
+during the timed region), the decode-attention roofline, the pages' generation
+throughput, and the CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps 31] [--warmup 2] [--config 5]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s (s=512,n=32) + attn HBM GB/s, dequant-GEMM MFMA % of peak"
+PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+CONFIGS = {
+    1: dict(workload="opt-125m-shape 4-bit block decode", l=2, h1=768, h2=3072, nh=12, hd=64,
+            w="q4", kv="q4", gbs=4, nb=1, s=32, n=8),
+    2: dict(workload="opt-1.3b-shape fp16 block decode", l=24, h1=2048, h2=8192, nh=32, hd=64,
+            w="f16", kv="f16", gbs=32, nb=4, s=512, n=32),
+    3: dict(workload="opt-30b-shape 4-bit block decode", l=48, h1=7168, h2=28672, nh=56, hd=128,
+            w="q4", kv="q4", gbs=48, nb=3, s=512, n=32),
+    5: dict(workload="opt-175b-shape 4-bit block decode", l=96, h1=12288, h2=49152, nh=96,
+            hd=128, w="q4", kv="q4", gbs=48, nb=3, s=512, n=32),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_model(cfg, keep_layer0_host: bool):
+    import torch
+    import synth
+    from throughput_oriented_offloaded_amd import _lib as L
+    from throughput_oriented_offloaded_amd.model import DeviceLayer, Model, Shape
+
+    fmt = lambda f: L.FG_FMT_Q4G64 if f == "q4" else L.FG_FMT_F16  # noqa: E731
+    sh = Shape(n_layers=cfg["l"], h1=cfg["h1"], h2=cfg["h2"], n_heads=cfg["nh"], head_dim=cfg["hd"])
+    bls = cfg["gbs"] * cfg["nb"]
+    layers, host0 = [], None
+    L.fg_trace_enable(True)            # time the weight quantizer (init, not in the step)
+    for j in range(sh.n_layers):
+        W = synth.layer_weights(sh.h1, sh.h2, j, seed=0, device="cuda")
+        if j == 0 and keep_layer0_host:
+            host0 = {k: v.cpu() for k, v in W.items()}
+        layers.append(DeviceLayer.from_fp16(W, fmt(cfg["w"])))
+        del W
+        if j % 16 == 0:
+            log(f"  layer {j}/{sh.n_layers} ready")
+    torch.cuda.synchronize()
+    quant = L.fg_trace_collect().get("quant_g4")
+    L.fg_trace_enable(False)
+    torch.cuda.empty_cache()
+    emb = synth.embeddings(sh.h1, cfg["s"] + cfg["n"], seed=0, device="cuda")
+    return sh, layers, emb, host0, quant, fmt
+
+
+def roofline(tr, kind, bound):
+    r = tr.get(kind)
+    if not r or r["ms"] <= 0:
+        return None
+    sec = r["ms"] / 1e3
+    if bound == "mfma":
+        ach = r["flops"] / sec / 1e12
+        peak, unit = PEAK_F16_TFLOPS, "TFLOP/s"
+    else:
+        ach = r["bytes"] / sec / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    return {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+            "frac": round(ach / peak, 4), "traffic": None, "kernel": kind,
+            "launches": r["count"], "avg_launch_us": round(r["ms"] * 1e3 / r["count"], 2),
+            "algorithmic_per_launch": (r["flops"] if bound == "mfma" else r["bytes"]) / r["count"]}
+
+
+def cpu_baseline(cfg, host0, emb, budget_s: float = 20.0):
+    """The oracle (as it is) on the host cores: one decoder layer's decode step
+    for a sample of sequences at context s + n/2, plus the LM head for them;
+    decode tokens/s = rows / (l * t_layer + t_head)."""
+    import numpy as np
+    import oracle
+    import synth
+    d = oracle.Dims(cfg["h1"], cfg["h2"], cfg["nh"], cfg["hd"])
+    rows, pos = 2, cfg["s"] + cfg["n"] // 2
+    Wn = {k: v.numpy().view(np.uint16) for k, v in host0.items()}
+    if cfg["w"] == "q4":
+        Wn = oracle.dequant_layer(d, oracle.quant_layer(d, Wn))
+    kh, vh = synth.kv_history(rows, cfg["nh"], pos, cfg["hd"], seed=7)
+    x = synth.activations(rows, cfg["h1"], seed=8).numpy().view(np.uint16)
+    E = emb["embed"].cpu().numpy().view(np.uint16)
+    g, b = emb["lnf_g"].cpu().numpy().view(np.uint16), emb["lnf_b"].cpu().numpy().view(np.uint16)
+    t_layer, reps, t0 = 0.0, 0, time.time()
+    while reps == 0 or (time.time() - t0 < budget_s and reps < 8):
+        cache = oracle.KVCache(cfg["kv"], rows, cfg["nh"], cfg["hd"], pos + 1)
+        cache.store(kh.numpy().view(np.uint16), vh.numpy().view(np.uint16), 0)
+        t = time.perf_counter()
+        oracle.layer_decode(d, Wn, x, pos, cache)
+        t_layer += time.perf_counter() - t
+        reps += 1
+    t_layer /= reps
+    t = time.perf_counter()
+    oracle.lm_head(x, g, b, E)
+    t_head = time.perf_counter() - t
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    tps = rows / (cfg["l"] * t_layer + t_head)
+    return {"value": round(tps, 5), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} sequences x 1 decode layer at context {pos} ({reps} reps, "
+                      f"{t_layer:.2f} s/layer) + LM head ({t_head:.2f} s); scaled to "
+                      f"{cfg['l']} layers"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=31)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=5, choices=sorted(CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-trace", action="store_true", help="time without per-kernel events")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the block decode is measured on a single "
+              "MI355X (sharding across GPUs is not part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from throughput_oriented_offloaded_amd import _lib as L
+    from throughput_oriented_offloaded_amd.model import Model
+    import synth
+
+    cfg = CONFIGS[args.config]
+    K, Wm = args.steps, args.warmup
+    bls, s, n = cfg["gbs"] * cfg["nb"], cfg["s"], cfg["n"]
+    torch.cuda.set_device(0)
+    want_cpu = not args.no_cpu_baseline
+    t_build = time.time()
+    log(f"building {cfg['workload']} ({cfg['l']} layers, bls {bls})")
+    sh, layers, emb, host0, quant, fmt = build_model(cfg, want_cpu)
+    max_len = s + max(n, K + 1, Wm + 1)
+    model = Model(sh, layers, emb, fmt(cfg["kv"]), bls, max_len)
+    tokens = synth.tokens(bls, s, seed=0, device="cuda")
+    torch.cuda.synchronize()
+    log(f"built in {time.time() - t_build:.1f} s; prefill s={s} ...")
+
+    t = time.perf_counter()
+    _, tok1 = model.prefill(tokens, cfg["gbs"], cfg["nb"])
+    torch.cuda.synchronize()
+    t_prefill = time.perf_counter() - t
+    log(f"prefill {t_prefill:.2f} s; warmup {Wm} steps")
+
+    tok = tok1
+    for i in range(Wm):
+        _, tok = model.decode_step(tok, s + i, cfg["gbs"], cfg["nb"])
+    torch.cuda.synchronize()
+
+    L.fg_trace_enable(not args.no_trace)
+    tok = tok1
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        _, tok = model.decode_step(tok, s + i, cfg["gbs"], cfg["nb"])
+    torch.cuda.synchronize()
+    t_dec = time.perf_counter() - t0
+    tr = L.fg_trace_collect() if not args.no_trace else {}
+    L.fg_trace_enable(False)
+    ok = bool(((tok >= 0) & (tok < sh.vocab)).all().item())
+    log(f"decode {K} steps in {t_dec:.3f} s ({t_dec / K * 1e3:.2f} ms/step); tokens valid: {ok}")
+
+    value = bls * K / t_dec
+    t_gen = t_prefill + t_dec / K * (n - 1)
+    gemm_kind = "gemm_q4" if cfg["w"] == "q4" else "gemm_f16"
+    attn_kind = "attn_decode_q4" if cfg["kv"] == "q4" else "attn_decode_f16"
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": Wm, "ms_per_step": round(t_dec / K * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": cfg["workload"], "layers": cfg["l"], "h1": cfg["h1"],
+                   "h2": cfg["h2"], "heads": cfg["nh"], "head_dim": cfg["hd"], "bls": bls,
+                   "gbs": cfg["gbs"], "num_gpu_batches": cfg["nb"], "s": s, "n": n,
+                   "weights": "q4g64" if cfg["w"] == "q4" else "f16",
+                   "kv_cache": "q4g64" if cfg["kv"] == "q4" else "f16",
+                   "parallelism": "single GPU"},
+        "roofline": roofline(tr, gemm_kind, "mfma"),
+        "roofline_attn": roofline(tr, attn_kind, "hbm"),
+        "generation_throughput": {"value": round(bls * n / t_gen, 2), "unit": "tokens/s",
+                                  "prefill_s": round(t_prefill, 3),
+                                  "definition": "bls*n/(t_prefill + (n-1) decode steps)"},
+        "kernels": {k: {"launches": v["count"], "ms_per_step": round(v["ms"] / K, 3),
+                        "avg_us": round(v["ms"] * 1e3 / v["count"], 2),
+                        "TFLOP/s": round(v["flops"] / (v["ms"] / 1e3) / 1e12, 2) if v["flops"] else None,
+                        "GB/s": round(v["bytes"] / (v["ms"] / 1e3) / 1e9, 1)}
+                    for k, v in tr.items()},
+        "tokens_valid": ok,
+    }
+    if quant:
+        out["weight_quant"] = {"GB/s": round(quant["bytes"] / (quant["ms"] / 1e3) / 1e9, 1),
+                               "frac": round(quant["bytes"] / (quant["ms"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                               "launches": quant["count"]}
+    if want_cpu:
+        del model, layers
+        torch.cuda.empty_cache()
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(cfg, host0, emb)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

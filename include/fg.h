@@ -230,6 +230,23 @@ int64_t fg_weight_bytes(const fg_dims* d, int32_t n_layers, int32_t fmt);
 int64_t fg_kv_bytes(const fg_dims* d, int32_t n_layers, int32_t bls, int32_t s, int32_t n,
                     int32_t fmt);
 
+/* --------------------------------------------------------------- tracing */
+/*
+ * Per-kernel timing for roofline reports.  While enabled, each kernel launch
+ * of this library is bracketed by two HIP events recorded on its own launch
+ * stream and tagged with its kind and algorithmic work (flops; HBM bytes:
+ * weights once, activations in and out, KV history at 9/16 byte per element
+ * for 4-bit caches).  fg_trace_enable(on) discards earlier records and starts
+ * (on != 0) or stops recording.  fg_trace_collect waits for the recorded
+ * events and fills, per kind k < n_kinds, the launch count, summed duration
+ * (ms), summed flops and summed bytes; it returns the number of kinds (or a
+ * negative status).  fg_trace_kind_name names a kind.  Recording adds two
+ * event records per launch; it is off by default.
+ */
+int fg_trace_enable(int on);
+int fg_trace_collect(int32_t n_kinds, int64_t* count, double* ms, double* flops, double* bytes);
+const char* fg_trace_kind_name(int kind);
+
 #ifdef __cplusplus
 }
 #endif

@@ -76,6 +76,11 @@ _PROTOS = {
     "fg_workspace_bytes": (SZ, [ctypes.POINTER(Dims), I64, I32]),
     "fg_weight_bytes": (I64, [ctypes.POINTER(Dims), I32, I32]),
     "fg_kv_bytes": (I64, [ctypes.POINTER(Dims), I32, I32, I32, I32, I32]),
+    "fg_trace_enable": (ctypes.c_int, [ctypes.c_int]),
+    "fg_trace_collect": (ctypes.c_int, [I32, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_double)]),
+    "fg_trace_kind_name": (ctypes.c_char_p, [ctypes.c_int]),
 }
 for _name, (_res, _args) in _PROTOS.items():
     _f = getattr(_L, _name)
@@ -209,6 +214,25 @@ def fg_weight_bytes(d: Dims, n_layers, fmt) -> int:
 
 def fg_kv_bytes(d: Dims, n_layers, bls, s, n, fmt) -> int:
     return _L.fg_kv_bytes(ctypes.byref(d), n_layers, bls, s, n, fmt)
+
+
+def fg_trace_enable(on: bool):
+    _check("fg_trace_enable", _L.fg_trace_enable(int(on)))
+
+
+def fg_trace_collect(n_kinds: int = 32) -> dict:
+    """{kind name: {"count", "ms", "flops", "bytes"}} for kinds with launches."""
+    cnt = (I64 * n_kinds)()
+    ms, fl, by = ((ctypes.c_double * n_kinds)() for _ in range(3))
+    n = _L.fg_trace_collect(n_kinds, cnt, ms, fl, by)
+    if n < 0:
+        _check("fg_trace_collect", n)
+    out = {}
+    for k in range(n):
+        if cnt[k]:
+            out[_L.fg_trace_kind_name(k).decode()] = {"count": cnt[k], "ms": ms[k],
+                                                      "flops": fl[k], "bytes": by[k]}
+    return out
 
 
 def raw(name: str):

@@ -27,6 +27,7 @@
 // accumulated the same way: acc_d += (w sc) c_d, plus one scalar w mn per lane.
 #include "codec_dev.h"
 #include "fg_internal.h"
+#include "fg_trace.h"
 
 namespace fg {
 namespace {
@@ -381,6 +382,8 @@ int launch_kv_store(const __half* k, const __half* v, int64_t ld, const fg_kv* k
     const int64_t units = (int64_t)nseq * d->n_heads;
     const unsigned grid = (unsigned)cdiv(units, 4);
     const bool q4 = kv->fmt == FG_FMT_Q4G64;
+    const double ne = (double)nseq * nt * d->h1 * 2;       // K and V elements
+    TraceScope ts(TK_KV_STORE, st, 0.0, ne * 2 + (q4 ? ne / 2 + ne / 64 * 4 : ne * 2));
 #define FG_KV_STORE(HD_, Q_)                                                                 \
     kv_store_kernel<HD_, Q_><<<grid, 256, 0, st>>>(k, v, ld, kv->k, (__half*)kv->k_meta, kv->v, \
                                                    (__half*)kv->v_meta, kv->max_len, d->n_heads, \
@@ -402,6 +405,14 @@ int launch_attn_decode(const __half* q, const __half* k_new, const __half* v_new
     const int64_t units = (int64_t)bls * d->n_heads;
     const unsigned grid = (unsigned)cdiv(units, 4);
     const bool q4 = kv->fmt == FG_FMT_Q4G64;
+    // algorithmic HBM bytes: K and V history (4-bit: codes + meta = 9/16 B per
+    // element), the q / k_new / v_new rows, the output, the appended position
+    const double hist = 2.0 * bls * pos * d->h1;
+    const double per_elem = q4 ? 9.0 / 16.0 : 2.0;
+    const double bytes = hist * per_elem + (double)bls * d->h1 * 2 * 4 +
+                         (fuse ? 2.0 * bls * d->h1 * per_elem : 0.0);
+    TraceScope ts(q4 ? TK_ATTN_DECODE_Q4 : TK_ATTN_DECODE_F16, st,
+                  4.0 * bls * (pos + 1) * (double)d->h1, bytes);
 #define FG_ATTN(HD_, Q_, U_)                                                                  \
     attn_decode_kernel<HD_, Q_, U_><<<grid, 256, 0, st>>>(                                    \
         q, k_new, v_new, ld, kv->k, (__half*)kv->k_meta, kv->v, (__half*)kv->v_meta,          \

@@ -11,6 +11,7 @@
 // The attention flops are ~3% of the prefill's projection flops at the OPT
 // shapes, so this kernel stays on the vector ALUs.
 #include "fg_internal.h"
+#include "fg_trace.h"
 
 namespace fg {
 namespace {
@@ -157,6 +158,8 @@ int launch_attn_prefill(const __half* qkv, int32_t b, int32_t s, const fg_dims* 
     const int rows = 256 / (d->head_dim / 32);
     const int64_t grid = (int64_t)b * d->n_heads * cdiv(s, rows);
     if (grid > INT32_MAX) return set_error(FG_ERR_UNSUPPORTED, "prefill grid too large");
+    TraceScope ts(TK_ATTN_PREFILL, st, 4.0 * b * d->h1 * (double)s * (s + 1) / 2,
+                  (double)b * s * d->h1 * 2 * 4);
     if (d->head_dim == 128)
         attn_prefill_kernel<128><<<(unsigned)grid, 256, 0, st>>>(qkv, s, d->n_heads, out);
     else

@@ -12,6 +12,7 @@
 //    Min/max are taken in a first pass, codes in a second pass that hits L2.
 #include "codec_dev.h"
 #include "fg_internal.h"
+#include "fg_trace.h"
 
 namespace fg {
 namespace {
@@ -195,6 +196,8 @@ int grid_of(int64_t threads) { return (int)cdiv(threads, 256); }
 int launch_quant_g4(const __half* x, int64_t outer, int64_t axis, int64_t inner, uint8_t* codes,
                     __half* meta, hipStream_t st) {
     const int64_t ngroups = axis / G;
+    const double ne = (double)outer * axis * inner;
+    TraceScope ts(TK_QUANT, st, 0.0, ne * 2 + ne / 2 + ne / 64 * 4);
     if (inner == 1) {
         const int64_t n = outer * ngroups;
         quant_contig_kernel<<<grid_of(n * 8), 256, 0, st>>>(x, n, codes,
@@ -215,6 +218,8 @@ int launch_quant_g4(const __half* x, int64_t outer, int64_t axis, int64_t inner,
 int launch_dequant_g4(const uint8_t* codes, const __half* meta, int64_t outer, int64_t axis,
                       int64_t inner, __half* y, hipStream_t st) {
     const int64_t ngroups = axis / G;
+    const double ne = (double)outer * axis * inner;
+    TraceScope ts(TK_DEQUANT, st, 0.0, ne * 2 + ne / 2 + ne / 64 * 4);
     if (inner == 1) {
         const int64_t n = outer * ngroups;
         dequant_contig_kernel<<<grid_of(n * 8), 256, 0, st>>>(

@@ -1,0 +1,30 @@
+// Internal tracing hooks (see trace.hip).  A TraceScope placed around a kernel
+// launch records one event before and one after it on the same stream when
+// tracing is enabled; otherwise it does nothing.
+#pragma once
+
+#include "fg_internal.h"
+
+namespace fg {
+
+enum TraceKind {
+    TK_QUANT = 0, TK_DEQUANT, TK_GEMM_Q4, TK_GEMM_F16, TK_SPLITK_REDUCE, TK_ATTN_DECODE_Q4,
+    TK_ATTN_DECODE_F16, TK_KV_STORE, TK_ATTN_PREFILL, TK_LAYERNORM, TK_EMBED, TK_ARGMAX,
+    TK_COUNT
+};
+
+bool trace_on();
+
+class TraceScope {
+  public:
+    TraceScope(int kind, hipStream_t st, double flops, double bytes);
+    ~TraceScope();
+    TraceScope(const TraceScope&) = delete;
+    TraceScope& operator=(const TraceScope&) = delete;
+
+  private:
+    hipStream_t st_ = nullptr;
+    long idx_ = -1;
+};
+
+}  // namespace fg

@@ -24,6 +24,7 @@
 //    partials go to the workspace and a reduce kernel applies the epilogue in
 //    a fixed order (deterministic, independent of how many rows M holds).
 #include "fg_internal.h"
+#include "fg_trace.h"
 
 namespace fg {
 namespace {
@@ -393,6 +394,11 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
 
 template <class C>
 int run(const Params& p, const Plan& pl, hipStream_t st) {
+    // algorithmic work: 2MNK flops; weights once, activations in, outputs out
+    const double M = (double)p.M, N = (double)p.N, K = (double)p.K;
+    const double wbytes = C::Q4 ? N * K / 2 + N / 64 * K * 4 : N * K * 2;
+    const double bytes = wbytes + 2 * M * K + 2 * M * N * (p.residual ? 2 : 1) + (p.bias ? 2 * N : 0);
+    TraceScope ts(C::Q4 ? TK_GEMM_Q4 : TK_GEMM_F16, st, 2 * M * N * K, bytes);
     dim3 grid((unsigned)pl.nt, (unsigned)pl.mt, (unsigned)pl.S);
     gemm_kernel<C><<<grid, C::NT, 0, st>>>(p);
     FG_LAUNCHED("gemm_kernel");
@@ -445,6 +451,8 @@ int launch_linear(const LinearArgs& a, hipStream_t st) {
     if (st_ != FG_OK) return st_;
     if (pl.S > 1) {
         const int64_t n4 = a.M * a.N / 4;
+        TraceScope ts(TK_SPLITK_REDUCE, st, 0.0,
+                      (double)a.M * a.N * (4.0 * pl.S + 2.0 * (a.residual ? 2 : 1)));
         splitk_reduce_kernel<<<(unsigned)cdiv(n4, 256), 256, 0, st>>>(p, pl.S);
         FG_LAUNCHED("splitk_reduce_kernel");
     }

@@ -2,6 +2,7 @@
 // greedy argmax.  All HBM/latency-bound and tiny next to the projections and
 // attention; each row is one 256-thread workgroup reading 16-byte vectors.
 #include "fg_internal.h"
+#include "fg_trace.h"
 
 namespace fg {
 namespace {
@@ -158,6 +159,7 @@ __global__ __launch_bounds__(NT) void argmax_kernel(const __half* __restrict__ l
 int launch_layernorm(const __half* x, int64_t rows, int64_t h, const __half* g, const __half* b,
                      __half* y, hipStream_t st) {
     if (rows == 0) return FG_OK;
+    TraceScope ts(TK_LAYERNORM, st, 0.0, (double)rows * h * 4 + (double)h * 4);
     const int64_t nv = h / 8;
     if (nv <= NT * 2) {
         layernorm_kernel<2><<<(unsigned)rows, NT, 0, st>>>(x, h, g, b, y);
@@ -176,6 +178,7 @@ int launch_embed(const int32_t* tok, const int32_t* pos, int32_t pos_const, int6
                  int64_t rows, const __half* E, int64_t vocab, const __half* P, int64_t max_pos,
                  int64_t h1, __half* x, hipStream_t st) {
     if (rows == 0) return FG_OK;
+    TraceScope ts(TK_EMBED, st, 0.0, (double)rows * h1 * 6);
     embed_kernel<<<(unsigned)rows, NT, 0, st>>>(tok, pos, pos_const, pos_period, E, vocab, P,
                                                 max_pos, h1, x);
     FG_LAUNCHED("embed_kernel");
@@ -184,6 +187,7 @@ int launch_embed(const int32_t* tok, const int32_t* pos, int32_t pos_const, int6
 
 int launch_argmax(const __half* logits, int64_t rows, int64_t n, int32_t* out, hipStream_t st) {
     if (rows == 0) return FG_OK;
+    TraceScope ts(TK_ARGMAX, st, 0.0, (double)rows * n * 2);
     argmax_kernel<<<(unsigned)rows, NT, 0, st>>>(logits, n, out);
     FG_LAUNCHED("argmax_kernel");
     return FG_OK;

@@ -1,0 +1,97 @@
+// Kernel tracing: when enabled, every launch of the library is bracketed by two
+// HIP events recorded on the launch stream, tagged with its kind and the
+// algorithmic work of that launch (flops, HBM bytes).  fg_trace_collect waits
+// for the events and returns, per kind, the launch count, the summed
+// durations and the summed work, from which a caller derives achieved
+// TFLOP/s or GB/s per kernel.
+#include <mutex>
+#include <vector>
+
+#include "fg_trace.h"
+
+namespace fg {
+namespace {
+
+struct Rec {
+    int kind;
+    hipEvent_t a, b;
+    double flops, bytes;
+};
+
+std::mutex g_mu;
+bool g_on = false;
+std::vector<Rec> g_recs;
+std::vector<hipEvent_t> g_pool;   // free events
+
+hipEvent_t take() {
+    if (!g_pool.empty()) {
+        hipEvent_t e = g_pool.back();
+        g_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+const char* kNames[TK_COUNT] = {
+    "quant_g4", "dequant_g4", "gemm_q4", "gemm_f16", "splitk_reduce", "attn_decode_q4",
+    "attn_decode_f16", "kv_store", "attn_prefill", "layernorm", "embed", "argmax"};
+
+}  // namespace
+
+bool trace_on() { return g_on; }
+
+TraceScope::TraceScope(int kind, hipStream_t st, double flops, double bytes) {
+    if (!g_on) return;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_on) return;
+    Rec r{kind, take(), take(), flops, bytes};
+    if (!r.a || !r.b) return;
+    if (hipEventRecord(r.a, st) != hipSuccess) return;
+    st_ = st;
+    idx_ = (long)g_recs.size();
+    g_recs.push_back(r);
+}
+
+TraceScope::~TraceScope() {
+    if (idx_ < 0) return;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (idx_ < (long)g_recs.size()) (void)hipEventRecord(g_recs[idx_].b, st_);
+}
+
+}  // namespace fg
+
+extern "C" int fg_trace_enable(int on) {
+    std::lock_guard<std::mutex> lk(fg::g_mu);
+    for (auto& r : fg::g_recs) {
+        fg::g_pool.push_back(r.a);
+        fg::g_pool.push_back(r.b);
+    }
+    fg::g_recs.clear();
+    fg::g_on = on != 0;
+    return FG_OK;
+}
+
+extern "C" const char* fg_trace_kind_name(int kind) {
+    return (kind >= 0 && kind < fg::TK_COUNT) ? fg::kNames[kind] : "";
+}
+
+extern "C" int fg_trace_collect(int32_t n_kinds, int64_t* count, double* ms, double* flops,
+                                double* bytes) {
+    fg::clear_error();
+    FG_CHECK_ARG(count && ms && flops && bytes, "null output array");
+    FG_CHECK_ARG(n_kinds >= fg::TK_COUNT, "need room for %d kinds", (int)fg::TK_COUNT);
+    for (int k = 0; k < n_kinds; ++k) { count[k] = 0; ms[k] = flops[k] = bytes[k] = 0.0; }
+    std::lock_guard<std::mutex> lk(fg::g_mu);
+    for (auto& r : fg::g_recs) {
+        FG_HIP(hipEventSynchronize(r.b));
+        float t = 0.f;
+        FG_HIP(hipEventElapsedTime(&t, r.a, r.b));
+        count[r.kind] += 1;
+        ms[r.kind] += t;
+        flops[r.kind] += r.flops;
+        bytes[r.kind] += r.bytes;
+    }
+    return fg::TK_COUNT;
+}
