@@ -10,28 +10,23 @@
 // KV Cache 压缩"): the 4-bit codes are unpacked to fp16 in registers and fed to
 // v_mfma_f32_16x16x32_f16 with fp32 accumulation.
 //
-// Structure (gfx950, wave64):
-//  * MFMA A operand = weight rows (16 n x 32 k), B operand = activation rows
-//    (32 k x 16 m); each lane's 4 accumulators are 4 consecutive output
-//    columns n of one row m, so stores are 8-16 B per lane.
-//  * Workgroup tile BM x BN, k-step 64, double-buffered in LDS.  For 4-bit
-//    weights LDS holds the packed codes (two output rows per byte) and the
-//    (min, scale) rows of the tile's groups; every lane dequantizes its own
-//    8-element fragment once and reuses it for all the m blocks of its wave.
-//  * Dequantization with packed fp16: nibble -> (0x6400 | q) = 1024 + q via
-//    v_perm_b32, minus 1024 (exact), then one fp16 FMA q * scale + min.
-//  * Split-K over grid.z when the tile count alone cannot fill the CUs; fp32
-//    partials go to the workspace and a reduce kernel applies the epilogue in
-//    a fixed order (deterministic, independent of how many rows M holds).
-#include "fg_internal.h"
+// Two kernel families:
+//  * decode-shaped contractions (M up to a few hundred rows) run the
+//    pipelined kernel of gemm_pipe.hip;
+//  * large-M contractions (the prefill, M = gbs * s) run the tiled kernel
+//    below: 128 x 128 tiles of 2 x 2 waves, k-step 64 double-buffered in LDS
+//    through registers.  MFMA A operand = weight rows (16 n x 32 k), B operand
+//    = activation rows (32 k x 16 m), so each lane's 4 accumulators are 4
+//    consecutive output columns.
+// When the tile count alone cannot fill the CUs the contraction is split over
+// grid.z; fp32 partials go to the workspace and a reduce kernel applies the
+// epilogue in a fixed order (deterministic, independent of the row count).
+#include "gemm_common.h"
 #include "fg_trace.h"
 
 namespace fg {
+namespace gemm {
 namespace {
-
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef float f4 __attribute__((ext_vector_type(4)));
 
 template <int MB_, int NB_, int WM_, int WN_, bool Q4_>
 struct Cfg {
@@ -58,56 +53,6 @@ struct Cfg {
     static constexpr int M_IT = (M_CH + NT - 1) / NT;
     static_assert(!Q4 || NB * 16 == 64, "4-bit tiles give each wave one 64-row group");
 };
-
-struct Params {
-    const __half* x;
-    int64_t M, K, ldx;
-    const void* w;
-    const __half* meta;
-    int64_t N;
-    const __half* bias;
-    int32_t act;
-    const __half* residual;
-    __half* y;
-    int64_t ldy;
-    float* part;       // split-K partials [S][M][N] or null
-    int64_t kchunk;    // k range per split (multiple of 64)
-};
-
-__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-    return (uint32_t)__half_as_ushort(__float2half_rn(a)) |
-           ((uint32_t)__half_as_ushort(__float2half_rn(b)) << 16);
-}
-
-__device__ __forceinline__ float h2f(uint32_t bits16) {
-    return __half2float(__ushort_as_half((unsigned short)(bits16 & 0xffffu)));
-}
-
-// 8 consecutive k codes of one weight row (nibble `sh` of 8 bytes) -> fp16
-// w = q * scale + min, with (min, scale) pairs matching the k pairs.
-__device__ __forceinline__ h8 dequant8(uint2 c, uint32_t sh, const uint4& mn, const uint4& sc) {
-    const uint32_t d0 = (c.x >> sh) & 0x0f0f0f0fu;
-    const uint32_t d1 = (c.y >> sh) & 0x0f0f0f0fu;
-    const uint32_t magic = 0x64646464u;
-    uint32_t p[4];
-    p[0] = __builtin_amdgcn_perm(magic, d0, 0x04010400u);
-    p[1] = __builtin_amdgcn_perm(magic, d0, 0x04030402u);
-    p[2] = __builtin_amdgcn_perm(magic, d1, 0x04010400u);
-    p[3] = __builtin_amdgcn_perm(magic, d1, 0x04030402u);
-    const uint32_t mw[4] = {mn.x, mn.y, mn.z, mn.w};
-    const uint32_t sw[4] = {sc.x, sc.y, sc.z, sc.w};
-    const h2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-    h8 out;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        h2 q = __builtin_bit_cast(h2, p[i]) - k1024;     // exact: integer 0..15
-        h2 w = __builtin_elementwise_fma(q, __builtin_bit_cast(h2, sw[i]),
-                                         __builtin_bit_cast(h2, mw[i]));
-        out[2 * i] = w[0];
-        out[2 * i + 1] = w[1];
-    }
-    return out;
-}
 
 template <class C>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(Params p) {
@@ -282,30 +227,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(Params p) {
 #pragma unroll
         for (int mb = 0; mb < C::MB; ++mb) {
             const int64_t m = m0 + (wm * C::MB + mb) * 16 + r16;
-            if (m >= p.M) continue;
-            const f4 v = acc[nb][mb];
-            if (p.part) {
-                float* dst = p.part + ((int64_t)blockIdx.z * p.M + m) * p.N + n;
-                *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-            } else {
-                float o[4] = {v[0], v[1], v[2], v[3]};
-                if (p.bias) {
-                    const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n);
-                    o[0] += h2f(bb.x); o[1] += h2f(bb.x >> 16);
-                    o[2] += h2f(bb.y); o[3] += h2f(bb.y >> 16);
-                }
-                if (p.act == 1) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) o[i] = fmaxf(o[i], 0.f);
-                }
-                if (p.residual) {
-                    const uint2 rr = *reinterpret_cast<const uint2*>(p.residual + m * p.ldy + n);
-                    o[0] += h2f(rr.x); o[1] += h2f(rr.x >> 16);
-                    o[2] += h2f(rr.y); o[3] += h2f(rr.y >> 16);
-                }
-                *reinterpret_cast<uint2*>(p.y + m * p.ldy + n) =
-                    make_uint2(pack_h2(o[0], o[1]), pack_h2(o[2], o[3]));
-            }
+            if (m < p.M) store4(p, m, n, acc[nb][mb], blockIdx.z);
         }
     }
 }
@@ -338,53 +260,43 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(Params p, int S) {
 }
 
 // ----------------------------------------------------------- configurations
-// Decode-shaped (M = bls up to 144 per tile): four waves side by side along
-// N, each owning one 64-row weight group and every m row of the tile.
-using DecQ9 = Cfg<9, 4, 1, 4, true>;
-using DecQ8 = Cfg<8, 4, 1, 4, true>;
-using DecQ4 = Cfg<4, 4, 1, 4, true>;
-using DecQ1 = Cfg<1, 4, 1, 4, true>;
-using DecF9 = Cfg<9, 4, 1, 4, false>;
-using DecF8 = Cfg<8, 4, 1, 4, false>;
-using DecF4 = Cfg<4, 4, 1, 4, false>;
-using DecF1 = Cfg<1, 4, 1, 4, false>;
 // Prefill-shaped (M = gbs * s): 2 x 2 waves, 128 x 128 tile.
 using PreQ = Cfg<4, 4, 2, 2, true>;
 using PreF = Cfg<4, 4, 2, 2, false>;
 
+// Rows up to which the pipelined decode kernel is used.
+constexpr int64_t PIPE_MAX_M = 4 * 144;
+
 struct Plan {
-    int kind;        // which configuration
+    bool pipe;       // pipelined decode kernel (else the tiled kernel)
+    int MB;          // pipelined kernel: 16-row blocks per M tile
     int BM, BN;
     int64_t mt, nt;  // tiles
     int S;           // k splits
     int64_t kchunk;
 };
 
-template <bool Q4>
+// Split the k range until the launch has about two workgroups per CU of the
+// 256-CU part (a constant, so the plan and its workspace size depend on the
+// shape only), keeping at least 4 k-steps of 64 per split.
 Plan make_plan(int64_t M, int64_t N, int64_t K) {
     Plan pl{};
-    // pick the m tile
-    if (M > 4 * 144) {
-        pl.kind = 4; pl.BM = 128; pl.BN = 128;
-    } else if (M > 128 || M % 144 == 0) {
-        pl.kind = 0; pl.BM = 144; pl.BN = 256;
-    } else if (M > 64) {
-        pl.kind = 1; pl.BM = 128; pl.BN = 256;
-    } else if (M > 16) {
-        pl.kind = 2; pl.BM = 64; pl.BN = 256;
+    pl.pipe = M <= PIPE_MAX_M;
+    if (pl.pipe) {
+        pl.MB = pipe_mb_for(M);
+        pl.BM = pl.MB * 16;
+        pl.BN = 256;
     } else {
-        pl.kind = 3; pl.BM = 16; pl.BN = 256;
+        pl.BM = 128;
+        pl.BN = 128;
     }
     pl.mt = cdiv(M, pl.BM);
     pl.nt = cdiv(N, pl.BN);
     const int64_t ksteps = K / 64;
     const int64_t tiles = pl.mt * pl.nt;
-    // two workgroups per CU of the 256-CU part; kept a constant so that the
-    // plan (and the workspace size it implies) is a pure function of the shape
-    const int64_t target = 512;
     int S = 1;
-    if (tiles < target) {
-        S = (int)std::min<int64_t>(cdiv(target, tiles), 16);
+    if (tiles < 512) {
+        S = (int)std::min<int64_t>(cdiv(512, tiles), 16);
         S = (int)std::min<int64_t>(S, std::max<int64_t>(1, ksteps / 4));
     }
     pl.kchunk = cdiv(ksteps, S) * 64;
@@ -393,12 +305,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
 }
 
 template <class C>
-int run(const Params& p, const Plan& pl, hipStream_t st) {
-    // algorithmic work: 2MNK flops; weights once, activations in, outputs out
-    const double M = (double)p.M, N = (double)p.N, K = (double)p.K;
-    const double wbytes = C::Q4 ? N * K / 2 + N / 64 * K * 4 : N * K * 2;
-    const double bytes = wbytes + 2 * M * K + 2 * M * N * (p.residual ? 2 : 1) + (p.bias ? 2 * N : 0);
-    TraceScope ts(C::Q4 ? TK_GEMM_Q4 : TK_GEMM_F16, st, 2 * M * N * K, bytes);
+int run_tiled(const Params& p, const Plan& pl, hipStream_t st) {
     dim3 grid((unsigned)pl.nt, (unsigned)pl.mt, (unsigned)pl.S);
     gemm_kernel<C><<<grid, C::NT, 0, st>>>(p);
     FG_LAUNCHED("gemm_kernel");
@@ -406,16 +313,18 @@ int run(const Params& p, const Plan& pl, hipStream_t st) {
 }
 
 }  // namespace
+}  // namespace gemm
 
-size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t fmt) {
-    const Plan pl = fmt == FG_FMT_Q4G64 ? make_plan<true>(M, N, K) : make_plan<false>(M, N, K);
+size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t) {
+    const gemm::Plan pl = gemm::make_plan(M, N, K);
     return pl.S > 1 ? (size_t)pl.S * M * N * sizeof(float) : 0;
 }
 
 int launch_linear(const LinearArgs& a, hipStream_t st) {
+    using namespace gemm;
     if (a.M == 0 || a.N == 0) return FG_OK;
     const bool q4 = a.fmt == FG_FMT_Q4G64;
-    const Plan pl = q4 ? make_plan<true>(a.M, a.N, a.K) : make_plan<false>(a.M, a.N, a.K);
+    const Plan pl = make_plan(a.M, a.N, a.K);
     Params p{};
     p.x = a.x; p.M = a.M; p.K = a.K; p.ldx = a.ldx;
     p.w = a.w; p.meta = a.meta; p.N = a.N;
@@ -430,25 +339,19 @@ int launch_linear(const LinearArgs& a, hipStream_t st) {
                              a.ws ? a.ws_bytes : (size_t)0);
         p.part = static_cast<float*>(a.ws);
     }
-    int st_ = FG_OK;
-    if (q4) {
-        switch (pl.kind) {
-            case 0: st_ = run<DecQ9>(p, pl, st); break;
-            case 1: st_ = run<DecQ8>(p, pl, st); break;
-            case 2: st_ = run<DecQ4>(p, pl, st); break;
-            case 3: st_ = run<DecQ1>(p, pl, st); break;
-            default: st_ = run<PreQ>(p, pl, st); break;
-        }
-    } else {
-        switch (pl.kind) {
-            case 0: st_ = run<DecF9>(p, pl, st); break;
-            case 1: st_ = run<DecF8>(p, pl, st); break;
-            case 2: st_ = run<DecF4>(p, pl, st); break;
-            case 3: st_ = run<DecF1>(p, pl, st); break;
-            default: st_ = run<PreF>(p, pl, st); break;
-        }
+    {
+        // algorithmic work: 2MNK flops; weights once, activations in, outputs out
+        const double M = (double)p.M, N = (double)p.N, K = (double)p.K;
+        const double wbytes = q4 ? N * K / 2 + N / 64 * K * 4 : N * K * 2;
+        const double bytes = wbytes + 2 * M * K + 2 * M * N * (p.residual ? 2 : 1) + (p.bias ? 2 * N : 0);
+        TraceScope ts(q4 ? TK_GEMM_Q4 : TK_GEMM_F16, st, 2 * M * N * K, bytes);
+        int rc;
+        if (pl.pipe)
+            rc = launch_pipe(p, pl.MB, q4, pl.S, st);
+        else
+            rc = q4 ? run_tiled<PreQ>(p, pl, st) : run_tiled<PreF>(p, pl, st);
+        if (rc != FG_OK) return rc;
     }
-    if (st_ != FG_OK) return st_;
     if (pl.S > 1) {
         const int64_t n4 = a.M * a.N / 4;
         TraceScope ts(TK_SPLITK_REDUCE, st, 0.0,

@@ -1,0 +1,101 @@
+// Pieces shared by the projection GEMM kernels (gemm.hip, gemm_pipe.hip).
+#pragma once
+
+#include "fg_internal.h"
+
+namespace fg {
+namespace gemm {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// y = act(x W^T + bias) + residual over one k-split; partials to `part` when
+// the contraction is split over grid.z.
+struct Params {
+    const __half* x;
+    int64_t M, K, ldx;
+    const void* w;       // fp16 [N, K] or 4-bit codes [N/2, K]
+    const __half* meta;  // 4-bit (min, scale) rows [N/64, 2, K]
+    int64_t N;
+    const __half* bias;
+    int32_t act;
+    const __half* residual;
+    __half* y;
+    int64_t ldy;
+    float* part;         // split-K partials [S][M][N] or null
+    int64_t kchunk;      // k range of one split (multiple of 64)
+};
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+    return (uint32_t)__half_as_ushort(__float2half_rn(a)) |
+           ((uint32_t)__half_as_ushort(__float2half_rn(b)) << 16);
+}
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+    return __half2float(__ushort_as_half((unsigned short)(bits16 & 0xffffu)));
+}
+
+// 8 consecutive k codes of one weight row (nibble `sh` of 8 bytes) -> fp16
+// w = q * scale + min with the (min, scale) pairs of those k: nibble ->
+// (0x6400 | q) = 1024 + q via v_perm_b32, minus 1024 (exact), one fp16 FMA
+// (q * scale is exact, so one rounding: the multiply-then-add result except in
+// double-rounding corner cases of the fp32 definition).
+__device__ __forceinline__ h8 dequant8(uint2 c, uint32_t sh, const uint4& mn, const uint4& sc) {
+    const uint32_t d0 = (c.x >> sh) & 0x0f0f0f0fu;
+    const uint32_t d1 = (c.y >> sh) & 0x0f0f0f0fu;
+    const uint32_t magic = 0x64646464u;
+    uint32_t p[4];
+    p[0] = __builtin_amdgcn_perm(magic, d0, 0x04010400u);
+    p[1] = __builtin_amdgcn_perm(magic, d0, 0x04030402u);
+    p[2] = __builtin_amdgcn_perm(magic, d1, 0x04010400u);
+    p[3] = __builtin_amdgcn_perm(magic, d1, 0x04030402u);
+    const uint32_t mw[4] = {mn.x, mn.y, mn.z, mn.w};
+    const uint32_t sw[4] = {sc.x, sc.y, sc.z, sc.w};
+    const h2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+    h8 out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h2 q = __builtin_bit_cast(h2, p[i]) - k1024;
+        h2 w = __builtin_elementwise_fma(q, __builtin_bit_cast(h2, sw[i]),
+                                         __builtin_bit_cast(h2, mw[i]));
+        out[2 * i] = w[0];
+        out[2 * i + 1] = w[1];
+    }
+    return out;
+}
+
+// Epilogue of one lane: 4 consecutive output columns n..n+3 of row m.
+__device__ __forceinline__ void store4(const Params& p, int64_t m, int64_t n, const f4& v, int z) {
+    if (p.part) {
+        float* dst = p.part + ((int64_t)z * p.M + m) * p.N + n;
+        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        return;
+    }
+    float o[4] = {v[0], v[1], v[2], v[3]};
+    if (p.bias) {
+        const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n);
+        o[0] += h2f(bb.x); o[1] += h2f(bb.x >> 16);
+        o[2] += h2f(bb.y); o[3] += h2f(bb.y >> 16);
+    }
+    if (p.act == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = fmaxf(o[i], 0.f);
+    }
+    if (p.residual) {
+        const uint2 rr = *reinterpret_cast<const uint2*>(p.residual + m * p.ldy + n);
+        o[0] += h2f(rr.x); o[1] += h2f(rr.x >> 16);
+        o[2] += h2f(rr.y); o[3] += h2f(rr.y >> 16);
+    }
+    *reinterpret_cast<uint2*>(p.y + m * p.ldy + n) =
+        make_uint2(pack_h2(o[0], o[1]), pack_h2(o[2], o[3]));
+}
+
+// Launch of the pipelined decode-shaped kernel (gemm_pipe.hip): M tiles of
+// MB*16 rows, N tiles of 256, `S` k-splits (p.kchunk set by the caller).
+int launch_pipe(const Params& p, int MB, bool q4, int S, hipStream_t st);
+// LDS tile of the pipelined kernel: rows per M tile for a given M.
+int pipe_mb_for(int64_t M);
+
+}  // namespace gemm
+}  // namespace fg
