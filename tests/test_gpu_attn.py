@@ -53,6 +53,9 @@ CASES = [  # fmt, bls, nh, hd, pos
     ("q4", 2, 2, 128, 17), ("q4", 1, 3, 128, 64), ("q4", 2, 2, 128, 65), ("q4", 1, 2, 128, 200),
     ("q4", 2, 1, 128, 527), ("q4", 3, 5, 64, 33), ("q4", 2, 12, 64, 39), ("q4", 1, 1, 64, 0),
     ("f16", 2, 3, 128, 0), ("f16", 3, 5, 128, 40), ("f16", 2, 2, 64, 77), ("f16", 1, 32, 64, 130),
+    # histories longer than one LDS chunk of scores (8192 positions): running maximum
+    ("q4", 1, 2, 64, 8192), ("q4", 1, 2, 128, 8193), ("q4", 2, 1, 64, 17000),
+    ("f16", 1, 2, 64, 9000),
 ]
 
 
@@ -87,39 +90,56 @@ def test_decode_attention_and_append(L, fmt, bls, nh, hd, pos):
         assert_close(np16(out2), ref2, f"{fmt} attention pos {pos + 1} (unfused)")
 
 
-def test_decode_attention_full_shape_sampled(L):
-    """OPT-175B shape (96 heads x 128) at bls = 144, context 528 (s + n/2): the
-    launch the benchmark times; sampled (sequence, head) pairs against the oracle."""
+def _sampled_check(L, fmt, bls, nh, hd, pos, lmax, seed):
+    """Device cache filled by one append per position from synthetic rows on
+    the device; the decode launch checked on sampled (sequence, head) pairs."""
     import torch
     from throughput_oriented_offloaded_amd.model import DeviceKV
     import synth
-    bls, nh, hd, pos, lmax = 144, 96, 128, 528, 544
     h1 = nh * hd
     d = L.dims(h1, 4 * h1, nh, hd)
-    kv = DeviceKV(L.FG_FMT_Q4G64, bls, nh, hd, lmax, "cuda")
-    kh, vh = synth.kv_history(bls, nh, pos, hd, seed=5, device="cuda")
+    fmt_id = L.FG_FMT_Q4G64 if fmt == "q4" else L.FG_FMT_F16
+    append = L.fg_kv_append_q4 if fmt == "q4" else L.fg_kv_append_f16
+    attn = L.fg_attn_decode_q4 if fmt == "q4" else L.fg_attn_decode_f16
+    kv = DeviceKV(fmt_id, bls, nh, hd, lmax, "cuda")
+    kh, vh = synth.kv_history(bls, nh, pos, hd, seed=seed, device="cuda")
     for p in range(pos):   # append every history position (one launch each)
-        L.fg_kv_append_q4(kh[:, p].contiguous(), vh[:, p].contiguous(), h1, kv.struct, bls, d, p)
-    qkv = synth.activations(bls, 3 * h1, seed=6, device="cuda", std=2.0)
+        append(kh[:, p].contiguous(), vh[:, p].contiguous(), h1, kv.struct, bls, d, p)
+    qkv = synth.activations(bls, 3 * h1, seed=seed + 1, device="cuda", std=2.0)
     out = torch.empty((bls, h1), dtype=torch.float16, device="cuda")
-    L.fg_attn_decode_q4(qkv, qkv[:, h1:], qkv[:, 2 * h1:], 3 * h1, kv.struct, bls, d, pos, 1, out)
+    attn(qkv, qkv[:, h1:], qkv[:, 2 * h1:], 3 * h1, kv.struct, bls, d, pos, 1, out)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(1)
+    rng = np.random.default_rng(seed)
     seqs = sorted(set([0, bls - 1] + list(rng.integers(0, bls, 3))))
     for b in seqs:
         heads = sorted(set([0, nh - 1] + list(rng.integers(0, nh, 3))))
         khb = np16(kh[b]).reshape(pos, nh, hd)[:, heads]          # [pos, H, hd]
         vhb = np16(vh[b]).reshape(pos, nh, hd)[:, heads]
-        oc = oracle.KVCache("q4", 1, len(heads), hd, lmax)
-        oc.store(khb.reshape(1, pos, -1), vhb.reshape(1, pos, -1), 0)
-        # device cache rows of these heads equal the oracle's codes
-        assert np.array_equal(kv.k[b, heads, :pos].cpu().numpy(), oc.k[0, :, :pos])
-        assert np.array_equal(np16(kv.vm[b, heads, :pos]), oc.vm[0, :, :pos])
+        oc = oracle.KVCache(fmt, 1, len(heads), hd, lmax)
+        if pos:
+            oc.store(khb.reshape(1, pos, -1), vhb.reshape(1, pos, -1), 0)
+        # device cache rows of these heads equal the oracle's
+        assert np.array_equal(kv.k[b, heads, :pos].cpu().numpy().view(oc.k.dtype), oc.k[0, :, :pos])
+        if fmt == "q4":
+            assert np.array_equal(np16(kv.vm[b, heads, :pos]), oc.vm[0, :, :pos])
         q3 = np16(qkv[b]).reshape(3, nh, hd)[:, heads].reshape(1, -1)
         hist = oc.history()
         ref = oracle.attn_decode(q3, 1, len(heads), hd, hist[0], hist[1], lmax, pos)
         got = np16(out[b]).reshape(nh, hd)[heads].reshape(1, -1)
-        assert_close(got, ref, f"seq {b} heads {heads}")
+        assert_close(got, ref, f"{fmt} pos {pos} seq {b} heads {heads}")
+
+
+def test_decode_attention_full_shape_sampled(L):
+    """OPT-175B shape (96 heads x 128) at bls = 144, context 528 (s + n/2): the
+    launch the benchmark times; sampled (sequence, head) pairs against the oracle."""
+    _sampled_check(L, "q4", 144, 96, 128, 528, 544, seed=5)
+
+
+@pytest.mark.parametrize("fmt,pos", [("q4", 0), ("q4", 37), ("f16", 61), ("q4", 8300)])
+def test_decode_attention_one_wave_per_head(L, fmt, pos):
+    """2048 (sequence, head) pairs: the launch with one wavefront per pair,
+    short, ragged and multi-chunk histories."""
+    _sampled_check(L, fmt, 32, 64, 64, pos, pos + 2, seed=11 + pos)
 
 
 @pytest.mark.parametrize("b,s,nh,hd", [(1, 1, 1, 128), (2, 5, 3, 128), (1, 64, 2, 128),

@@ -9,22 +9,34 @@
 // dim (section "权重压缩与 KV Cache 压缩"; bjbfmj.com walkthrough §6.3
 // group_dim 2) and dequantized in registers while it streams.
 //
-// Mapping (MI355X, wave64): one wavefront per (sequence, head).  A lane owns
-// 32 consecutive dims of the head (16 B of codes, inside one 64-group) and one
-// "slot" of positions: hd=128 -> 4 lanes per position, 16 positions per
-// wavefront step; hd=64 -> 2 lanes per position, 32 per step.  Each lane keeps
-// its own online-softmax state (running max, sum, 32 accumulators) over the
-// positions of its slot; the slots are merged once at the end with wavefront
-// shuffles.  No LDS and no barriers: the kernel is a pure HBM stream of
-// codes + metadata (9/16 byte per cached element).
+// Mapping (MI355X, wave64): one workgroup of NW wavefronts per (sequence,
+// head).  A lane owns 32 consecutive dims of the head (16 B of 4-bit codes,
+// inside one 64-group, or 64 B of fp16) and one position per step: hd=128 ->
+// 4 lanes per position, 16 positions per wavefront step.  The history is
+// processed in two passes per chunk of positions:
+//   1. scores of all positions into LDS (K stream), chunk maximum;
+//   2. softmax weights from LDS, weighted V sum (V stream).
+// so the running maximum changes once per chunk, not once per position.  The
+// per-lane partial sums are merged at the end with DPP row reductions and LDS.
+// The cache rows are streamed with non-temporal loads (each byte is read once
+// per step), and every load is unconditional (positions past the end are
+// clamped to the last valid row and masked afterwards) so the compiler keeps
+// several loads in flight per lane.
+//
+// Arithmetic of the 4-bit path.  A nibble c becomes the fp16 value 1024 + c
+// with one byte permute (0x64 as the high byte), and v_dot2_f32_f16 multiplies
+// two fp16 pairs exactly and accumulates in fp32:
+//   score:  sum_{d in D} q_d (mn_g + sc_g c_d)
+//             = mn_g * S_q + sc_g * (sum_d q_d (1024 + c_d) - 1024 S_q),
+//   output: sum_p w_p (mn_p + sc_p c_pd)
+//             = sum_p w_p mn_p + sum_p w^_p (1024 + c_pd) - 1024 sum_p w^_p,
+// with S_q the sum of the lane's q values and w^_p = fp16(w_p sc_p); the V sum
+// pairs two positions per dot2 (the same dim of positions p, p').
 //
 // Reading of the current token (stated in fg.h): positions < pos come from the
 // cache; position pos uses the fresh fp16 k, v.
-//
-// Score with 4-bit keys, per lane (its dims D inside group g):
-//   sum_{d in D} q_d (mn_g + sc_g c_d) = mn_g * sum_D q_d + sc_g * sum_D q_d c_d,
-// so each element costs one byte->float conversion and one FMA.  V is
-// accumulated the same way: acc_d += (w sc) c_d, plus one scalar w mn per lane.
+#include <algorithm>
+
 #include "codec_dev.h"
 #include "fg_internal.h"
 #include "fg_trace.h"
@@ -33,6 +45,12 @@ namespace fg {
 namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
+// positions per chunk of scores in LDS (32 KB); longer histories take several
+// chunks with a running maximum
+constexpr int kAttnChunk = 8192;
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float lo_half(uint32_t w) {
     return __half2float(__ushort_as_half((unsigned short)(w & 0xffffu)));
@@ -40,48 +58,134 @@ __device__ __forceinline__ float lo_half(uint32_t w) {
 __device__ __forceinline__ float hi_half(uint32_t w) {
     return __half2float(__ushort_as_half((unsigned short)(w >> 16)));
 }
-
-// Byte j of a dword as float (compiles to v_cvt_f32_ubyte{j}).
-template <int J>
-__device__ __forceinline__ float ub(uint32_t w) {
-    return (float)((w >> (8 * J)) & 0xffu);
+__device__ __forceinline__ h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
+__device__ __forceinline__ float dot2(uint32_t a, h2 b, float c) {
+    return __builtin_amdgcn_fdot2(as_h2(a), b, c, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 CTRL, 0xF, 0xF, false));
+}
+// sum over the LPP lanes of one position (lane ^ 1, lane ^ 2 inside a quad)
+template <int LPP>
+__device__ __forceinline__ float pos_sum(float v) {
+    v += dpp<0xB1>(v);
+    if constexpr (LPP == 4) v += dpp<0x4E>(v);
+    return v;
+}
+// sum over the lanes of one row of 16 that own the same dims (lane % LPP)
+template <int LPP>
+__device__ __forceinline__ float row_sum(float v) {
+    v += dpp<0x128>(v);   // row_ror:8
+    v += dpp<0x124>(v);   // row_ror:4
+    if constexpr (LPP == 2) v += dpp<0x122>(v);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+__device__ __forceinline__ uint4 ld_stream(const uint8_t* p) {
+    const u4v t = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
 }
 
-// sum_{i<32} q[i] * code_i over 16 bytes of packed nibbles (element 2j of a
-// byte pair in the low nibble).
-__device__ __forceinline__ float dot_codes(const uint4& c, const float q[32]) {
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    float s0 = 0.f, s1 = 0.f;
+constexpr uint32_t MAGIC = 0x64646464u;   // fp16 0x64XX = 1024 + XX for XX < 16
+constexpr uint32_t SEL_B01 = 0x04010400u; // (1024 + byte 0, 1024 + byte 1)
+constexpr uint32_t SEL_B23 = 0x04030402u; // (1024 + byte 2, 1024 + byte 3)
+constexpr uint32_t SEL_LO = 0x05040100u;  // (low half of a, low half of b)
+constexpr uint32_t SEL_HI = 0x07060302u;  // (high half of a, high half of b)
+
+// One lane's share of a cache row: 32 dims.
+template <bool Q4> struct Row;
+template <> struct Row<true> { uint4 c; };                      // 16 B of nibbles
+template <> struct Row<false> { uint4 c[4]; };                  // 64 B of fp16
+
+template <bool Q4>
+__device__ __forceinline__ Row<Q4> load_row(const uint8_t* p) {
+    Row<Q4> r;
+    if constexpr (Q4) {
+        r.c = ld_stream(p);
+    } else {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t lo = w[k] & 0x0f0f0f0fu;
-        const uint32_t hi = (w[k] >> 4) & 0x0f0f0f0fu;
-        s0 = fmaf(q[8 * k + 0], ub<0>(lo), s0);
-        s1 = fmaf(q[8 * k + 1], ub<0>(hi), s1);
-        s0 = fmaf(q[8 * k + 2], ub<1>(lo), s0);
-        s1 = fmaf(q[8 * k + 3], ub<1>(hi), s1);
-        s0 = fmaf(q[8 * k + 4], ub<2>(lo), s0);
-        s1 = fmaf(q[8 * k + 5], ub<2>(hi), s1);
-        s0 = fmaf(q[8 * k + 6], ub<3>(lo), s0);
-        s1 = fmaf(q[8 * k + 7], ub<3>(hi), s1);
+        for (int k = 0; k < 4; ++k) r.c[k] = ld_stream(p + 16 * k);
     }
-    return s0 + s1;
+    return r;
 }
 
-__device__ __forceinline__ void acc_codes(const uint4& c, float ws, float acc[32]) {
+// q of the lane's 32 dims as fp16 pairs.  4-bit path: in nibble-unpack order
+// (q0,q2),(q4,q6),(q1,q3),(q5,q7) per 8 dims; fp16 path: natural pairs.
+template <bool Q4>
+__device__ __forceinline__ void load_q(const __half* src, h2 qp[16]) {
+    const uint4* q4 = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint4 r = q4[k];
+        if constexpr (Q4) {
+            qp[4 * k + 0] = as_h2(__builtin_amdgcn_perm(r.y, r.x, SEL_LO));
+            qp[4 * k + 1] = as_h2(__builtin_amdgcn_perm(r.w, r.z, SEL_LO));
+            qp[4 * k + 2] = as_h2(__builtin_amdgcn_perm(r.y, r.x, SEL_HI));
+            qp[4 * k + 3] = as_h2(__builtin_amdgcn_perm(r.w, r.z, SEL_HI));
+        } else {
+            qp[4 * k + 0] = as_h2(r.x);
+            qp[4 * k + 1] = as_h2(r.y);
+            qp[4 * k + 2] = as_h2(r.z);
+            qp[4 * k + 3] = as_h2(r.w);
+        }
+    }
+}
+
+// 4-bit: sum_d q_d (1024 + c_d) over the lane's 32 dims, starting from acc.
+__device__ __forceinline__ float kdot_q4(const uint4& c, const h2 qp[16], float acc) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const uint32_t lo = w[k] & 0x0f0f0f0fu;
-        const uint32_t hi = (w[k] >> 4) & 0x0f0f0f0fu;
-        acc[8 * k + 0] = fmaf(ws, ub<0>(lo), acc[8 * k + 0]);
-        acc[8 * k + 1] = fmaf(ws, ub<0>(hi), acc[8 * k + 1]);
-        acc[8 * k + 2] = fmaf(ws, ub<1>(lo), acc[8 * k + 2]);
-        acc[8 * k + 3] = fmaf(ws, ub<1>(hi), acc[8 * k + 3]);
-        acc[8 * k + 4] = fmaf(ws, ub<2>(lo), acc[8 * k + 4]);
-        acc[8 * k + 5] = fmaf(ws, ub<2>(hi), acc[8 * k + 5]);
-        acc[8 * k + 6] = fmaf(ws, ub<3>(lo), acc[8 * k + 6]);
-        acc[8 * k + 7] = fmaf(ws, ub<3>(hi), acc[8 * k + 7]);
+        const uint32_t lo = w[k] & 0x0f0f0f0fu, hi = (w[k] >> 4) & 0x0f0f0f0fu;
+        acc = dot2(__builtin_amdgcn_perm(MAGIC, lo, SEL_B01), qp[4 * k + 0], acc);
+        acc = dot2(__builtin_amdgcn_perm(MAGIC, lo, SEL_B23), qp[4 * k + 1], acc);
+        acc = dot2(__builtin_amdgcn_perm(MAGIC, hi, SEL_B01), qp[4 * k + 2], acc);
+        acc = dot2(__builtin_amdgcn_perm(MAGIC, hi, SEL_B23), qp[4 * k + 3], acc);
+    }
+    return acc;
+}
+
+// 4-bit: acc_d += wA (1024 + cA_d) + wB (1024 + cB_d) over 32 dims of two
+// positions A, B (bytes of A and B interleaved first, so one permute builds
+// the fp16 pair of one dim).
+__device__ __forceinline__ void vacc_q4(const uint4& a, const uint4& b, h2 w, float acc[32]) {
+    const uint32_t A[4] = {a.x, a.y, a.z, a.w}, B[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t X = __builtin_amdgcn_perm(B[k], A[k], 0x05010400u);   // A0 B0 A1 B1
+        const uint32_t Y = __builtin_amdgcn_perm(B[k], A[k], 0x07030602u);   // A2 B2 A3 B3
+        const uint32_t xl = X & 0x0f0f0f0fu, xh = (X >> 4) & 0x0f0f0f0fu;
+        const uint32_t yl = Y & 0x0f0f0f0fu, yh = (Y >> 4) & 0x0f0f0f0fu;
+        acc[8 * k + 0] = dot2(__builtin_amdgcn_perm(MAGIC, xl, SEL_B01), w, acc[8 * k + 0]);
+        acc[8 * k + 2] = dot2(__builtin_amdgcn_perm(MAGIC, xl, SEL_B23), w, acc[8 * k + 2]);
+        acc[8 * k + 1] = dot2(__builtin_amdgcn_perm(MAGIC, xh, SEL_B01), w, acc[8 * k + 1]);
+        acc[8 * k + 3] = dot2(__builtin_amdgcn_perm(MAGIC, xh, SEL_B23), w, acc[8 * k + 3]);
+        acc[8 * k + 4] = dot2(__builtin_amdgcn_perm(MAGIC, yl, SEL_B01), w, acc[8 * k + 4]);
+        acc[8 * k + 6] = dot2(__builtin_amdgcn_perm(MAGIC, yl, SEL_B23), w, acc[8 * k + 6]);
+        acc[8 * k + 5] = dot2(__builtin_amdgcn_perm(MAGIC, yh, SEL_B01), w, acc[8 * k + 5]);
+        acc[8 * k + 7] = dot2(__builtin_amdgcn_perm(MAGIC, yh, SEL_B23), w, acc[8 * k + 7]);
+    }
+}
+
+// fp16: acc_d += wA vA_d + wB vB_d over 32 dims of two positions.
+__device__ __forceinline__ void vacc_f16(const Row<false>& a, const Row<false>& b, h2 w,
+                                         float acc[32]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t A[4] = {a.c[k].x, a.c[k].y, a.c[k].z, a.c[k].w};
+        const uint32_t B[4] = {b.c[k].x, b.c[k].y, b.c[k].z, b.c[k].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[8 * k + 2 * i] = dot2(__builtin_amdgcn_perm(B[i], A[i], SEL_LO), w, acc[8 * k + 2 * i]);
+            acc[8 * k + 2 * i + 1] =
+                dot2(__builtin_amdgcn_perm(B[i], A[i], SEL_HI), w, acc[8 * k + 2 * i + 1]);
+        }
     }
 }
 
@@ -102,213 +206,276 @@ __device__ __forceinline__ void load32h(const __half* p, float v[32]) {
 // Quantize 32 fp16 values that form half of a 64-group whose other half sits
 // in the neighbouring lane (lane ^ 1); returns the 16 code bytes and the
 // (min, scale) fp16 bits of the group.
-__device__ __forceinline__ uint4 quant_half_group(const float v[32], uint32_t& meta_bits) {
-    float mn = v[0], mx = v[0];
+__device__ __forceinline__ uint4 quant_half_group(const uint4 r[4], uint32_t& meta_bits) {
+    // 32 fp16 values kept packed (16 registers); each is widened where used
+    const uint32_t w[16] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w,
+                            r[2].x, r[2].y, r[2].z, r[2].w, r[3].x, r[3].y, r[3].z, r[3].w};
+    float mn = lo_half(w[0]), mx = mn;
 #pragma unroll
-    for (int i = 1; i < 32; ++i) {
-        mn = fminf(mn, v[i]);
-        mx = fmaxf(mx, v[i]);
+    for (int i = 0; i < 16; ++i) {
+        const float a = lo_half(w[i]), c = hi_half(w[i]);
+        mn = fminf(mn, fminf(a, c));
+        mx = fmaxf(mx, fmaxf(a, c));
     }
     mn = fminf(mn, __shfl_xor(mn, 1));
     mx = fmaxf(mx, __shfl_xor(mx, 1));
     const QParams p = qparams(mn, mx);
     meta_bits = qmeta_bits(p);
-    uint32_t w[4];
-#pragma unroll
+    uint32_t out[4];
+#pragma unroll 1
     for (int k = 0; k < 4; ++k) {
         uint32_t x = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x |= qcode(v[8 * k + j], p) << (4 * j);
-        w[k] = x;
+        for (int j = 0; j < 4; ++j) {
+            x |= qcode(lo_half(w[4 * k + j]), p) << (8 * j);
+            x |= qcode(hi_half(w[4 * k + j]), p) << (8 * j + 4);
+        }
+        out[k] = x;
     }
-    return make_uint4(w[0], w[1], w[2], w[3]);
+    return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
-template <int HD, bool Q4, int U>
-__global__ __launch_bounds__(256) void attn_decode_kernel(
+// the lane's 32 fp16 values of a row (16 B aligned)
+__device__ __forceinline__ void load32p(const __half* p, uint4 r[4]) {
+    const uint4* p4 = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = p4[k];
+}
+
+// NW wavefronts per (sequence, head); MULTI: the history may exceed one chunk
+// of `chunk` positions (scores in dynamic LDS), merged with a running maximum.
+template <int HD, bool Q4, int NW, bool MULTI>
+__device__ __forceinline__ void attn_decode_body(
     const __half* __restrict__ q, const __half* __restrict__ k_new,
     const __half* __restrict__ v_new, int64_t ld, void* __restrict__ kc,
     __half* __restrict__ km, void* __restrict__ vc, __half* __restrict__ vm, int32_t lmax,
-    int32_t nh, int32_t bls, int32_t pos, int fuse, __half* __restrict__ out) {
-    constexpr int LPP = HD / 32;       // lanes per position
-    constexpr int SLOTS = 64 / LPP;    // positions per wavefront step
-    constexpr int GPH = HD / 64;       // 64-groups per head
-    const int lane = threadIdx.x & 63;
-    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (b, h)
-    if (unit >= (int64_t)bls * nh) return;
-    const int64_t b = unit / nh;
-    const int h = (int)(unit % nh);
-    const int qi = lane % LPP;          // which 32 dims
-    const int slot = lane / LPP;
-    const int g = (qi * 32) / 64;       // group of those dims
+    int32_t nh, int32_t pos, int32_t chunk, int fuse, __half* __restrict__ out) {
+    constexpr int LPP = HD / 32;           // lanes per position
+    constexpr int SLOTS = 64 / LPP;        // positions per wavefront step
+    constexpr int GPH = HD / 64;           // 64-groups per head
+    constexpr int WGP = NW * SLOTS;        // positions per workgroup step
+    constexpr int ROWS = 4;                // rows of 16 lanes
+    constexpr int RB = Q4 ? HD / 2 : HD * 2;   // bytes of one cache row
+    constexpr int U1 = Q4 ? 4 : 2;         // steps per batch of loads, pass 1
+    constexpr int U2 = Q4 ? 2 : 1;         // pairs of steps per batch, pass 2
+    extern __shared__ float smem[];
+    float* sS = smem;                                   // [chunk] scores (log2 units)
+    float* sRed = smem + chunk;                         // [NW*ROWS*LPP][32]
+    float* sFix = sRed + NW * ROWS * LPP * 32;          // [NW*ROWS*LPP]
+    float* sL = sFix + NW * ROWS * LPP;                 // [NW*ROWS]
+    float* sMax = sL + NW * ROWS;                       // [NW]
 
-    // q pre-scaled so that scores come out in log2 units
-    const float qs = LOG2E / sqrtf((float)HD);
-    float qv[32];
-    load32h(q + b * ld + h * HD + qi * 32, qv);
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t unit = blockIdx.x;                    // (b, h)
+    const int64_t b = unit / nh;
+    const int h = (int)(unit - b * nh);
+    const int qi = lane % LPP;                          // which 32 dims
+    const int slot = lane / LPP;
+    const int g = qi >> 1;                              // 64-group of those dims
+    const int lp = wv * SLOTS + slot;                   // position offset in a step
+    const int64_t row0 = unit * (int64_t)lmax;          // cache row of (b, h, 0)
+    const uint8_t* kcp = (const uint8_t*)kc + row0 * RB + qi * (RB / LPP);
+    const uint8_t* vcp = (const uint8_t*)vc + row0 * RB + qi * (RB / LPP);
+    const uint32_t* kmp = reinterpret_cast<const uint32_t*>(km) + row0 * GPH + g;
+    const uint32_t* vmp = reinterpret_cast<const uint32_t*>(vm) + row0 * GPH + g;
+    const float qscale = LOG2E / sqrtf((float)HD);      // scores in log2 units
+    const h2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+
+    h2 qp[16];
+    load_q<Q4>(q + b * ld + h * HD + qi * 32, qp);
     float qsum = 0.f;
+    if constexpr (Q4) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        qv[i] *= qs;
-        qsum += qv[i];
+        for (int i = 0; i < 16; ++i) qsum = __builtin_amdgcn_fdot2(qp[i], one2, qsum, false);
+    }
+    const float qoff = -1024.0f * qsum;
+
+    // score of the current token (fresh fp16 k, same pair order as qp)
+    float snew;
+    {
+        h2 kp[16];
+        load_q<Q4>(k_new + b * ld + h * HD + qi * 32, kp);
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s = __builtin_amdgcn_fdot2(kp[i], qp[i], s, false);
+        snew = pos_sum<LPP>(s) * qscale;
     }
 
-    const int64_t head_row0 = unit * (int64_t)lmax;   // cache row of (b, h, position 0)
-    float m = -INFINITY, l = 0.f, accm = 0.f;
     float acc[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = 0.f;
+    float l = 0.f, fix = 0.f;      // fix: sum w mn - 1024 sum w^ (4-bit only)
+    float M = snew;                // running maximum (log2 units)
 
-    for (int base = 0; base < pos; base += SLOTS * U) {
-        float sc[U];
-        if constexpr (Q4) {
-            uint4 kcode[U], vcode[U];
-            uint32_t kmeta[U], vmeta[U];
+    auto run_chunk = [&](int c0, int n) {
+        const int last = c0 + n - 1;                    // last valid position
+        const int nst = (n + WGP - 1) / WGP;
+        // pass 1: scores
+        float mloc = -INFINITY;
+        auto kscore = [&](int j, const Row<Q4>& r, uint32_t meta) {
+            float s;
+            if constexpr (Q4) {
+                s = lo_half(meta) * qsum + hi_half(meta) * kdot_q4(r.c, qp, qoff);
+            } else {
+                s = 0.f;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int p = base + u * SLOTS + slot;
-                if (p < pos) {
-                    const int64_t row = head_row0 + p;
-                    kcode[u] = *reinterpret_cast<const uint4*>((const uint8_t*)kc + row * (HD / 2) + qi * 16);
-                    vcode[u] = *reinterpret_cast<const uint4*>((const uint8_t*)vc + row * (HD / 2) + qi * 16);
-                    kmeta[u] = *reinterpret_cast<const uint32_t*>(km + (row * GPH + g) * 2);
-                    vmeta[u] = *reinterpret_cast<const uint32_t*>(vm + (row * GPH + g) * 2);
-                } else {
-                    kcode[u] = vcode[u] = make_uint4(0, 0, 0, 0);
-                    kmeta[u] = vmeta[u] = 0;
+                for (int k = 0; k < 4; ++k) {
+                    s = dot2(r.c[k].x, qp[4 * k + 0], s);
+                    s = dot2(r.c[k].y, qp[4 * k + 1], s);
+                    s = dot2(r.c[k].z, qp[4 * k + 2], s);
+                    s = dot2(r.c[k].w, qp[4 * k + 3], s);
                 }
             }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float part = lo_half(kmeta[u]) * qsum + hi_half(kmeta[u]) * dot_codes(kcode[u], qv);
-#pragma unroll
-                for (int off = 1; off < LPP; off <<= 1) part += __shfl_xor(part, off);
-                sc[u] = (base + u * SLOTS + slot < pos) ? part : -INFINITY;
+            s = pos_sum<LPP>(s) * qscale;
+            const int pl = j * WGP + lp;
+            if (pl < n) {
+                mloc = fmaxf(mloc, s);
+                if (qi == 0) sS[pl] = s;
             }
-            float mnew = m;
+        };
+        int j = 0;
+        for (; j + U1 <= nst; j += U1) {
+            Row<Q4> r[U1];
+            uint32_t meta[U1];
 #pragma unroll
-            for (int u = 0; u < U; ++u) mnew = fmaxf(mnew, sc[u]);
-            if (mnew != -INFINITY) {
-                const float alpha = exp2f(m - mnew);
+            for (int u = 0; u < U1; ++u) {
+                const int64_t p = min(c0 + (j + u) * WGP + lp, last);
+                r[u] = load_row<Q4>(kcp + p * RB);
+                if constexpr (Q4) meta[u] = kmp[p * GPH];
+            }
+#pragma unroll
+            for (int u = 0; u < U1; ++u) kscore(j + u, r[u], Q4 ? meta[u] : 0u);
+        }
+        for (; j < nst; ++j) {
+            const int64_t p = min(c0 + j * WGP + lp, last);
+            const Row<Q4> r = load_row<Q4>(kcp + p * RB);
+            const uint32_t meta = Q4 ? kmp[p * GPH] : 0u;
+            kscore(j, r, meta);
+        }
+        mloc = wave_max(mloc);
+        if (lane == 0) sMax[wv] = mloc;
+        __syncthreads();
+        float mc = sMax[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) mc = fmaxf(mc, sMax[w]);
+        if constexpr (MULTI) {
+            if (mc > M) {               // uniform over the workgroup
+                const float alpha = exp2f(M - mc);
                 l *= alpha;
-                accm *= alpha;
+                fix *= alpha;
 #pragma unroll
                 for (int i = 0; i < 32; ++i) acc[i] *= alpha;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const float w = exp2f(sc[u] - mnew);
-                    l += w;
-                    accm = fmaf(w, lo_half(vmeta[u]), accm);
-                    acc_codes(vcode[u], w * hi_half(vmeta[u]), acc);
-                }
-                m = mnew;
+                M = mc;
             }
         } else {
-            float kv[U][32];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int p = base + u * SLOTS + slot;
-                if (p < pos) {
-                    load32h((const __half*)kc + (head_row0 + p) * HD + qi * 32, kv[u]);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 32; ++i) kv[u][i] = 0.f;
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float part = 0.f;
-#pragma unroll
-                for (int i = 0; i < 32; ++i) part = fmaf(qv[i], kv[u][i], part);
-#pragma unroll
-                for (int off = 1; off < LPP; off <<= 1) part += __shfl_xor(part, off);
-                sc[u] = (base + u * SLOTS + slot < pos) ? part : -INFINITY;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int p = base + u * SLOTS + slot;
-                if (p < pos) {
-                    load32h((const __half*)vc + (head_row0 + p) * HD + qi * 32, kv[u]);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 32; ++i) kv[u][i] = 0.f;
-                }
-            }
-            float mnew = m;
-#pragma unroll
-            for (int u = 0; u < U; ++u) mnew = fmaxf(mnew, sc[u]);
-            if (mnew != -INFINITY) {
-                const float alpha = exp2f(m - mnew);
-                l *= alpha;
-#pragma unroll
-                for (int i = 0; i < 32; ++i) acc[i] *= alpha;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const float w = exp2f(sc[u] - mnew);
-                    l += w;
-#pragma unroll
-                    for (int i = 0; i < 32; ++i) acc[i] = fmaf(w, kv[u][i], acc[i]);
-                }
-                m = mnew;
-            }
+            M = fmaxf(M, mc);
         }
+        // pass 2: weighted V over pairs of steps (j, j + 1)
+        auto vpair = [&](int ja, const Row<Q4>& ra, const Row<Q4>& rb, uint32_t ma, uint32_t mb) {
+            const int pa = ja * WGP + lp, pb = pa + WGP;
+            const bool oka = pa < n, okb = pb < n;
+            const float wa = oka ? exp2f(sS[oka ? pa : 0] - M) : 0.f;
+            const float wb = okb ? exp2f(sS[okb ? pb : 0] - M) : 0.f;
+            if constexpr (Q4) {
+                const uint32_t mA = oka ? ma : 0u, mB = okb ? mb : 0u;
+                l += wa + wb;
+                h2 wh;
+                wh[0] = (_Float16)(wa * hi_half(mA));
+                wh[1] = (_Float16)(wb * hi_half(mB));
+                fix = fmaf(wa, lo_half(mA), fmaf(wb, lo_half(mB), fix));
+                fix = __builtin_amdgcn_fdot2(wh, -1024.0f * one2, fix, false);
+                vacc_q4(ra.c, rb.c, wh, acc);
+            } else {
+                h2 wh;
+                wh[0] = (_Float16)wa;
+                wh[1] = (_Float16)wb;
+                l = __builtin_amdgcn_fdot2(wh, one2, l, false);
+                vacc_f16(ra, rb, wh, acc);
+            }
+        };
+        const int npr = (nst + 1) / 2;
+        int pr = 0;
+        for (; pr + U2 <= npr; pr += U2) {
+            Row<Q4> ra[U2], rb[U2];
+            uint32_t ma[U2], mb[U2];
+#pragma unroll
+            for (int u = 0; u < U2; ++u) {
+                const int pa = c0 + 2 * (pr + u) * WGP + lp;
+                const int64_t qa = min(pa, last), qb = min(pa + WGP, last);
+                ra[u] = load_row<Q4>(vcp + qa * RB);
+                rb[u] = load_row<Q4>(vcp + qb * RB);
+                if constexpr (Q4) {
+                    ma[u] = vmp[qa * GPH];
+                    mb[u] = vmp[qb * GPH];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U2; ++u)
+                vpair(2 * (pr + u), ra[u], rb[u], Q4 ? ma[u] : 0u, Q4 ? mb[u] : 0u);
+        }
+        for (; pr < npr; ++pr) {
+            const int pa = c0 + 2 * pr * WGP + lp;
+            const int64_t qa = min(pa, last), qb = min(pa + WGP, last);
+            const Row<Q4> ra = load_row<Q4>(vcp + qa * RB);
+            const Row<Q4> rb = load_row<Q4>(vcp + qb * RB);
+            const uint32_t ma = Q4 ? vmp[qa * GPH] : 0u, mb = Q4 ? vmp[qb * GPH] : 0u;
+            vpair(2 * pr, ra, rb, ma, mb);
+        }
+    };
+    if constexpr (MULTI) {
+        for (int c0 = 0; c0 < pos; c0 += chunk) {
+            run_chunk(c0, min(chunk, pos - c0));
+            __syncthreads();            // sS and sMax are rewritten by the next chunk
+        }
+    } else if (pos > 0) {
+        run_chunk(0, pos);
     }
 
-    // the current token: fresh fp16 k, v
-    float kn[32], vn[32];
-    load32h(k_new + b * ld + h * HD + qi * 32, kn);
-    load32h(v_new + b * ld + h * HD + qi * 32, vn);
-    float snew = 0.f;
+    // merge the lanes: row sums (DPP) -> LDS -> one thread per output dim
 #pragma unroll
-    for (int i = 0; i < 32; ++i) snew = fmaf(qv[i], kn[i], snew);
+    for (int i = 0; i < 32; ++i) acc[i] = row_sum<LPP>(acc[i]);
+    fix = row_sum<LPP>(fix);
+    l = row_sum<LPP>(l);
+    if ((lane & 15) < LPP) {
+        const int r = (wv * ROWS + (lane >> 4)) * LPP + qi;
+        float4* dst = reinterpret_cast<float4*>(sRed + r * 32);
 #pragma unroll
-    for (int off = 1; off < LPP; off <<= 1) snew += __shfl_xor(snew, off);
-
-    // merge the slots of the wavefront
-    float M = fmaxf(m, snew);
-#pragma unroll
-    for (int off = LPP; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-    const float f = (m == -INFINITY) ? 0.f : exp2f(m - M);
-    l *= f;
-    accm *= f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] *= f;
-#pragma unroll
-    for (int off = LPP; off < 64; off <<= 1) {
-        l += __shfl_xor(l, off);
-        accm += __shfl_xor(accm, off);
-#pragma unroll
-        for (int i = 0; i < 32; ++i) acc[i] += __shfl_xor(acc[i], off);
+        for (int i = 0; i < 8; ++i)
+            dst[i] = make_float4(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
+        sFix[r] = fix;
+        if (qi == 0) sL[wv * ROWS + (lane >> 4)] = l;
     }
+    __syncthreads();
     const float wn = exp2f(snew - M);
-    const float inv = 1.0f / (l + wn);
-
-    if (slot == 0) {
-        uint32_t o[16];
+    for (int d = threadIdx.x; d < HD; d += NW * 64) {
+        const int dq = d >> 5, e = d & 31;
+        float s = 0.f, L = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const float a0 = (acc[2 * j] + accm + wn * vn[2 * j]) * inv;
-            const float a1 = (acc[2 * j + 1] + accm + wn * vn[2 * j + 1]) * inv;
-            o[j] = (uint32_t)__half_as_ushort(__float2half_rn(a0)) |
-                   ((uint32_t)__half_as_ushort(__float2half_rn(a1)) << 16);
+        for (int r = 0; r < NW * ROWS; ++r) {
+            s += sRed[(r * LPP + dq) * 32 + e] + sFix[r * LPP + dq];
+            L += sL[r];
         }
-        uint4* op = reinterpret_cast<uint4*>(out + b * (int64_t)nh * HD + h * HD + qi * 32);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) op[k] = make_uint4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+        const float vnd = __half2float(v_new[b * ld + h * HD + d]);
+        out[b * (int64_t)nh * HD + h * HD + d] = __float2half_rn((s + wn * vnd) / (L + wn));
     }
 
-    if (fuse) {
-        const int64_t row = head_row0 + pos;
+    // append the current token at row pos (the passes above read rows < pos
+    // only), K then V
+    if (fuse && wv == 0) {
+        const int64_t row = row0 + pos;
         if constexpr (Q4) {
-            uint32_t kmb, vmb;
-            const uint4 kq = quant_half_group(kn, kmb);   // all lanes: shuffles need the full wave
-            const uint4 vq = quant_half_group(vn, vmb);
-            if (slot == 0) {
-                *reinterpret_cast<uint4*>((uint8_t*)kc + row * (HD / 2) + qi * 16) = kq;
-                *reinterpret_cast<uint4*>((uint8_t*)vc + row * (HD / 2) + qi * 16) = vq;
-                if ((qi & 1) == 0) {
-                    *reinterpret_cast<uint32_t*>(km + (row * GPH + g) * 2) = kmb;
-                    *reinterpret_cast<uint32_t*>(vm + (row * GPH + g) * 2) = vmb;
+#pragma unroll 1
+            for (int t = 0; t < 2; ++t) {
+                const __half* src = (t == 0 ? k_new : v_new) + b * ld + h * HD + qi * 32;
+                uint4 x[4];
+                load32p(src, x);
+                uint32_t mbits;
+                const uint4 code = quant_half_group(x, mbits);   // all lanes: shuffles need the full wave
+                if (slot == 0) {
+                    *reinterpret_cast<uint4*>((uint8_t*)(t == 0 ? kc : vc) + row * (HD / 2) + qi * 16) = code;
+                    if ((qi & 1) == 0)
+                        *reinterpret_cast<uint32_t*>((t == 0 ? km : vm) + (row * GPH + g) * 2) = mbits;
                 }
             }
         } else if (slot == 0) {
@@ -320,7 +487,30 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
             for (int k = 0; k < 4; ++k) { kd[k] = ks[k]; vd[k] = vs[k]; }
         }
     }
+
 }
+
+#define FG_ATTN_PARAMS                                                                      \
+    const __half *__restrict__ q, const __half *__restrict__ k_new,                          \
+        const __half *__restrict__ v_new, int64_t ld, void *__restrict__ kc,                 \
+        __half *__restrict__ km, void *__restrict__ vc, __half *__restrict__ vm,             \
+        int32_t lmax, int32_t nh, int32_t pos, int32_t chunk, int fuse, __half *__restrict__ out
+#define FG_ATTN_ARGS q, k_new, v_new, ld, kc, km, vc, vm, lmax, nh, pos, chunk, fuse, out
+
+// history in one chunk: register budget of 6 (4-bit) or 5 (fp16) wavefronts per SIMD
+template <int HD, bool Q4, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(Q4 ? 6 : 5)))
+void attn_decode_kernel(FG_ATTN_PARAMS) {
+    attn_decode_body<HD, Q4, NW, false>(FG_ATTN_ARGS);
+}
+
+// histories longer than one chunk
+template <int HD, bool Q4, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_decode_multi_kernel(FG_ATTN_PARAMS) {
+    attn_decode_body<HD, Q4, NW, true>(FG_ATTN_ARGS);
+}
+#undef FG_ATTN_ARGS
+#undef FG_ATTN_PARAMS
 
 // Store nt positions (t0..t0+nt-1) of nseq sequences (seq0..) into the cache.
 // One wavefront per (sequence, head); lanes as in the attention kernel.
@@ -349,9 +539,9 @@ __global__ __launch_bounds__(256) void kv_store_kernel(const __half* __restrict_
         const __half* vs = v + (bl * nt + tt) * ld + h * HD + qi * 32;
         const int64_t row = head_row0 + t0 + tt;
         if constexpr (Q4) {
-            float kv[32], vv[32];
-            load32h(ks, kv);
-            load32h(vs, vv);
+            uint4 kv[4], vv[4];
+            load32p(ks, kv);
+            load32p(vs, vv);
             uint32_t kmb, vmb;
             const uint4 kq = quant_half_group(kv, kmb);
             const uint4 vq = quant_half_group(vv, vmb);
@@ -403,7 +593,6 @@ int launch_attn_decode(const __half* q, const __half* k_new, const __half* v_new
                        __half* out, hipStream_t st) {
     if (bls == 0) return FG_OK;
     const int64_t units = (int64_t)bls * d->n_heads;
-    const unsigned grid = (unsigned)cdiv(units, 4);
     const bool q4 = kv->fmt == FG_FMT_Q4G64;
     // algorithmic HBM bytes: K and V history (4-bit: codes + meta = 9/16 B per
     // element), the q / k_new / v_new rows, the output, the appended position
@@ -413,15 +602,35 @@ int launch_attn_decode(const __half* q, const __half* k_new, const __half* v_new
                          (fuse ? 2.0 * bls * d->h1 * per_elem : 0.0);
     TraceScope ts(q4 ? TK_ATTN_DECODE_Q4 : TK_ATTN_DECODE_F16, st,
                   4.0 * bls * (pos + 1) * (double)d->h1, bytes);
-#define FG_ATTN(HD_, Q_, U_)                                                                  \
-    attn_decode_kernel<HD_, Q_, U_><<<grid, 256, 0, st>>>(                                    \
-        q, k_new, v_new, ld, kv->k, (__half*)kv->k_meta, kv->v, (__half*)kv->v_meta,          \
-        kv->max_len, d->n_heads, bls, pos, fuse, out)
+    // one wavefront per (sequence, head) when there are enough of them to fill
+    // the chip; otherwise four, splitting the positions
+    const int nw = units >= 2048 ? 1 : 4;
+    const bool multi = pos > kAttnChunk;
+    const int chunk = multi ? kAttnChunk : (int)std::max<int64_t>(cdiv(pos, 64) * 64, 64);
+    const int lpp = d->head_dim / 32;
+    const size_t lds = sizeof(float) * ((size_t)chunk + nw * 4 * lpp * 33 + nw * 4 + nw);
+#define FG_ATTN(HD_, Q_, NW_, MU_)                                                           \
+    (MU_ ? attn_decode_multi_kernel<HD_, Q_, NW_> : attn_decode_kernel<HD_, Q_, NW_>)         \
+        <<<(unsigned)units, NW_ * 64, lds, st>>>(                                            \
+        q, k_new, v_new, ld, kv->k, (__half*)kv->k_meta, kv->v, (__half*)kv->v_meta,         \
+        kv->max_len, d->n_heads, pos, chunk, fuse, out)
+#define FG_ATTN_NW(HD_, Q_, MU_)                        \
+    do {                                                \
+        if (nw == 1) FG_ATTN(HD_, Q_, 1, MU_);          \
+        else FG_ATTN(HD_, Q_, 4, MU_);                  \
+    } while (0)
+#define FG_ATTN_MU(HD_, Q_)                             \
+    do {                                                \
+        if (multi) FG_ATTN_NW(HD_, Q_, true);           \
+        else FG_ATTN_NW(HD_, Q_, false);                \
+    } while (0)
     if (d->head_dim == 128) {
-        if (q4) FG_ATTN(128, true, 4); else FG_ATTN(128, false, 2);
+        if (q4) FG_ATTN_MU(128, true); else FG_ATTN_MU(128, false);
     } else {
-        if (q4) FG_ATTN(64, true, 4); else FG_ATTN(64, false, 2);
+        if (q4) FG_ATTN_MU(64, true); else FG_ATTN_MU(64, false);
     }
+#undef FG_ATTN_MU
+#undef FG_ATTN_NW
 #undef FG_ATTN
     FG_LAUNCHED("attn_decode_kernel");
     return FG_OK;
