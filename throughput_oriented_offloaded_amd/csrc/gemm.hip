@@ -12,7 +12,7 @@
 //
 // Two kernel families:
 //  * decode-shaped contractions (M up to a few hundred rows) run the
-//    pipelined kernel of gemm_pipe.hip;
+//    stream-K pipelined kernel of gemm_sk.hip;
 //  * large-M contractions (the prefill, M = gbs * s) run the tiled kernel
 //    below: 128 x 128 tiles of 2 x 2 waves, k-step 64 double-buffered in LDS
 //    through registers.  MFMA A operand = weight rows (16 n x 32 k), B operand
@@ -267,31 +267,20 @@ using PreF = Cfg<4, 4, 2, 2, false>;
 // Rows up to which the pipelined decode kernel is used.
 constexpr int64_t PIPE_MAX_M = 4 * 144;
 
+// Tiled (prefill-shaped) launch: 128 x 128 tiles, the k range split until the
+// launch has about two workgroups per CU of the 256-CU part (a constant, so
+// the plan and its workspace size depend on the shape only), keeping at least
+// 4 k-steps of 64 per split.
 struct Plan {
-    bool pipe;       // pipelined decode kernel (else the tiled kernel)
-    int MB;          // pipelined kernel: 16-row blocks per M tile
-    int BM, BN;
     int64_t mt, nt;  // tiles
     int S;           // k splits
     int64_t kchunk;
 };
 
-// Split the k range until the launch has about two workgroups per CU of the
-// 256-CU part (a constant, so the plan and its workspace size depend on the
-// shape only), keeping at least 4 k-steps of 64 per split.
 Plan make_plan(int64_t M, int64_t N, int64_t K) {
     Plan pl{};
-    pl.pipe = M <= PIPE_MAX_M;
-    if (pl.pipe) {
-        pl.MB = pipe_mb_for(M);
-        pl.BM = pl.MB * 16;
-        pl.BN = 256;
-    } else {
-        pl.BM = 128;
-        pl.BN = 128;
-    }
-    pl.mt = cdiv(M, pl.BM);
-    pl.nt = cdiv(N, pl.BN);
+    pl.mt = cdiv(M, 128);
+    pl.nt = cdiv(N, 128);
     const int64_t ksteps = K / 64;
     const int64_t tiles = pl.mt * pl.nt;
     int S = 1;
@@ -316,6 +305,10 @@ int run_tiled(const Params& p, const Plan& pl, hipStream_t st) {
 }  // namespace gemm
 
 size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t) {
+    if (M <= gemm::PIPE_MAX_M) {
+        const gemm::SkSched sc = gemm::sk_schedule(M, N, K);
+        return sc.slots > 1 ? (size_t)sc.slots * M * N * sizeof(float) : 0;
+    }
     const gemm::Plan pl = gemm::make_plan(M, N, K);
     return pl.S > 1 ? (size_t)pl.S * M * N * sizeof(float) : 0;
 }
@@ -324,32 +317,45 @@ int launch_linear(const LinearArgs& a, hipStream_t st) {
     using namespace gemm;
     if (a.M == 0 || a.N == 0) return FG_OK;
     const bool q4 = a.fmt == FG_FMT_Q4G64;
-    const Plan pl = make_plan(a.M, a.N, a.K);
     Params p{};
     p.x = a.x; p.M = a.M; p.K = a.K; p.ldx = a.ldx;
     p.w = a.w; p.meta = a.meta; p.N = a.N;
     p.bias = a.bias; p.act = a.act; p.residual = a.residual;
     p.y = a.y; p.ldy = a.ldy;
-    p.kchunk = pl.kchunk;
     p.part = nullptr;
-    if (pl.S > 1) {
-        const size_t need = (size_t)pl.S * a.M * a.N * sizeof(float);
+    // algorithmic work: 2MNK flops; weights once, activations in, outputs out
+    const double Md = (double)p.M, Nd = (double)p.N, Kd = (double)p.K;
+    const double wbytes = q4 ? Nd * Kd / 2 + Nd / 64 * Kd * 4 : Nd * Kd * 2;
+    const double gbytes = wbytes + 2 * Md * Kd + 2 * Md * Nd * (p.residual ? 2 : 1) + (p.bias ? 2 * Nd : 0);
+    auto need_ws = [&](size_t need) -> int {
         if (!a.ws || a.ws_bytes < need)
             return set_error(FG_ERR_CAPACITY, "linear needs %zu workspace bytes, got %zu", need,
                              a.ws ? a.ws_bytes : (size_t)0);
         p.part = static_cast<float*>(a.ws);
+        return FG_OK;
+    };
+
+    if (a.M <= PIPE_MAX_M) {
+        const SkSched sc = sk_schedule(a.M, a.N, a.K);
+        if (sc.slots > 1) FG_TRY(need_ws((size_t)sc.slots * a.M * a.N * sizeof(float)));
+        {
+            TraceScope ts(q4 ? TK_GEMM_Q4 : TK_GEMM_F16, st, 2 * Md * Nd * Kd, gbytes);
+            FG_TRY(launch_sk(p, sc, q4, st));
+        }
+        if (sc.slots > 1) {
+            TraceScope ts(TK_SPLITK_REDUCE, st, 0.0,
+                          Md * Nd * (4.0 * sc.slots + 2.0 * (a.residual ? 2 : 1)));
+            FG_TRY(launch_sk_reduce(p, sc, st));
+        }
+        return FG_OK;
     }
+
+    const Plan pl = make_plan(a.M, a.N, a.K);
+    p.kchunk = pl.kchunk;
+    if (pl.S > 1) FG_TRY(need_ws((size_t)pl.S * a.M * a.N * sizeof(float)));
     {
-        // algorithmic work: 2MNK flops; weights once, activations in, outputs out
-        const double M = (double)p.M, N = (double)p.N, K = (double)p.K;
-        const double wbytes = q4 ? N * K / 2 + N / 64 * K * 4 : N * K * 2;
-        const double bytes = wbytes + 2 * M * K + 2 * M * N * (p.residual ? 2 : 1) + (p.bias ? 2 * N : 0);
-        TraceScope ts(q4 ? TK_GEMM_Q4 : TK_GEMM_F16, st, 2 * M * N * K, bytes);
-        int rc;
-        if (pl.pipe)
-            rc = launch_pipe(p, pl.MB, q4, pl.S, st);
-        else
-            rc = q4 ? run_tiled<PreQ>(p, pl, st) : run_tiled<PreF>(p, pl, st);
+        TraceScope ts(q4 ? TK_GEMM_Q4 : TK_GEMM_F16, st, 2 * Md * Nd * Kd, gbytes);
+        const int rc = q4 ? run_tiled<PreQ>(p, pl, st) : run_tiled<PreF>(p, pl, st);
         if (rc != FG_OK) return rc;
     }
     if (pl.S > 1) {

@@ -1,4 +1,4 @@
-// Pieces shared by the projection GEMM kernels (gemm.hip, gemm_pipe.hip).
+// Pieces shared by the projection GEMM kernels (gemm.hip, gemm_sk.hip).
 #pragma once
 
 #include "fg_internal.h"
@@ -65,13 +65,9 @@ __device__ __forceinline__ h8 dequant8(uint2 c, uint32_t sh, const uint4& mn, co
     return out;
 }
 
-// Epilogue of one lane: 4 consecutive output columns n..n+3 of row m.
-__device__ __forceinline__ void store4(const Params& p, int64_t m, int64_t n, const f4& v, int z) {
-    if (p.part) {
-        float* dst = p.part + ((int64_t)z * p.M + m) * p.N + n;
-        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-        return;
-    }
+// Epilogue of one lane: 4 consecutive output columns n..n+3 of row m, with
+// bias, ReLU and residual, written as fp16.
+__device__ __forceinline__ void store4_final(const Params& p, int64_t m, int64_t n, const f4& v) {
     float o[4] = {v[0], v[1], v[2], v[3]};
     if (p.bias) {
         const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n);
@@ -91,11 +87,51 @@ __device__ __forceinline__ void store4(const Params& p, int64_t m, int64_t n, co
         make_uint2(pack_h2(o[0], o[1]), pack_h2(o[2], o[3]));
 }
 
-// Launch of the pipelined decode-shaped kernel (gemm_pipe.hip): M tiles of
-// MB*16 rows, N tiles of 256, `S` k-splits (p.kchunk set by the caller).
-int launch_pipe(const Params& p, int MB, bool q4, int S, hipStream_t st);
-// LDS tile of the pipelined kernel: rows per M tile for a given M.
-int pipe_mb_for(int64_t M);
+// Same, or the fp32 partial of k-split z when the contraction is split.
+__device__ __forceinline__ void store4(const Params& p, int64_t m, int64_t n, const f4& v, int z) {
+    if (p.part) {
+        float* dst = p.part + ((int64_t)z * p.M + m) * p.N + n;
+        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        return;
+    }
+    store4_final(p, m, n, v);
+}
+
+// s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory
+// operations are outstanding / until every LDS operation has completed
+constexpr int vmcnt_wait(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+constexpr int LGKM_ZERO = 15 | (3 << 14) | (7 << 4);
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane.
+// The LDS base travels in M0 (wave-uniform).
+__device__ __forceinline__ void dma16(const void* g, const void* lds) {
+    const uint32_t l = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)lds);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(g)
+                 : "memory", "m0");
+}
+// Same, addressed as a wave-uniform 64-bit base (SGPRs) plus a 32-bit
+// per-lane byte offset.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, const void* lds) {
+    const uint32_t l = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)lds);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(l), "v"(voff), "s"(base)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Stream-K schedule of the decode-shaped kernel (gemm_sk.hip): T = tiles x nk
+// iterations (tile, 64-wide k-step) split evenly over G workgroups.
+constexpr int kSkGroups = 256;   // one workgroup per CU of the 256-CU part
+struct SkSched {
+    int64_t T, G, nk;     // iterations, workgroups, k-steps per tile
+    int64_t ntn, bm, bn;  // N tiles, tile rows, tile columns
+    int64_t slots;        // partial slots per output element (1: none needed)
+};
+SkSched sk_schedule(int64_t M, int64_t N, int64_t K);
+int launch_sk(const Params& p, const SkSched& sc, bool q4, hipStream_t st);
+int launch_sk_reduce(const Params& p, const SkSched& sc, hipStream_t st);
+
 
 }  // namespace gemm
 }  // namespace fg

@@ -1,0 +1,493 @@
+// Decode-shaped projection GEMM (M = bls rows, a few hundred at most):
+// y = act(x W^T + bias) + residual with W in fp16 or in the group-wise 4-bit
+// format, on a stream-K schedule.
+//
+// Why this shape of kernel (gfx950 measurements):
+//  * MFMA issue from a single wavefront per SIMD reaches about half of the
+//    matrix-core peak; two wavefronts per SIMD reach about 80%.  A workgroup
+//    is 8 wavefronts: 4 columns of 64 weight rows (one 4-bit group each) times
+//    2 k-halves.  The two wavefronts of a SIMD own the same outputs and the two
+//    32-wide halves of every 64-wide k-step; their fp32 accumulators are added
+//    through LDS at the end.  Every m row of the tile (up to 144) stays in the
+//    tile, so each dequantized weight fragment feeds MB MFMAs.
+//  * Dequantization runs on the fp32 VALU path: nibble -> v_cvt_f32_ubyte,
+//    w = fma(q, scale, min) (the codec's multiply-then-add: q * scale is exact
+//    in binary32, so the one rounding of the FMA equals the rounding of the
+//    add), v_cvt_pk_f16_f32 into the MFMA operand.  Packed fp16 arithmetic
+//    next to MFMA issue costs far more matrix-core throughput than these.
+//  * Global -> LDS traffic uses direct-to-LDS loads (global_load_lds_dwordx4)
+//    into an NS-deep ring of stage buffers [meta | X tile | weight tile], with
+//    explicit s_waitcnt vmcnt + s_barrier publication and XOR swizzles that
+//    keep fragment reads free of bank conflicts.
+//  * Software pipelining across k-steps: the codes, metadata and activation
+//    fragments of step i+1 are read from LDS while the last MFMAs of step i
+//    issue, and each weight fragment is dequantized while the MFMAs of the
+//    previous fragment run.
+//  * Stream-K: exactly G workgroups, each taking an equal contiguous share of
+//    the (tile, k-step) iterations, so no tail of partly filled rounds.  A tile
+//    covered by one workgroup is written with its epilogue; a tile shared by
+//    several leaves fp32 partials in per-segment slots, summed in segment order
+//    (deterministic) by sk_reduce_kernel.
+#include "gemm_common.h"
+
+namespace fg {
+namespace gemm {
+namespace {
+
+template <int MB_, bool Q4_, int NS_>
+struct SK {
+    static constexpr int MB = MB_, NS = NS_, WN = 4, NW = 8;
+    static constexpr bool Q4 = Q4_;
+    static constexpr int BM = MB * 16, BN = WN * 64, BK = 64, NT = NW * 64;
+    static constexpr int M_INS = Q4 ? 1 : 0;            // (min, scale) rows of 4 groups: 1 KB
+    static constexpr int X_INS = BM / 8;                 // activation tile: BM rows x 128 B
+    static constexpr int C_INS = Q4 ? BN / 32 : BN / 8;  // 4-bit codes or fp16 weight rows
+    static constexpr int INS = M_INS + X_INS + C_INS;    // 1 KB load instructions per stage
+    static constexpr int LWL = INS / NW;                 // loads per wavefront ...
+    static constexpr int XW = INS % NW;                  // ... plus one for the first XW
+    static constexpr int LWH = LWL + (XW ? 1 : 0);
+    static constexpr int M_BYTES = M_INS * 1024;
+    static constexpr int X_BYTES = BM * 128;
+    static constexpr int STAGE = INS * 1024;
+    // k-half merge: 8 regions (column x 2 fragments) of MB KB in the stage buffers
+    static constexpr int PER_BUF = STAGE / (MB * 1024);
+    static_assert(PER_BUF >= 1 && (8 + PER_BUF - 1) / PER_BUF <= NS, "merge space");
+    static_assert(LWH * (NS - 1) <= 63, "vmcnt range");
+};
+
+__device__ __forceinline__ float lo16(uint32_t w) {
+    return __half2float(__ushort_as_half((unsigned short)(w & 0xffffu)));
+}
+__device__ __forceinline__ float hi16(uint32_t w) {
+    return __half2float(__ushort_as_half((unsigned short)(w >> 16)));
+}
+// byte J of a dword as float (v_cvt_f32_ubyteJ)
+template <int J>
+__device__ __forceinline__ float ubf(uint32_t w) {
+    return (float)((w >> (8 * J)) & 0xffu);
+}
+
+// An empty register constraint: the value is materialised in a VGPR as is, so
+// the compiler neither re-derives it nor fuses its producer into a consumer.
+template <class T>
+__device__ __forceinline__ void opaque(T& v) {
+    asm volatile("" : "+v"(v));
+}
+
+// Two fp32 values -> packed fp16 pair, round to nearest even.  Written as the
+// instruction itself so the FMA producing the inputs stays an fp32 FMA (the
+// compiler would otherwise fold it into a mixed-precision FMA).
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+    uint32_t r;
+    asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// workgroup holding iteration x of T split over G: ceil((x + 1) G / T) - 1
+__device__ __host__ __forceinline__ int64_t sk_owner(int64_t x, int64_t T, int64_t G) {
+    return ((x + 1) * G + T - 1) / T - 1;
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void sk_kernel(Params p, SkSched sc) {
+    __shared__ __align__(16) unsigned char sb0[C::STAGE];
+    __shared__ __align__(16) unsigned char sb1[C::STAGE];
+    __shared__ __align__(16) unsigned char sb2[C::NS > 2 ? C::STAGE : 16];
+    __shared__ __align__(16) unsigned char sb3[C::NS > 3 ? C::STAGE : 16];
+    __shared__ __align__(16) unsigned char sb4[C::NS > 4 ? C::STAGE : 16];
+    auto buf = [&](int s) -> unsigned char* {
+        return s == 0 ? sb0 : (s == 1 ? sb1 : (s == 2 ? sb2 : (s == 3 ? sb3 : sb4)));
+    };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kh = wave >> 2, wc = wave & 3;      // k-half, weight column
+    const bool hiw = wave < C::XW;                // issues LWH loads per stage
+    const int r16 = lane & 15, q = lane >> 4;
+    const uint32_t shn = (uint32_t)(r16 & 1) * 4u;   // nibble of this lane's weight row
+    const int64_t g = blockIdx.x;
+    const int64_t it_beg = g * sc.T / sc.G, it_end = (g + 1) * sc.T / sc.G;
+
+    for (int64_t it = it_beg; it < it_end;) {
+        const int64_t tile = it / sc.nk;
+        const int kb = (int)(it - tile * sc.nk);
+        const int ke = (int)(min(it_end, (tile + 1) * sc.nk) - tile * sc.nk);
+        it = tile * sc.nk + ke;
+        const int64_t tm = tile / sc.ntn, tn = tile - tm * sc.ntn;
+        const int64_t n0 = tn * C::BN, m0 = tm * C::BM;
+        const int nk = ke - kb;
+        const int64_t kbeg = (int64_t)kb * C::BK;
+
+        f4 acc[4][C::MB];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < C::MB; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+        // load slots of this wave: a wave-uniform base (tile origin at kbeg)
+        // and a per-lane byte offset inside the tile; rows past M or N are
+        // clamped (their results are never stored)
+        const char* sbase[C::LWH];
+        uint32_t voff[C::LWH];
+        int ksh[C::LWH];
+#pragma unroll
+        for (int i = 0; i < C::LWH; ++i) {
+            const int j = min(wave + i * C::NW, C::INS - 1);
+            if (j < C::M_INS) {
+                const int c = j * 64 + lane;
+                const int row = c >> 3, col = c & 7;            // row = group * 2 + (min | scale)
+                const int64_t gg = min(n0 / 64 + (row >> 1), p.N / 64 - 1) - n0 / 64;
+                sbase[i] = (const char*)(p.meta + (n0 / 64) * 2 * p.K + kbeg);
+                voff[i] = (uint32_t)(((gg * 2 + (row & 1)) * p.K + col * 8) * 2);
+                ksh[i] = 1;
+            } else if (j < C::M_INS + C::X_INS) {
+                const int c = (j - C::M_INS) * 64 + lane;
+                const int row = c >> 3, kc = (c & 7) ^ (row & 7);
+                const int64_t gr = min(m0 + row, p.M - 1) - m0;
+                sbase[i] = (const char*)(p.x + m0 * p.ldx + kbeg);
+                voff[i] = (uint32_t)((gr * p.ldx + kc * 8) * 2);
+                ksh[i] = 1;
+            } else {
+                const int c = (j - C::M_INS - C::X_INS) * 64 + lane;
+                if constexpr (C::Q4) {
+                    const int row = c >> 2, ch = (c & 3) ^ ((row >> 1) & 3);
+                    const int64_t gr = min(n0 / 2 + row, p.N / 2 - 1) - n0 / 2;
+                    sbase[i] = (const char*)p.w + (n0 / 2) * p.K + kbeg;
+                    voff[i] = (uint32_t)(gr * p.K + ch * 16);
+                    ksh[i] = 0;
+                } else {
+                    const int row = c >> 3, kc = (c & 7) ^ (row & 7);
+                    const int64_t gr = min(n0 + row, p.N - 1) - n0;
+                    sbase[i] = (const char*)((const __half*)p.w + n0 * p.K + kbeg);
+                    voff[i] = (uint32_t)((gr * p.K + kc * 8) * 2);
+                    ksh[i] = 1;
+                }
+            }
+            // wave-uniform: keep base and shift in scalar registers
+            // (readfirstlane returns a signed int: widen through uint32_t)
+            const uint64_t bb = (uint64_t)(uintptr_t)sbase[i];
+            const uint32_t bhi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(bb >> 32));
+            const uint32_t blo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bb);
+            sbase[i] = (const char*)(uintptr_t)(((uint64_t)bhi << 32) | (uint64_t)blo);
+            ksh[i] = __builtin_amdgcn_readfirstlane(ksh[i]);
+        }
+        // stages past the end reload the last one, so every stage issues the
+        // same number of loads per wave (the vmcnt arithmetic holds)
+        auto issue = [&](unsigned char* base, int ks) {
+            const int64_t koff = (int64_t)min(ks, nk - 1) * C::BK;
+#pragma unroll
+            for (int i = 0; i < C::LWH; ++i) {
+                if (i < C::LWL || hiw) {
+                    const int j = wave + i * C::NW;
+                    dma16s(sbase[i] + (koff << ksh[i]), voff[i], base + j * 1024);
+                }
+            }
+        };
+
+        auto read_x = [&](const unsigned char* base, int mb) -> h8 {
+            const int row = mb * 16 + r16;
+            const int kc = (kh * 4 + q) ^ (row & 7);
+            return *reinterpret_cast<const h8*>(base + C::M_BYTES + (row * 8 + kc) * 16);
+        };
+        // weight fragment source of column block nb: 4-bit codes (8 k of one
+        // row, one nibble each) or fp16 rows
+        auto read_c = [&](const unsigned char* base, int nb) -> uint2 {
+            const int nl = wc * 64 + nb * 16 + r16;
+            const int row = nl >> 1, ch = (kh * 2 + (q >> 1)) ^ ((row >> 1) & 3);
+            return *reinterpret_cast<const uint2*>(base + C::M_BYTES + C::X_BYTES + (row * 4 + ch) * 16 +
+                                                   (q & 1) * 8);
+        };
+        auto read_w16 = [&](const unsigned char* base, int nb) -> h8 {
+            const int nl = wc * 64 + nb * 16 + r16;
+            const int kc = (kh * 4 + q) ^ (nl & 7);
+            return *reinterpret_cast<const h8*>(base + C::X_BYTES + (nl * 8 + kc) * 16);
+        };
+        float mnf[8], scf[8];
+        auto load_meta = [&](const unsigned char* base, uint4& mn, uint4& sc4) {
+            mn = *reinterpret_cast<const uint4*>(base + (wc * 2 + 0) * 128 + (kh * 32 + q * 8) * 2);
+            sc4 = *reinterpret_cast<const uint4*>(base + (wc * 2 + 1) * 128 + (kh * 32 + q * 8) * 2);
+        };
+        auto cvt_meta = [&](const uint4& mn, const uint4& sc4) {
+            const uint32_t a[4] = {mn.x, mn.y, mn.z, mn.w}, s4[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                mnf[2 * i] = lo16(a[i]);
+                mnf[2 * i + 1] = hi16(a[i]);
+                scf[2 * i] = lo16(s4[i]);
+                scf[2 * i + 1] = hi16(s4[i]);
+            }
+            // keep them as fp32 registers (no fusion into mixed-precision FMAs)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) opaque(mnf[i]), opaque(scf[i]);
+        };
+        auto dequant = [&](uint2 c) -> h8 {
+            uint32_t d0 = (c.x >> shn) & 0x0f0f0f0fu, d1 = (c.y >> shn) & 0x0f0f0f0fu;
+            opaque(d0), opaque(d1);   // one v_cvt_f32_ubyteN per code, no re-extraction
+            float w[8];
+            w[0] = __builtin_fmaf(ubf<0>(d0), scf[0], mnf[0]);
+            w[1] = __builtin_fmaf(ubf<1>(d0), scf[1], mnf[1]);
+            w[2] = __builtin_fmaf(ubf<2>(d0), scf[2], mnf[2]);
+            w[3] = __builtin_fmaf(ubf<3>(d0), scf[3], mnf[3]);
+            w[4] = __builtin_fmaf(ubf<0>(d1), scf[4], mnf[4]);
+            w[5] = __builtin_fmaf(ubf<1>(d1), scf[5], mnf[5]);
+            w[6] = __builtin_fmaf(ubf<2>(d1), scf[6], mnf[6]);
+            w[7] = __builtin_fmaf(ubf<3>(d1), scf[7], mnf[7]);
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = pk_f16(w[2 * i], w[2 * i + 1]);
+            return __builtin_bit_cast(h8, make_uint4(o[0], o[1], o[2], o[3]));
+        };
+        // interleave MFMAs with the VALU work of the same region (the
+        // compiler would otherwise issue long VALU runs, then MFMA bursts)
+        auto pattern_mv = [&]() {
+#pragma unroll
+            for (int mb = 0; mb < C::MB; ++mb) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // 3 VALU
+            }
+        };
+        // last fragment: the next step's codes / metadata were just requested,
+        // so the first MFMAs carry only activation-fragment reads and the
+        // VALU work (metadata conversion, first dequantization) follows
+        auto pattern_mdv = [&]() {
+#pragma unroll
+            for (int mb = 0; mb < C::MB; ++mb) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+                if (mb >= 4) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            }
+        };
+
+        h8 xf[C::MB];
+        uint2 cr[4];
+        h8 wf16[4];
+        h8 wcur;
+        // prologue: NS stages in flight; publish stage 0 and read its fragments
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s) issue(buf(s), s);
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(C::LWL * (C::NS - 1)));
+        __builtin_amdgcn_s_barrier();
+        {
+            const unsigned char* b0 = buf(0);
+            if constexpr (C::Q4) {
+                uint4 mn, sc4;
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) cr[nb] = read_c(b0, nb);
+                load_meta(b0, mn, sc4);
+                cvt_meta(mn, sc4);
+                wcur = dequant(cr[0]);
+            } else {
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) wf16[nb] = read_w16(b0, nb);
+                wcur = wf16[0];
+            }
+#pragma unroll
+            for (int mb = 0; mb < C::MB; ++mb) xf[mb] = read_x(b0, mb);
+        }
+
+        // each k-step enters with its activation fragments, codes / weights,
+        // metadata and first weight fragment in registers
+        for (int kt = 0; kt < nk; kt += C::NS) {
+#pragma unroll
+            for (int s = 0; s < C::NS; ++s) {
+                const int i = kt + s;
+                if (i < nk) {
+                    const unsigned char* nxt = buf((s + 1) % C::NS);
+                    uint4 mn_n, sc_n;
+#pragma unroll
+                    for (int nb = 0; nb < 3; ++nb) {
+                        const h8 wnext = C::Q4 ? dequant(cr[nb + 1]) : wf16[nb + 1];
+#pragma unroll
+                        for (int mb = 0; mb < C::MB; ++mb)
+                            acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wcur, xf[mb], acc[nb][mb], 0, 0, 0);
+                        if constexpr (C::Q4) pattern_mv();
+                        wcur = wnext;
+                    }
+                    // stage i+1 has landed for every wave (the wait is the one
+                    // of the waves with fewer loads: stronger for the others),
+                    // and no wave still reads stage i: refill its buffer with
+                    // stage i+NS and read the next codes / metadata / weights
+                    __builtin_amdgcn_s_waitcnt(vmcnt_wait(C::LWL * (C::NS - 2)));
+                    __builtin_amdgcn_s_waitcnt(LGKM_ZERO);
+                    __builtin_amdgcn_s_barrier();
+                    issue(buf(s), i + C::NS);
+                    if constexpr (C::Q4) {
+#pragma unroll
+                        for (int nb = 0; nb < 4; ++nb) cr[nb] = read_c(nxt, nb);
+                        load_meta(nxt, mn_n, sc_n);
+                    } else {
+#pragma unroll
+                        for (int nb = 0; nb < 3; ++nb) wf16[nb] = read_w16(nxt, nb);
+                    }
+                    // last fragment: each activation fragment is replaced by
+                    // the next step's right after its last use; the next
+                    // step's metadata and first weight fragment are prepared
+                    h8 w0n;
+                    if constexpr (C::Q4) {
+                        cvt_meta(mn_n, sc_n);
+                        w0n = dequant(cr[0]);
+                    } else {
+                        w0n = wf16[0];
+                    }
+#pragma unroll
+                    for (int mb = 0; mb < C::MB; ++mb) {
+                        acc[3][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wcur, xf[mb], acc[3][mb], 0, 0, 0);
+                        xf[mb] = read_x(nxt, mb);
+                    }
+                    if constexpr (C::Q4) pattern_mdv();
+                    if constexpr (!C::Q4) wf16[3] = read_w16(nxt, 3);
+                    wcur = w0n;
+                }
+            }
+        }
+        // no load may still be writing LDS when the buffers are reused
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+        __builtin_amdgcn_s_waitcnt(LGKM_ZERO);
+        __builtin_amdgcn_s_barrier();
+
+        // add the two k-halves (kh = 1 -> LDS -> kh = 0), two fragments per round
+        const int64_t gf = sk_owner(tile * sc.nk, sc.T, sc.G);
+        const int64_t gl = sk_owner((tile + 1) * sc.nk - 1, sc.T, sc.G);
+        const bool full = gf == gl;
+        const int slot = (int)(g - gf);
+        const int nq = q * 4;
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int r = wc * 2 + j;
+                float4* reg = reinterpret_cast<float4*>(buf(r / C::PER_BUF) + (r % C::PER_BUF) * C::MB * 1024);
+                const int nb = rd * 2 + j;
+                if (kh == 1) {
+#pragma unroll
+                    for (int mb = 0; mb < C::MB; ++mb)
+                        reg[mb * 64 + lane] = make_float4(acc[nb][mb][0], acc[nb][mb][1], acc[nb][mb][2], acc[nb][mb][3]);
+                }
+            }
+            __syncthreads();
+            if (kh == 0) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int r = wc * 2 + j;
+                    const float4* reg = reinterpret_cast<const float4*>(buf(r / C::PER_BUF) + (r % C::PER_BUF) * C::MB * 1024);
+                    const int nb = rd * 2 + j;
+                    const int64_t n = n0 + wc * 64 + nb * 16 + nq;
+#pragma unroll
+                    for (int mb = 0; mb < C::MB; ++mb) {
+                        const float4 o = reg[mb * 64 + lane];
+                        f4 v = acc[nb][mb];
+                        v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
+                        const int64_t m = m0 + mb * 16 + r16;
+                        if (m < p.M && n < p.N) {
+                            if (full) {
+                                store4_final(p, m, n, v);
+                            } else {
+                                float* dst = p.part + ((int64_t)slot * p.M + m) * p.N + n;
+                                *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+                            }
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// Sum the per-segment partials of shared tiles in segment order, then bias /
+// ReLU / residual.  Tiles written whole by one workgroup are skipped.
+__global__ __launch_bounds__(256) void sk_reduce_kernel(Params p, SkSched sc) {
+    const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;   // element (m, n..n+3)
+    if (idx >= p.M * p.N) return;
+    const int64_t m = idx / p.N, n = idx % p.N;
+    const int64_t tile = (m / sc.bm) * sc.ntn + n / sc.bn;
+    const int64_t gf = sk_owner(tile * sc.nk, sc.T, sc.G);
+    const int64_t gl = sk_owner((tile + 1) * sc.nk - 1, sc.T, sc.G);
+    if (gf == gl) return;
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t s = 0; s <= gl - gf; ++s) {
+        const float4 v = *reinterpret_cast<const float4*>(p.part + (s * p.M + m) * p.N + n);
+        o[0] += v.x; o[1] += v.y; o[2] += v.z; o[3] += v.w;
+    }
+    if (p.bias) {
+        const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n);
+        o[0] += h2f(bb.x); o[1] += h2f(bb.x >> 16);
+        o[2] += h2f(bb.y); o[3] += h2f(bb.y >> 16);
+    }
+    if (p.act == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = fmaxf(o[i], 0.f);
+    }
+    if (p.residual) {
+        const uint2 rr = *reinterpret_cast<const uint2*>(p.residual + m * p.ldy + n);
+        o[0] += h2f(rr.x); o[1] += h2f(rr.x >> 16);
+        o[2] += h2f(rr.y); o[3] += h2f(rr.y >> 16);
+    }
+    *reinterpret_cast<uint2*>(p.y + m * p.ldy + n) = make_uint2(pack_h2(o[0], o[1]), pack_h2(o[2], o[3]));
+}
+
+template <class C>
+int run(const Params& p, const SkSched& sc, hipStream_t st) {
+    sk_kernel<C><<<(unsigned)sc.G, C::NT, 0, st>>>(p, sc);
+    FG_LAUNCHED("sk_kernel");
+    return FG_OK;
+}
+
+}  // namespace
+
+// 16-row blocks per M tile: every row of a decode block stays in one tile
+// (up to 144 rows); 128-row tiles when they pad less (e.g. M = 256).
+int sk_mb_for(int64_t M) {
+    if (M <= 16) return 1;
+    if (M <= 32) return 2;
+    if (M <= 64) return 4;
+    if (M <= 128) return 8;
+    return cdiv(M, 128) * 128 < cdiv(M, 144) * 144 ? 8 : 9;
+}
+
+SkSched sk_schedule(int64_t M, int64_t N, int64_t K) {
+    SkSched sc{};
+    sc.bm = sk_mb_for(M) * 16;
+    sc.bn = 256;
+    sc.ntn = cdiv(N, sc.bn);
+    const int64_t tiles = cdiv(M, sc.bm) * sc.ntn;
+    sc.nk = K / 64;
+    sc.T = tiles * sc.nk;
+    // one workgroup per CU of the 256-CU part (a constant, so the schedule and
+    // its workspace depend on the shape only), at least 4 k-steps each
+    sc.G = std::max<int64_t>(1, std::min<int64_t>(kSkGroups, sc.T / 4));
+    // most segments any tile is cut into (1 when every workgroup covers whole tiles)
+    const int64_t per = sc.T / sc.G;   // each workgroup takes per or per + 1 iterations
+    sc.slots = (sc.T % sc.G == 0 && per % sc.nk == 0) ? 1 : cdiv(sc.nk, per) + 1;
+    return sc;
+}
+
+int launch_sk(const Params& p, const SkSched& sc, bool q4, hipStream_t st) {
+    const int MB = (int)(sc.bm / 16);
+    if (q4) {
+        switch (MB) {
+            case 1: return run<SK<1, true, 5>>(p, sc, st);
+            case 2: return run<SK<2, true, 5>>(p, sc, st);
+            case 4: return run<SK<4, true, 5>>(p, sc, st);
+            case 8: return run<SK<8, true, 5>>(p, sc, st);
+            default: return run<SK<9, true, 5>>(p, sc, st);
+        }
+    }
+    switch (MB) {
+        case 1: return run<SK<1, false, 3>>(p, sc, st);
+        case 2: return run<SK<2, false, 3>>(p, sc, st);
+        case 4: return run<SK<4, false, 3>>(p, sc, st);
+        case 8: return run<SK<8, false, 3>>(p, sc, st);
+        default: return run<SK<9, false, 3>>(p, sc, st);
+    }
+}
+
+int launch_sk_reduce(const Params& p, const SkSched& sc, hipStream_t st) {
+    const int64_t n4 = p.M * p.N / 4;
+    sk_reduce_kernel<<<(unsigned)cdiv(n4, 256), 256, 0, st>>>(p, sc);
+    FG_LAUNCHED("sk_reduce_kernel");
+    return FG_OK;
+}
+
+}  // namespace gemm
+}  // namespace fg
