@@ -221,6 +221,65 @@ int fg_layer_decode_block(const fg_dims* d, const fg_layer_w* w, void* x, int32_
  * (decode: rows = bls; prefill: rows = gbs * s). */
 size_t fg_workspace_bytes(const fg_dims* d, int64_t rows, int32_t fmt_w);
 
+/* ------------------------------------------------------ block schedule */
+/*
+ * Every layer of one pass, in block order ([P2] "一个层级流水的伪代码":
+ * token step outermost, then layers, then the block's GPU batches):
+ * fg_model_prefill runs fg_layer_prefill for layers 0..n_layers-1,
+ * fg_model_decode_step runs fg_layer_decode_block for them.  w and kv are
+ * arrays of n_layers; the other arguments are those of the per-layer calls.
+ *
+ * Weight tiering ([P2] "三条关键数据通路如何重叠": the next layer's
+ * weights are prefetched while the current layer computes; [P1] §6.4 CPU
+ * weights in pinned memory moved by load_weight).  With tier != NULL, layer j
+ * with tier[j].qk_host != NULL keeps half of its fp16 weights in pinned host
+ * memory (fmt must be FG_FMT_F16):
+ *   qk_host: pinned host fp16 [2*h1, h1]  = the W_Q, W_K rows of W_qkv;
+ *   v_dev:   device fp16 [h1, h1]         = the W_V rows of W_qkv;
+ *   w1_host: pinned host fp16 [h2, h1]    = W_1;
+ * that layer's w->w_qkv and w->w_1 are then not read.  Before the layer runs,
+ * [W_Q; W_K] and W_1 are copied host -> device and W_V device -> device into
+ * one of the two stage buffers of `sc`, on copy_stream, ordered by events:
+ * the copy of a tiered layer is issued while the tiered layer before it
+ * computes, and waits until the layer two tiered layers back has released
+ * its buffer.  copy_stream must differ from stream (both default priority).
+ * flags (decode and prefill):
+ *   FG_SCHED_FIRST_STAGED  the first tiered layer was already staged by the
+ *                          previous call (issued with FG_SCHED_STAGE_NEXT);
+ *   FG_SCHED_STAGE_NEXT    after the last layer, stage the first tiered layer
+ *                          for the next call.
+ * Without tiering (tier == NULL) sc, copy_stream and flags are ignored and
+ * may be NULL / 0.  The stage buffers are owned by the caller and must not be
+ * touched while a call's work is in flight.
+ */
+enum { FG_SCHED_FIRST_STAGED = 1, FG_SCHED_STAGE_NEXT = 2 };
+
+typedef struct {
+    const void* qk_host;
+    const void* v_dev;
+    const void* w1_host;
+} fg_tier_w;
+
+typedef struct fg_sched fg_sched;   /* opaque: stage buffers + copy events */
+
+/* Bytes of ONE stage buffer for tiered layers of shape d: fp16 W_qkv
+ * [3*h1, h1] followed (256-byte aligned) by fp16 W_1 [h2, h1]. */
+size_t fg_stage_bytes(const fg_dims* d);
+/* stage: caller-owned device memory of 2 * stage_bytes (two buffers), with
+ * stage_bytes >= fg_stage_bytes of every shape it will serve.  Creates the
+ * copy / release events on the current device (host-side allocation, once). */
+int fg_sched_create(fg_sched** out, void* stage, size_t stage_bytes);
+int fg_sched_destroy(fg_sched* sc);
+
+int fg_model_prefill(fg_sched* sc, const fg_dims* d, int32_t n_layers, const fg_layer_w* w,
+                     const fg_tier_w* tier, const fg_kv* kv, void* x, int32_t gbs, int32_t nb,
+                     int32_t s, void* ws, size_t ws_bytes, void* stream, void* copy_stream,
+                     int32_t flags);
+int fg_model_decode_step(fg_sched* sc, const fg_dims* d, int32_t n_layers, const fg_layer_w* w,
+                         const fg_tier_w* tier, const fg_kv* kv, void* x, int32_t gbs,
+                         int32_t nb, int32_t pos, void* ws, size_t ws_bytes, void* stream,
+                         void* copy_stream, int32_t flags);
+
 /* --------------------------------------------------------------- sizes */
 /* Bytes of the six layer matrices of n_layers layers ([P2]: M_W =
  * l (8 h1^2 + 4 h1 h2) in fp16; 4-bit: codes + 4 bytes of meta per 64). */

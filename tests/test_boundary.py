@@ -139,3 +139,42 @@ def test_workspace_grows_with_rows(L):
     b = L.fg_workspace_bytes(d, 48 * 512, 1)
     assert 0 < a < b
     assert L.fg_linear_workspace_bytes(144, 12288, 49152) % 4 == 0
+
+
+def test_stage_bytes_closed_form(L):
+    for h1, h2 in ((768, 3072), (9216, 36864), (2048, 8192)):
+        d = L.dims(h1, h2, h1 // 64, 64)
+        q = -(-3 * h1 * h1 * 2 // 256) * 256
+        w1 = -(-h2 * h1 * 2 // 256) * 256
+        assert L.fg_stage_bytes(d) == q + w1
+    # OPT-66B shape: the staged half of one layer is 6 h1^2 fp16 of its 12 h1^2
+    d = L.dims(9216, 36864, 72, 128)
+    assert 2 * 9216 * 9216 * 2 + 36864 * 9216 * 2 == 6 * 9216 * 9216 * 2
+
+
+def test_model_pass_rejects_bad_arguments(L):
+    """The block-schedule entry points validate every layer before enqueueing
+    anything (no GPU needed: these all fail on the host)."""
+    p = 1 << 20
+    d = L.dims(256, 1024, 2, 128)
+    ws_need = L.fg_workspace_bytes(d, 4, 1)
+    w = (L.LayerW * 2)(L.LayerW(1, *([p] * 16)), L.LayerW(1, *([p] * 16)))
+    kvs = (L.KV * 2)(_kv(L, max_len=16, n_seq=4), _kv(L, max_len=16, n_seq=4))
+    f = L.raw("fg_model_decode_step")
+    V = ctypes.c_void_p
+    assert f(None, ctypes.byref(d), 0, w, None, kvs, V(p), 2, 2, 3, V(p), ws_need, None, None, 0) \
+        == L.FG_ERR_INVALID                            # no layers
+    w[1].m_o = None                                    # second layer broken: nothing may run
+    assert f(None, ctypes.byref(d), 2, w, None, kvs, V(p), 2, 2, 3, V(p), ws_need, None, None, 0) \
+        == L.FG_ERR_INVALID
+    assert "metadata" in L.last_error()
+    w[1].m_o = p
+    tier = (L.TierW * 2)(L.TierW(p, p, p), L.TierW())
+    assert f(None, ctypes.byref(d), 2, w, tier, kvs, V(p), 2, 2, 3, V(p), ws_need, None, None, 0) \
+        == L.FG_ERR_INVALID                            # tiering without a scheduler
+    assert "scheduler" in L.last_error()
+    g = L.raw("fg_model_prefill")
+    assert g(None, ctypes.byref(d), 2, w, None, kvs, V(p), 2, 2, 17, V(p), 1 << 40, None, None, 0) \
+        == L.FG_ERR_INVALID                            # s > max_len
+    assert L.raw("fg_sched_create")(None, V(p), 256) == L.FG_ERR_INVALID
+    assert L.raw("fg_sched_destroy")(None) == L.FG_OK

@@ -51,6 +51,13 @@ class KV(ctypes.Structure):
                 ("max_len", I32), ("n_seq", I32)]
 
 
+class TierW(ctypes.Structure):
+    _fields_ = [("qk_host", P), ("v_dev", P), ("w1_host", P)]
+
+
+FG_SCHED_FIRST_STAGED, FG_SCHED_STAGE_NEXT = 1, 2
+
+
 _PROTOS = {
     "fg_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "fg_last_error": (ctypes.c_char_p, []),
@@ -74,6 +81,15 @@ _PROTOS = {
     "fg_layer_decode_block": (ctypes.c_int, [ctypes.POINTER(Dims), ctypes.POINTER(LayerW), P, I32, I32,
                                              I32, ctypes.POINTER(KV), P, SZ, P]),
     "fg_workspace_bytes": (SZ, [ctypes.POINTER(Dims), I64, I32]),
+    "fg_stage_bytes": (SZ, [ctypes.POINTER(Dims)]),
+    "fg_sched_create": (ctypes.c_int, [ctypes.POINTER(P), P, SZ]),
+    "fg_sched_destroy": (ctypes.c_int, [P]),
+    "fg_model_prefill": (ctypes.c_int, [P, ctypes.POINTER(Dims), I32, ctypes.POINTER(LayerW),
+                                        ctypes.POINTER(TierW), ctypes.POINTER(KV), P, I32, I32, I32,
+                                        P, SZ, P, P, I32]),
+    "fg_model_decode_step": (ctypes.c_int, [P, ctypes.POINTER(Dims), I32, ctypes.POINTER(LayerW),
+                                            ctypes.POINTER(TierW), ctypes.POINTER(KV), P, I32, I32,
+                                            I32, P, SZ, P, P, I32]),
     "fg_weight_bytes": (I64, [ctypes.POINTER(Dims), I32, I32]),
     "fg_kv_bytes": (I64, [ctypes.POINTER(Dims), I32, I32, I32, I32, I32]),
     "fg_trace_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -202,6 +218,44 @@ def fg_layer_decode_block(d: Dims, w: LayerW, x, gbs, nb, pos, kv: KV, ws, ws_by
     _check("fg_layer_decode_block", _L.fg_layer_decode_block(ctypes.byref(d), ctypes.byref(w), ptr(x),
                                                              gbs, nb, pos, ctypes.byref(kv), ptr(ws),
                                                              ws_bytes, stream_ptr(stream)))
+
+
+def fg_stage_bytes(d: Dims) -> int:
+    return _L.fg_stage_bytes(ctypes.byref(d))
+
+
+def fg_sched_create(stage, stage_bytes) -> int:
+    """Scheduler handle over the caller's two stage buffers (2 * stage_bytes)."""
+    h = P()
+    _check("fg_sched_create", _L.fg_sched_create(ctypes.byref(h), ptr(stage), stage_bytes))
+    return h.value
+
+
+def fg_sched_destroy(h):
+    _check("fg_sched_destroy", _L.fg_sched_destroy(h))
+
+
+def _arr(T, items):
+    return (T * len(items))(*items) if items is not None else None
+
+
+def fg_model_prefill(sched, d: Dims, layers, tier, kvs, x, gbs, nb, s, ws, ws_bytes, stream=None,
+                     copy_stream=None, flags=0):
+    """layers: ctypes array of LayerW; tier: array of TierW or None; kvs: array of KV."""
+    _check("fg_model_prefill", _L.fg_model_prefill(sched, ctypes.byref(d), len(layers), layers, tier,
+                                                   kvs, ptr(x), gbs, nb, s, ptr(ws), ws_bytes,
+                                                   stream_ptr(stream),
+                                                   copy_stream.cuda_stream if copy_stream else None,
+                                                   flags))
+
+
+def fg_model_decode_step(sched, d: Dims, layers, tier, kvs, x, gbs, nb, pos, ws, ws_bytes,
+                         stream=None, copy_stream=None, flags=0):
+    _check("fg_model_decode_step", _L.fg_model_decode_step(sched, ctypes.byref(d), len(layers),
+                                                           layers, tier, kvs, ptr(x), gbs, nb, pos,
+                                                           ptr(ws), ws_bytes, stream_ptr(stream),
+                                                           copy_stream.cuda_stream if copy_stream
+                                                           else None, flags))
 
 
 def fg_workspace_bytes(d: Dims, rows, fmt_w) -> int:

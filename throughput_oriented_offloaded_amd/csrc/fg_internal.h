@@ -88,6 +88,15 @@ struct LinearArgs {
 };
 int launch_linear(const LinearArgs& a, hipStream_t st);
 size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t fmt);
+// One decoder layer (layer.hip): arguments validated, then (unless
+// check_only) enqueued on st.
+int layer_decode(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, int32_t nb,
+                 int32_t pos, const fg_kv* kv, void* ws, size_t ws_bytes, hipStream_t st,
+                 bool check_only);
+int layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, int32_t nb,
+                  int32_t s, const fg_kv* kv, void* ws, size_t ws_bytes, hipStream_t st,
+                  bool check_only);
+size_t layer_ws_bytes(const fg_dims* d, int64_t rows, int32_t fmt);
 
 int launch_layernorm(const __half* x, int64_t rows, int64_t h, const __half* g, const __half* b,
                      __half* y, hipStream_t st);

@@ -87,18 +87,10 @@ int lin(const fg_layer_w* w, int which, const __half* x, int64_t M, int64_t K, i
 }
 
 }  // namespace
-}  // namespace fg
 
-extern "C" size_t fg_workspace_bytes(const fg_dims* d, int64_t rows, int32_t fmt_w) {
-    if (!d || rows < 0 || d->h1 <= 0 || d->h2 <= 0) return 0;
-    return fg::layout(d, rows, fmt_w).total;
-}
-
-extern "C" int fg_layer_decode_block(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs,
-                                     int32_t nb, int32_t pos, const fg_kv* kv, void* ws,
-                                     size_t ws_bytes, void* stream) {
-    using namespace fg;
-    clear_error();
+int layer_decode(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, int32_t nb,
+                 int32_t pos, const fg_kv* kv, void* ws, size_t ws_bytes, hipStream_t st,
+                 bool check_only) {
     FG_TRY(check_layer(d, w, x, kv, ws));
     FG_CHECK_ARG(gbs >= 1 && nb >= 1 && (int64_t)gbs * nb <= kv->n_seq,
                  "block %d x %d exceeds the cache's %d sequences", gbs, nb, kv->n_seq);
@@ -108,7 +100,7 @@ extern "C" int fg_layer_decode_block(const fg_dims* d, const fg_layer_w* w, void
     const WsLayout L = layout(d, bls, w->fmt);
     if (ws_bytes < L.total)
         return set_error(FG_ERR_CAPACITY, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
-    hipStream_t st = as_stream(stream);
+    if (check_only) return FG_OK;
     unsigned char* base = static_cast<unsigned char*>(ws);
     __half* a = (__half*)(base + L.a);
     __half* qkv = (__half*)(base + L.qkv);
@@ -129,11 +121,9 @@ extern "C" int fg_layer_decode_block(const fg_dims* d, const fg_layer_w* w, void
     return FG_OK;
 }
 
-extern "C" int fg_layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs,
-                                int32_t nb, int32_t s, const fg_kv* kv, void* ws, size_t ws_bytes,
-                                void* stream) {
-    using namespace fg;
-    clear_error();
+int layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, int32_t nb,
+                  int32_t s, const fg_kv* kv, void* ws, size_t ws_bytes, hipStream_t st,
+                  bool check_only) {
     FG_TRY(check_layer(d, w, x, kv, ws));
     FG_CHECK_ARG(gbs >= 1 && nb >= 1 && (int64_t)gbs * nb <= kv->n_seq,
                  "block %d x %d exceeds the cache's %d sequences", gbs, nb, kv->n_seq);
@@ -143,7 +133,7 @@ extern "C" int fg_layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, 
     const WsLayout L = layout(d, rows, w->fmt);
     if (ws_bytes < L.total)
         return set_error(FG_ERR_CAPACITY, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
-    hipStream_t st = as_stream(stream);
+    if (check_only) return FG_OK;
     unsigned char* base = static_cast<unsigned char*>(ws);
     __half* a = (__half*)(base + L.a);
     __half* qkv = (__half*)(base + L.qkv);
@@ -165,4 +155,27 @@ extern "C" int fg_layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, 
         FG_TRY(lin(w, 3, f, rows, h2, h1, 0, xh, xh, part, pb, st));
     }
     return FG_OK;
+}
+
+size_t layer_ws_bytes(const fg_dims* d, int64_t rows, int32_t fmt) { return layout(d, rows, fmt).total; }
+
+}  // namespace fg
+
+extern "C" size_t fg_workspace_bytes(const fg_dims* d, int64_t rows, int32_t fmt_w) {
+    if (!d || rows < 0 || d->h1 <= 0 || d->h2 <= 0) return 0;
+    return fg::layer_ws_bytes(d, rows, fmt_w);
+}
+
+extern "C" int fg_layer_decode_block(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs,
+                                     int32_t nb, int32_t pos, const fg_kv* kv, void* ws,
+                                     size_t ws_bytes, void* stream) {
+    fg::clear_error();
+    return fg::layer_decode(d, w, x, gbs, nb, pos, kv, ws, ws_bytes, fg::as_stream(stream), false);
+}
+
+extern "C" int fg_layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs,
+                                int32_t nb, int32_t s, const fg_kv* kv, void* ws, size_t ws_bytes,
+                                void* stream) {
+    fg::clear_error();
+    return fg::layer_prefill(d, w, x, gbs, nb, s, kv, ws, ws_bytes, fg::as_stream(stream), false);
 }

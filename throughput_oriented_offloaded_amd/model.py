@@ -1,11 +1,13 @@
-"""OPT-style decoder driven through the C ABI: device-resident weights (fp16
-or group-wise 4-bit), per-layer KV caches, prefill and zig-zag block decode.
+"""OPT-style decoder driven through the C ABI: weights in HBM (fp16 or
+group-wise 4-bit) or, for fp16, half of each layer in pinned host memory;
+per-layer KV caches; prefill and zig-zag block decode.
 
-Every step runs in libfg.so's kernels; this module owns the device buffers
-(allocated with torch) and issues the per-layer calls in the block order of
-"FlexGen 完全拆解" (pinghaoyang.com.cn), section "一个层级流水的伪代码": token
-step outermost, then layers, with the block's GPU batches innermost (inside
-fg_layer_decode_block / fg_layer_prefill).
+Every step runs in libfg.so: this module owns the buffers (allocated with
+torch) and hands whole passes to the library's block schedule
+(fg_model_prefill / fg_model_decode_step: layers in order, the block's GPU
+batches innermost, host-resident weights staged on a side stream; "FlexGen
+完全拆解" (pinghaoyang.com.cn), sections "一个层级流水的伪代码" and "三条关键
+数据通路如何重叠").
 """
 from __future__ import annotations
 
@@ -53,7 +55,7 @@ class DeviceLayer:
         s = L.LayerW()
         s.fmt = fmt
         for name in MATS:
-            setattr(s, "w_" + name, L.ptr(t["w_" + name]))
+            setattr(s, "w_" + name, L.ptr(t.get("w_" + name)))
             setattr(s, "m_" + name, L.ptr(t.get("m_" + name)))
             setattr(s, "b_" + name, L.ptr(t["b_" + name]))
         for k in ("ln1_g", "ln1_b", "ln2_g", "ln2_b"):
@@ -72,6 +74,31 @@ class DeviceLayer:
             else:
                 t["w_" + name] = w
         return cls(fmt, t)
+
+
+class TierLayer:
+    """The host-resident half of one fp16 layer: W_Q, W_K rows of W_qkv and W_1
+    in pinned host memory, W_V rows on the device (staged next to them)."""
+
+    def __init__(self, W: dict):
+        h1 = W["w_qkv"].shape[1]
+        qkv = W["w_qkv"]
+        self.qk_host = torch.empty((2 * h1, h1), dtype=torch.float16, pin_memory=True)
+        self.qk_host.copy_(qkv[:2 * h1])
+        self.v_dev = qkv[2 * h1:].clone()
+        self.w1_host = torch.empty(tuple(W["w_1"].shape), dtype=torch.float16, pin_memory=True)
+        self.w1_host.copy_(W["w_1"])
+        self.struct = L.TierW(L.ptr(self.qk_host), L.ptr(self.v_dev), L.ptr(self.w1_host))
+
+    @staticmethod
+    def split(W: dict, fmt: int):
+        """(DeviceLayer without W_qkv / W_1, TierLayer) from fp16 device weights."""
+        assert fmt == L.FG_FMT_F16, "tiering keeps fp16 weights"
+        tl = TierLayer(W)
+        t = {k: v for k, v in W.items() if k not in ("w_qkv", "w_1")}
+        t["w_qkv"] = None
+        t["w_1"] = None
+        return DeviceLayer(fmt, t), tl
 
 
 class DeviceKV:
@@ -102,7 +129,8 @@ class Model:
     with embed [vocab, h1], pos [max_pos, h1], lnf_g, lnf_b (fp16, device)."""
 
     def __init__(self, shape: Shape, layers, emb: dict, kv_fmt: int, n_seq: int, max_len: int,
-                 device="cuda"):
+                 device="cuda", tier=None):
+        """tier: None, or one TierLayer (or None) per layer for weight tiering."""
         self.shape, self.layers, self.emb = shape, layers, emb
         self.d = shape.dims
         self.n_seq, self.max_len = n_seq, max_len
@@ -110,6 +138,36 @@ class Model:
                    for _ in layers]
         self.device = device
         self._ws = None
+        n = len(layers)
+        self._w_arr = (L.LayerW * n)(*[lay.struct for lay in layers])
+        self._kv_arr = (L.KV * n)(*[kv.struct for kv in self.kv])
+        self.tier = tier
+        self._sched = None
+        self._tier_arr = None
+        if tier is not None:
+            assert len(tier) == n
+            self._tier_arr = (L.TierW * n)(*[t.struct if t is not None else L.TierW()
+                                            for t in tier])
+            sb = L.fg_stage_bytes(self.d)
+            self._stage = torch.empty(2 * sb, dtype=torch.uint8, device=device)
+            self._sched = L.fg_sched_create(self._stage, sb)
+            self._copy_stream = torch.cuda.Stream(device=device)
+            self._staged = False
+
+    def __del__(self):
+        if getattr(self, "_sched", None):
+            torch.cuda.synchronize(self.device)
+            L.fg_sched_destroy(self._sched)
+            self._sched = None
+
+    def _sched_args(self):
+        """(sched, tier array, copy stream, flags) of the next pass; with tiering
+        every pass also stages the first tiered layer for the following one."""
+        if self._sched is None:
+            return None, None, None, 0
+        flags = L.FG_SCHED_STAGE_NEXT | (L.FG_SCHED_FIRST_STAGED if self._staged else 0)
+        self._staged = True
+        return self._sched, self._tier_arr, self._copy_stream, flags
 
     def workspace(self, rows: int) -> torch.Tensor:
         fmt = self.layers[0].fmt
@@ -143,9 +201,9 @@ class Model:
         L.fg_embed(tokens.reshape(-1), pos, bls * s, self.emb["embed"], sh.vocab, self.emb["pos"],
                    self.emb["pos"].shape[0], sh.h1, x, stream=stream)
         ws = self.workspace(gbs * s)
-        for lay, kv in zip(self.layers, self.kv):
-            L.fg_layer_prefill(self.d, lay.struct, x, gbs, nb, s, kv.struct, ws, ws.numel(),
-                               stream=stream)
+        sc, tier, cp, flags = self._sched_args()
+        L.fg_model_prefill(sc, self.d, self._w_arr, tier, self._kv_arr, x, gbs, nb, s, ws,
+                           ws.numel(), stream=stream, copy_stream=cp, flags=flags)
         last = x.view(bls, s, sh.h1)[:, s - 1, :].contiguous()
         return self._head(last, stream)
 
@@ -155,9 +213,9 @@ class Model:
         bls = gbs * nb
         x = self.embed_step(tok, pos, stream)
         ws = self.workspace(bls)
-        for lay, kv in zip(self.layers, self.kv):
-            L.fg_layer_decode_block(self.d, lay.struct, x, gbs, nb, pos, kv.struct, ws, ws.numel(),
-                                    stream=stream)
+        sc, tier, cp, flags = self._sched_args()
+        L.fg_model_decode_step(sc, self.d, self._w_arr, tier, self._kv_arr, x, gbs, nb, pos, ws,
+                               ws.numel(), stream=stream, copy_stream=cp, flags=flags)
         return self._head(x, stream)
 
     def embed_step(self, tok: torch.Tensor, pos: int, stream=None) -> torch.Tensor:
