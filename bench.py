@@ -38,6 +38,9 @@ CONFIGS = {
             w="f16", kv="f16", gbs=32, nb=4, s=512, n=32),
     3: dict(workload="opt-30b-shape 4-bit block decode", l=48, h1=7168, h2=28672, nh=56, hd=128,
             w="q4", kv="q4", gbs=48, nb=3, s=512, n=32),
+    4: dict(workload="opt-66b-shape fp16 block decode, 50% of weights in pinned host memory",
+            l=64, h1=9216, h2=36864, nh=72, hd=128, w="f16", kv="q4", gbs=32, nb=8, s=512, n=32,
+            tier=True),
     5: dict(workload="opt-175b-shape 4-bit block decode", l=96, h1=12288, h2=49152, nh=96,
             hd=128, w="q4", kv="q4", gbs=48, nb=3, s=512, n=32),
 }
@@ -51,18 +54,22 @@ def build_model(cfg, keep_layer0_host: bool):
     import torch
     import synth
     from throughput_oriented_offloaded_amd import _lib as L
-    from throughput_oriented_offloaded_amd.model import DeviceLayer, Model, Shape
+    from throughput_oriented_offloaded_amd.model import DeviceLayer, Model, Shape, TierLayer
 
     fmt = lambda f: L.FG_FMT_Q4G64 if f == "q4" else L.FG_FMT_F16  # noqa: E731
     sh = Shape(n_layers=cfg["l"], h1=cfg["h1"], h2=cfg["h2"], n_heads=cfg["nh"], head_dim=cfg["hd"])
-    bls = cfg["gbs"] * cfg["nb"]
-    layers, host0 = [], None
+    layers, tier, host0 = [], ([] if cfg.get("tier") else None), None
     L.fg_trace_enable(True)            # time the weight quantizer (init, not in the step)
     for j in range(sh.n_layers):
         W = synth.layer_weights(sh.h1, sh.h2, j, seed=0, device="cuda")
         if j == 0 and keep_layer0_host:
             host0 = {k: v.cpu() for k, v in W.items()}
-        layers.append(DeviceLayer.from_fp16(W, fmt(cfg["w"])))
+        if tier is not None:           # half of the fp16 weights to pinned host memory
+            dl, tl = TierLayer.split(W, fmt(cfg["w"]))
+            layers.append(dl)
+            tier.append(tl)
+        else:
+            layers.append(DeviceLayer.from_fp16(W, fmt(cfg["w"])))
         del W
         if j % 16 == 0:
             log(f"  layer {j}/{sh.n_layers} ready")
@@ -71,7 +78,24 @@ def build_model(cfg, keep_layer0_host: bool):
     L.fg_trace_enable(False)
     torch.cuda.empty_cache()
     emb = synth.embeddings(sh.h1, cfg["s"] + cfg["n"], seed=0, device="cuda")
-    return sh, layers, emb, host0, quant, fmt
+    return sh, layers, tier, emb, host0, quant, fmt
+
+
+def h2d_probe(src, reps: int = 5) -> float:
+    """Pinned host -> device hipMemcpyAsync bandwidth on a side stream (GB/s);
+    src: an existing pinned host tensor (pinned memory is a bounded resource)."""
+    import torch
+    dst = torch.empty(src.numel() * src.element_size(), dtype=torch.uint8, device="cuda")
+    s8 = src.view(-1).view(torch.uint8)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        dst.copy_(s8, non_blocking=True)
+        st.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            dst.copy_(s8, non_blocking=True)
+        st.synchronize()
+    return dst.numel() * reps / (time.perf_counter() - t) / 1e9
 
 
 def roofline(tr, kind, bound):
@@ -153,9 +177,9 @@ def main():
     want_cpu = not args.no_cpu_baseline
     t_build = time.time()
     log(f"building {cfg['workload']} ({cfg['l']} layers, bls {bls})")
-    sh, layers, emb, host0, quant, fmt = build_model(cfg, want_cpu)
+    sh, layers, tier, emb, host0, quant, fmt = build_model(cfg, want_cpu)
     max_len = s + max(n, K + 1, Wm + 1)
-    model = Model(sh, layers, emb, fmt(cfg["kv"]), bls, max_len)
+    model = Model(sh, layers, emb, fmt(cfg["kv"]), bls, max_len, tier=tier)
     tokens = synth.tokens(bls, s, seed=0, device="cuda")
     torch.cuda.synchronize()
     log(f"built in {time.time() - t_build:.1f} s; prefill s={s} ...")
@@ -211,12 +235,25 @@ def main():
                     for k, v in tr.items()},
         "tokens_valid": ok,
     }
+    if tier is not None:
+        # weight tiering: bytes moved over PCIe per step against a pinned copy probe
+        hb = sum(t.host_bytes for t in tier)
+        probe = h2d_probe(tier[0]._host)
+        step = t_dec / K
+        kern_s = sum(v["ms"] for v in tr.values()) / 1e3 / K if tr else None
+        out["tiering"] = {
+            "host_bytes_per_step": hb, "achieved_GBs": round(hb / step / 1e9, 2),
+            "probe_h2d_GBs": round(probe, 2), "frac_of_probe": round(hb / step / 1e9 / probe, 4),
+            "copy_s_at_probe": round(hb / probe / 1e9, 4),
+            "kernel_s_per_step": round(kern_s, 4) if kern_s else None,
+            "overlap_efficiency": round(max(hb / probe / 1e9, kern_s or 0.0) / step, 4),
+            "definition": "overlap = max(copy time at probe rate, kernel time) / step time"}
     if quant:
         out["weight_quant"] = {"GB/s": round(quant["bytes"] / (quant["ms"] / 1e3) / 1e9, 1),
                                "frac": round(quant["bytes"] / (quant["ms"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
                                "launches": quant["count"]}
     if want_cpu:
-        del model, layers
+        del model, layers, tier
         torch.cuda.empty_cache()
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(cfg, host0, emb)

@@ -82,13 +82,22 @@ class TierLayer:
 
     def __init__(self, W: dict):
         h1 = W["w_qkv"].shape[1]
+        h2 = W["w_1"].shape[0]
         qkv = W["w_qkv"]
-        self.qk_host = torch.empty((2 * h1, h1), dtype=torch.float16, pin_memory=True)
+        # one pinned block per layer ([W_Q; W_K] then W_1): the host allocator
+        # rounds blocks up, so two separate tensors would waste more memory
+        nq, n1 = 2 * h1 * h1, h2 * h1
+        self._host = torch.empty(nq + n1, dtype=torch.float16, pin_memory=True)
+        self.qk_host = self._host[:nq].view(2 * h1, h1)
+        self.w1_host = self._host[nq:].view(h2, h1)
         self.qk_host.copy_(qkv[:2 * h1])
-        self.v_dev = qkv[2 * h1:].clone()
-        self.w1_host = torch.empty(tuple(W["w_1"].shape), dtype=torch.float16, pin_memory=True)
         self.w1_host.copy_(W["w_1"])
+        self.v_dev = qkv[2 * h1:].clone()
         self.struct = L.TierW(L.ptr(self.qk_host), L.ptr(self.v_dev), L.ptr(self.w1_host))
+
+    @property
+    def host_bytes(self) -> int:
+        return self._host.numel() * 2
 
     @staticmethod
     def split(W: dict, fmt: int):
