@@ -98,7 +98,70 @@ def h2d_probe(src, reps: int = 5) -> float:
     return dst.numel() * reps / (time.perf_counter() - t) / 1e9
 
 
-def roofline(tr, kind, bound):
+def profile_layer(cfg, reps: int):
+    """One decoder layer at the config's shape for hardware-counter runs: the
+    prefill fills its cache to s, then `reps` decode steps of the whole block
+    (the launches the step times), then a plain 1 GiB device-to-device copy
+    (reads and writes 1 GiB: the calibration of the byte counters)."""
+    import torch
+    import synth
+    from throughput_oriented_offloaded_amd import _lib as L
+    from throughput_oriented_offloaded_amd.model import DeviceKV, DeviceLayer, Shape
+    fmt = lambda f: L.FG_FMT_Q4G64 if f == "q4" else L.FG_FMT_F16  # noqa: E731
+    sh = Shape(n_layers=1, h1=cfg["h1"], h2=cfg["h2"], n_heads=cfg["nh"], head_dim=cfg["hd"])
+    gbs, nb, s = cfg["gbs"], cfg["nb"], cfg["s"]
+    bls, d = gbs * nb, sh.dims
+    lay = DeviceLayer.from_fp16(synth.layer_weights(sh.h1, sh.h2, 0, seed=0, device="cuda"),
+                                fmt(cfg["w"]))
+    kv = DeviceKV(fmt(cfg["kv"]), bls, sh.n_heads, sh.head_dim, s + reps, "cuda")
+    ws_b = max(L.fg_workspace_bytes(d, gbs * s, lay.fmt), L.fg_workspace_bytes(d, bls, lay.fmt))
+    ws = torch.empty(ws_b, dtype=torch.uint8, device="cuda")
+    x = synth.activations(bls * s, sh.h1, seed=1, device="cuda")
+    L.fg_layer_prefill(d, lay.struct, x, gbs, nb, s, kv.struct, ws, ws_b)
+    del x
+    xd = synth.activations(bls, sh.h1, seed=2, device="cuda")
+    torch.cuda.synchronize()
+    log(f"profile-layer: {cfg['workload']}, {reps} decode steps from position {s}")
+    for r in range(reps):
+        L.fg_layer_decode_block(d, lay.struct, xd, gbs, nb, s + r, kv.struct, ws, ws_b)
+    torch.cuda.synchronize()
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("profile-layer: done")
+
+
+# HBM bytes per launch from hardware counters (rocprofv3 FETCH_SIZE / WRITE_SIZE,
+# calibrated on a copy of known size), committed per workload with the sha256
+# of the measured kernel's sources; reported only while those are unchanged.
+TRAFFIC_FILES = {5: "opt175b_q4_decode_hbm_traffic.md"}
+KERNEL_SOURCES = {"gemm_q4": ["gemm_sk.hip", "gemm_common.h"],
+                  "attn_decode_q4": ["attn_decode.hip", "codec_dev.h"]}
+
+
+def measured_traffic(config: int, kind: str):
+    import hashlib
+    import re
+    name = TRAFFIC_FILES.get(config)
+    if not name or kind not in KERNEL_SOURCES:
+        return None
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "throughput_oriented_offloaded_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    for line in open(path):
+        m = re.match(r"traffic (\S+) (\d+) ([0-9a-f]{64})\s*$", line)
+        if m and m.group(1) == kind:
+            return int(m.group(2)) if m.group(3) == h.hexdigest() else None
+    return None
+
+
+def roofline(tr, kind, bound, config=None):
     r = tr.get(kind)
     if not r or r["ms"] <= 0:
         return None
@@ -110,12 +173,12 @@ def roofline(tr, kind, bound):
         ach = r["bytes"] / sec / 1e9
         peak, unit = PEAK_HBM_GBS, "GB/s"
     return {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
-            "frac": round(ach / peak, 4), "traffic": None, "kernel": kind,
+            "frac": round(ach / peak, 4), "traffic": measured_traffic(config, kind), "kernel": kind,
             "launches": r["count"], "avg_launch_us": round(r["ms"] * 1e3 / r["count"], 2),
             "algorithmic_per_launch": (r["flops"] if bound == "mfma" else r["bytes"]) / r["count"]}
 
 
-def cpu_baseline(cfg, host0, emb, budget_s: float = 20.0):
+def cpu_baseline(cfg, host0, emb, budget_s: float = 15.0):
     """The oracle (as it is) on the host cores: one decoder layer's decode step
     for a sample of sequences at context s + n/2, plus the LM head for them;
     decode tokens/s = rows / (l * t_layer + t_head)."""
@@ -123,7 +186,7 @@ def cpu_baseline(cfg, host0, emb, budget_s: float = 20.0):
     import oracle
     import synth
     d = oracle.Dims(cfg["h1"], cfg["h2"], cfg["nh"], cfg["hd"])
-    rows, pos = 2, cfg["s"] + cfg["n"] // 2
+    rows, pos = 4, cfg["s"] + cfg["n"] // 2
     Wn = {k: v.numpy().view(np.uint16) for k, v in host0.items()}
     if cfg["w"] == "q4":
         Wn = oracle.dequant_layer(d, oracle.quant_layer(d, Wn))
@@ -132,7 +195,7 @@ def cpu_baseline(cfg, host0, emb, budget_s: float = 20.0):
     E = emb["embed"].cpu().numpy().view(np.uint16)
     g, b = emb["lnf_g"].cpu().numpy().view(np.uint16), emb["lnf_b"].cpu().numpy().view(np.uint16)
     t_layer, reps, t0 = 0.0, 0, time.time()
-    while reps == 0 or (time.time() - t0 < budget_s and reps < 8):
+    while reps == 0 or (time.time() - t0 < budget_s and reps < 200):
         cache = oracle.KVCache(cfg["kv"], rows, cfg["nh"], cfg["hd"], pos + 1)
         cache.store(kh.numpy().view(np.uint16), vh.numpy().view(np.uint16), 0)
         t = time.perf_counter()
@@ -159,6 +222,9 @@ def main():
     ap.add_argument("--config", type=int, default=5, choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true", help="time without per-kernel events")
+    ap.add_argument("--profile-layer", type=int, default=0, metavar="R",
+                    help="counter-collection driver: one layer of the config (prefilled to s), "
+                         "R decode steps, then a 1 GiB device copy that calibrates byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the block decode is measured on a single "
@@ -171,6 +237,9 @@ def main():
     import synth
 
     cfg = CONFIGS[args.config]
+    if args.profile_layer:
+        profile_layer(cfg, args.profile_layer)
+        return
     K, Wm = args.steps, args.warmup
     bls, s, n = cfg["gbs"] * cfg["nb"], cfg["s"], cfg["n"]
     torch.cuda.set_device(0)
@@ -223,8 +292,8 @@ def main():
                    "weights": "q4g64" if cfg["w"] == "q4" else "f16",
                    "kv_cache": "q4g64" if cfg["kv"] == "q4" else "f16",
                    "parallelism": "single GPU"},
-        "roofline": roofline(tr, gemm_kind, "mfma"),
-        "roofline_attn": roofline(tr, attn_kind, "hbm"),
+        "roofline": roofline(tr, gemm_kind, "mfma", args.config),
+        "roofline_attn": roofline(tr, attn_kind, "hbm", args.config),
         "generation_throughput": {"value": round(bls * n / t_gen, 2), "unit": "tokens/s",
                                   "prefill_s": round(t_prefill, 3),
                                   "definition": "bls*n/(t_prefill + (n-1) decode steps)"},
