@@ -303,6 +303,10 @@ int64_t fg_kv_bytes(const fg_dims* d, int32_t n_layers, int32_t bls, int32_t s, 
  * event records per launch; it is off by default.
  */
 int fg_trace_enable(int on);
+/* Bit k of mask selects kind k for recording while tracing is on (default:
+ * all kinds).  Launches of unselected kinds carry no events at all, so a
+ * caller can time the kernels it reports without slowing the others. */
+int fg_trace_kinds(uint64_t mask);
 int fg_trace_collect(int32_t n_kinds, int64_t* count, double* ms, double* flops, double* bytes);
 const char* fg_trace_kind_name(int kind);
 

@@ -93,6 +93,7 @@ _PROTOS = {
     "fg_weight_bytes": (I64, [ctypes.POINTER(Dims), I32, I32]),
     "fg_kv_bytes": (I64, [ctypes.POINTER(Dims), I32, I32, I32, I32, I32]),
     "fg_trace_enable": (ctypes.c_int, [ctypes.c_int]),
+    "fg_trace_kinds": (ctypes.c_int, [ctypes.c_uint64]),
     "fg_trace_collect": (ctypes.c_int, [I32, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_double)]),
@@ -272,6 +273,16 @@ def fg_kv_bytes(d: Dims, n_layers, bls, s, n, fmt) -> int:
 
 def fg_trace_enable(on: bool):
     _check("fg_trace_enable", _L.fg_trace_enable(int(on)))
+
+
+TRACE_KINDS = ["quant_g4", "dequant_g4", "gemm_q4", "gemm_f16", "splitk_reduce", "attn_decode_q4",
+               "attn_decode_f16", "kv_store", "attn_prefill", "layernorm", "embed", "argmax"]
+
+
+def fg_trace_kinds(names=None):
+    """Record only the named kinds (None: all) while tracing is on."""
+    mask = (1 << 64) - 1 if names is None else sum(1 << TRACE_KINDS.index(n) for n in names)
+    _check("fg_trace_kinds", _L.fg_trace_kinds(mask))
 
 
 def fg_trace_collect(n_kinds: int = 32) -> dict:

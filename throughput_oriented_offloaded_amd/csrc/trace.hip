@@ -20,6 +20,7 @@ struct Rec {
 
 std::mutex g_mu;
 bool g_on = false;
+uint64_t g_mask = ~0ull;          // kinds that are recorded while tracing is on
 std::vector<Rec> g_recs;
 std::vector<hipEvent_t> g_pool;   // free events
 
@@ -43,7 +44,7 @@ const char* kNames[TK_COUNT] = {
 bool trace_on() { return g_on; }
 
 TraceScope::TraceScope(int kind, hipStream_t st, double flops, double bytes) {
-    if (!g_on) return;
+    if (!g_on || !((g_mask >> kind) & 1ull)) return;
     std::lock_guard<std::mutex> lk(g_mu);
     if (!g_on) return;
     Rec r{kind, take(), take(), flops, bytes};
@@ -70,6 +71,12 @@ extern "C" int fg_trace_enable(int on) {
     }
     fg::g_recs.clear();
     fg::g_on = on != 0;
+    return FG_OK;
+}
+
+extern "C" int fg_trace_kinds(uint64_t mask) {
+    std::lock_guard<std::mutex> lk(fg::g_mu);
+    fg::g_mask = mask;
     return FG_OK;
 }
 
