@@ -50,6 +50,8 @@ SHAPES = [  # M, N, K
     (1, 64, 64), (4, 2304, 768), (4, 768, 3072), (16, 256, 128), (17, 320, 192),
     (100, 192, 256), (128, 512, 256), (144, 768, 768), (144, 3072, 768), (144, 768, 3072),
     (145, 256, 128), (300, 512, 192), (700, 384, 128), (1000, 128, 64), (2048, 256, 256),
+    # 32-row-block decode tiles: 96 rows (ragged N), 128 x 2, exactly 160
+    (72, 320, 192), (96, 768, 1024), (256, 1024, 512), (160, 512, 2048),
 ]
 
 
@@ -99,3 +101,41 @@ def test_linear_rows_independent_of_batch_split(L):
     L.fg_linear(dev16(x[perm]), M, K, L.FG_FMT_Q4G64, codes, meta, N, None, 0, None, y2, ws, wsb)
     torch.cuda.synchronize()
     assert torch.equal(y1[torch.from_numpy(perm).cuda()], y2)
+
+
+@pytest.mark.parametrize("M,N,K", [(144, 768, 3072), (144, 4096, 4096), (40, 1024, 8192)])
+def test_linear_shared_tiles_any_workspace(L, M, N, K):
+    """Tiles split over many workgroups (fp32 partials in the workspace, summed
+    in segment order): correct from a workspace full of garbage, bit-identical
+    over repeated calls on the same workspace and after another shape used it."""
+    import torch
+    rng = np.random.default_rng(M + N + K)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    b = (rng.standard_normal(N) * 0.02).astype(np.float16)
+    codes = torch.empty((N // 2, K), dtype=torch.uint8, device="cuda")
+    meta = torch.empty((N // 64, 2, K), dtype=torch.float16, device="cuda")
+    L.fg_quant_group4(dev16(w), 1, N, K, codes, meta)
+    rc, rm = oracle.quant_weight(w)
+    wsb = L.fg_linear_workspace_bytes(M, N, K)
+    assert wsb > 0, "shape must share tiles"
+    ws = torch.full((wsb,), 0xFF, dtype=torch.uint8, device="cuda")
+    xd, bd = dev16(x), dev16(b)
+    ys = []
+    for _ in range(4):
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        L.fg_linear(xd, M, K, L.FG_FMT_Q4G64, codes, meta, N, bd, 0, None, y, ws, wsb)
+        ys.append(y)
+    # another shape through the same workspace, then this one again
+    y_o = torch.empty((M, 256), dtype=torch.float16, device="cuda")
+    L.fg_linear(xd, M, K, L.FG_FMT_Q4G64, codes, meta, 256, None, 0, None, y_o, ws, wsb)
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    L.fg_linear(xd, M, K, L.FG_FMT_Q4G64, codes, meta, N, bd, 0, None, y, ws, wsb)
+    ys.append(y)
+    torch.cuda.synchronize()
+    ref = oracle.linear(x, oracle.dequant_weight(rc, rm, N, K), b)
+    assert_close(np16(ys[0]), ref, f"q4 shared tiles {M}x{N}x{K}")
+    for i, yi in enumerate(ys[1:], 1):
+        assert torch.equal(yi, ys[0]), f"call {i} differs bitwise"
+    ref_o = oracle.linear(x, oracle.dequant_weight(rc[:128], rm[:4], 256, K), None)
+    assert_close(np16(y_o), ref_o, "q4 first 256 columns")

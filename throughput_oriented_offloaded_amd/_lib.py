@@ -276,7 +276,8 @@ def fg_trace_enable(on: bool):
 
 
 TRACE_KINDS = ["quant_g4", "dequant_g4", "gemm_q4", "gemm_f16", "splitk_reduce", "attn_decode_q4",
-               "attn_decode_f16", "kv_store", "attn_prefill", "layernorm", "embed", "argmax"]
+               "attn_decode_f16", "kv_store", "attn_prefill", "layernorm", "embed", "argmax",
+               "reduce_layernorm"]
 
 
 def fg_trace_kinds(names=None):

@@ -85,14 +85,23 @@ struct LinearArgs {
     int64_t ldy;
     void* ws;
     size_t ws_bytes;
+    // optional: LayerNorm (gamma ln_g, beta ln_b) of every finished output
+    // row (width N, requires ldy == N) into ln_y [M, N], fused with the
+    // split-k sum where there is one
+    const __half* ln_g;
+    const __half* ln_b;
+    __half* ln_y;
 };
 int launch_linear(const LinearArgs& a, hipStream_t st);
 size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t fmt);
 // One decoder layer (layer.hip): arguments validated, then (unless
 // check_only) enqueued on st.
+// ln1_done: the layer's input LayerNorm is already in the workspace (the
+// previous layer fused it); next: if not null, that layer's input LayerNorm is
+// fused into this layer's last residual sum.
 int layer_decode(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, int32_t nb,
                  int32_t pos, const fg_kv* kv, void* ws, size_t ws_bytes, hipStream_t st,
-                 bool check_only);
+                 bool check_only, bool ln1_done, const fg_layer_w* next);
 int layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, int32_t nb,
                   int32_t s, const fg_kv* kv, void* ws, size_t ws_bytes, hipStream_t st,
                   bool check_only);

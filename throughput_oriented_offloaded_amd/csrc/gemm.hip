@@ -316,6 +316,7 @@ size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t) {
 int launch_linear(const LinearArgs& a, hipStream_t st) {
     using namespace gemm;
     if (a.M == 0 || a.N == 0) return FG_OK;
+    if (a.ln_y && a.ldy != a.N) return set_error(FG_ERR_INVALID, "layernorm of the output needs ldy == N");
     const bool q4 = a.fmt == FG_FMT_Q4G64;
     Params p{};
     p.x = a.x; p.M = a.M; p.K = a.K; p.ldx = a.ldx;
@@ -342,12 +343,17 @@ int launch_linear(const LinearArgs& a, hipStream_t st) {
             TraceScope ts(q4 ? TK_GEMM_Q4 : TK_GEMM_F16, st, 2 * Md * Nd * Kd, gbytes);
             FG_TRY(launch_sk(p, sc, q4, st));
         }
+        if (sc.slots > 1 && a.ln_y) {
+            TraceScope ts(TK_REDUCE_LN, st, 0.0,
+                          Md * Nd * (4.0 * sc.slots + 2.0 * (a.residual ? 3 : 2)) + 4 * Nd);
+            return launch_sk_reduce_ln(p, sc, a.ln_g, a.ln_b, a.ln_y, st);
+        }
         if (sc.slots > 1) {
             TraceScope ts(TK_SPLITK_REDUCE, st, 0.0,
                           Md * Nd * (4.0 * sc.slots + 2.0 * (a.residual ? 2 : 1)));
             FG_TRY(launch_sk_reduce(p, sc, st));
         }
-        return FG_OK;
+        return a.ln_y ? launch_layernorm(a.y, a.M, a.N, a.ln_g, a.ln_b, a.ln_y, st) : FG_OK;
     }
 
     const Plan pl = make_plan(a.M, a.N, a.K);
@@ -365,7 +371,7 @@ int launch_linear(const LinearArgs& a, hipStream_t st) {
         splitk_reduce_kernel<<<(unsigned)cdiv(n4, 256), 256, 0, st>>>(p, pl.S);
         FG_LAUNCHED("splitk_reduce_kernel");
     }
-    return FG_OK;
+    return a.ln_y ? launch_layernorm(a.y, a.M, a.N, a.ln_g, a.ln_b, a.ln_y, st) : FG_OK;
 }
 
 }  // namespace fg

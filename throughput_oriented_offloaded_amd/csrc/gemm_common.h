@@ -127,10 +127,21 @@ struct SkSched {
     int64_t T, G, nk;     // iterations, workgroups, k-steps per tile
     int64_t ntn, bm, bn;  // N tiles, tile rows, tile columns
     int64_t slots;        // partial slots per output element (1: none needed)
+    int32_t wide;         // 1: 32-row blocks on 32x32x16 MFMA (gemm_sk32.hip)
 };
+
+// workgroup holding iteration x of T split over G: ceil((x + 1) G / T) - 1
+__device__ __host__ __forceinline__ int64_t sk_owner(int64_t x, int64_t T, int64_t G) {
+    return ((x + 1) * G + T - 1) / T - 1;
+}
 SkSched sk_schedule(int64_t M, int64_t N, int64_t K);
 int launch_sk(const Params& p, const SkSched& sc, bool q4, hipStream_t st);
+int launch_sk32(const Params& p, const SkSched& sc, bool q4, hipStream_t st);
 int launch_sk_reduce(const Params& p, const SkSched& sc, hipStream_t st);
+// sk_reduce fused with the LayerNorm of each finished row (width N, ldy == N,
+// N <= 32768) into ln_y [M, N]
+int launch_sk_reduce_ln(const Params& p, const SkSched& sc, const __half* g, const __half* b,
+                        __half* ln_y, hipStream_t st);
 
 
 }  // namespace gemm

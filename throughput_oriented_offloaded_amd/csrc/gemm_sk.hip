@@ -29,6 +29,7 @@
 //    several leaves fp32 partials in per-segment slots, summed in segment order
 //    (deterministic) by sk_reduce_kernel.
 #include "gemm_common.h"
+#include "rowops.h"
 
 namespace fg {
 namespace gemm {
@@ -83,10 +84,6 @@ __device__ __forceinline__ uint32_t pk_f16(float a, float b) {
     return r;
 }
 
-// workgroup holding iteration x of T split over G: ceil((x + 1) G / T) - 1
-__device__ __host__ __forceinline__ int64_t sk_owner(int64_t x, int64_t T, int64_t G) {
-    return ((x + 1) * G + T - 1) / T - 1;
-}
 
 template <class C>
 __global__ __launch_bounds__(C::NT) void sk_kernel(Params p, SkSched sc) {
@@ -426,6 +423,99 @@ __global__ __launch_bounds__(256) void sk_reduce_kernel(Params p, SkSched sc) {
     *reinterpret_cast<uint2*>(p.y + m * p.ldy + n) = make_uint2(pack_h2(o[0], o[1]), pack_h2(o[2], o[3]));
 }
 
+// The same sum for whole rows, fused with the LayerNorm of the finished
+// fp16 row (the next sublayer's input).  One 1024-thread workgroup per row,
+// 4 columns per thread and unit; every partial of a row is requested before
+// any is used (the slot loads are unrolled up to SMAX with clamped addresses),
+// and tiles written whole by one workgroup are read back from y.
+constexpr int kLnTiles = 128;   // column tiles of a row: h <= 32768
+constexpr int kLnThreads = 1024;
+
+template <int MAXU, int SMAX>
+__global__ __launch_bounds__(kLnThreads) void sk_reduce_ln_kernel(Params p, SkSched sc,
+                                                                 const __half* __restrict__ g,
+                                                                 const __half* __restrict__ b,
+                                                                 __half* __restrict__ ln_y) {
+    constexpr int NT = kLnThreads;
+    __shared__ float sh[NT / 64];
+    __shared__ int s_ns[kLnTiles];   // segments of each column tile of this row
+    const int64_t m = blockIdx.x;
+    const int64_t tm = m / sc.bm;
+    for (int t = threadIdx.x; t < sc.ntn; t += NT) {
+        const int64_t tile = tm * sc.ntn + t;
+        s_ns[t] = (int)(sk_owner((tile + 1) * sc.nk - 1, sc.T, sc.G) - sk_owner(tile * sc.nk, sc.T, sc.G) + 1);
+    }
+    __syncthreads();
+    const int nu = (int)(p.N / 4);
+    const int64_t MN = p.M * p.N;
+    __half* yr = p.y + m * p.ldy;
+    const __half* rr = p.residual ? p.residual + m * p.ldy : nullptr;
+    const float* pr = p.part + m * p.N;
+    float v[MAXU][4];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXU; ++i) {
+        const int u = min((int)threadIdx.x + i * NT, nu - 1);   // clamped: loads stay in the row
+        const int64_t n = (int64_t)u * 4;
+        const int ns = s_ns[n / sc.bn];
+        // whole tile: y is final; shared tile: partials + bias / ReLU / residual
+        const __half* src16 = ns == 1 ? yr + n : (rr ? rr + n : nullptr);
+        const uint2 h16 = src16 ? *reinterpret_cast<const uint2*>(src16) : make_uint2(0u, 0u);
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < SMAX; ++q) {
+            const f4 o = *reinterpret_cast<const f4*>(pr + min(q, ns - 1) * MN + n);
+            if (q < ns) acc += o;
+        }
+        for (int q = SMAX; q < ns; ++q) acc += *reinterpret_cast<const f4*>(pr + q * MN + n);
+        if (p.bias) {
+            const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n);
+            acc[0] += h2f(bb.x); acc[1] += h2f(bb.x >> 16); acc[2] += h2f(bb.y); acc[3] += h2f(bb.y >> 16);
+        }
+        if (p.act == 1) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = fmaxf(acc[j], 0.f);
+        }
+        if (rr) {
+            acc[0] += h2f(h16.x); acc[1] += h2f(h16.x >> 16); acc[2] += h2f(h16.y); acc[3] += h2f(h16.y >> 16);
+        }
+        const uint2 w = ns == 1 ? h16 : make_uint2(pack_h2(acc[0], acc[1]), pack_h2(acc[2], acc[3]));
+        const bool mine = (int)threadIdx.x + i * NT < nu;
+        if (mine && ns > 1) *reinterpret_cast<uint2*>(yr + n) = w;
+        // the LayerNorm sees the row as stored (fp16)
+        v[i][0] = h2f(w.x); v[i][1] = h2f(w.x >> 16); v[i][2] = h2f(w.y); v[i][3] = h2f(w.y >> 16);
+        if (mine) s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+    }
+    const float mean = row::block_sum<NT>(s, sh) / (float)p.N;
+    float qs = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXU; ++i) {
+        if ((int)threadIdx.x + i * NT < nu) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float d = v[i][j] - mean;
+                qs += d * d;
+            }
+        }
+    }
+    const float var = row::block_sum<NT>(qs, sh) / (float)p.N;
+    const float rstd = 1.0f / sqrtf(var + 1e-5f);
+    __half* out = ln_y + m * p.N;
+#pragma unroll
+    for (int i = 0; i < MAXU; ++i) {
+        const int u = (int)threadIdx.x + i * NT;
+        if (u < nu) {
+            const uint2 gg = *reinterpret_cast<const uint2*>(g + u * 4);
+            const uint2 be = *reinterpret_cast<const uint2*>(b + u * 4);
+            const float gv[4] = {h2f(gg.x), h2f(gg.x >> 16), h2f(gg.y), h2f(gg.y >> 16)};
+            const float bv[4] = {h2f(be.x), h2f(be.x >> 16), h2f(be.y), h2f(be.y >> 16)};
+            *reinterpret_cast<uint2*>(out + u * 4) =
+                make_uint2(pack_h2((v[i][0] - mean) * rstd * gv[0] + bv[0], (v[i][1] - mean) * rstd * gv[1] + bv[1]),
+                           pack_h2((v[i][2] - mean) * rstd * gv[2] + bv[2], (v[i][3] - mean) * rstd * gv[3] + bv[3]));
+        }
+    }
+}
+
 template <class C>
 int run(const Params& p, const SkSched& sc, hipStream_t st) {
     sk_kernel<C><<<(unsigned)sc.G, C::NT, 0, st>>>(p, sc);
@@ -435,19 +525,30 @@ int run(const Params& p, const SkSched& sc, hipStream_t st) {
 
 }  // namespace
 
-// 16-row blocks per M tile: every row of a decode block stays in one tile
-// (up to 144 rows); 128-row tiles when they pad less (e.g. M = 256).
-int sk_mb_for(int64_t M) {
-    if (M <= 16) return 1;
-    if (M <= 32) return 2;
-    if (M <= 64) return 4;
-    if (M <= 128) return 8;
-    return cdiv(M, 128) * 128 < cdiv(M, 144) * 144 ? 8 : 9;
+// Tile rows.  Up to 64 rows: one tile of 16-row blocks (16x16x32 kernel
+// here).  Beyond, the candidates are 128- or 144-row tiles of this kernel and
+// 96-, 128- or 160-row tiles of the 32x32x16 kernel (gemm_sk32.hip): the
+// fewest tiles along M (each one streams the weights once), then the least
+// padding, then this kernel.  Measured on gfx950 at equal padding the two
+// kernels run within 1-2% of each other (the 32x32x16 one issues far less
+// VALU per flop but the clock drops accordingly), so the fit decides.
+int64_t sk_rows_for(int64_t M, int32_t& wide) {
+    wide = 0;
+    if (M <= 64) return M <= 16 ? 16 : (M <= 32 ? 32 : 64);
+    struct Cand { int64_t bm; int32_t wide; };
+    const Cand cands[] = {{128, 0}, {144, 0}, {96, 1}, {128, 1}, {160, 1}};
+    Cand best = cands[0];
+    for (const Cand& c : cands) {
+        const int64_t t = cdiv(M, c.bm), tb = cdiv(M, best.bm);
+        if (t < tb || (t == tb && t * c.bm < tb * best.bm)) best = c;
+    }
+    wide = best.wide;
+    return best.bm;
 }
 
 SkSched sk_schedule(int64_t M, int64_t N, int64_t K) {
     SkSched sc{};
-    sc.bm = sk_mb_for(M) * 16;
+    sc.bm = sk_rows_for(M, sc.wide);
     sc.bn = 256;
     sc.ntn = cdiv(N, sc.bn);
     const int64_t tiles = cdiv(M, sc.bm) * sc.ntn;
@@ -463,6 +564,7 @@ SkSched sk_schedule(int64_t M, int64_t N, int64_t K) {
 }
 
 int launch_sk(const Params& p, const SkSched& sc, bool q4, hipStream_t st) {
+    if (sc.wide) return launch_sk32(p, sc, q4, st);
     const int MB = (int)(sc.bm / 16);
     if (q4) {
         switch (MB) {
@@ -486,6 +588,28 @@ int launch_sk_reduce(const Params& p, const SkSched& sc, hipStream_t st) {
     const int64_t n4 = p.M * p.N / 4;
     sk_reduce_kernel<<<(unsigned)cdiv(n4, 256), 256, 0, st>>>(p, sc);
     FG_LAUNCHED("sk_reduce_kernel");
+    return FG_OK;
+}
+
+int launch_sk_reduce_ln(const Params& p, const SkSched& sc, const __half* g, const __half* b,
+                        __half* ln_y, hipStream_t st) {
+    const int64_t nu = p.N / 4;
+    if (p.N % 8 != 0 || p.ldy != p.N || sc.ntn > kLnTiles || nu > kLnThreads * 8)
+        return set_error(FG_ERR_UNSUPPORTED, "fused reduce + layernorm: width %lld", (long long)p.N);
+    const unsigned rows = (unsigned)p.M;
+    const int mu = nu <= kLnThreads ? 1 : (nu <= 2 * kLnThreads ? 2 : (nu <= 4 * kLnThreads ? 4 : 8));
+    const int sm = sc.slots <= 2 ? 2 : (sc.slots <= 4 ? 4 : 8);
+#define FG_RLN(U, S) sk_reduce_ln_kernel<U, S><<<rows, kLnThreads, 0, st>>>(p, sc, g, b, ln_y)
+#define FG_RLN_S(U) (sm == 2 ? FG_RLN(U, 2) : (sm == 4 ? FG_RLN(U, 4) : FG_RLN(U, 8)))
+    switch (mu) {
+        case 1: FG_RLN_S(1); break;
+        case 2: FG_RLN_S(2); break;
+        case 4: FG_RLN_S(4); break;
+        default: FG_RLN_S(8); break;
+    }
+#undef FG_RLN_S
+#undef FG_RLN
+    FG_LAUNCHED("sk_reduce_ln_kernel");
     return FG_OK;
 }
 

@@ -72,11 +72,15 @@ int check_layer(const fg_dims* d, const fg_layer_w* w, const void* x, const fg_k
     return FG_OK;
 }
 
+// ln_g / ln_b / ln_y: optional LayerNorm of the output rows (fused with the
+// split-k sum when the GEMM has one)
 int lin(const fg_layer_w* w, int which, const __half* x, int64_t M, int64_t K, int64_t N,
-        int32_t act, const __half* res, __half* y, void* part, size_t part_bytes, hipStream_t st) {
+        int32_t act, const __half* res, __half* y, void* part, size_t part_bytes, hipStream_t st,
+        const void* ln_g = nullptr, const void* ln_b = nullptr, __half* ln_y = nullptr) {
     LinearArgs a{};
     a.x = x; a.M = M; a.K = K; a.ldx = K; a.fmt = w->fmt; a.N = N; a.act = act;
     a.residual = res; a.y = y; a.ldy = N; a.ws = part; a.ws_bytes = part_bytes;
+    a.ln_g = (const __half*)ln_g; a.ln_b = (const __half*)ln_b; a.ln_y = ln_y;
     switch (which) {
         case 0: a.w = w->w_qkv; a.meta = (const __half*)w->m_qkv; a.bias = (const __half*)w->b_qkv; break;
         case 1: a.w = w->w_o; a.meta = (const __half*)w->m_o; a.bias = (const __half*)w->b_o; break;
@@ -90,7 +94,7 @@ int lin(const fg_layer_w* w, int which, const __half* x, int64_t M, int64_t K, i
 
 int layer_decode(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, int32_t nb,
                  int32_t pos, const fg_kv* kv, void* ws, size_t ws_bytes, hipStream_t st,
-                 bool check_only) {
+                 bool check_only, bool ln1_done, const fg_layer_w* next) {
     FG_TRY(check_layer(d, w, x, kv, ws));
     FG_CHECK_ARG(gbs >= 1 && nb >= 1 && (int64_t)gbs * nb <= kv->n_seq,
                  "block %d x %d exceeds the cache's %d sequences", gbs, nb, kv->n_seq);
@@ -111,13 +115,16 @@ int layer_decode(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, in
     __half* xh = (__half*)x;
     const int64_t h1 = d->h1, h2 = d->h2;
 
-    FG_TRY(launch_layernorm(xh, bls, h1, (const __half*)w->ln1_g, (const __half*)w->ln1_b, a, st));
+    if (!ln1_done)
+        FG_TRY(launch_layernorm(xh, bls, h1, (const __half*)w->ln1_g, (const __half*)w->ln1_b, a, st));
     FG_TRY(lin(w, 0, a, bls, h1, 3 * h1, 0, nullptr, qkv, part, pb, st));
     FG_TRY(launch_attn_decode(qkv, qkv + h1, qkv + 2 * h1, 3 * h1, kv, (int32_t)bls, d, pos, 1, o, st));
-    FG_TRY(lin(w, 1, o, bls, h1, h1, 0, xh, xh, part, pb, st));
-    FG_TRY(launch_layernorm(xh, bls, h1, (const __half*)w->ln2_g, (const __half*)w->ln2_b, a, st));
+    FG_TRY(lin(w, 1, o, bls, h1, h1, 0, xh, xh, part, pb, st, w->ln2_g, w->ln2_b, a));
     FG_TRY(lin(w, 2, a, bls, h1, h2, 1, nullptr, f, part, pb, st));
-    FG_TRY(lin(w, 3, f, bls, h2, h1, 0, xh, xh, part, pb, st));
+    if (next)   // the next layer's first LayerNorm, fused with this residual sum
+        FG_TRY(lin(w, 3, f, bls, h2, h1, 0, xh, xh, part, pb, st, next->ln1_g, next->ln1_b, a));
+    else
+        FG_TRY(lin(w, 3, f, bls, h2, h1, 0, xh, xh, part, pb, st));
     return FG_OK;
 }
 
@@ -149,8 +156,7 @@ int layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, i
         FG_TRY(lin(w, 0, a, rows, h1, 3 * h1, 0, nullptr, qkv, part, pb, st));
         FG_TRY(launch_attn_prefill(qkv, gbs, s, d, o, st));
         FG_TRY(launch_kv_store(qkv + h1, qkv + 2 * h1, 3 * h1, kv, k * gbs, gbs, 0, s, d, st));
-        FG_TRY(lin(w, 1, o, rows, h1, h1, 0, xh, xh, part, pb, st));
-        FG_TRY(launch_layernorm(xh, rows, h1, (const __half*)w->ln2_g, (const __half*)w->ln2_b, a, st));
+        FG_TRY(lin(w, 1, o, rows, h1, h1, 0, xh, xh, part, pb, st, w->ln2_g, w->ln2_b, a));
         FG_TRY(lin(w, 2, a, rows, h1, h2, 1, nullptr, f, part, pb, st));
         FG_TRY(lin(w, 3, f, rows, h2, h1, 0, xh, xh, part, pb, st));
     }
@@ -170,7 +176,8 @@ extern "C" int fg_layer_decode_block(const fg_dims* d, const fg_layer_w* w, void
                                      int32_t nb, int32_t pos, const fg_kv* kv, void* ws,
                                      size_t ws_bytes, void* stream) {
     fg::clear_error();
-    return fg::layer_decode(d, w, x, gbs, nb, pos, kv, ws, ws_bytes, fg::as_stream(stream), false);
+    return fg::layer_decode(d, w, x, gbs, nb, pos, kv, ws, ws_bytes, fg::as_stream(stream), false,
+                            false, nullptr);
 }
 
 extern "C" int fg_layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs,

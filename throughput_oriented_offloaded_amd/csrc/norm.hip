@@ -1,41 +1,15 @@
 // Row-wise kernels of the decoder: LayerNorm, token + position embedding,
 // greedy argmax.  All HBM/latency-bound and tiny next to the projections and
 // attention; each row is one 256-thread workgroup reading 16-byte vectors.
-#include "fg_internal.h"
 #include "fg_trace.h"
+#include "rowops.h"
 
 namespace fg {
 namespace {
 
-constexpr int NT = 256;
-
-__device__ __forceinline__ float block_sum(float v, float* sh) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    __syncthreads();
-    if (l == 0) sh[w] = v;
-    __syncthreads();
-    float t = 0.f;
-#pragma unroll
-    for (int i = 0; i < NT / 64; ++i) t += sh[i];
-    return t;
-}
-
-__device__ __forceinline__ void load8(const __half* p, float v[8]) {
-    uint4 r = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __half2float(__ushort_as_half((unsigned short)(w[i] & 0xffff)));
-        v[2 * i + 1] = __half2float(__ushort_as_half((unsigned short)(w[i] >> 16)));
-    }
-}
-
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-    return (uint32_t)__half_as_ushort(__float2half_rn(a)) |
-           ((uint32_t)__half_as_ushort(__float2half_rn(b)) << 16);
-}
+using row::NT;
+using row::load8;
+using row::pack2;
 
 // LayerNorm of one row per workgroup; up to MAXV 8-element vectors per thread
 // stay in registers between the mean, variance and output passes.
@@ -45,8 +19,8 @@ __global__ __launch_bounds__(NT) void layernorm_kernel(const __half* __restrict_
                                                        const __half* __restrict__ b,
                                                        __half* __restrict__ y) {
     __shared__ float sh[NT / 64];
-    const int64_t row = blockIdx.x;
-    const __half* xr = x + row * h;
+    const int64_t r = blockIdx.x;
+    const __half* xr = x + r * h;
     const int nv = (int)(h / 8);
     float v[MAXV][8];
     float s = 0.f;
@@ -59,37 +33,7 @@ __global__ __launch_bounds__(NT) void layernorm_kernel(const __half* __restrict_
             for (int j = 0; j < 8; ++j) s += v[i][j];
         }
     }
-    const float mean = block_sum(s, sh) / (float)h;
-    float q = 0.f;
-#pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
-        const int vi = threadIdx.x + i * NT;
-        if (vi < nv) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float d = v[i][j] - mean;
-                q += d * d;
-            }
-        }
-    }
-    const float var = block_sum(q, sh) / (float)h;
-    const float rstd = 1.0f / sqrtf(var + 1e-5f);
-#pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
-        const int vi = threadIdx.x + i * NT;
-        if (vi < nv) {
-            float gv[8], bv[8];
-            load8(g + vi * 8, gv);
-            load8(b + vi * 8, bv);
-            uint4 o;
-            uint32_t* ow = reinterpret_cast<uint32_t*>(&o);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                ow[j] = pack2((v[i][2 * j] - mean) * rstd * gv[2 * j] + bv[2 * j],
-                              (v[i][2 * j + 1] - mean) * rstd * gv[2 * j + 1] + bv[2 * j + 1]);
-            *reinterpret_cast<uint4*>(y + row * h + vi * 8) = o;
-        }
-    }
+    row::layernorm_row<MAXV>(v, s, h, g, b, y + r * h, sh);
 }
 
 __global__ __launch_bounds__(NT) void embed_kernel(const int32_t* __restrict__ tok,

@@ -212,6 +212,9 @@ extern "C" int fg_model_decode_step(fg_sched* sc, const fg_dims* d, int32_t n_la
     hipStream_t st = as_stream(stream);
     return run_layers(sc, d, n_layers, w, tier, st, as_stream(copy_stream), flags,
                       [&](int32_t j, const fg_layer_w& wj, bool chk) {
-                          return layer_decode(d, &wj, x, gbs, nb, pos, &kv[j], ws, ws_bytes, st, chk);
+                          // each layer's input LayerNorm runs fused into the
+                          // previous layer's last residual sum
+                          return layer_decode(d, &wj, x, gbs, nb, pos, &kv[j], ws, ws_bytes, st, chk,
+                                              j > 0, j + 1 < n_layers ? &w[j + 1] : nullptr);
                       });
 }
