@@ -137,7 +137,7 @@ def profile_layer(cfg, reps: int):
 # calibrated on a copy of known size), committed per workload with the sha256
 # of the measured kernel's sources; reported only while those are unchanged.
 TRAFFIC_FILES = {5: "opt175b_q4_decode_hbm_traffic.md"}
-KERNEL_SOURCES = {"gemm_q4": ["gemm_sk.hip", "gemm_common.h"],
+KERNEL_SOURCES = {"gemm_q4": ["gemm_sk.hip", "gemm_sk32.hip", "gemm_common.h"],
                   "attn_decode_q4": ["attn_decode.hip", "codec_dev.h"]}
 
 
