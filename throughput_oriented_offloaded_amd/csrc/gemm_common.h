@@ -123,12 +123,35 @@ __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, const vo
 // Stream-K schedule of the decode-shaped kernel (gemm_sk.hip): T = tiles x nk
 // iterations (tile, 64-wide k-step) split evenly over G workgroups.
 constexpr int kSkGroups = 256;   // one workgroup per CU of the 256-CU part
+constexpr int64_t kSkDpRows = 576;   // above: data-parallel whole tiles (prefill shapes)
 struct SkSched {
     int64_t T, G, nk;     // iterations, workgroups, k-steps per tile
     int64_t ntn, bm, bn;  // N tiles, tile rows, tile columns
     int64_t slots;        // partial slots per output element (1: none needed)
     int32_t wide;         // 1: 32-row blocks on 32x32x16 MFMA (gemm_sk32.hip)
+    int32_t dp;           // 1: data-parallel, whole tiles g, g + G, ... (large M)
+    int64_t tiles, mt;    // output tiles; M tiles
+    int64_t band;         // dp: M tiles per band of the tile order
 };
+
+// Output tile of linear index `tile`.  Stream-K: row-major (tm, tn).  Data-
+// parallel: bands of `band` M tiles, M tile fastest inside a band, so the G
+// tiles in flight at once cover about band x G/band tiles and share their
+// activation and weight slices through L2 and the infinity cache.
+__device__ __host__ __forceinline__ void sk_tile_coords(const SkSched& sc, int64_t tile, int64_t& tm,
+                                                        int64_t& tn) {
+    if (!sc.dp) {
+        tm = tile / sc.ntn;
+        tn = tile - tm * sc.ntn;
+        return;
+    }
+    const int64_t per_band = sc.band * sc.ntn;
+    const int64_t b = tile / per_band, r = tile - b * per_band;
+    const int64_t left = sc.mt - b * sc.band;
+    const int64_t gm = left < sc.band ? left : sc.band;      // the last band may be narrower
+    tm = b * sc.band + r % gm;
+    tn = r / gm;
+}
 
 // workgroup holding iteration x of T split over G: ceil((x + 1) G / T) - 1
 __device__ __host__ __forceinline__ int64_t sk_owner(int64_t x, int64_t T, int64_t G) {

@@ -105,12 +105,25 @@ __global__ __launch_bounds__(C::NT) void sk_kernel(Params p, SkSched sc) {
     const int64_t g = blockIdx.x;
     const int64_t it_beg = g * sc.T / sc.G, it_end = (g + 1) * sc.T / sc.G;
 
-    for (int64_t it = it_beg; it < it_end;) {
-        const int64_t tile = it / sc.nk;
-        const int kb = (int)(it - tile * sc.nk);
-        const int ke = (int)(min(it_end, (tile + 1) * sc.nk) - tile * sc.nk);
-        it = tile * sc.nk + ke;
-        const int64_t tm = tile / sc.ntn, tn = tile - tm * sc.ntn;
+    int64_t it = it_beg, next_tile = g;
+    for (;;) {
+        int64_t tile;
+        int kb, ke;
+        if (sc.dp) {   // whole tiles g, g + G, ...
+            tile = next_tile;
+            if (tile >= sc.tiles) break;
+            next_tile += sc.G;
+            kb = 0;
+            ke = (int)sc.nk;
+        } else {       // stream-K: this workgroup's share of the iterations
+            if (it >= it_end) break;
+            tile = it / sc.nk;
+            kb = (int)(it - tile * sc.nk);
+            ke = (int)(min(it_end, (tile + 1) * sc.nk) - tile * sc.nk);
+            it = tile * sc.nk + ke;
+        }
+        int64_t tm, tn;
+        sk_tile_coords(sc, tile, tm, tn);
         const int64_t n0 = tn * C::BN, m0 = tm * C::BM;
         const int nk = ke - kb;
         const int64_t kbeg = (int64_t)kb * C::BK;
@@ -345,7 +358,7 @@ __global__ __launch_bounds__(C::NT) void sk_kernel(Params p, SkSched sc) {
         // add the two k-halves (kh = 1 -> LDS -> kh = 0), two fragments per round
         const int64_t gf = sk_owner(tile * sc.nk, sc.T, sc.G);
         const int64_t gl = sk_owner((tile + 1) * sc.nk - 1, sc.T, sc.G);
-        const bool full = gf == gl;
+        const bool full = sc.dp || gf == gl;
         const int slot = (int)(g - gf);
         const int nq = q * 4;
 #pragma unroll
@@ -548,12 +561,26 @@ int64_t sk_rows_for(int64_t M, int32_t& wide) {
 
 SkSched sk_schedule(int64_t M, int64_t N, int64_t K) {
     SkSched sc{};
-    sc.bm = sk_rows_for(M, sc.wide);
     sc.bn = 256;
     sc.ntn = cdiv(N, sc.bn);
-    const int64_t tiles = cdiv(M, sc.bm) * sc.ntn;
     sc.nk = K / 64;
-    sc.T = tiles * sc.nk;
+    if (M > kSkDpRows) {
+        // many tiles per workgroup: data-parallel whole tiles, no partials;
+        // 128- or 144-row tiles, whichever pads M less
+        sc.dp = 1;
+        sc.bm = cdiv(M, 144) * 144 <= cdiv(M, 128) * 128 ? 144 : 128;
+        sc.mt = cdiv(M, sc.bm);
+        sc.tiles = sc.mt * sc.ntn;
+        sc.T = sc.tiles * sc.nk;
+        sc.G = std::min<int64_t>(kSkGroups, sc.tiles);
+        sc.band = 16;
+        sc.slots = 1;
+        return sc;
+    }
+    sc.bm = sk_rows_for(M, sc.wide);
+    sc.mt = cdiv(M, sc.bm);
+    sc.tiles = sc.mt * sc.ntn;
+    sc.T = sc.tiles * sc.nk;
     // one workgroup per CU of the 256-CU part (a constant, so the schedule and
     // its workspace depend on the shape only), at least 4 k-steps each
     sc.G = std::max<int64_t>(1, std::min<int64_t>(kSkGroups, sc.T / 4));
