@@ -77,31 +77,39 @@ def test_decode_block_matches_oracle(L, fmt, kvfmt, P):
         assert same > 0.9, f"appended codes agree on only {same:.3f}"
 
 
-@pytest.mark.parametrize("fmt", ["q4", "f16"])
-def test_prefill_matches_oracle(L, fmt):
+# FFN wide enough (h2 > 32768) that FC2 keeps its 4-bit weights in the
+# prefill-shaped GEMMs while the other three run from fp16 copies
+WIDE_FF = dict(h1=128, h2=33024, nh=2, hd=64)
+
+
+@pytest.mark.parametrize("shp,fmt,s", [
+    (OPT125, "q4", 37), (OPT125, "f16", 37),
+    # 600 rows per GPU batch: the prefill-shaped (data-parallel) GEMMs
+    (OPT125, "q4", 300), (OPT125, "f16", 300), (WIDE_FF, "q4", 300)])
+def test_prefill_matches_oracle(L, shp, fmt, s):
     import torch
     from throughput_oriented_offloaded_amd.model import DeviceKV
-    gbs, nb, s = 2, 2, 37
+    gbs, nb = 2, 2
     bls = gbs * nb
-    dl, Wn, od = _layer(L, OPT125, fmt, seed=7)
-    d = L.dims(OPT125["h1"], OPT125["h2"], OPT125["nh"], OPT125["hd"])
-    kv = DeviceKV(dl.fmt, bls, OPT125["nh"], OPT125["hd"], s + 2, "cuda")
-    x = synth.activations(bls * s, OPT125["h1"], seed=8)
+    dl, Wn, od = _layer(L, shp, fmt, seed=7)
+    d = L.dims(shp["h1"], shp["h2"], shp["nh"], shp["hd"])
+    kv = DeviceKV(dl.fmt, bls, shp["nh"], shp["hd"], s + 2, "cuda")
+    x = synth.activations(bls * s, shp["h1"], seed=8)
     xd = x.cuda()
     ws = torch.empty(L.fg_workspace_bytes(d, gbs * s, dl.fmt), dtype=torch.uint8, device="cuda")
     L.fg_layer_prefill(d, dl.struct, xd, gbs, nb, s, kv.struct, ws, ws.numel())
     torch.cuda.synchronize()
-    oc = oracle.KVCache("q4" if fmt == "q4" else "f16", bls, OPT125["nh"], OPT125["hd"], s + 2)
+    oc = oracle.KVCache("q4" if fmt == "q4" else "f16", bls, shp["nh"], shp["hd"], s + 2)
     ref = oracle.layer_prefill(od, Wn, x.numpy().view(np.uint16), bls, s, oc)
     assert_close(np16(xd), ref, f"prefill {fmt}")
     # cached history: dequantized K, V within tolerance of the oracle's
     from helpers import f32
     if fmt == "q4":
-        h1 = OPT125["h1"]
-        kd = torch.empty((bls * OPT125["nh"] * (s + 2), OPT125["hd"]), dtype=torch.float16, device="cuda")
-        L.fg_dequant_group4(kv.k, kv.km, bls * OPT125["nh"] * (s + 2), OPT125["hd"], 1, kd)
+        h1 = shp["h1"]
+        kd = torch.empty((bls * shp["nh"] * (s + 2), shp["hd"]), dtype=torch.float16, device="cuda")
+        L.fg_dequant_group4(kv.k, kv.km, bls * shp["nh"] * (s + 2), shp["hd"], 1, kd)
         torch.cuda.synchronize()
-        got = np16(kd).reshape(bls, OPT125["nh"], s + 2, OPT125["hd"])[:, :, :s]
+        got = np16(kd).reshape(bls, shp["nh"], s + 2, shp["hd"])[:, :, :s]
         want = oc.history()[0][:, :, :s]
         assert np.abs(f32(got) - f32(want)).max() <= 0.15 * np.abs(f32(want)).max()
         assert np.mean(kv.k[:, :, :s].cpu().numpy() == oc.k[:, :, :s]) > 0.9

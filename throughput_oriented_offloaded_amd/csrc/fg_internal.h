@@ -94,6 +94,8 @@ struct LinearArgs {
 };
 int launch_linear(const LinearArgs& a, hipStream_t st);
 size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t fmt);
+// M rows take the data-parallel (prefill-shaped) GEMM schedule
+bool linear_is_dp(int64_t M);
 // One decoder layer (layer.hip): arguments validated, then (unless
 // check_only) enqueued on st.
 // ln1_done: the layer's input LayerNorm is already in the workspace (the

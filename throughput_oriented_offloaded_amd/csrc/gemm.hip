@@ -23,6 +23,8 @@
 
 namespace fg {
 
+bool linear_is_dp(int64_t M) { return M > gemm::kSkDpRows; }
+
 size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t) {
     const gemm::SkSched sc = gemm::sk_schedule(M, N, K);
     return sc.slots > 1 ? (size_t)sc.slots * M * N * sizeof(float) : 0;

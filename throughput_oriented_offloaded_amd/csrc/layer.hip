@@ -17,8 +17,21 @@ namespace fg {
 namespace {
 
 struct WsLayout {
-    size_t a, qkv, o, f, part, total;
+    size_t a, qkv, o, f, part, wdq, total;
 };
+
+// fp16 copies of a 4-bit layer's weight matrices for the prefill-shaped
+// GEMMs.  Only matrices whose contraction length K keeps the weight slices of
+// one band of tiles in flight (16 x 256 rows x K x 2 B) within the 256 MB
+// infinity cache: beyond that the fp16 path re-reads its weights from HBM and
+// the 4-bit path is faster (measured on the OPT-175B FC2, K = 49152).
+constexpr int64_t kPrefillF16MaxK = 32768;
+bool prefill_dequant(int64_t rows, int32_t fmt) { return fmt == FG_FMT_Q4G64 && linear_is_dp(rows); }
+bool dq_fc2(const fg_dims* d) { return d->h2 <= kPrefillF16MaxK; }
+size_t wdq_elems(const fg_dims* d) {
+    const size_t h1 = d->h1, h2 = d->h2;
+    return 3 * h1 * h1 + h1 * h1 + h2 * h1 + (dq_fc2(d) ? h1 * h2 : 0);
+}
 
 size_t part_bytes(const fg_dims* d, int64_t rows, int32_t fmt) {
     const int64_t h1 = d->h1, h2 = d->h2;
@@ -40,6 +53,8 @@ WsLayout layout(const fg_dims* d, int64_t rows, int32_t fmt) {
     L.f = off;   off = align_up(off + (size_t)rows * d->h2 * 2, A);
     L.part = off;
     off = align_up(off + part_bytes(d, rows, fmt), A);
+    L.wdq = off;
+    if (prefill_dequant(rows, fmt)) off = align_up(off + wdq_elems(d) * 2, A);
     L.total = off;
     return L;
 }
@@ -73,12 +88,15 @@ int check_layer(const fg_dims* d, const fg_layer_w* w, const void* x, const fg_k
 }
 
 // ln_g / ln_b / ln_y: optional LayerNorm of the output rows (fused with the
-// split-k sum when the GEMM has one)
+// split-k sum when the GEMM has one); dq: bit `which` set when that matrix's
+// pointer holds an fp16 copy of 4-bit weights
 int lin(const fg_layer_w* w, int which, const __half* x, int64_t M, int64_t K, int64_t N,
         int32_t act, const __half* res, __half* y, void* part, size_t part_bytes, hipStream_t st,
-        const void* ln_g = nullptr, const void* ln_b = nullptr, __half* ln_y = nullptr) {
+        const void* ln_g = nullptr, const void* ln_b = nullptr, __half* ln_y = nullptr,
+        unsigned dq = 0) {
     LinearArgs a{};
     a.x = x; a.M = M; a.K = K; a.ldx = K; a.fmt = w->fmt; a.N = N; a.act = act;
+    if (dq & (1 << which)) a.fmt = FG_FMT_F16;   // restored to fp16 for this call
     a.residual = res; a.y = y; a.ldy = N; a.ws = part; a.ws_bytes = part_bytes;
     a.ln_g = (const __half*)ln_g; a.ln_b = (const __half*)ln_b; a.ln_y = ln_y;
     switch (which) {
@@ -111,7 +129,7 @@ int layer_decode(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, in
     __half* o = (__half*)(base + L.o);
     __half* f = (__half*)(base + L.f);
     void* part = base + L.part;
-    const size_t pb = L.total - L.part;
+    const size_t pb = L.wdq - L.part;
     __half* xh = (__half*)x;
     const int64_t h1 = d->h1, h2 = d->h2;
 
@@ -147,18 +165,42 @@ int layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, i
     __half* o = (__half*)(base + L.o);
     __half* f = (__half*)(base + L.f);
     void* part = base + L.part;
-    const size_t pb = L.total - L.part;
+    const size_t pb = L.wdq - L.part;
     const int64_t h1 = d->h1, h2 = d->h2;
 
+    // Prefill-shaped GEMMs with 4-bit weights: each matrix is restored to fp16
+    // once per layer (the compression is for storage and transfer; compute is
+    // fp16) and every GPU batch of the block multiplies on the fp16 path.
+    // Re-dequantizing a weight tile for every tile of rows, as the fused kernel
+    // would, costs more than this one pass at these row counts.
+    fg_layer_w wl = *w;
+    unsigned dq = 0;   // matrices multiplied from an fp16 copy (bit = which)
+    if (prefill_dequant(rows, w->fmt)) {
+        dq = dq_fc2(d) ? 0xFu : 0x7u;
+        __half* p_qkv = (__half*)(base + L.wdq);
+        __half* p_o = p_qkv + 3 * h1 * h1;
+        __half* p_1 = p_o + h1 * h1;
+        __half* p_2 = p_1 + h2 * h1;
+        FG_TRY(launch_dequant_g4((const uint8_t*)w->w_qkv, (const __half*)w->m_qkv, 1, 3 * h1, h1, p_qkv, st));
+        FG_TRY(launch_dequant_g4((const uint8_t*)w->w_o, (const __half*)w->m_o, 1, h1, h1, p_o, st));
+        FG_TRY(launch_dequant_g4((const uint8_t*)w->w_1, (const __half*)w->m_1, 1, h2, h1, p_1, st));
+        if (dq_fc2(d)) FG_TRY(launch_dequant_g4((const uint8_t*)w->w_2, (const __half*)w->m_2, 1, h1, h2, p_2, st));
+        wl.w_qkv = p_qkv; wl.w_o = p_o; wl.w_1 = p_1;
+        wl.m_qkv = wl.m_o = wl.m_1 = nullptr;
+        if (dq_fc2(d)) {
+            wl.w_2 = p_2;
+            wl.m_2 = nullptr;
+        }
+    }
     for (int32_t k = 0; k < nb; ++k) {     // GPU batches of the block, one layer resident
         __half* xh = (__half*)x + (int64_t)k * rows * h1;
-        FG_TRY(launch_layernorm(xh, rows, h1, (const __half*)w->ln1_g, (const __half*)w->ln1_b, a, st));
-        FG_TRY(lin(w, 0, a, rows, h1, 3 * h1, 0, nullptr, qkv, part, pb, st));
+        FG_TRY(launch_layernorm(xh, rows, h1, (const __half*)wl.ln1_g, (const __half*)wl.ln1_b, a, st));
+        FG_TRY(lin(&wl, 0, a, rows, h1, 3 * h1, 0, nullptr, qkv, part, pb, st, nullptr, nullptr, nullptr, dq));
         FG_TRY(launch_attn_prefill(qkv, gbs, s, d, o, st));
         FG_TRY(launch_kv_store(qkv + h1, qkv + 2 * h1, 3 * h1, kv, k * gbs, gbs, 0, s, d, st));
-        FG_TRY(lin(w, 1, o, rows, h1, h1, 0, xh, xh, part, pb, st, w->ln2_g, w->ln2_b, a));
-        FG_TRY(lin(w, 2, a, rows, h1, h2, 1, nullptr, f, part, pb, st));
-        FG_TRY(lin(w, 3, f, rows, h2, h1, 0, xh, xh, part, pb, st));
+        FG_TRY(lin(&wl, 1, o, rows, h1, h1, 0, xh, xh, part, pb, st, wl.ln2_g, wl.ln2_b, a, dq));
+        FG_TRY(lin(&wl, 2, a, rows, h1, h2, 1, nullptr, f, part, pb, st, nullptr, nullptr, nullptr, dq));
+        FG_TRY(lin(&wl, 3, f, rows, h2, h1, 0, xh, xh, part, pb, st, nullptr, nullptr, nullptr, dq));
     }
     return FG_OK;
 }
