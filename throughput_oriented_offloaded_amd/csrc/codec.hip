@@ -151,6 +151,68 @@ __global__ __launch_bounds__(256) void quant_strided_kernel(const __half* __rest
     }
 }
 
+// Strided groups, 4 columns per thread, the whole 64-row group held in
+// registers (64 x 8 B): every row is loaded once, all loads issued before any
+// is used; consecutive threads own consecutive columns, so a workgroup reads
+// 2 KB contiguous per row.  Min / max on packed fp16 pairs (exact: the inputs
+// are fp16); the codes use the codec's fp32 formula.
+__global__ __launch_bounds__(256) void quant_strided_reg_kernel(const __half* __restrict__ x,
+                                                                int64_t outer, int64_t axis,
+                                                                int64_t inner,
+                                                                uint8_t* __restrict__ codes,
+                                                                __half* __restrict__ meta) {
+    typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+    const int64_t ngroups = axis / G;
+    const int64_t ncol = inner / 4;
+    const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (tid >= outer * ngroups * ncol) return;
+    const int64_t ci = tid % ncol;
+    const int64_t og = tid / ncol;
+    const int64_t g = og % ngroups, o = og / ngroups;
+    const int64_t i0 = ci * 4;
+    const __half* base = x + (o * axis + g * G) * inner + i0;
+
+    uint2 r[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) r[j] = *reinterpret_cast<const uint2*>(base + (int64_t)j * inner);
+    h2v lo_mn = __builtin_bit_cast(h2v, r[0].x), lo_mx = lo_mn;   // columns 0, 1
+    h2v hi_mn = __builtin_bit_cast(h2v, r[0].y), hi_mx = hi_mn;   // columns 2, 3
+#pragma unroll
+    for (int j = 1; j < G; ++j) {
+        const h2v a = __builtin_bit_cast(h2v, r[j].x), b = __builtin_bit_cast(h2v, r[j].y);
+        lo_mn = __builtin_elementwise_min(lo_mn, a);
+        lo_mx = __builtin_elementwise_max(lo_mx, a);
+        hi_mn = __builtin_elementwise_min(hi_mn, b);
+        hi_mx = __builtin_elementwise_max(hi_mx, b);
+    }
+    QParams p[4];
+    p[0] = qparams((float)lo_mn[0], (float)lo_mx[0]);
+    p[1] = qparams((float)lo_mn[1], (float)lo_mx[1]);
+    p[2] = qparams((float)hi_mn[0], (float)hi_mx[0]);
+    p[3] = qparams((float)hi_mn[1], (float)hi_mx[1]);
+
+    uint8_t* cbase = codes + (o * (axis / 2) + g * (G / 2)) * inner + i0;
+#pragma unroll
+    for (int j = 0; j < G; j += 2) {
+        const uint32_t A[2] = {r[j].x, r[j].y}, B[2] = {r[j + 1].x, r[j + 1].y};
+        uint32_t word = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float a = h2f_bits(A[c >> 1] >> (16 * (c & 1)));
+            const float b = h2f_bits(B[c >> 1] >> (16 * (c & 1)));
+            word |= (qcode(a, p[c]) | (qcode(b, p[c]) << 4)) << (8 * c);
+        }
+        *reinterpret_cast<uint32_t*>(cbase + (int64_t)(j / 2) * inner) = word;
+    }
+    __half* mbase = meta + (o * ngroups + g) * 2 * inner + i0;
+    uint32_t mb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) mb[c] = qmeta_bits(p[c]);
+    *reinterpret_cast<uint2*>(mbase) = make_uint2((mb[0] & 0xffffu) | (mb[1] << 16), (mb[2] & 0xffffu) | (mb[3] << 16));
+    *reinterpret_cast<uint2*>(mbase + inner) =
+        make_uint2((mb[0] >> 16) | (mb[1] & 0xffff0000u), (mb[2] >> 16) | (mb[3] & 0xffff0000u));
+}
+
 template <int C>
 __global__ __launch_bounds__(256) void dequant_strided_kernel(const uint8_t* __restrict__ codes,
                                                               const __half* __restrict__ meta,
@@ -180,11 +242,23 @@ __global__ __launch_bounds__(256) void dequant_strided_kernel(const uint8_t* __r
             word = *reinterpret_cast<const uint32_t*>(cbase + (int64_t)(j / 2) * inner);
         else
             word = cbase[(int64_t)(j / 2) * inner];
+        if constexpr (C == 4) {
+            uint32_t e[4], f[4];   // rows j, j + 1 of the 4 columns
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-            uint32_t byte = (word >> (8 * c)) & 0xffu;
-            ybase[(int64_t)j * inner + c] = dq_value(byte & 15u, mn[c], sc[c]);
-            ybase[(int64_t)(j + 1) * inner + c] = dq_value(byte >> 4, mn[c], sc[c]);
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t byte = (word >> (8 * c)) & 0xffu;
+                e[c] = __half_as_ushort(dq_value(byte & 15u, mn[c], sc[c]));
+                f[c] = __half_as_ushort(dq_value(byte >> 4, mn[c], sc[c]));
+            }
+            *reinterpret_cast<uint2*>(ybase + (int64_t)j * inner) = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+            *reinterpret_cast<uint2*>(ybase + (int64_t)(j + 1) * inner) = make_uint2(f[0] | (f[1] << 16), f[2] | (f[3] << 16));
+        } else {
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                uint32_t byte = (word >> (8 * c)) & 0xffu;
+                ybase[(int64_t)j * inner + c] = dq_value(byte & 15u, mn[c], sc[c]);
+                ybase[(int64_t)(j + 1) * inner + c] = dq_value(byte >> 4, mn[c], sc[c]);
+            }
         }
     }
 }
@@ -204,9 +278,9 @@ int launch_quant_g4(const __half* x, int64_t outer, int64_t axis, int64_t inner,
                                                            reinterpret_cast<uint32_t*>(meta));
         FG_LAUNCHED("quant_contig_kernel");
     } else if (inner % 4 == 0) {
-        quant_strided_kernel<4><<<grid_of(outer * ngroups * (inner / 4)), 256, 0, st>>>(
+        quant_strided_reg_kernel<<<grid_of(outer * ngroups * (inner / 4)), 256, 0, st>>>(
             x, outer, axis, inner, codes, meta);
-        FG_LAUNCHED("quant_strided_kernel<4>");
+        FG_LAUNCHED("quant_strided_reg_kernel");
     } else {
         quant_strided_kernel<1><<<grid_of(outer * ngroups * inner), 256, 0, st>>>(
             x, outer, axis, inner, codes, meta);
