@@ -1,4 +1,4 @@
-// Pieces shared by the projection GEMM kernels (gemm.hip, gemm_sk.hip).
+// Pieces shared by the projection GEMM kernels (gemm.hip, gemm_sk.hip, gemm_sk32.hip).
 #pragma once
 
 #include "fg_internal.h"
@@ -10,8 +10,8 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-// y = act(x W^T + bias) + residual over one k-split; partials to `part` when
-// the contraction is split over grid.z.
+// y = act(x W^T + bias) + residual; tiles shared between workgroups leave
+// fp32 partials in `part`.
 struct Params {
     const __half* x;
     int64_t M, K, ldx;
@@ -23,8 +23,7 @@ struct Params {
     const __half* residual;
     __half* y;
     int64_t ldy;
-    float* part;         // split-K partials [S][M][N] or null
-    int64_t kchunk;      // k range of one split (multiple of 64)
+    float* part;         // stream-K partials [slots][M][N] or null
 };
 
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
@@ -38,9 +37,10 @@ __device__ __forceinline__ float h2f(uint32_t bits16) {
 
 // 8 consecutive k codes of one weight row (nibble `sh` of 8 bytes) -> fp16
 // w = q * scale + min with the (min, scale) pairs of those k: nibble ->
-// (0x6400 | q) = 1024 + q via v_perm_b32, minus 1024 (exact), one fp16 FMA
-// (q * scale is exact, so one rounding: the multiply-then-add result except in
-// double-rounding corner cases of the fp32 definition).
+// (0x6400 | q) = 1024 + q via v_perm_b32, minus 1024 (exact), then one fused
+// fp16 multiply-add, so q * scale + min is rounded once, to fp16 (the fp32
+// definition rounds to fp32 first; the two differ only where that first
+// rounding lands on an fp16 tie).
 __device__ __forceinline__ h8 dequant8(uint2 c, uint32_t sh, const uint4& mn, const uint4& sc) {
     const uint32_t d0 = (c.x >> sh) & 0x0f0f0f0fu;
     const uint32_t d1 = (c.y >> sh) & 0x0f0f0f0fu;
@@ -85,16 +85,6 @@ __device__ __forceinline__ void store4_final(const Params& p, int64_t m, int64_t
     }
     *reinterpret_cast<uint2*>(p.y + m * p.ldy + n) =
         make_uint2(pack_h2(o[0], o[1]), pack_h2(o[2], o[3]));
-}
-
-// Same, or the fp32 partial of k-split z when the contraction is split.
-__device__ __forceinline__ void store4(const Params& p, int64_t m, int64_t n, const f4& v, int z) {
-    if (p.part) {
-        float* dst = p.part + ((int64_t)z * p.M + m) * p.N + n;
-        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-        return;
-    }
-    store4_final(p, m, n, v);
 }
 
 // s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory

@@ -406,7 +406,8 @@ __global__ __launch_bounds__(C::NT) void sk_kernel(Params p, SkSched sc) {
 
 // Sum the per-segment partials of shared tiles in segment order, then bias /
 // ReLU / residual.  Tiles written whole by one workgroup are skipped.
-__global__ __launch_bounds__(256) void sk_reduce_kernel(Params p, SkSched sc) {
+// Generic form (64-bit indices): any shape.
+__global__ __launch_bounds__(256) void sk_reduce64_kernel(Params p, SkSched sc) {
     const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;   // element (m, n..n+3)
     if (idx >= p.M * p.N) return;
     const int64_t m = idx / p.N, n = idx % p.N;
@@ -434,6 +435,48 @@ __global__ __launch_bounds__(256) void sk_reduce_kernel(Params p, SkSched sc) {
         o[2] += h2f(rr.y); o[3] += h2f(rr.y >> 16);
     }
     *reinterpret_cast<uint2*>(p.y + m * p.ldy + n) = make_uint2(pack_h2(o[0], o[1]), pack_h2(o[2], o[3]));
+}
+
+// Decode shapes (the host checks that the schedule fits 32-bit arithmetic):
+// one workgroup per (row, 1024 columns), so no index division per element;
+// the segments of a 256-column tile from two 32-bit divisions; the slot
+// loads unrolled up to SMAX with clamped addresses, all in flight at once.
+template <int SMAX>
+__global__ __launch_bounds__(256) void sk_reduce_kernel(Params p, SkSched sc) {
+    const int m = blockIdx.y;
+    const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (n >= p.N) return;
+    const uint32_t T = (uint32_t)sc.T, G = (uint32_t)sc.G, nk = (uint32_t)sc.nk;
+    const uint32_t tile = (uint32_t)(m / (int)sc.bm) * (uint32_t)sc.ntn + (uint32_t)(n >> 8);
+    const uint32_t gf = ((tile * nk + 1) * G + T - 1) / T - 1;           // owner of the tile's first step
+    const uint32_t gl = ((tile + 1) * nk * G + T - 1) / T - 1;           // owner of its last step
+    if (gf == gl) return;
+    const int ns = (int)(gl - gf + 1);
+    const int64_t MN = p.M * p.N;
+    const float* pr = p.part + (int64_t)m * p.N + n;
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < SMAX; ++q) {
+        const f4 o = *reinterpret_cast<const f4*>(pr + min(q, ns - 1) * MN);
+        if (q < ns) acc += o;
+    }
+    for (int q = SMAX; q < ns; ++q) acc += *reinterpret_cast<const f4*>(pr + q * MN);
+    if (p.bias) {
+        const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n);
+        acc[0] += h2f(bb.x); acc[1] += h2f(bb.x >> 16);
+        acc[2] += h2f(bb.y); acc[3] += h2f(bb.y >> 16);
+    }
+    if (p.act == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaxf(acc[i], 0.f);
+    }
+    if (p.residual) {
+        const uint2 rr = *reinterpret_cast<const uint2*>(p.residual + (int64_t)m * p.ldy + n);
+        acc[0] += h2f(rr.x); acc[1] += h2f(rr.x >> 16);
+        acc[2] += h2f(rr.y); acc[3] += h2f(rr.y >> 16);
+    }
+    *reinterpret_cast<uint2*>(p.y + (int64_t)m * p.ldy + n) =
+        make_uint2(pack_h2(acc[0], acc[1]), pack_h2(acc[2], acc[3]));
 }
 
 // The same sum for whole rows, fused with the LayerNorm of the finished
@@ -470,7 +513,7 @@ __global__ __launch_bounds__(kLnThreads) void sk_reduce_ln_kernel(Params p, SkSc
     for (int i = 0; i < MAXU; ++i) {
         const int u = min((int)threadIdx.x + i * NT, nu - 1);   // clamped: loads stay in the row
         const int64_t n = (int64_t)u * 4;
-        const int ns = s_ns[n / sc.bn];
+        const int ns = s_ns[n >> 8];   // 256-column tiles
         // whole tile: y is final; shared tile: partials + bias / ReLU / residual
         const __half* src16 = ns == 1 ? yr + n : (rr ? rr + n : nullptr);
         const uint2 h16 = src16 ? *reinterpret_cast<const uint2*>(src16) : make_uint2(0u, 0u);
@@ -612,8 +655,18 @@ int launch_sk(const Params& p, const SkSched& sc, bool q4, hipStream_t st) {
 }
 
 int launch_sk_reduce(const Params& p, const SkSched& sc, hipStream_t st) {
-    const int64_t n4 = p.M * p.N / 4;
-    sk_reduce_kernel<<<(unsigned)cdiv(n4, 256), 256, 0, st>>>(p, sc);
+    const bool fits32 = sc.bn == 256 && p.M <= 65535 && p.N % 4 == 0 &&
+                        ((uint64_t)sc.T + 1) * (uint64_t)sc.G + (uint64_t)sc.T < (1ull << 32);
+    if (!fits32) {
+        const int64_t n4 = p.M * p.N / 4;
+        sk_reduce64_kernel<<<(unsigned)cdiv(n4, 256), 256, 0, st>>>(p, sc);
+        FG_LAUNCHED("sk_reduce64_kernel");
+        return FG_OK;
+    }
+    const dim3 grid((unsigned)cdiv(p.N, 1024), (unsigned)p.M);
+    if (sc.slots <= 2) sk_reduce_kernel<2><<<grid, 256, 0, st>>>(p, sc);
+    else if (sc.slots <= 4) sk_reduce_kernel<4><<<grid, 256, 0, st>>>(p, sc);
+    else sk_reduce_kernel<8><<<grid, 256, 0, st>>>(p, sc);
     FG_LAUNCHED("sk_reduce_kernel");
     return FG_OK;
 }
@@ -621,7 +674,7 @@ int launch_sk_reduce(const Params& p, const SkSched& sc, hipStream_t st) {
 int launch_sk_reduce_ln(const Params& p, const SkSched& sc, const __half* g, const __half* b,
                         __half* ln_y, hipStream_t st) {
     const int64_t nu = p.N / 4;
-    if (p.N % 8 != 0 || p.ldy != p.N || sc.ntn > kLnTiles || nu > kLnThreads * 8)
+    if (p.N % 8 != 0 || p.ldy != p.N || sc.bn != 256 || sc.ntn > kLnTiles || nu > kLnThreads * 8)
         return set_error(FG_ERR_UNSUPPORTED, "fused reduce + layernorm: width %lld", (long long)p.N);
     const unsigned rows = (unsigned)p.M;
     const int mu = nu <= kLnThreads ? 1 : (nu <= 2 * kLnThreads ? 2 : (nu <= 4 * kLnThreads ? 4 : 8));
