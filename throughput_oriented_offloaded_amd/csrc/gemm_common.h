@@ -87,6 +87,38 @@ __device__ __forceinline__ void store4_final(const Params& p, int64_t m, int64_t
         make_uint2(pack_h2(o[0], o[1]), pack_h2(o[2], o[3]));
 }
 
+// Epilogue of one lane: 8 consecutive output columns n..n+7 of row m (two
+// 8-byte halves: bias, residual and y need only 8-byte alignment).
+__device__ __forceinline__ void store8_final(const Params& p, int64_t m, int64_t n, const float (&v)[8]) {
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = v[i];
+    if (p.bias) {
+#pragma unroll
+        for (int hlf = 0; hlf < 2; ++hlf) {
+            const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n + 4 * hlf);
+            o[4 * hlf + 0] += h2f(bb.x); o[4 * hlf + 1] += h2f(bb.x >> 16);
+            o[4 * hlf + 2] += h2f(bb.y); o[4 * hlf + 3] += h2f(bb.y >> 16);
+        }
+    }
+    if (p.act == 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = fmaxf(o[i], 0.f);
+    }
+    if (p.residual) {
+#pragma unroll
+        for (int hlf = 0; hlf < 2; ++hlf) {
+            const uint2 rr = *reinterpret_cast<const uint2*>(p.residual + m * p.ldy + n + 4 * hlf);
+            o[4 * hlf + 0] += h2f(rr.x); o[4 * hlf + 1] += h2f(rr.x >> 16);
+            o[4 * hlf + 2] += h2f(rr.y); o[4 * hlf + 3] += h2f(rr.y >> 16);
+        }
+    }
+#pragma unroll
+    for (int hlf = 0; hlf < 2; ++hlf)
+        *reinterpret_cast<uint2*>(p.y + m * p.ldy + n + 4 * hlf) =
+            make_uint2(pack_h2(o[4 * hlf], o[4 * hlf + 1]), pack_h2(o[4 * hlf + 2], o[4 * hlf + 3]));
+}
+
 // s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory
 // operations are outstanding / until every LDS operation has completed
 constexpr int vmcnt_wait(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }

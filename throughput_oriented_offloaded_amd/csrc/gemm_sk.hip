@@ -17,12 +17,21 @@
 //    next to MFMA issue costs far more matrix-core throughput than these.
 //  * Global -> LDS traffic uses direct-to-LDS loads (global_load_lds_dwordx4)
 //    into an NS-deep ring of stage buffers [meta | X tile | weight tile], with
-//    explicit s_waitcnt vmcnt + s_barrier publication and XOR swizzles that
-//    keep fragment reads free of bank conflicts.
-//  * Software pipelining across k-steps: the codes, metadata and activation
-//    fragments of step i+1 are read from LDS while the last MFMAs of step i
-//    issue, and each weight fragment is dequantized while the MFMAs of the
-//    previous fragment run.
+//    explicit s_waitcnt vmcnt + s_barrier publication and XOR swizzles.
+//  * 4-bit k-steps: stages are published two ahead, so step i reads step
+//    i+1's codes and (min, scale) row at its start and dequantizes step i+1's
+//    four weight fragments in the MFMA shadows of its own rows; activation
+//    fragments stream two rows ahead.  The step is a fixed sequence of
+//    single-instruction volatile asm statements (each MFMA followed by 3-4
+//    VALU instructions): the compiler's scheduler otherwise packed the MFMAs
+//    together and ran the dequantization as one long VALU burst.
+//  * Column pairs: lane-row i of column blocks 2p and 2p + 1 holds weight
+//    columns 32p + 2i and 32p + 2i + 1, the two nibbles of one code byte, so
+//    one 8-byte LDS read feeds two fragments; the (min, scale) values reach
+//    every lane through row_newbcast DPP sources of the fp16 -> fp32
+//    conversions, from one 2-byte read per lane.
+//  * fp16 k-steps: stage i+1 is published at the end of step i and the next
+//    step's fragments are read while the last MFMAs of step i issue.
 //  * Stream-K: exactly G workgroups, each taking an equal contiguous share of
 //    the (tile, k-step) iterations, so no tail of partly filled rounds.  A tile
 //    covered by one workgroup is written with its epilogue; a tile shared by
@@ -56,34 +65,131 @@ struct SK {
     static_assert(LWH * (NS - 1) <= 63, "vmcnt range");
 };
 
-__device__ __forceinline__ float lo16(uint32_t w) {
-    return __half2float(__ushort_as_half((unsigned short)(w & 0xffffu)));
-}
-__device__ __forceinline__ float hi16(uint32_t w) {
-    return __half2float(__ushort_as_half((unsigned short)(w >> 16)));
-}
 // byte J of a dword as float (v_cvt_f32_ubyteJ)
 template <int J>
 __device__ __forceinline__ float ubf(uint32_t w) {
     return (float)((w >> (8 * J)) & 0xffu);
 }
 
-// An empty register constraint: the value is materialised in a VGPR as is, so
-// the compiler neither re-derives it nor fuses its producer into a consumer.
+// Single instructions as volatile asm statements.  Volatile asm keeps its
+// order relative to other volatile asm and to memory operations, so a k-step
+// written as a sequence of them issues exactly in that order: each MFMA
+// followed by the VALU work that fills its shadow.  The compiler's hazard
+// tracking does not see inside asm, so callers keep the required distances:
+// an s_nop before a DPP read or an MFMA operand read of a VGPR that a VALU
+// instruction may have just written, and before any non-MFMA read of an MFMA
+// result.
+// An empty register constraint: the value is materialised in a VGPR as is
+// and the compiler cannot derive anything from it.
 template <class T>
-__device__ __forceinline__ void opaque(T& v) {
-    asm volatile("" : "+v"(v));
+__device__ __forceinline__ void pin(T& v) {
+    asm("" : "+v"(v));
 }
 
-// Two fp32 values -> packed fp16 pair, round to nearest even.  Written as the
-// instruction itself so the FMA producing the inputs stays an fp32 FMA (the
-// compiler would otherwise fold it into a mixed-precision FMA).
-__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
-    uint32_t r;
-    asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-    return r;
+namespace op {
+__device__ __forceinline__ void mfma(f4& c, const h8& a, const h8& b) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void nop1() { asm volatile("s_nop 1"); }
+__device__ __forceinline__ void nop_mfma_result() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
+// fp16 in the low half of lane J of each 16-lane row -> fp32 in every lane
+template <int J>
+__device__ __forceinline__ void bcast_f16(float& d, uint32_t v) {
+    asm volatile("v_cvt_f32_f16_dpp %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf" : "=v"(d) : "v"(v), "i"(J));
+}
+__device__ __forceinline__ void lo_nibbles(uint32_t& d, uint32_t v) {
+    asm volatile("v_and_b32 %0, 0xf0f0f0f, %1" : "=v"(d) : "v"(v));
+}
+__device__ __forceinline__ void shr4(uint32_t& d, uint32_t v) {
+    asm volatile("v_lshrrev_b32 %0, 4, %1" : "=v"(d) : "v"(v));
+}
+template <int J>
+__device__ __forceinline__ void ubyte(float& d, uint32_t v) {
+    if constexpr (J == 0) asm volatile("v_cvt_f32_ubyte0 %0, %1" : "=v"(d) : "v"(v));
+    if constexpr (J == 1) asm volatile("v_cvt_f32_ubyte1 %0, %1" : "=v"(d) : "v"(v));
+    if constexpr (J == 2) asm volatile("v_cvt_f32_ubyte2 %0, %1" : "=v"(d) : "v"(v));
+    if constexpr (J == 3) asm volatile("v_cvt_f32_ubyte3 %0, %1" : "=v"(d) : "v"(v));
+}
+__device__ __forceinline__ void fma(float& d, float a, float b, float c) {
+    asm volatile("v_fma_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+}
+// two fp32 -> packed fp16 pair, round to nearest even
+__device__ __forceinline__ void pk(uint32_t& d, float a, float b) {
+    asm volatile("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+}
+}  // namespace op
+
+// VALU work of one 4-bit k-step, as a list of NOPS single instructions:
+//  0..15: the (min, scale) row broadcasts, fp16 -> fp32 (min of k 0..7, then
+//         scale of k 0..7);
+//  then per column pair p and code dword hh (k 4hh..4hh+3), 23 instructions:
+//         low / high nibbles of the dword (even / odd column of each byte),
+//         4 + 4 conversions, 4 + 4 FMAs q * scale + min, 4 packs into the
+//         fp16 fragments of column blocks 2p (even) and 2p + 1 (odd).
+struct Dq {
+    static constexpr int NOPS = 16 + 4 * 23;
+    float mn[8], sc[8];
+    uint32_t de, dd;
+    float fe[4], fo[4];
+};
+template <int K>
+__device__ __forceinline__ void dq_op(Dq& S, uint32_t mv, const uint2 (&cn)[2], uint32_t (&wn)[4][4]) {
+    if constexpr (K < 8) {
+        if constexpr (K == 0) op::nop1();   // DPP source: no VALU write just before
+        op::bcast_f16<K>(S.mn[K], mv);
+    } else if constexpr (K < 16) {
+        op::bcast_f16<K>(S.sc[K - 8], mv);
+    } else {
+        constexpr int c = (K - 16) / 23, o = (K - 16) % 23, pp = c >> 1, hh = c & 1;
+        const uint32_t cw = hh ? cn[pp].y : cn[pp].x;
+        if constexpr (o == 0) op::lo_nibbles(S.de, cw);
+        else if constexpr (o == 1) op::shr4(S.dd, cw);
+        else if constexpr (o == 2) op::lo_nibbles(S.dd, S.dd);
+        else if constexpr (o < 7) op::ubyte<o - 3>(S.fe[o - 3], S.de);
+        else if constexpr (o < 11) op::fma(S.fe[o - 7], S.fe[o - 7], S.sc[4 * hh + o - 7], S.mn[4 * hh + o - 7]);
+        else if constexpr (o < 15) op::ubyte<o - 11>(S.fo[o - 11], S.dd);
+        else if constexpr (o < 19) op::fma(S.fo[o - 15], S.fo[o - 15], S.sc[4 * hh + o - 15], S.mn[4 * hh + o - 15]);
+        else if constexpr (o == 19) op::pk(wn[2 * pp][2 * hh], S.fe[0], S.fe[1]);
+        else if constexpr (o == 20) op::pk(wn[2 * pp][2 * hh + 1], S.fe[2], S.fe[3]);
+        else if constexpr (o == 21) op::pk(wn[2 * pp + 1][2 * hh], S.fo[0], S.fo[1]);
+        else op::pk(wn[2 * pp + 1][2 * hh + 1], S.fo[2], S.fo[3]);
+    }
+}
+template <int K, int E>
+__device__ __forceinline__ void dq_ops(Dq& S, uint32_t mv, const uint2 (&cn)[2], uint32_t (&wn)[4][4]) {
+    if constexpr (K < E) {
+        dq_op<K>(S, mv, cn, wn);
+        dq_ops<K + 1, E>(S, mv, cn, wn);
+    }
 }
 
+// One 4-bit k-step: MB rows of 4 MFMAs (one activation fragment, the 4
+// weight fragments of this step).  The VALU list of the next step's
+// fragments fills the MFMA shadows of rows 1..MB-1 evenly (row 0 waits for
+// the codes just requested); activation fragments are read PD rows ahead.
+template <int MB, int PD, int ROW, class RX, class RXN>
+__device__ __forceinline__ void q4_rows(f4 (&acc)[4][MB], const uint32_t (&w)[4][4], h8 (&xq)[MB], h8 (&xn)[PD],
+                                        Dq& S, uint32_t mv, const uint2 (&cn)[2], uint32_t (&wn)[4][4],
+                                        const RX& read_cur, const RXN& read_nxt) {
+    if constexpr (ROW < MB) {
+        constexpr int NSLOT = MB > 1 ? 4 * (MB - 1) : 4;
+        if constexpr (ROW + PD < MB) xq[ROW + PD] = read_cur(ROW + PD);
+        else xn[ROW + PD - MB] = read_nxt(ROW + PD - MB);
+        auto slot = [&](auto nbc) {
+            constexpr int nb = decltype(nbc)::value;
+            op::mfma(acc[nb][ROW], __builtin_bit_cast(h8, make_uint4(w[nb][0], w[nb][1], w[nb][2], w[nb][3])), xq[ROW]);
+            if constexpr (MB == 1 || ROW > 0) {
+                constexpr int sidx = (MB > 1 ? (ROW - 1) * 4 : 0) + nb;
+                dq_ops<sidx * Dq::NOPS / NSLOT, (sidx + 1) * Dq::NOPS / NSLOT>(S, mv, cn, wn);
+            }
+        };
+        slot(std::integral_constant<int, 0>{});
+        slot(std::integral_constant<int, 1>{});
+        slot(std::integral_constant<int, 2>{});
+        slot(std::integral_constant<int, 3>{});
+        q4_rows<MB, PD, ROW + 1>(acc, w, xq, xn, S, mv, cn, wn, read_cur, read_nxt);
+    }
+}
 
 template <class C>
 __global__ __launch_bounds__(C::NT) void sk_kernel(Params p, SkSched sc) {
@@ -199,154 +305,144 @@ __global__ __launch_bounds__(C::NT) void sk_kernel(Params p, SkSched sc) {
             const int kc = (kh * 4 + q) ^ (row & 7);
             return *reinterpret_cast<const h8*>(base + C::M_BYTES + (row * 8 + kc) * 16);
         };
-        // weight fragment source of column block nb: 4-bit codes (8 k of one
-        // row, one nibble each) or fp16 rows
-        auto read_c = [&](const unsigned char* base, int nb) -> uint2 {
-            const int nl = wc * 64 + nb * 16 + r16;
-            const int row = nl >> 1, ch = (kh * 2 + (q >> 1)) ^ ((row >> 1) & 3);
-            return *reinterpret_cast<const uint2*>(base + C::M_BYTES + C::X_BYTES + (row * 4 + ch) * 16 +
-                                                   (q & 1) * 8);
-        };
+        // fp16 weight fragment of column block nb: lane-row i holds column
+        // wc*64 + 16nb + i
         auto read_w16 = [&](const unsigned char* base, int nb) -> h8 {
             const int nl = wc * 64 + nb * 16 + r16;
             const int kc = (kh * 4 + q) ^ (nl & 7);
             return *reinterpret_cast<const h8*>(base + C::X_BYTES + (nl * 8 + kc) * 16);
         };
-        float mnf[8], scf[8];
-        auto load_meta = [&](const unsigned char* base, uint4& mn, uint4& sc4) {
-            mn = *reinterpret_cast<const uint4*>(base + (wc * 2 + 0) * 128 + (kh * 32 + q * 8) * 2);
-            sc4 = *reinterpret_cast<const uint4*>(base + (wc * 2 + 1) * 128 + (kh * 32 + q * 8) * 2);
+        // activation fragment rows: row mb*16 + r16 (chunk swizzle by r16 & 7)
+        const uint32_t xoff = (uint32_t)(C::M_BYTES + (r16 * 8 + ((kh * 4 + q) ^ (r16 & 7))) * 16);
+        // (min, scale) of this lane's 8 k: lane t of each 16-lane row reads one
+        // fp16 value (t < 8: min of k0 + t, else scale of k0 + t - 8); the row
+        // broadcasts of the dequantization list spread them to every lane
+        const uint32_t moff = (uint32_t)((wc * 2 + (r16 >> 3)) * 128 + (kh * 32 + q * 8 + (r16 & 7)) * 2);
+        auto load_meta = [&](const unsigned char* base) -> uint32_t {
+            return *reinterpret_cast<const unsigned short*>(base + moff);
         };
-        auto cvt_meta = [&](const uint4& mn, const uint4& sc4) {
-            const uint32_t a[4] = {mn.x, mn.y, mn.z, mn.w}, s4[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                mnf[2 * i] = lo16(a[i]);
-                mnf[2 * i + 1] = hi16(a[i]);
-                scf[2 * i] = lo16(s4[i]);
-                scf[2 * i + 1] = hi16(s4[i]);
-            }
-            // keep them as fp32 registers (no fusion into mixed-precision FMAs)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) opaque(mnf[i]), opaque(scf[i]);
-        };
-        auto dequant = [&](uint2 c) -> h8 {
-            uint32_t d0 = (c.x >> shn) & 0x0f0f0f0fu, d1 = (c.y >> shn) & 0x0f0f0f0fu;
-            opaque(d0), opaque(d1);   // one v_cvt_f32_ubyteN per code, no re-extraction
-            float w[8];
-            w[0] = __builtin_fmaf(ubf<0>(d0), scf[0], mnf[0]);
-            w[1] = __builtin_fmaf(ubf<1>(d0), scf[1], mnf[1]);
-            w[2] = __builtin_fmaf(ubf<2>(d0), scf[2], mnf[2]);
-            w[3] = __builtin_fmaf(ubf<3>(d0), scf[3], mnf[3]);
-            w[4] = __builtin_fmaf(ubf<0>(d1), scf[4], mnf[4]);
-            w[5] = __builtin_fmaf(ubf<1>(d1), scf[5], mnf[5]);
-            w[6] = __builtin_fmaf(ubf<2>(d1), scf[6], mnf[6]);
-            w[7] = __builtin_fmaf(ubf<3>(d1), scf[7], mnf[7]);
-            uint32_t o[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = pk_f16(w[2 * i], w[2 * i + 1]);
-            return __builtin_bit_cast(h8, make_uint4(o[0], o[1], o[2], o[3]));
-        };
-        // interleave MFMAs with the VALU work of the same region (the
-        // compiler would otherwise issue long VALU runs, then MFMA bursts)
-        auto pattern_mv = [&]() {
-#pragma unroll
-            for (int mb = 0; mb < C::MB; ++mb) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // 3 VALU
-            }
-        };
-        // last fragment: the next step's codes / metadata were just requested,
-        // so the first MFMAs carry only activation-fragment reads and the
-        // VALU work (metadata conversion, first dequantization) follows
-        auto pattern_mdv = [&]() {
-#pragma unroll
-            for (int mb = 0; mb < C::MB; ++mb) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
-                if (mb >= 4) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-            }
+        // 4-bit codes of column pair pp: lane-row i of column blocks 2pp / 2pp+1
+        // holds weight columns wc*64 + 32pp + 2i / 2i+1, the two nibbles of
+        // one code byte, so one 8-byte read (8 k) feeds both fragments
+        const int cch = (kh * 2 + (q >> 1)) ^ ((r16 >> 1) & 3);
+        const uint32_t coff = (uint32_t)(C::M_BYTES + C::X_BYTES + (wc * 32 + r16) * 64 + cch * 16 + (q & 1) * 8);
+        auto read_cp = [&](const unsigned char* base, int pp) -> uint2 {
+            return *reinterpret_cast<const uint2*>(base + coff + pp * 1024);
         };
 
-        h8 xf[C::MB];
-        uint2 cr[4];
-        h8 wf16[4];
-        h8 wcur;
-        // prologue: NS stages in flight; publish stage 0 and read its fragments
+        if constexpr (C::Q4) {
+            // 4-bit weights.  Stages are published two ahead: at the barrier
+            // that ends step i every stage up to i + 2 has landed.  Step i
+            // reads step i+1's codes and metadata first and dequantizes its
+            // four weight fragments in the MFMA shadows of its own rows; the
+            // two fragment sets alternate between wa and wb (the loop runs two
+            // turns of the stage ring per iteration), so nothing is copied.
+            constexpr int PD = C::MB < 2 ? C::MB : 2;
+            static_assert(C::NS >= 3, "stages published two ahead");
+            Dq S;
+            uint32_t wa[4][4], wb[4][4];
+            h8 xc[PD];
 #pragma unroll
-        for (int s = 0; s < C::NS; ++s) issue(buf(s), s);
-        __builtin_amdgcn_s_waitcnt(vmcnt_wait(C::LWL * (C::NS - 1)));
-        __builtin_amdgcn_s_barrier();
-        {
-            const unsigned char* b0 = buf(0);
-            if constexpr (C::Q4) {
-                uint4 mn, sc4;
+            for (int st = 0; st < C::NS; ++st) issue(buf(st), st);
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(C::LWL * (C::NS - 2)));
+            __builtin_amdgcn_s_barrier();
+            {
+                const unsigned char* b0 = buf(0);
+                const uint2 c0[2] = {read_cp(b0, 0), read_cp(b0, 1)};
+                dq_ops<0, Dq::NOPS>(S, load_meta(b0), c0, wa);
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) cr[nb] = read_c(b0, nb);
-                load_meta(b0, mn, sc4);
-                cvt_meta(mn, sc4);
-                wcur = dequant(cr[0]);
-            } else {
+                for (int j = 0; j < PD; ++j) xc[j] = read_x(b0, j);
+            }
+            auto q4_step = [&](int st, int i, uint32_t(&w)[4][4], uint32_t(&wn)[4][4]) {
+                const unsigned char* cur = buf(st);
+                const unsigned char* nxt = buf((st + 1) % C::NS);
+                const uint2 cn[2] = {read_cp(nxt, 0), read_cp(nxt, 1)};
+                const uint32_t mv = load_meta(nxt);
+                h8 xq[C::MB], xn[PD];
+#pragma unroll
+                for (int j = 0; j < PD; ++j) xq[j] = xc[j];
+                // activation fragment of row mb at xo + 2 KB * mb (the lane
+                // offset is pinned per step so that the row offsets stay
+                // immediates instead of nine hoisted registers)
+                uint32_t xo = xoff;
+                pin(xo);
+                op::nop1();   // MFMA operands: no VALU write just before
+                q4_rows<C::MB, PD, 0>(acc, w, xq, xn, S, mv, cn, wn,
+                                      [&](int mb) { return *reinterpret_cast<const h8*>(cur + xo + mb * 2048); },
+                                      [&](int j) { return *reinterpret_cast<const h8*>(nxt + xo + j * 2048); });
+#pragma unroll
+                for (int j = 0; j < PD; ++j) xc[j] = xn[j];
+                // stages up to i+2 have landed for every wave (the wait is the
+                // one of the waves with fewer loads: stronger for the others)
+                // and no wave still reads stage i: refill its buffer with
+                // stage i+NS
+                __builtin_amdgcn_s_waitcnt(vmcnt_wait(C::LWL * (C::NS - 3)));
+                __builtin_amdgcn_s_waitcnt(LGKM_ZERO);
+                __builtin_amdgcn_s_barrier();
+                issue(buf(st), i + C::NS);
+            };
+            for (int kt = 0; kt < nk; kt += 2 * C::NS) {
+#pragma unroll
+                for (int u = 0; u < 2 * C::NS; ++u) {
+                    const int i = kt + u;
+                    if (i < nk) {
+                        if (u & 1) q4_step(u % C::NS, i, wb, wa);
+                        else q4_step(u % C::NS, i, wa, wb);
+                    }
+                }
+            }
+            op::nop_mfma_result();
+        } else {
+            // fp16 weights: stage i+1 is published at the end of step i; the
+            // next step's fragments are read during its last column block
+            h8 xf[C::MB];
+            h8 wf16[4];
+            h8 wcur;
+#pragma unroll
+            for (int st = 0; st < C::NS; ++st) issue(buf(st), st);
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(C::LWL * (C::NS - 1)));
+            __builtin_amdgcn_s_barrier();
+            {
+                const unsigned char* b0 = buf(0);
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb) wf16[nb] = read_w16(b0, nb);
                 wcur = wf16[0];
+#pragma unroll
+                for (int mb = 0; mb < C::MB; ++mb) xf[mb] = read_x(b0, mb);
             }
+            for (int kt = 0; kt < nk; kt += C::NS) {
 #pragma unroll
-            for (int mb = 0; mb < C::MB; ++mb) xf[mb] = read_x(b0, mb);
-        }
-
-        // each k-step enters with its activation fragments, codes / weights,
-        // metadata and first weight fragment in registers
-        for (int kt = 0; kt < nk; kt += C::NS) {
+                for (int st = 0; st < C::NS; ++st) {
+                    const int i = kt + st;
+                    if (i < nk) {
+                        const unsigned char* nxt = buf((st + 1) % C::NS);
 #pragma unroll
-            for (int s = 0; s < C::NS; ++s) {
-                const int i = kt + s;
-                if (i < nk) {
-                    const unsigned char* nxt = buf((s + 1) % C::NS);
-                    uint4 mn_n, sc_n;
+                        for (int nb = 0; nb < 3; ++nb) {
+                            const h8 wnext = wf16[nb + 1];
 #pragma unroll
-                    for (int nb = 0; nb < 3; ++nb) {
-                        const h8 wnext = C::Q4 ? dequant(cr[nb + 1]) : wf16[nb + 1];
-#pragma unroll
-                        for (int mb = 0; mb < C::MB; ++mb)
-                            acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wcur, xf[mb], acc[nb][mb], 0, 0, 0);
-                        if constexpr (C::Q4) pattern_mv();
-                        wcur = wnext;
-                    }
-                    // stage i+1 has landed for every wave (the wait is the one
-                    // of the waves with fewer loads: stronger for the others),
-                    // and no wave still reads stage i: refill its buffer with
-                    // stage i+NS and read the next codes / metadata / weights
-                    __builtin_amdgcn_s_waitcnt(vmcnt_wait(C::LWL * (C::NS - 2)));
-                    __builtin_amdgcn_s_waitcnt(LGKM_ZERO);
-                    __builtin_amdgcn_s_barrier();
-                    issue(buf(s), i + C::NS);
-                    if constexpr (C::Q4) {
-#pragma unroll
-                        for (int nb = 0; nb < 4; ++nb) cr[nb] = read_c(nxt, nb);
-                        load_meta(nxt, mn_n, sc_n);
-                    } else {
+                            for (int mb = 0; mb < C::MB; ++mb)
+                                acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wcur, xf[mb], acc[nb][mb], 0, 0, 0);
+                            wcur = wnext;
+                        }
+                        // stage i+1 has landed for every wave and no wave still
+                        // reads stage i: refill its buffer with stage i+NS
+                        __builtin_amdgcn_s_waitcnt(vmcnt_wait(C::LWL * (C::NS - 2)));
+                        __builtin_amdgcn_s_waitcnt(LGKM_ZERO);
+                        __builtin_amdgcn_s_barrier();
+                        issue(buf(st), i + C::NS);
 #pragma unroll
                         for (int nb = 0; nb < 3; ++nb) wf16[nb] = read_w16(nxt, nb);
-                    }
-                    // last fragment: each activation fragment is replaced by
-                    // the next step's right after its last use; the next
-                    // step's metadata and first weight fragment are prepared
-                    h8 w0n;
-                    if constexpr (C::Q4) {
-                        cvt_meta(mn_n, sc_n);
-                        w0n = dequant(cr[0]);
-                    } else {
-                        w0n = wf16[0];
-                    }
+                        const h8 w0n = wf16[0];
+                        // each activation fragment is replaced by the next
+                        // step's right after its last use
 #pragma unroll
-                    for (int mb = 0; mb < C::MB; ++mb) {
-                        acc[3][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wcur, xf[mb], acc[3][mb], 0, 0, 0);
-                        xf[mb] = read_x(nxt, mb);
+                        for (int mb = 0; mb < C::MB; ++mb) {
+                            acc[3][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wcur, xf[mb], acc[3][mb], 0, 0, 0);
+                            xf[mb] = read_x(nxt, mb);
+                        }
+                        wf16[3] = read_w16(nxt, 3);
+                        wcur = w0n;
                     }
-                    if constexpr (C::Q4) pattern_mdv();
-                    if constexpr (!C::Q4) wf16[3] = read_w16(nxt, 3);
-                    wcur = w0n;
                 }
             }
         }
@@ -375,7 +471,31 @@ __global__ __launch_bounds__(C::NT) void sk_kernel(Params p, SkSched sc) {
                 }
             }
             __syncthreads();
-            if (kh == 0) {
+            if (C::Q4 && kh == 0) {
+                // column pair rd: acc[2rd + h][mb][t] is column 8q + 2t + h of
+                // the pair's 32, so a lane holds 8 consecutive columns
+                const float4* reg0 = reinterpret_cast<const float4*>(buf((wc * 2) / C::PER_BUF) + ((wc * 2) % C::PER_BUF) * C::MB * 1024);
+                const float4* reg1 = reinterpret_cast<const float4*>(buf((wc * 2 + 1) / C::PER_BUF) + ((wc * 2 + 1) % C::PER_BUF) * C::MB * 1024);
+                const int64_t n = n0 + wc * 64 + rd * 32 + q * 8;
+#pragma unroll
+                for (int mb = 0; mb < C::MB; ++mb) {
+                    const float4 o0 = reg0[mb * 64 + lane], o1 = reg1[mb * 64 + lane];
+                    const f4 a0 = acc[rd * 2][mb], a1 = acc[rd * 2 + 1][mb];
+                    float v[8] = {a0[0] + o0.x, a1[0] + o1.x, a0[1] + o0.y, a1[1] + o1.y,
+                                  a0[2] + o0.z, a1[2] + o1.z, a0[3] + o0.w, a1[3] + o1.w};
+                    const int64_t m = m0 + mb * 16 + r16;
+                    if (m < p.M && n < p.N) {
+                        if (full) {
+                            store8_final(p, m, n, v);
+                        } else {
+                            float* dst = p.part + ((int64_t)slot * p.M + m) * p.N + n;
+                            *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+                            *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
+                        }
+                    }
+                }
+            }
+            if (!C::Q4 && kh == 0) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const int r = wc * 2 + j;
