@@ -67,6 +67,29 @@ def test_linear_f16(L, M, N, K):
     assert_close(got, ref, f"f16 {M}x{N}x{K}")
 
 
+# more than 576 rows with fp16 weights: the 256 x 256-tile kernel (ragged M
+# and N, a partial last group of tile-rows, K of one and of many stages)
+TILE_SHAPES = [(577, 256, 64), (1300, 1000, 320), (4100, 2304, 256), (2600, 768, 1024), (1024, 8, 64)]
+
+
+@pytest.mark.parametrize("M,N,K", TILE_SHAPES)
+def test_linear_f16_large_m(L, M, N, K):
+    got, ref = _run(L, "f16", M, N, K)
+    assert_close(got, ref, f"f16 {M}x{N}x{K}")
+
+
+def test_linear_large_m_epilogues(L):
+    got, ref = _run(L, "f16", 1000, 512, 1024, act=1)
+    assert_close(got, ref, "relu")
+    assert np.all(got.view(np.float16) >= 0)
+    got, ref = _run(L, "f16", 1000, 512, 512, residual=True)
+    assert_close(got, ref, "residual")
+    got, ref = _run(L, "f16", 1000, 512, 512, residual=True, inplace=True)
+    assert_close(got, ref, "residual in place")
+    got, ref = _run(L, "f16", 700, 264, 192, bias=False)
+    assert_close(got, ref, "no bias")
+
+
 @pytest.mark.parametrize("fmt", ["q4", "f16"])
 def test_linear_epilogues(L, fmt):
     got, ref = _run(L, fmt, 144, 512, 1024, act=1)

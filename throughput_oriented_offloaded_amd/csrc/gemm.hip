@@ -15,9 +15,10 @@
 //    workgroups share the (tile, k-step) iterations; tiles split between
 //    workgroups leave fp32 partials that a reduce kernel sums in a fixed
 //    order (deterministic) and finishes with the epilogue;
-//  * large-M contractions (the prefill, M = gbs * s): the same kernel takes
-//    whole tiles g, g + 256, ... in a banded order that keeps the tiles in
-//    flight at once sharing their activation and weight slices.
+//  * large-M contractions (the prefill, M = gbs * s): fp16 weights go to the
+//    256 x 256-tile kernel of gemm_tile.hip; 4-bit weights (the prefill
+//    restores them to fp16 first) take whole stream-K tiles g, g + 256, ...
+//    in a banded order.
 #include "gemm_common.h"
 #include "fg_trace.h"
 
@@ -53,6 +54,13 @@ int launch_linear(const LinearArgs& a, hipStream_t st) {
         return FG_OK;
     };
 
+    if (!q4 && linear_is_dp(a.M) && tile_fits(p)) {
+        {
+            TraceScope ts(TK_GEMM_F16, st, 2 * Md * Nd * Kd, gbytes);
+            FG_TRY(launch_tile(p, st));
+        }
+        return a.ln_y ? launch_layernorm(a.y, a.M, a.N, a.ln_g, a.ln_b, a.ln_y, st) : FG_OK;
+    }
     const SkSched sc = sk_schedule(a.M, a.N, a.K);
     if (sc.slots > 1) FG_TRY(need_ws((size_t)sc.slots * a.M * a.N * sizeof(float)));
     {

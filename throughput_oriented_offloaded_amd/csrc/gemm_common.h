@@ -183,6 +183,9 @@ SkSched sk_schedule(int64_t M, int64_t N, int64_t K);
 int launch_sk(const Params& p, const SkSched& sc, bool q4, hipStream_t st);
 int launch_sk32(const Params& p, const SkSched& sc, bool q4, hipStream_t st);
 int launch_sk_reduce(const Params& p, const SkSched& sc, hipStream_t st);
+// large-M fp16 GEMM (gemm_tile.hip): 256 x 256 tiles, whole K per workgroup
+bool tile_fits(const Params& p);
+int launch_tile(const Params& p, hipStream_t st);
 // sk_reduce fused with the LayerNorm of each finished row (width N, ldy == N,
 // N <= 32768) into ln_y [M, N]
 int launch_sk_reduce_ln(const Params& p, const SkSched& sc, const __half* g, const __half* b,

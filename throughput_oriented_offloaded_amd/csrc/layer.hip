@@ -20,17 +20,12 @@ struct WsLayout {
     size_t a, qkv, o, f, part, wdq, total;
 };
 
-// fp16 copies of a 4-bit layer's weight matrices for the prefill-shaped
-// GEMMs.  Only matrices whose contraction length K keeps the weight slices of
-// one band of tiles in flight (16 x 256 rows x K x 2 B) within the 256 MB
-// infinity cache: beyond that the fp16 path re-reads its weights from HBM and
-// the 4-bit path is faster (measured on the OPT-175B FC2, K = 49152).
-constexpr int64_t kPrefillF16MaxK = 32768;
+// fp16 copies of a 4-bit layer's four weight matrices for the prefill-shaped
+// GEMMs (the large-M fp16 kernel).
 bool prefill_dequant(int64_t rows, int32_t fmt) { return fmt == FG_FMT_Q4G64 && linear_is_dp(rows); }
-bool dq_fc2(const fg_dims* d) { return d->h2 <= kPrefillF16MaxK; }
 size_t wdq_elems(const fg_dims* d) {
     const size_t h1 = d->h1, h2 = d->h2;
-    return 3 * h1 * h1 + h1 * h1 + h2 * h1 + (dq_fc2(d) ? h1 * h2 : 0);
+    return 3 * h1 * h1 + h1 * h1 + 2 * h2 * h1;
 }
 
 size_t part_bytes(const fg_dims* d, int64_t rows, int32_t fmt) {
@@ -176,7 +171,7 @@ int layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, i
     fg_layer_w wl = *w;
     unsigned dq = 0;   // matrices multiplied from an fp16 copy (bit = which)
     if (prefill_dequant(rows, w->fmt)) {
-        dq = dq_fc2(d) ? 0xFu : 0x7u;
+        dq = 0xFu;
         __half* p_qkv = (__half*)(base + L.wdq);
         __half* p_o = p_qkv + 3 * h1 * h1;
         __half* p_1 = p_o + h1 * h1;
@@ -184,13 +179,9 @@ int layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, i
         FG_TRY(launch_dequant_g4((const uint8_t*)w->w_qkv, (const __half*)w->m_qkv, 1, 3 * h1, h1, p_qkv, st));
         FG_TRY(launch_dequant_g4((const uint8_t*)w->w_o, (const __half*)w->m_o, 1, h1, h1, p_o, st));
         FG_TRY(launch_dequant_g4((const uint8_t*)w->w_1, (const __half*)w->m_1, 1, h2, h1, p_1, st));
-        if (dq_fc2(d)) FG_TRY(launch_dequant_g4((const uint8_t*)w->w_2, (const __half*)w->m_2, 1, h1, h2, p_2, st));
-        wl.w_qkv = p_qkv; wl.w_o = p_o; wl.w_1 = p_1;
-        wl.m_qkv = wl.m_o = wl.m_1 = nullptr;
-        if (dq_fc2(d)) {
-            wl.w_2 = p_2;
-            wl.m_2 = nullptr;
-        }
+        FG_TRY(launch_dequant_g4((const uint8_t*)w->w_2, (const __half*)w->m_2, 1, h1, h2, p_2, st));
+        wl.w_qkv = p_qkv; wl.w_o = p_o; wl.w_1 = p_1; wl.w_2 = p_2;
+        wl.m_qkv = wl.m_o = wl.m_1 = wl.m_2 = nullptr;
     }
     for (int32_t k = 0; k < nb; ++k) {     // GPU batches of the block, one layer resident
         __half* xh = (__half*)x + (int64_t)k * rows * h1;
