@@ -67,10 +67,12 @@ def lib():
             L.or_linear.argtypes = [P, I64, I64, I64, P, I64, P, I32, P, P, I64]
             L.or_attn_prefill.argtypes = [P, I64, I64, I64, I64, P]
             L.or_attn_decode.argtypes = [P, P, P, I64, I64, I64, I64, P, P, I64, I64, P]
+            L.or_attn_decode_topk.argtypes = [P, P, P, I64, I64, I64, I64, P, P, I64, I64, I64, P]
             L.or_embed.argtypes = [P, P, I64, P, P, I64, P]
             L.or_argmax.argtypes = [P, I64, I64, P]
             for f in ("or_quant_g4", "or_dequant_g4", "or_layernorm", "or_linear",
-                      "or_attn_prefill", "or_attn_decode", "or_embed", "or_argmax"):
+                      "or_attn_prefill", "or_attn_decode", "or_attn_decode_topk", "or_embed",
+                      "or_argmax"):
                 getattr(L, f).restype = None
             _lib = L
     return _lib
@@ -182,6 +184,32 @@ def attn_decode(qkv, b: int, nh: int, hd: int, khist, vhist, lmax: int, pos: int
                      ctypes.c_void_p(base + 4 * h1), 3 * h1, b, nh, hd, _ptr(kh), _ptr(vh),
                      lmax, pos, _ptr(out))
     return out
+
+
+def attn_decode_topk(qkv, b: int, nh: int, hd: int, khist, vhist, lmax: int, pos: int,
+                     topk: int) -> np.ndarray:
+    """[P2] "权重压缩与 KV Cache 压缩", Top-K sparse attention: as attn_decode,
+    but V is summed only over the topk cached positions of highest score (ties:
+    lower position first) plus the current token; the softmax normalizer keeps
+    every score (no renormalization)."""
+    qkv = _u16(qkv)
+    h1 = nh * hd
+    assert qkv.shape == (b, 3 * h1)
+    kh, vh = _u16(khist), _u16(vhist)
+    assert kh.shape == (b, nh, lmax, hd) and vh.shape == kh.shape and 0 <= pos < lmax
+    assert 0 <= topk <= pos
+    out = np.empty((b, h1), np.uint16)
+    base = qkv.ctypes.data
+    lib().or_attn_decode_topk(ctypes.c_void_p(base), ctypes.c_void_p(base + 2 * h1),
+                              ctypes.c_void_p(base + 4 * h1), 3 * h1, b, nh, hd, _ptr(kh), _ptr(vh),
+                              lmax, pos, topk, _ptr(out))
+    return out
+
+
+def topk_count(pos: int, frac: float = 0.1) -> int:
+    """Number of cached positions whose V is read at sparsity frac: the pages'
+    10%, rounded up (at least one position whenever there is history)."""
+    return min(pos, -(-int(round(frac * 1_000_000)) * pos // 1_000_000))
 
 
 def embed(tok, pos, E, P) -> np.ndarray:

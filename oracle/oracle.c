@@ -16,6 +16,7 @@
 
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
 
 /* ---------------------------------------------------------------- binary16 */
 /* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
@@ -264,6 +265,74 @@ void or_attn_decode(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_
             for (int64_t c = 0; c < hd; ++c) {
                 double o = 0.0;
                 for (int64_t p = 0; p <= pos; ++p) {
+                    const uint16_t* vr = (p < pos) ? vh + p * hd : v_new + bi * ld + h * hd;
+                    o += sc[p] * H2D(vr[c]);
+                }
+                out[bi * h1 + h * hd + c] = or_d2h(o / sum);
+            }
+        }
+    }
+}
+
+/* Top-K sparse-V decode attention ([P2] "权重压缩与 KV Cache 压缩": scores
+ * from all Keys, then only the Values of the highest-scoring 10% are loaded).
+ * Readings where the page is silent: the softmax is over every score (all
+ * are computed); the V sum covers the topk cached positions of highest score
+ * (ties: lower position first) plus the current token, whose fresh v needs no
+ * cache read; the weights are not renormalized over the selected set. */
+typedef struct {
+    double s;
+    int64_t p;
+} or_scored;
+
+static int or_scored_desc(const void* a, const void* b) {
+    const or_scored* x = (const or_scored*)a;
+    const or_scored* y = (const or_scored*)b;
+    if (x->s != y->s) return x->s > y->s ? -1 : 1;
+    return x->p < y->p ? -1 : (x->p > y->p ? 1 : 0);
+}
+
+void or_attn_decode_topk(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                         int64_t ld, int64_t b, int64_t nh, int64_t hd, const uint16_t* khist,
+                         const uint16_t* vhist, int64_t lmax, int64_t pos, int64_t topk,
+                         uint16_t* out) {
+    const int64_t h1 = nh * hd;
+    const double scale = 1.0 / sqrt((double)hd);
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t bi = 0; bi < b; ++bi) {
+        for (int64_t h = 0; h < nh; ++h) {
+            double sc[pos + 1];
+            or_scored order[pos > 0 ? pos : 1];
+            unsigned char sel[pos > 0 ? pos : 1];
+            const uint16_t* qr = q + bi * ld + h * hd;
+            const uint16_t* kh = khist + (bi * nh + h) * lmax * hd;
+            const uint16_t* vh = vhist + (bi * nh + h) * lmax * hd;
+            double mx = -INFINITY;
+            for (int64_t p = 0; p <= pos; ++p) {
+                const uint16_t* kr = (p < pos) ? kh + p * hd : k_new + bi * ld + h * hd;
+                double d = 0.0;
+                for (int64_t c = 0; c < hd; ++c) d += H2D(qr[c]) * H2D(kr[c]);
+                sc[p] = d * scale;
+                if (sc[p] > mx) mx = sc[p];
+            }
+            /* the topk cached positions of highest score */
+            for (int64_t p = 0; p < pos; ++p) {
+                order[p].s = sc[p];
+                order[p].p = p;
+                sel[p] = 0;
+            }
+            qsort(order, (size_t)pos, sizeof(or_scored), or_scored_desc);
+            for (int64_t i = 0; i < topk && i < pos; ++i) sel[order[i].p] = 1;
+            /* softmax weights over every position */
+            double sum = 0.0;
+            for (int64_t p = 0; p <= pos; ++p) {
+                sc[p] = exp(sc[p] - mx);
+                sum += sc[p];
+            }
+            for (int64_t c = 0; c < hd; ++c) {
+                double o = 0.0;
+                for (int64_t p = 0; p <= pos; ++p) {
+                    if (p < pos && !sel[p]) continue;
                     const uint16_t* vr = (p < pos) ? vh + p * hd : v_new + bi * ld + h * hd;
                     o += sc[p] * H2D(vr[c]);
                 }

@@ -73,6 +73,14 @@ void or_attn_decode(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_
                     int64_t ld, int64_t b, int64_t nh, int64_t hd, const uint16_t* khist,
                     const uint16_t* vhist, int64_t lmax, int64_t pos, uint16_t* out);
 
+/* Decode attention with Top-K sparse V: softmax over every score, V summed
+ * over the topk cached positions of highest score (ties: lower position) and
+ * the current token, no renormalization. */
+void or_attn_decode_topk(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                         int64_t ld, int64_t b, int64_t nh, int64_t hd, const uint16_t* khist,
+                         const uint16_t* vhist, int64_t lmax, int64_t pos, int64_t topk,
+                         uint16_t* out);
+
 /* Embedding: x[r] = fp16(E[tok[r]] + P[pos[r]]). */
 void or_embed(const int32_t* tok, const int32_t* pos, int64_t rows, const uint16_t* E,
               const uint16_t* P, int64_t h1, uint16_t* x);

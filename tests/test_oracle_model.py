@@ -341,3 +341,63 @@ def test_ssd_pass_and_compression_saving():
     assert oracle.q4_bytes(n) * 32 == 2 * n * 9
     saving = 1 - oracle.q4_bytes(n) / (2 * n)
     assert saving == 0.71875 and abs(saving - 0.70) < 0.03
+
+
+# ------------------------------------------------------- Top-K sparse V
+def test_attn_topk_all_positions_is_dense_attention():
+    """topk = pos reads every V row: bit-identical to the dense definition."""
+    rng = np.random.default_rng(21)
+    b, nh, hd, L = 2, 3, 64, 40
+    h1 = nh * hd
+    qkv = rnd(rng, (b, 3 * h1))
+    kh, vh = rnd(rng, (b, nh, L, hd)), rnd(rng, (b, nh, L, hd))
+    for pos in (0, 1, 17, 39):
+        dense = oracle.attn_decode(qkv, b, nh, hd, kh, vh, L, pos)
+        assert np.array_equal(oracle.attn_decode_topk(qkv, b, nh, hd, kh, vh, L, pos, pos), dense)
+
+
+def test_attn_topk_equal_scores_take_lowest_positions():
+    """Equal scores everywhere (zero keys): every weight is 1 / (pos + 1) and the
+    tie rule keeps the lowest positions, so out = (v_0 + ... + v_{k-1} + v_new) / (pos + 1)."""
+    rng = np.random.default_rng(22)
+    b, nh, hd, L, pos = 2, 2, 64, 20, 13
+    h1 = nh * hd
+    qkv = rnd(rng, (b, 3 * h1))
+    qkv[:, h1:2 * h1] = 0
+    kh = np.zeros((b, nh, L, hd), np.float16)
+    vh = rnd(rng, (b, nh, L, hd))
+    for k in (0, 1, 5, 13):
+        got = as64(oracle.attn_decode_topk(qkv, b, nh, hd, kh, vh, L, pos, k))
+        for bi in range(b):
+            for h in range(nh):
+                sl = slice(h * hd, (h + 1) * hd)
+                want = (vh[bi, h, :k].astype(np.float64).sum(0) + qkv[bi, 2 * h1:][sl].astype(np.float64)) / (pos + 1)
+                assert np.allclose(got[bi, sl], want, atol=1e-3, rtol=1e-3)
+
+
+def test_attn_topk_keeps_weights_of_the_selected_rows():
+    """Keys built so that the score grows with the position: the top k are the
+    last k rows, and the result equals dense attention over a V whose other
+    rows are zero (the weights of the selected rows are the full softmax's:
+    no renormalization)."""
+    rng = np.random.default_rng(23)
+    b, nh, hd, L, pos = 2, 2, 64, 32, 25
+    h1 = nh * hd
+    qkv = rnd(rng, (b, 3 * h1))
+    kh = np.empty((b, nh, L, hd), np.float16)
+    for bi in range(b):
+        for h in range(nh):
+            qv = qkv[bi, h * hd:(h + 1) * hd].astype(np.float64)
+            for p in range(L):
+                kh[bi, h, p] = f16(qv * (0.02 * p) / np.sqrt(hd))
+    vh = rnd(rng, (b, nh, L, hd))
+    for k in (1, 3, 10):
+        vz = vh.copy()
+        vz[:, :, :pos - k] = 0
+        dense = oracle.attn_decode(qkv, b, nh, hd, kh, vz, L, pos)
+        assert np.array_equal(oracle.attn_decode_topk(qkv, b, nh, hd, kh, vh, L, pos, k), dense)
+
+
+def test_topk_count_rounds_up():
+    assert [oracle.topk_count(p) for p in (0, 1, 9, 10, 11, 528)] == [0, 1, 1, 1, 2, 53]
+    assert oracle.topk_count(100, 1.0) == 100 and oracle.topk_count(100, 0.0) == 0
