@@ -178,6 +178,46 @@ def roofline(tr, kind, bound, config=None):
             "algorithmic_per_launch": (r["flops"] if bound == "mfma" else r["bytes"]) / r["count"]}
 
 
+def topk_attention(model, cfg, L, pos: int, frac: float = 0.1, reps: int = 10):
+    """Top-K sparse-V decode attention ([P2] "权重压缩与 KV Cache 压缩": V read
+    for the highest-scoring 10% only) on layer 0's cache at history length pos,
+    timed with the same HIP-event tracing, beside the dense kernel on the same
+    cache.  Returns the sparse kernel's roofline plus both average durations."""
+    import torch
+    sh, bls = model.shape, model.n_seq
+    h1 = sh.h1
+    topk = min(pos, -(-int(round(frac * 1_000_000)) * pos // 1_000_000))
+    g = torch.Generator(device="cuda").manual_seed(11)
+    qkv = (torch.randn((bls, 3 * h1), generator=g, device="cuda") * 2).half()
+    out = torch.empty((bls, h1), dtype=torch.float16, device="cuda")
+    kv = model.kv[0].struct
+    q4 = cfg["kv"] == "q4"
+    sparse = L.fg_attn_decode_topk_q4 if q4 else L.fg_attn_decode_topk_f16
+    dense = L.fg_attn_decode_q4 if q4 else L.fg_attn_decode_f16
+    ks, kd = ("attn_topk_q4", "attn_decode_q4") if q4 else ("attn_topk_f16", "attn_decode_f16")
+    args = (qkv, qkv[:, h1:], qkv[:, 2 * h1:], 3 * h1, kv, bls, model.d, pos)
+    for _ in range(3):
+        sparse(*args, topk, 0, out)
+        dense(*args, 0, out)
+    torch.cuda.synchronize()
+    L.fg_trace_kinds([ks, kd])
+    L.fg_trace_enable(True)
+    for _ in range(reps):
+        sparse(*args, topk, 0, out)
+        dense(*args, 0, out)
+    torch.cuda.synchronize()
+    tr = L.fg_trace_collect()
+    L.fg_trace_enable(False)
+    L.fg_trace_kinds(None)
+    r = roofline(tr, ks, "hbm")
+    if r:
+        r.update({"pos": pos, "topk": topk, "dense_avg_launch_us": round(tr[kd]["ms"] * 1e3 / tr[kd]["count"], 2),
+                  "definition": "softmax over every score; V of the topk highest-scoring cached "
+                                "positions plus the current token; bytes count the K history, the "
+                                "topk V rows read, q/k/v and the output"})
+    return r
+
+
 def cpu_baseline(cfg, host0, emb, budget_s: float = 15.0):
     """The oracle (as it is) on the host cores: one decoder layer's decode step
     for a sample of sequences at context s + n/2, plus the LM head for them;
@@ -312,6 +352,8 @@ def main():
                     for k, v in tr_warm.items()},
         "tokens_valid": ok,
     }
+    if not args.no_trace and s + K // 2 <= 8192:
+        out["roofline_attn_topk"] = topk_attention(model, cfg, L, s + K // 2)
     if tier is not None:
         # weight tiering: bytes moved over PCIe per step against a pinned copy probe
         hb = sum(t.host_bytes for t in tier)

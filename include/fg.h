@@ -154,6 +154,24 @@ int fg_attn_decode_f16(const void* q, const void* k_new, const void* v_new, int6
                        int32_t fuse_append, void* out, void* stream);
 
 /*
+ * Decode attention with Top-K sparse V ([P2] "权重压缩与 KV Cache 压缩": the
+ * scores use every Key, and only the Values of the highest-scoring positions
+ * are read).  As fg_attn_decode_*, except that the V sum covers the `topk`
+ * cached positions of highest score (ties: lower position first) plus the
+ * current token (its fresh v_new), while the softmax normalizer keeps every
+ * score (no renormalization over the selected set).  The pages' setting is
+ * topk = ceil(0.1 * pos).  Requires 0 <= topk <= pos and pos <= 8192 (the
+ * whole history's scores are held on chip); FG_ERR_UNSUPPORTED above that.
+ * topk = pos equals the dense result.
+ */
+int fg_attn_decode_topk_q4(const void* q, const void* k_new, const void* v_new, int64_t ld,
+                           const fg_kv* kv, int32_t bls, const fg_dims* d, int32_t pos,
+                           int32_t topk, int32_t fuse_append, void* out, void* stream);
+int fg_attn_decode_topk_f16(const void* q, const void* k_new, const void* v_new, int64_t ld,
+                            const fg_kv* kv, int32_t bls, const fg_dims* d, int32_t pos,
+                            int32_t topk, int32_t fuse_append, void* out, void* stream);
+
+/*
  * Causal prompt attention ([P2] prefill over all s prompt tokens):
  * qkv fp16 [b*s, 3*h1] rows (q | k | v); out fp16 [b*s, h1];
  * row t of a sequence attends to its rows 0..t.

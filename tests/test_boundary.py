@@ -106,6 +106,12 @@ def test_attention_rejects_bad_arguments(L):
     assert f(p, p, p, 768, ctypes.byref(kv), 4, ctypes.byref(bad), 3, 1, p, None) == L.FG_ERR_INVALID
     d96 = L.dims(192, 768, 2, 96)
     assert f(p, p, p, 768, ctypes.byref(kv), 4, ctypes.byref(d96), 3, 1, p, None) == L.FG_ERR_UNSUPPORTED
+    # Top-K: 0 <= topk <= pos, and the history's scores must fit on chip
+    t = L.raw("fg_attn_decode_topk_q4")
+    assert t(p, p, p, 768, ctypes.byref(kv), 4, ctypes.byref(d), 3, 4, 1, p, None) == L.FG_ERR_INVALID
+    assert "topk" in L.last_error()
+    assert t(p, p, p, 768, ctypes.byref(kv), 4, ctypes.byref(d), 3, -1, 1, p, None) == L.FG_ERR_INVALID
+    assert t(p, p, p, 768, ctypes.byref(kv16), 4, ctypes.byref(d), 3, 1, 1, p, None) == L.FG_ERR_INVALID
 
 
 def test_layer_rejects_bad_arguments(L):

@@ -154,3 +154,127 @@ def test_prefill_attention(L, b, s, nh, hd):
     L.fg_attn_prefill(dev16(qkv), b, s, L.dims(h1, 4 * h1, nh, hd), out)
     torch.cuda.synchronize()
     assert_close(np16(out), oracle.attn_prefill(qkv, b, s, nh, hd), f"prefill b{b} s{s}")
+
+
+# ------------------------------------------------------------ Top-K sparse V
+SPARSE_CASES = [  # fmt, bls, nh, hd, pos, topk
+    ("q4", 1, 1, 128, 0, 0), ("q4", 3, 5, 128, 1, 1), ("q4", 2, 3, 128, 17, 2),
+    ("q4", 2, 2, 128, 64, 0), ("q4", 2, 2, 128, 64, 64), ("q4", 2, 2, 128, 200, 20),
+    ("q4", 1, 2, 64, 527, 53), ("q4", 2, 3, 64, 130, 13),
+    ("f16", 2, 3, 128, 40, 4), ("f16", 1, 4, 64, 130, 13), ("f16", 2, 2, 128, 33, 33),
+    # one wavefront per (sequence, head)
+    ("q4", 16, 128, 64, 100, 10), ("f16", 16, 128, 64, 70, 7),
+]
+
+
+def _score_gaps(qkv, kh, bls, nh, hd, pos, topk):
+    """Smallest gap, over all (sequence, head), between the topk-th and the
+    next score (fp64, natural units)."""
+    gap = np.inf
+    k64 = oracle.to_f16(kh).astype(np.float64)
+    for b in range(bls):
+        for h in range(nh):
+            q = qkv[b, h * hd:(h + 1) * hd].astype(np.float64)
+            s = np.sort(k64[b, h, :pos] @ q)[::-1] / np.sqrt(hd)
+            gap = min(gap, s[topk - 1] - s[topk])
+    return gap
+
+
+def _setup_ranked(L, fmt, bls, nh, hd, P, lmax, seed):
+    """As _setup, with keys c_p u + noise and queries along u (u a random +-1
+    vector per head, c_p a random permutation of evenly spaced values): every
+    head's scores are spread evenly, so the selection does not depend on the
+    score rounding of either side (the 4-bit score path carries absolute
+    errors around 1e-4)."""
+    import torch
+    from throughput_oriented_offloaded_amd.model import DeviceKV
+    rng = np.random.default_rng(seed)
+    h1 = nh * hd
+    d = L.dims(h1, 4 * h1, nh, hd)
+    fmt_id = L.FG_FMT_Q4G64 if fmt == "q4" else L.FG_FMT_F16
+    kv = DeviceKV(fmt_id, bls, nh, hd, lmax, "cuda")
+    u = rng.choice([-1.0, 1.0], size=(bls, nh, hd))
+    c = np.stack([rng.permutation(P) for _ in range(bls * nh)]).reshape(bls, nh, P) * (3.0 / max(P, 1))
+    k = c[..., None] * u[:, :, None, :] + rng.standard_normal((bls, nh, P, hd)) * 1e-3
+    kx = k.transpose(0, 2, 1, 3).reshape(bls, P, h1).astype(np.float16)
+    vx = (rng.standard_normal((bls, P, h1)) * 2).astype(np.float16)
+    append = L.fg_kv_append_q4 if fmt == "q4" else L.fg_kv_append_f16
+    kd, vd = dev16(kx), dev16(vx)
+    for p in range(P):
+        append(kd[:, p].contiguous(), vd[:, p].contiguous(), h1, kv.struct, bls, d, p)
+    oc = oracle.KVCache(fmt, bls, nh, hd, lmax)
+    if P:
+        oc.store(kx, vx, 0)
+    qkv = (rng.standard_normal((bls, 3 * h1)) * 2).astype(np.float16)
+    qkv[:, :h1] = (u.reshape(bls, h1) * 0.5 + rng.standard_normal((bls, h1)) * 0.01).astype(np.float16)
+    return d, kv, oc, qkv
+
+
+@pytest.mark.parametrize("fmt,bls,nh,hd,pos,topk", SPARSE_CASES)
+def test_decode_attention_topk(L, fmt, bls, nh, hd, pos, topk):
+    import torch
+    lmax = pos + 3
+    d, kv, oc, qkv = _setup_ranked(L, fmt, bls, nh, hd, pos, lmax, seed=pos * 17 + nh + topk)
+    h1 = nh * hd
+    kh, vh = oc.history()
+    if 0 < topk < pos:
+        assert _score_gaps(qkv, kh, bls, nh, hd, pos, topk) > 2e-3
+    buf = dev16(qkv)
+    out = torch.empty((bls, h1), dtype=torch.float16, device="cuda")
+    fn = L.fg_attn_decode_topk_q4 if fmt == "q4" else L.fg_attn_decode_topk_f16
+    fn(buf, buf[:, h1:], buf[:, 2 * h1:], 3 * h1, kv.struct, bls, d, pos, topk, 1, out)
+    torch.cuda.synchronize()
+    ref = oracle.attn_decode_topk(qkv, bls, nh, hd, kh, vh, lmax, pos, topk)
+    assert_close(np16(out), ref, f"{fmt} top-{topk} attention pos {pos}")
+    q3 = qkv.reshape(bls, 1, 3, h1)
+    oc.store(q3[:, :, 1], q3[:, :, 2], pos)
+    _cache_equal(kv, oc, pos + 1)
+
+
+@pytest.mark.parametrize("fmt", ["q4", "f16"])
+def test_decode_attention_topk_ties_take_lowest_positions(L, fmt):
+    """Zero keys: every score is equal, and the selection must be the lowest
+    positions on both sides."""
+    import torch
+    from throughput_oriented_offloaded_amd.model import DeviceKV
+    bls, nh, hd, pos, topk = 2, 3, 128, 50, 7
+    h1 = nh * hd
+    lmax = pos + 1
+    rng = np.random.default_rng(5)
+    d = L.dims(h1, 4 * h1, nh, hd)
+    fmt_id = L.FG_FMT_Q4G64 if fmt == "q4" else L.FG_FMT_F16
+    kv = DeviceKV(fmt_id, bls, nh, hd, lmax, "cuda")
+    oc = oracle.KVCache(fmt, bls, nh, hd, lmax)
+    kx = np.zeros((bls, pos, h1), np.float16)
+    vx = (rng.standard_normal((bls, pos, h1)) * 2).astype(np.float16)
+    append = L.fg_kv_append_q4 if fmt == "q4" else L.fg_kv_append_f16
+    kd, vd = dev16(kx), dev16(vx)
+    for p in range(pos):
+        append(kd[:, p].contiguous(), vd[:, p].contiguous(), h1, kv.struct, bls, d, p)
+    oc.store(kx, vx, 0)
+    qkv = (rng.standard_normal((bls, 3 * h1)) * 2).astype(np.float16)
+    qkv[:, h1:2 * h1] = 0
+    buf = dev16(qkv)
+    out = torch.empty((bls, h1), dtype=torch.float16, device="cuda")
+    fn = L.fg_attn_decode_topk_q4 if fmt == "q4" else L.fg_attn_decode_topk_f16
+    fn(buf, buf[:, h1:], buf[:, 2 * h1:], 3 * h1, kv.struct, bls, d, pos, topk, 0, out)
+    torch.cuda.synchronize()
+    kh, vh = oc.history()
+    ref = oracle.attn_decode_topk(qkv, bls, nh, hd, kh, vh, lmax, pos, topk)
+    assert_close(np16(out), ref, f"{fmt} top-{topk} ties")
+
+
+def test_decode_attention_topk_all_equals_dense(L):
+    """topk = pos takes the sparse kernel through every V row: same result as
+    the dense kernel within rounding."""
+    import torch
+    fmt, bls, nh, hd, pos = "q4", 4, 8, 128, 300
+    d, kv, oc, qkv = _setup(L, fmt, bls, nh, hd, pos, pos + 1, seed=77)
+    h1 = nh * hd
+    buf = dev16(qkv)
+    a = torch.empty((bls, h1), dtype=torch.float16, device="cuda")
+    b = torch.empty_like(a)
+    L.fg_attn_decode_q4(buf, buf[:, h1:], buf[:, 2 * h1:], 3 * h1, kv.struct, bls, d, pos, 0, a)
+    L.fg_attn_decode_topk_q4(buf, buf[:, h1:], buf[:, 2 * h1:], 3 * h1, kv.struct, bls, d, pos, pos, 0, b)
+    torch.cuda.synchronize()
+    assert_close(np16(b), np16(a), "top-pos vs dense")

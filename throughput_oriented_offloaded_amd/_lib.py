@@ -70,6 +70,10 @@ _PROTOS = {
                                          I32, I32, P, P]),
     "fg_attn_decode_f16": (ctypes.c_int, [P, P, P, I64, ctypes.POINTER(KV), I32, ctypes.POINTER(Dims),
                                           I32, I32, P, P]),
+    "fg_attn_decode_topk_q4": (ctypes.c_int, [P, P, P, I64, ctypes.POINTER(KV), I32, ctypes.POINTER(Dims),
+                                              I32, I32, I32, P, P]),
+    "fg_attn_decode_topk_f16": (ctypes.c_int, [P, P, P, I64, ctypes.POINTER(KV), I32, ctypes.POINTER(Dims),
+                                               I32, I32, I32, P, P]),
     "fg_attn_prefill": (ctypes.c_int, [P, I32, I32, ctypes.POINTER(Dims), P, P]),
     "fg_linear": (ctypes.c_int, [P, I64, I64, I32, P, P, I64, P, I32, P, P, P, SZ, P]),
     "fg_linear_workspace_bytes": (SZ, [I64, I64, I64]),
@@ -181,6 +185,20 @@ def fg_attn_decode_f16(q, k_new, v_new, ld, kv: KV, bls, d: Dims, pos, fuse_appe
                                                        int(fuse_append), ptr(out), stream_ptr(stream)))
 
 
+def fg_attn_decode_topk_q4(q, k_new, v_new, ld, kv: KV, bls, d: Dims, pos, topk, fuse_append, out,
+                           stream=None):
+    _check("fg_attn_decode_topk_q4", _L.fg_attn_decode_topk_q4(
+        ptr(q), ptr(k_new), ptr(v_new), ld, ctypes.byref(kv), bls, ctypes.byref(d), pos, topk,
+        int(fuse_append), ptr(out), stream_ptr(stream)))
+
+
+def fg_attn_decode_topk_f16(q, k_new, v_new, ld, kv: KV, bls, d: Dims, pos, topk, fuse_append, out,
+                            stream=None):
+    _check("fg_attn_decode_topk_f16", _L.fg_attn_decode_topk_f16(
+        ptr(q), ptr(k_new), ptr(v_new), ld, ctypes.byref(kv), bls, ctypes.byref(d), pos, topk,
+        int(fuse_append), ptr(out), stream_ptr(stream)))
+
+
 def fg_attn_prefill(qkv, b, s, d: Dims, out, stream=None):
     _check("fg_attn_prefill", _L.fg_attn_prefill(ptr(qkv), b, s, ctypes.byref(d), ptr(out),
                                                  stream_ptr(stream)))
@@ -277,7 +295,7 @@ def fg_trace_enable(on: bool):
 
 TRACE_KINDS = ["quant_g4", "dequant_g4", "gemm_q4", "gemm_f16", "splitk_reduce", "attn_decode_q4",
                "attn_decode_f16", "kv_store", "attn_prefill", "layernorm", "embed", "argmax",
-               "reduce_layernorm"]
+               "reduce_layernorm", "attn_topk_q4", "attn_topk_f16"]
 
 
 def fg_trace_kinds(names=None):

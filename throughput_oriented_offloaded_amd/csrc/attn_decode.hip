@@ -89,6 +89,21 @@ __device__ __forceinline__ float wave_max(float v) {
     for (int off = 1; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
     return v;
 }
+__device__ __forceinline__ int wave_isum(int v) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
+    return v;
+}
+__device__ __forceinline__ float wave_fsum(float v) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
+    return v;
+}
+// order-preserving unsigned key of a float (larger score, larger key)
+__device__ __forceinline__ uint32_t score_key(float s) {
+    const uint32_t u = __float_as_uint(s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 __device__ __forceinline__ uint4 ld_stream(const uint8_t* p) {
     const u4v t = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p));
     return make_uint4(t.x, t.y, t.z, t.w);
@@ -250,12 +265,13 @@ __device__ __forceinline__ void load32p(const __half* p, uint4 r[4]) {
 
 // NW wavefronts per (sequence, head); MULTI: the history may exceed one chunk
 // of `chunk` positions (scores in dynamic LDS), merged with a running maximum.
-template <int HD, bool Q4, int NW, bool MULTI>
+template <int HD, bool Q4, int NW, bool MULTI, bool SPARSE = false>
 __device__ __forceinline__ void attn_decode_body(
     const __half* __restrict__ q, const __half* __restrict__ k_new,
     const __half* __restrict__ v_new, int64_t ld, void* __restrict__ kc,
     __half* __restrict__ km, void* __restrict__ vc, __half* __restrict__ vm, int32_t lmax,
-    int32_t nh, int32_t pos, int32_t chunk, int fuse, __half* __restrict__ out) {
+    int32_t nh, int32_t pos, int32_t chunk, int fuse, int32_t topk, __half* __restrict__ out) {
+    static_assert(!(MULTI && SPARSE), "Top-K selection needs every score of the history in LDS");
     constexpr int LPP = HD / 32;           // lanes per position
     constexpr int SLOTS = 64 / LPP;        // positions per wavefront step
     constexpr int GPH = HD / 64;           // 64-groups per head
@@ -270,6 +286,12 @@ __device__ __forceinline__ void attn_decode_body(
     float* sFix = sRed + NW * ROWS * LPP * 32;          // [NW*ROWS*LPP]
     float* sL = sFix + NW * ROWS * LPP;                 // [NW*ROWS]
     float* sMax = sL + NW * ROWS;                       // [NW]
+    // Top-K: per-wave counts, (selected count, normalizer over all scores),
+    // selected positions in index order
+    int* sCnt = reinterpret_cast<int*>(sMax + NW);      // [NW]
+    int* sSel = sCnt + NW;                              // [1]
+    float* sLall = reinterpret_cast<float*>(sSel + 1);  // [1]
+    int* sIdx = sSel + 2;                               // [chunk]
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -377,15 +399,16 @@ __device__ __forceinline__ void attn_decode_body(
         } else {
             M = fmaxf(M, mc);
         }
-        // pass 2: weighted V over pairs of steps (j, j + 1)
-        auto vpair = [&](int ja, const Row<Q4>& ra, const Row<Q4>& rb, uint32_t ma, uint32_t mb) {
-            const int pa = ja * WGP + lp, pb = pa + WGP;
-            const bool oka = pa < n, okb = pb < n;
+        // pass 2: weighted V of positions pa, pb (dense: pairs of steps j, j+1;
+        // Top-K: pairs of entries of the selected list, the normalizer having
+        // been taken over every score)
+        auto vacc2 = [&](int pa, int pb, bool oka, bool okb, const Row<Q4>& ra, const Row<Q4>& rb,
+                         uint32_t ma, uint32_t mb) {
             const float wa = oka ? exp2f(sS[oka ? pa : 0] - M) : 0.f;
             const float wb = okb ? exp2f(sS[okb ? pb : 0] - M) : 0.f;
             if constexpr (Q4) {
                 const uint32_t mA = oka ? ma : 0u, mB = okb ? mb : 0u;
-                l += wa + wb;
+                if constexpr (!SPARSE) l += wa + wb;
                 h2 wh;
                 wh[0] = (_Float16)(wa * hi_half(mA));
                 wh[1] = (_Float16)(wb * hi_half(mB));
@@ -396,10 +419,146 @@ __device__ __forceinline__ void attn_decode_body(
                 h2 wh;
                 wh[0] = (_Float16)wa;
                 wh[1] = (_Float16)wb;
-                l = __builtin_amdgcn_fdot2(wh, one2, l, false);
+                if constexpr (!SPARSE) l = __builtin_amdgcn_fdot2(wh, one2, l, false);
                 vacc_f16(ra, rb, wh, acc);
             }
         };
+        auto vpair = [&](int ja, const Row<Q4>& ra, const Row<Q4>& rb, uint32_t ma, uint32_t mb) {
+            const int pa = ja * WGP + lp, pb = pa + WGP;
+            vacc2(pa, pb, pa < n, pb < n, ra, rb, ma, mb);
+        };
+        if constexpr (SPARSE) {
+            // the topk positions of highest score, ties to the lower position:
+            // tau = the topk-th largest key (bitwise search: count(key >= tau)
+            // >= topk), then wave 0 lists the positions in index order with
+            // key > tau, and the first topk - count(key > tau) with key == tau
+            // counts are wave ballots (a scalar popcount per key slot), summed
+            // over the wavefronts through LDS
+            auto block_count = [&](int c) -> int {
+                if constexpr (NW == 1) {
+                    return c;
+                } else {
+                    if (lane == 0) sCnt[wv] = c;
+                    __syncthreads();
+                    int t = 0;
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) t += sCnt[w];
+                    __syncthreads();
+                    return t;
+                }
+            };
+            constexpr int KR = 10;                      // keys held per lane
+            const int kk = topk < n ? topk : n;
+            uint32_t tau = 0;
+            int n_gt = 0;
+            if (kk > 0 && kk < n) {
+                if (n <= KR * NW * 64) {
+                    uint32_t kr[KR];
+#pragma unroll
+                    for (int i = 0; i < KR; ++i) {
+                        const int p = threadIdx.x + i * NW * 64;
+                        kr[i] = p < n ? score_key(sS[p]) : 0u;   // 0: below every real key
+                    }
+                    auto count_ge = [&](uint32_t c) -> int {
+                        int t = 0;
+#pragma unroll
+                        for (int i = 0; i < KR; ++i) t += (int)__builtin_popcountll(__ballot(kr[i] >= c));
+                        return t;
+                    };
+                    for (int bit = 31; bit >= 0; --bit) {
+                        const uint32_t cand = tau | (1u << bit);
+                        if (block_count(count_ge(cand)) >= kk) tau = cand;
+                    }
+                    n_gt = block_count(count_ge(tau + 1u));
+                } else {
+                    auto count_ge = [&](uint32_t c) -> int {
+                        int t = 0;
+                        for (int p0 = 0; p0 < n; p0 += NW * 64) {
+                            const int p = p0 + threadIdx.x;
+                            t += (int)__builtin_popcountll(__ballot(p < n && score_key(sS[p < n ? p : 0]) >= c));
+                        }
+                        return t;
+                    };
+                    for (int bit = 31; bit >= 0; --bit) {
+                        const uint32_t cand = tau | (1u << bit);
+                        if (block_count(count_ge(cand)) >= kk) tau = cand;
+                    }
+                    n_gt = block_count(count_ge(tau + 1u));
+                }
+            }
+            if (wv == 0) {
+                const int need_eq = kk - n_gt;
+                int cnt = 0, eq_seen = 0;
+                float lsum = 0.f;
+                for (int base = 0; base < n; base += 64) {
+                    const int p = base + lane;
+                    const bool valid = p < n;
+                    const float sp = valid ? sS[p] : 0.f;
+                    bool sel;
+                    if (kk >= n) {
+                        sel = valid;
+                    } else if (kk == 0) {
+                        sel = false;
+                    } else {
+                        const uint32_t key = score_key(sp);
+                        const bool eq = valid && key == tau;
+                        const uint64_t eqm = __ballot(eq);
+                        const int rank = eq_seen + (int)__builtin_amdgcn_mbcnt_hi(
+                            (uint32_t)(eqm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eqm, 0u));
+                        eq_seen += (int)__builtin_popcountll(eqm);
+                        sel = (valid && key > tau) || (eq && rank < need_eq);
+                    }
+                    const uint64_t sm = __ballot(sel);
+                    const int off = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(sm >> 32),
+                                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)sm, 0u));
+                    if (sel) sIdx[cnt + off] = p;
+                    cnt += (int)__builtin_popcountll(sm);
+                    if (valid) lsum += exp2f(sp - M);
+                }
+                lsum = wave_fsum(lsum);
+                if (lane == 0) {
+                    sSel[0] = cnt;
+                    sLall[0] = lsum;
+                }
+            }
+            __syncthreads();
+            const int nsel = sSel[0];
+            const int npr = (nsel + 2 * WGP - 1) / (2 * WGP);
+            auto epos = [&](int e) -> int { return sIdx[e < nsel ? e : nsel - 1]; };
+            int pr = 0;
+            for (; pr + U2 <= npr; pr += U2) {
+                Row<Q4> ra[U2], rb[U2];
+                uint32_t ma[U2], mb[U2];
+                int pa[U2], pb[U2];
+#pragma unroll
+                for (int u = 0; u < U2; ++u) {
+                    const int ea = 2 * (pr + u) * WGP + lp;
+                    pa[u] = epos(ea);
+                    pb[u] = epos(ea + WGP);
+                    ra[u] = load_row<Q4>(vcp + (int64_t)pa[u] * RB);
+                    rb[u] = load_row<Q4>(vcp + (int64_t)pb[u] * RB);
+                    if constexpr (Q4) {
+                        ma[u] = vmp[(int64_t)pa[u] * GPH];
+                        mb[u] = vmp[(int64_t)pb[u] * GPH];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U2; ++u) {
+                    const int ea = 2 * (pr + u) * WGP + lp;
+                    vacc2(pa[u], pb[u], ea < nsel, ea + WGP < nsel, ra[u], rb[u],
+                          Q4 ? ma[u] : 0u, Q4 ? mb[u] : 0u);
+                }
+            }
+            for (; pr < npr; ++pr) {
+                const int ea = 2 * pr * WGP + lp;
+                const int pa = epos(ea), pb = epos(ea + WGP);
+                const Row<Q4> ra = load_row<Q4>(vcp + (int64_t)pa * RB);
+                const Row<Q4> rb = load_row<Q4>(vcp + (int64_t)pb * RB);
+                const uint32_t ma = Q4 ? vmp[(int64_t)pa * GPH] : 0u, mb = Q4 ? vmp[(int64_t)pb * GPH] : 0u;
+                vacc2(pa, pb, ea < nsel, ea + WGP < nsel, ra, rb, ma, mb);
+            }
+            return;
+        }
         const int npr = (nst + 1) / 2;
         int pr = 0;
         for (; pr + U2 <= npr; pr += U2) {
@@ -462,6 +621,7 @@ __device__ __forceinline__ void attn_decode_body(
             s += sRed[(r * LPP + dq) * 32 + e] + sFix[r * LPP + dq];
             L += sL[r];
         }
+        if constexpr (SPARSE) L = pos > 0 ? sLall[0] : 0.f;   // every score's weight
         const float vnd = __half2float(v_new[b * ld + h * HD + d]);
         out[b * (int64_t)nh * HD + h * HD + d] = __float2half_rn((s + wn * vnd) / (L + wn));
     }
@@ -500,8 +660,9 @@ __device__ __forceinline__ void attn_decode_body(
     const __half *__restrict__ q, const __half *__restrict__ k_new,                          \
         const __half *__restrict__ v_new, int64_t ld, void *__restrict__ kc,                 \
         __half *__restrict__ km, void *__restrict__ vc, __half *__restrict__ vm,             \
-        int32_t lmax, int32_t nh, int32_t pos, int32_t chunk, int fuse, __half *__restrict__ out
-#define FG_ATTN_ARGS q, k_new, v_new, ld, kc, km, vc, vm, lmax, nh, pos, chunk, fuse, out
+        int32_t lmax, int32_t nh, int32_t pos, int32_t chunk, int fuse, int32_t topk,              \
+        __half *__restrict__ out
+#define FG_ATTN_ARGS q, k_new, v_new, ld, kc, km, vc, vm, lmax, nh, pos, chunk, fuse, topk, out
 
 // history in one chunk: register budget of 6 (4-bit) or 5 (fp16) wavefronts per SIMD
 template <int HD, bool Q4, int NW>
@@ -514,6 +675,14 @@ void attn_decode_kernel(FG_ATTN_PARAMS) {
 template <int HD, bool Q4, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_decode_multi_kernel(FG_ATTN_PARAMS) {
     attn_decode_body<HD, Q4, NW, true>(FG_ATTN_ARGS);
+}
+
+// Top-K sparse V (history in one chunk): register budget of 5 wavefronts per
+// SIMD (the selection and the gathered pass need a few more registers)
+template <int HD, bool Q4, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(5)))
+void attn_decode_topk_kernel(FG_ATTN_PARAMS) {
+    attn_decode_body<HD, Q4, NW, false, true>(FG_ATTN_ARGS);
 }
 #undef FG_ATTN_ARGS
 #undef FG_ATTN_PARAMS
@@ -596,30 +765,39 @@ int launch_kv_store(const __half* k, const __half* v, int64_t ld, const fg_kv* k
 
 int launch_attn_decode(const __half* q, const __half* k_new, const __half* v_new, int64_t ld,
                        const fg_kv* kv, int32_t bls, const fg_dims* d, int32_t pos, int fuse,
-                       __half* out, hipStream_t st) {
+                       __half* out, hipStream_t st, int32_t topk) {
     if (bls == 0) return FG_OK;
+    const bool sparse = topk >= 0;
+    if (sparse && pos > kAttnTopkMaxPos)
+        return set_error(FG_ERR_UNSUPPORTED, "Top-K attention: history %d longer than %d", pos,
+                         kAttnTopkMaxPos);
     const int64_t units = (int64_t)bls * d->n_heads;
     const bool q4 = kv->fmt == FG_FMT_Q4G64;
-    // algorithmic HBM bytes: K and V history (4-bit: codes + meta = 9/16 B per
-    // element), the q / k_new / v_new rows, the output, the appended position
-    const double hist = 2.0 * bls * pos * d->h1;
+    // algorithmic HBM bytes: K history and the V rows read (all, or the topk
+    // selected; 4-bit: codes + meta = 9/16 B per element), the q / k_new /
+    // v_new rows, the output, the appended position
+    const int32_t vrows = sparse ? std::min(topk, pos) : pos;
     const double per_elem = q4 ? 9.0 / 16.0 : 2.0;
-    const double bytes = hist * per_elem + (double)bls * d->h1 * 2 * 4 +
-                         (fuse ? 2.0 * bls * d->h1 * per_elem : 0.0);
-    TraceScope ts(q4 ? TK_ATTN_DECODE_Q4 : TK_ATTN_DECODE_F16, st,
-                  4.0 * bls * (pos + 1) * (double)d->h1, bytes);
+    const double bytes = (double)bls * (pos + vrows) * d->h1 * per_elem +
+                         (double)bls * d->h1 * 2 * 4 + (fuse ? 2.0 * bls * d->h1 * per_elem : 0.0);
+    const double flops = 2.0 * bls * (pos + 1) * (double)d->h1 + 2.0 * bls * (vrows + 1) * (double)d->h1;
+    TraceScope ts(sparse ? (q4 ? TK_ATTN_TOPK_Q4 : TK_ATTN_TOPK_F16)
+                         : (q4 ? TK_ATTN_DECODE_Q4 : TK_ATTN_DECODE_F16),
+                  st, flops, bytes);
     // one wavefront per (sequence, head) when there are enough of them to fill
     // the chip; otherwise four, splitting the positions
     const int nw = units >= 2048 ? 1 : 4;
     const bool multi = pos > kAttnChunk;
     const int chunk = multi ? kAttnChunk : (int)std::max<int64_t>(cdiv(pos, 64) * 64, 64);
     const int lpp = d->head_dim / 32;
-    const size_t lds = sizeof(float) * ((size_t)chunk + nw * 4 * lpp * 33 + nw * 4 + nw);
+    const size_t lds = sizeof(float) * ((size_t)chunk + nw * 4 * lpp * 33 + nw * 4 + nw) +
+                       (sparse ? sizeof(int) * ((size_t)nw + 2 + chunk) : 0);
 #define FG_ATTN(HD_, Q_, NW_, MU_)                                                           \
-    (MU_ ? attn_decode_multi_kernel<HD_, Q_, NW_> : attn_decode_kernel<HD_, Q_, NW_>)         \
+    (sparse ? attn_decode_topk_kernel<HD_, Q_, NW_>                                          \
+            : (MU_ ? attn_decode_multi_kernel<HD_, Q_, NW_> : attn_decode_kernel<HD_, Q_, NW_>)) \
         <<<(unsigned)units, NW_ * 64, lds, st>>>(                                            \
         q, k_new, v_new, ld, kv->k, (__half*)kv->k_meta, kv->v, (__half*)kv->v_meta,         \
-        kv->max_len, d->n_heads, pos, chunk, fuse, out)
+        kv->max_len, d->n_heads, pos, chunk, fuse, topk, out)
 #define FG_ATTN_NW(HD_, Q_, MU_)                        \
     do {                                                \
         if (nw == 1) FG_ATTN(HD_, Q_, 1, MU_);          \
@@ -693,6 +871,36 @@ extern "C" int fg_attn_decode_q4(const void* q, const void* k_new, const void* v
     return fg::launch_attn_decode((const __half*)q, (const __half*)k_new, (const __half*)v_new, ld,
                                   kv, bls, d, pos, fuse_append != 0, (__half*)out,
                                   fg::as_stream(stream));
+}
+
+extern "C" int fg_attn_decode_topk_q4(const void* q, const void* k_new, const void* v_new,
+                                      int64_t ld, const fg_kv* kv, int32_t bls, const fg_dims* d,
+                                      int32_t pos, int32_t topk, int32_t fuse_append, void* out,
+                                      void* stream) {
+    fg::clear_error();
+    FG_TRY(check_kv_call(q, k_new, v_new, ld, kv, bls, d, pos, FG_FMT_Q4G64));
+    FG_CHECK_ARG(out && (uintptr_t)out % 16 == 0, "out must be non-null and 16-byte aligned");
+    FG_CHECK_ARG(topk >= 0 && topk <= pos, "topk %d outside [0, pos %d]", topk, pos);
+    FG_CHECK_SUP(pos <= fg::kAttnTopkMaxPos, "Top-K attention: history %d longer than %d", pos,
+                 fg::kAttnTopkMaxPos);
+    return fg::launch_attn_decode((const __half*)q, (const __half*)k_new, (const __half*)v_new, ld,
+                                  kv, bls, d, pos, fuse_append != 0, (__half*)out,
+                                  fg::as_stream(stream), topk);
+}
+
+extern "C" int fg_attn_decode_topk_f16(const void* q, const void* k_new, const void* v_new,
+                                       int64_t ld, const fg_kv* kv, int32_t bls, const fg_dims* d,
+                                       int32_t pos, int32_t topk, int32_t fuse_append, void* out,
+                                       void* stream) {
+    fg::clear_error();
+    FG_TRY(check_kv_call(q, k_new, v_new, ld, kv, bls, d, pos, FG_FMT_F16));
+    FG_CHECK_ARG(out && (uintptr_t)out % 16 == 0, "out must be non-null and 16-byte aligned");
+    FG_CHECK_ARG(topk >= 0 && topk <= pos, "topk %d outside [0, pos %d]", topk, pos);
+    FG_CHECK_SUP(pos <= fg::kAttnTopkMaxPos, "Top-K attention: history %d longer than %d", pos,
+                 fg::kAttnTopkMaxPos);
+    return fg::launch_attn_decode((const __half*)q, (const __half*)k_new, (const __half*)v_new, ld,
+                                  kv, bls, d, pos, fuse_append != 0, (__half*)out,
+                                  fg::as_stream(stream), topk);
 }
 
 extern "C" int fg_attn_decode_f16(const void* q, const void* k_new, const void* v_new, int64_t ld,

@@ -120,9 +120,12 @@ int launch_argmax(const __half* logits, int64_t rows, int64_t n, int32_t* out, h
 // sequence seq0.  Row (b, t) of k/v is at k + ((b * nt) + t) * ld.
 int launch_kv_store(const __half* k, const __half* v, int64_t ld, const fg_kv* kv, int32_t seq0,
                     int32_t nseq, int32_t t0, int32_t nt, const fg_dims* d, hipStream_t st);
+// topk < 0: dense decode attention; topk >= 0: Top-K sparse V (V read for
+// the topk cached positions of highest score only)
 int launch_attn_decode(const __half* q, const __half* k_new, const __half* v_new, int64_t ld,
                        const fg_kv* kv, int32_t bls, const fg_dims* d, int32_t pos, int fuse,
-                       __half* out, hipStream_t st);
+                       __half* out, hipStream_t st, int32_t topk = -1);
+constexpr int32_t kAttnTopkMaxPos = 8192;   // Top-K: the whole history's scores in LDS
 int launch_attn_prefill(const __half* qkv, int32_t b, int32_t s, const fg_dims* d, __half* out,
                         hipStream_t st);
 
