@@ -218,6 +218,37 @@ def topk_attention(model, cfg, L, pos: int, frac: float = 0.1, reps: int = 10):
     return r
 
 
+def sparse_decode(model, cfg, L, tok1, steps: int, no_trace: bool, frac: float = 0.1):
+    """Whole decode steps with Top-K sparse V attention at the pages' 10%
+    (positions s .. s+steps-1, rewriting the cache rows the dense steps wrote):
+    throughput of the same block, and the attention time per step."""
+    import torch
+    s, bls = cfg["s"], cfg["gbs"] * cfg["nb"]
+    kind = "attn_topk_q4" if cfg["kv"] == "q4" else "attn_topk_f16"
+    model.attn_topk_ppm = int(round(frac * 1_000_000))
+    L.fg_trace_kinds([kind])
+    L.fg_trace_enable(not no_trace)
+    tok = tok1
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        _, tok = model.decode_step(tok, s + i, cfg["gbs"], cfg["nb"])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    tr = L.fg_trace_collect() if not no_trace else {}
+    L.fg_trace_enable(False)
+    L.fg_trace_kinds(None)
+    model.attn_topk_ppm = 0
+    r = {"value": round(bls * steps / dt, 2), "unit": "tokens/s", "steps": steps,
+         "ms_per_step": round(dt / steps * 1e3, 3), "frac": frac,
+         "definition": "block decode steps (every layer) with attention reading the V rows of "
+                       "ceil(frac * pos) top-scoring cached positions"}
+    if kind in tr:
+        r["attn_ms_per_step"] = round(tr[kind]["ms"] / steps, 3)
+    log(f"sparse-V decode: {r['ms_per_step']} ms/step")
+    return r
+
+
 def cpu_baseline(cfg, host0, emb, budget_s: float = 15.0):
     """The oracle (as it is) on the host cores: one decoder layer's decode step
     for a sample of sequences at context s + n/2, plus the LM head for them;
@@ -354,6 +385,8 @@ def main():
     }
     if not args.no_trace and s + K // 2 <= 8192:
         out["roofline_attn_topk"] = topk_attention(model, cfg, L, s + K // 2)
+    if s + K <= 8192:
+        out["decode_attn_topk"] = sparse_decode(model, cfg, L, tok1, min(K, 8), args.no_trace)
     if tier is not None:
         # weight tiering: bytes moved over PCIe per step against a pinned copy probe
         hb = sum(t.host_bytes for t in tier)

@@ -45,7 +45,8 @@ enum {
 const char* fg_status_str(int status);
 /* Detail of the calling thread's last failing call ("" if none). */
 const char* fg_last_error(void);
-/* ABI version, bumped on any incompatible change of this header. */
+/* ABI version, bumped on any incompatible change of this header (2: the
+ * block-decode entry points take attn_topk_ppm). */
 int fg_abi_version(void);
 
 /* ----------------------------------------------------------------- formats */
@@ -230,10 +231,17 @@ int fg_layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs
  * contraction over bls rows; attention runs per (sequence, head) with the
  * fused K, V append at pos.
  * x: fp16 [bls, h1], in/out.  ws: ws_bytes >= fg_workspace_bytes(d, bls, w->fmt).
+ *
+ * attn_topk_ppm selects Top-K sparse V attention ([P2] "权重压缩与 KV Cache
+ * 压缩"; the semantics of fg_attn_decode_topk_*) with
+ * topk = ceil(pos * attn_topk_ppm / 1e6) cached positions; the pages' 10% is
+ * 100000.  0, any value >= 1000000, and any step where that topk reaches pos
+ * (e.g. pos = 0) run dense attention.  Negative: FG_ERR_INVALID.  A sparse
+ * step with pos > 8192 returns FG_ERR_UNSUPPORTED before anything is enqueued.
  */
 int fg_layer_decode_block(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs,
                           int32_t nb, int32_t pos, const fg_kv* kv, void* ws, size_t ws_bytes,
-                          void* stream);
+                          void* stream, int32_t attn_topk_ppm);
 
 /* Device scratch needed by one layer pass over `rows` token rows
  * (decode: rows = bls; prefill: rows = gbs * s). */
@@ -269,6 +277,8 @@ size_t fg_workspace_bytes(const fg_dims* d, int64_t rows, int32_t fmt_w);
  * Without tiering (tier == NULL) sc, copy_stream and flags are ignored and
  * may be NULL / 0.  The stage buffers are owned by the caller and must not be
  * touched while a call's work is in flight.
+ * attn_topk_ppm (decode): as in fg_layer_decode_block, for every layer; every
+ * layer is checked before the first is enqueued.
  */
 enum { FG_SCHED_FIRST_STAGED = 1, FG_SCHED_STAGE_NEXT = 2 };
 
@@ -296,7 +306,7 @@ int fg_model_prefill(fg_sched* sc, const fg_dims* d, int32_t n_layers, const fg_
 int fg_model_decode_step(fg_sched* sc, const fg_dims* d, int32_t n_layers, const fg_layer_w* w,
                          const fg_tier_w* tier, const fg_kv* kv, void* x, int32_t gbs,
                          int32_t nb, int32_t pos, void* ws, size_t ws_bytes, void* stream,
-                         void* copy_stream, int32_t flags);
+                         void* copy_stream, int32_t flags, int32_t attn_topk_ppm);
 
 /* --------------------------------------------------------------- sizes */
 /* Bytes of the six layer matrices of n_layers layers ([P2]: M_W =

@@ -324,12 +324,15 @@ def layer_prefill(d: Dims, W: dict, x, b: int, s: int, cache: KVCache) -> np.nda
     return linear(f, W["w_2"], W["b_2"], residual=x)
 
 
-def layer_decode(d: Dims, W: dict, x, pos: int, cache: KVCache, fresh_current: bool = True):
+def layer_decode(d: Dims, W: dict, x, pos: int, cache: KVCache, fresh_current: bool = True,
+                 attn_topk: float = 0.0):
     """One pre-LN decoder layer for one new token per sequence at position pos.
 
     The new k, v are appended to the cache at pos.  Attention covers 0..pos:
     positions < pos from the (dequantized) cache; position pos from the fresh
-    fp16 k, v when fresh_current, else from its own quantized copy.
+    fp16 k, v when fresh_current, else from its own quantized copy.  With
+    attn_topk > 0 (fresh_current only) the V sum is the Top-K sparse one over
+    topk_count(pos, attn_topk) cached positions.
     Returns (x_out, attn_out, qkv)."""
     x = _u16(x)
     b = x.shape[0]
@@ -338,9 +341,14 @@ def layer_decode(d: Dims, W: dict, x, pos: int, cache: KVCache, fresh_current: b
     q3 = qkv.reshape(b, 1, 3, d.h1)
     if fresh_current:
         kh, vh = cache.history()
-        o = attn_decode(qkv, b, d.nh, d.hd, kh, vh, cache.lmax, pos)
+        if attn_topk > 0:
+            o = attn_decode_topk(qkv, b, d.nh, d.hd, kh, vh, cache.lmax, pos,
+                                 topk_count(pos, attn_topk))
+        else:
+            o = attn_decode(qkv, b, d.nh, d.hd, kh, vh, cache.lmax, pos)
         cache.store(q3[:, :, 1, :], q3[:, :, 2, :], pos)
     else:
+        assert attn_topk == 0
         cache.store(q3[:, :, 1, :], q3[:, :, 2, :], pos)
         kh, vh = cache.history()
         kq = np.ascontiguousarray(kh[:, :, pos, :]).reshape(b, d.h1)
@@ -402,11 +410,11 @@ class Model:
         logits = lm_head(last, self.lnf_g, self.lnf_b, self.E)
         return logits, argmax(logits)
 
-    def decode(self, tok, pos: int):
+    def decode(self, tok, pos: int, attn_topk: float = 0.0):
         tok = np.asarray(tok, np.int32).reshape(-1)
         x = embed(tok, np.full(tok.size, pos, np.int32), self.E, self.P)
         for W, c in zip(self.layers, self.caches):
-            x, _, _ = layer_decode(self.d, W, x, pos, c)
+            x, _, _ = layer_decode(self.d, W, x, pos, c, attn_topk=attn_topk)
         logits = lm_head(x, self.lnf_g, self.lnf_b, self.E)
         return logits, argmax(logits)
 

@@ -22,7 +22,7 @@ def test_exports_every_declared_symbol(L):
     for name in ("fg_quant_group4", "fg_dequant_group4", "fg_layer_prefill",
                  "fg_layer_decode_block", "fg_kv_append_q4", "fg_attn_decode_q4"):
         assert name in declared
-    assert L.raw("fg_abi_version")() == 1
+    assert L.raw("fg_abi_version")() == 2
 
 
 def test_status_strings(L):
@@ -123,14 +123,22 @@ def test_layer_rejects_bad_arguments(L):
     need = L.fg_workspace_bytes(d, 4, 1)
     assert need > 0
     st = f(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(p), 2, 2, 3, ctypes.byref(kv),
-           ctypes.c_void_p(p), need - 1, None)
+           ctypes.c_void_p(p), need - 1, None, 0)
     assert st == L.FG_ERR_CAPACITY
     st = f(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(p), 3, 2, 3, ctypes.byref(kv),
-           ctypes.c_void_p(p), need, None)
+           ctypes.c_void_p(p), need, None, 0)
     assert st == L.FG_ERR_INVALID                     # 6 sequences > n_seq
+    st = f(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(p), 2, 2, 3, ctypes.byref(kv),
+           ctypes.c_void_p(p), need, None, -1)
+    assert st == L.FG_ERR_INVALID                     # negative Top-K fraction
+    long_kv = _kv(L, max_len=9000, n_seq=4)
+    st = f(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(p), 2, 2, 8193, ctypes.byref(long_kv),
+           ctypes.c_void_p(p), need, None, 100000)
+    assert st == L.FG_ERR_UNSUPPORTED                 # sparse history beyond the on-chip scores
+    assert "Top-K" in L.last_error()
     w.m_o = None
     st = f(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(p), 2, 2, 3, ctypes.byref(kv),
-           ctypes.c_void_p(p), need, None)
+           ctypes.c_void_p(p), need, None, 0)
     assert st == L.FG_ERR_INVALID
     g = L.raw("fg_layer_prefill")
     w.m_o = p
@@ -168,17 +176,20 @@ def test_model_pass_rejects_bad_arguments(L):
     kvs = (L.KV * 2)(_kv(L, max_len=16, n_seq=4), _kv(L, max_len=16, n_seq=4))
     f = L.raw("fg_model_decode_step")
     V = ctypes.c_void_p
-    assert f(None, ctypes.byref(d), 0, w, None, kvs, V(p), 2, 2, 3, V(p), ws_need, None, None, 0) \
+    assert f(None, ctypes.byref(d), 0, w, None, kvs, V(p), 2, 2, 3, V(p), ws_need, None, None, 0, 0) \
         == L.FG_ERR_INVALID                            # no layers
     w[1].m_o = None                                    # second layer broken: nothing may run
-    assert f(None, ctypes.byref(d), 2, w, None, kvs, V(p), 2, 2, 3, V(p), ws_need, None, None, 0) \
+    assert f(None, ctypes.byref(d), 2, w, None, kvs, V(p), 2, 2, 3, V(p), ws_need, None, None, 0, 0) \
         == L.FG_ERR_INVALID
     assert "metadata" in L.last_error()
     w[1].m_o = p
     tier = (L.TierW * 2)(L.TierW(p, p, p), L.TierW())
-    assert f(None, ctypes.byref(d), 2, w, tier, kvs, V(p), 2, 2, 3, V(p), ws_need, None, None, 0) \
+    assert f(None, ctypes.byref(d), 2, w, tier, kvs, V(p), 2, 2, 3, V(p), ws_need, None, None, 0, 0) \
         == L.FG_ERR_INVALID                            # tiering without a scheduler
     assert "scheduler" in L.last_error()
+    long_kvs = (L.KV * 2)(_kv(L, max_len=9000, n_seq=4), _kv(L, max_len=9000, n_seq=4))
+    assert f(None, ctypes.byref(d), 2, w, None, long_kvs, V(p), 2, 2, 8193, V(p), ws_need, None,
+             None, 0, 100000) == L.FG_ERR_UNSUPPORTED   # sparse step past the on-chip scores
     g = L.raw("fg_model_prefill")
     assert g(None, ctypes.byref(d), 2, w, None, kvs, V(p), 2, 2, 17, V(p), 1 << 40, None, None, 0) \
         == L.FG_ERR_INVALID                            # s > max_len

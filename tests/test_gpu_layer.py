@@ -77,6 +77,85 @@ def test_decode_block_matches_oracle(L, fmt, kvfmt, P):
         assert same > 0.9, f"appended codes agree on only {same:.3f}"
 
 
+def _ranked_history(L, kvfmt, q, bls, P, lmax, seed):
+    """Cache of P positions whose keys are c_p sign(q_h) r_h per (sequence,
+    head): c_p a random permutation of evenly spaced values in [-1.5, 1.5) and
+    r_h = sqrt(hd) / |q_h|_1, so the head's scores are c_p (spaced 3 / P).  The
+    rows are two-level, which the 4-bit codec keeps exactly, and the selection
+    does not hinge on either side's rounding of q.  q: float [bls, nh, hd]."""
+    from throughput_oriented_offloaded_amd.model import DeviceKV
+    bls_, nh, hd = q.shape
+    h1 = nh * hd
+    rng = np.random.default_rng(seed)
+    c = np.stack([rng.permutation(P) for _ in range(bls * nh)]).reshape(bls, nh, P) * (3.0 / P) - 1.5
+    sg = np.where(q >= 0, 1.0, -1.0) * (np.sqrt(hd) / np.abs(q).sum(-1))[..., None]
+    k = c[..., None] * sg[:, :, None, :]
+    kx = k.transpose(0, 2, 1, 3).reshape(bls, P, h1).astype(np.float16)
+    vx = (rng.standard_normal((bls, P, h1)) * 2).astype(np.float16)
+    kv = DeviceKV(L.FG_FMT_Q4G64 if kvfmt == "q4" else L.FG_FMT_F16, bls, nh, hd, lmax, "cuda")
+    d = L.dims(h1, OPT125["h2"], nh, hd)
+    app = L.fg_kv_append_q4 if kvfmt == "q4" else L.fg_kv_append_f16
+    kd, vd = dev16(kx), dev16(vx)
+    for p in range(P):
+        app(kd[:, p].contiguous(), vd[:, p].contiguous(), h1, kv.struct, bls, d, p)
+    oc = oracle.KVCache(kvfmt, bls, nh, hd, lmax)
+    oc.store(kx, vx, 0)
+    return kv, oc, d
+
+
+@pytest.mark.parametrize("wfmt,kvfmt,P", [("q4", "q4", 40), ("f16", "f16", 40), ("q4", "f16", 300),
+                                          ("q4", "q4", 300)])
+def test_decode_block_topk_matches_oracle(L, wfmt, kvfmt, P):
+    """Top-K sparse V inside the block decode (attn_topk_ppm 100000: the pages'
+    10%, topk = ceil(P / 10)) against the oracle's layer at attn_topk 0.1; the
+    dense oracle is far outside the tolerance, so the sparse path was taken."""
+    import copy
+    import torch
+    bls, lmax = 6, P + 4
+    h1, nh, hd = OPT125["h1"], OPT125["nh"], OPT125["hd"]
+    dl, Wn, od = _layer(L, OPT125, wfmt, seed=31)
+    x = synth.activations(bls, h1, seed=32)
+    xn = x.numpy().view(np.uint16)
+    qkv = oracle.linear(oracle.layernorm(xn, Wn["ln1_g"], Wn["ln1_b"]), Wn["w_qkv"], Wn["b_qkv"])
+    q = oracle.to_f16(qkv[:, :h1]).astype(np.float64).reshape(bls, nh, hd)
+    kv, oc, d = _ranked_history(L, kvfmt, q, bls, P, lmax, seed=33)
+    topk = oracle.topk_count(P, 0.1)
+    k64 = oracle.to_f16(oc.history()[0]).astype(np.float64)
+    for b in range(bls):
+        for h in range(nh):
+            sc = np.sort(k64[b, h, :P] @ q[b, h])[::-1] / np.sqrt(hd)
+            assert sc[topk - 1] - sc[topk] > 0.5 * 3.0 / P, "scores not spread as built"
+    oc_dense = copy.deepcopy(oc)
+    xd = x.cuda()
+    ws = torch.empty(L.fg_workspace_bytes(d, bls, dl.fmt), dtype=torch.uint8, device="cuda")
+    L.fg_layer_decode_block(d, dl.struct, xd, 3, 2, P, kv.struct, ws, ws.numel(),
+                            attn_topk_ppm=100000)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle.layer_decode(od, Wn, xn, P, oc, attn_topk=0.1)
+    err, tol = assert_close(np16(xd), ref, f"top-k decode block {wfmt}/{kvfmt} pos {P}")
+    dense, _, _ = oracle.layer_decode(od, Wn, xn, P, oc_dense)
+    from helpers import f32
+    assert np.abs(f32(dense) - f32(ref)).max() > 4 * tol
+
+
+def test_decode_block_topk_dense_limits(L):
+    """attn_topk_ppm 0, 1000000 and any fraction whose count reaches pos all
+    give the dense block decode, bit for bit."""
+    import torch
+    bls, P, lmax = 6, 7, 12
+    dl, _, _ = _layer(L, OPT125, "q4", seed=41)
+    outs = []
+    for ppm in (0, 1000000, 900000):          # ceil(7 * 0.9) = 7 = pos
+        kv, _, d = _history(L, OPT125, "q4", bls, P, lmax, seed=42)
+        xd = synth.activations(bls, OPT125["h1"], seed=43).cuda()
+        ws = torch.empty(L.fg_workspace_bytes(d, bls, dl.fmt), dtype=torch.uint8, device="cuda")
+        L.fg_layer_decode_block(d, dl.struct, xd, 3, 2, P, kv.struct, ws, ws.numel(),
+                                attn_topk_ppm=ppm)
+        torch.cuda.synchronize()
+        outs.append(xd.clone())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
 # FFN wide enough (h2 > 32768) that FC2 keeps its 4-bit weights in the
 # prefill-shaped GEMMs while the other three run from fp16 copies
 WIDE_FF = dict(h1=128, h2=33024, nh=2, hd=64)

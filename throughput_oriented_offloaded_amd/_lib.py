@@ -83,7 +83,7 @@ _PROTOS = {
     "fg_layer_prefill": (ctypes.c_int, [ctypes.POINTER(Dims), ctypes.POINTER(LayerW), P, I32, I32, I32,
                                         ctypes.POINTER(KV), P, SZ, P]),
     "fg_layer_decode_block": (ctypes.c_int, [ctypes.POINTER(Dims), ctypes.POINTER(LayerW), P, I32, I32,
-                                             I32, ctypes.POINTER(KV), P, SZ, P]),
+                                             I32, ctypes.POINTER(KV), P, SZ, P, I32]),
     "fg_workspace_bytes": (SZ, [ctypes.POINTER(Dims), I64, I32]),
     "fg_stage_bytes": (SZ, [ctypes.POINTER(Dims)]),
     "fg_sched_create": (ctypes.c_int, [ctypes.POINTER(P), P, SZ]),
@@ -93,7 +93,7 @@ _PROTOS = {
                                         P, SZ, P, P, I32]),
     "fg_model_decode_step": (ctypes.c_int, [P, ctypes.POINTER(Dims), I32, ctypes.POINTER(LayerW),
                                             ctypes.POINTER(TierW), ctypes.POINTER(KV), P, I32, I32,
-                                            I32, P, SZ, P, P, I32]),
+                                            I32, P, SZ, P, P, I32, I32]),
     "fg_weight_bytes": (I64, [ctypes.POINTER(Dims), I32, I32]),
     "fg_kv_bytes": (I64, [ctypes.POINTER(Dims), I32, I32, I32, I32, I32]),
     "fg_trace_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -233,10 +233,12 @@ def fg_layer_prefill(d: Dims, w: LayerW, x, gbs, nb, s, kv: KV, ws, ws_bytes, st
                                                    stream_ptr(stream)))
 
 
-def fg_layer_decode_block(d: Dims, w: LayerW, x, gbs, nb, pos, kv: KV, ws, ws_bytes, stream=None):
+def fg_layer_decode_block(d: Dims, w: LayerW, x, gbs, nb, pos, kv: KV, ws, ws_bytes, stream=None,
+                          attn_topk_ppm=0):
     _check("fg_layer_decode_block", _L.fg_layer_decode_block(ctypes.byref(d), ctypes.byref(w), ptr(x),
                                                              gbs, nb, pos, ctypes.byref(kv), ptr(ws),
-                                                             ws_bytes, stream_ptr(stream)))
+                                                             ws_bytes, stream_ptr(stream),
+                                                             attn_topk_ppm))
 
 
 def fg_stage_bytes(d: Dims) -> int:
@@ -269,12 +271,12 @@ def fg_model_prefill(sched, d: Dims, layers, tier, kvs, x, gbs, nb, s, ws, ws_by
 
 
 def fg_model_decode_step(sched, d: Dims, layers, tier, kvs, x, gbs, nb, pos, ws, ws_bytes,
-                         stream=None, copy_stream=None, flags=0):
+                         stream=None, copy_stream=None, flags=0, attn_topk_ppm=0):
     _check("fg_model_decode_step", _L.fg_model_decode_step(sched, ctypes.byref(d), len(layers),
                                                            layers, tier, kvs, ptr(x), gbs, nb, pos,
                                                            ptr(ws), ws_bytes, stream_ptr(stream),
                                                            copy_stream.cuda_stream if copy_stream
-                                                           else None, flags))
+                                                           else None, flags, attn_topk_ppm))
 
 
 def fg_workspace_bytes(d: Dims, rows, fmt_w) -> int:

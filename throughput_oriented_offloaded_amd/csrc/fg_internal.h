@@ -100,10 +100,14 @@ bool linear_is_dp(int64_t M);
 // check_only) enqueued on st.
 // ln1_done: the layer's input LayerNorm is already in the workspace (the
 // previous layer fused it); next: if not null, that layer's input LayerNorm is
-// fused into this layer's last residual sum.
+// fused into this layer's last residual sum.  attn_topk_ppm: Top-K sparse V
+// over ceil(pos * ppm / 1e6) cached positions (0 or >= 1e6: dense).
 int layer_decode(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, int32_t nb,
                  int32_t pos, const fg_kv* kv, void* ws, size_t ws_bytes, hipStream_t st,
-                 bool check_only, bool ln1_done, const fg_layer_w* next);
+                 bool check_only, bool ln1_done, const fg_layer_w* next, int32_t attn_topk_ppm);
+// Top-K count of a decode step at position pos: -1 (dense) unless
+// 0 < ppm < 1e6 selects fewer than pos positions.
+int32_t attn_topk_count(int32_t pos, int32_t ppm);
 int layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, int32_t nb,
                   int32_t s, const fg_kv* kv, void* ws, size_t ws_bytes, hipStream_t st,
                   bool check_only);

@@ -105,14 +105,26 @@ int lin(const fg_layer_w* w, int which, const __half* x, int64_t M, int64_t K, i
 
 }  // namespace
 
+// Positions whose V a sparse step reads: the fraction ppm / 1e6 of the
+// history, rounded up; dense (-1) when that is the whole history.
+int32_t attn_topk_count(int32_t pos, int32_t ppm) {
+    if (ppm <= 0 || ppm >= 1000000) return -1;
+    const int64_t k = ((int64_t)pos * ppm + 999999) / 1000000;
+    return k < pos ? (int32_t)k : -1;
+}
+
 int layer_decode(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, int32_t nb,
                  int32_t pos, const fg_kv* kv, void* ws, size_t ws_bytes, hipStream_t st,
-                 bool check_only, bool ln1_done, const fg_layer_w* next) {
+                 bool check_only, bool ln1_done, const fg_layer_w* next, int32_t attn_topk_ppm) {
     FG_TRY(check_layer(d, w, x, kv, ws));
     FG_CHECK_ARG(gbs >= 1 && nb >= 1 && (int64_t)gbs * nb <= kv->n_seq,
                  "block %d x %d exceeds the cache's %d sequences", gbs, nb, kv->n_seq);
     FG_CHECK_ARG(pos >= 0 && pos < kv->max_len, "pos %d outside [0, max_len %d)", pos,
                  kv->max_len);
+    FG_CHECK_ARG(attn_topk_ppm >= 0, "attn_topk_ppm %d is negative", attn_topk_ppm);
+    const int32_t topk = attn_topk_count(pos, attn_topk_ppm);
+    FG_CHECK_SUP(topk < 0 || pos <= kAttnTopkMaxPos, "Top-K attention: history %d longer than %d",
+                 pos, kAttnTopkMaxPos);
     const int64_t bls = (int64_t)gbs * nb;
     const WsLayout L = layout(d, bls, w->fmt);
     if (ws_bytes < L.total)
@@ -131,7 +143,8 @@ int layer_decode(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, in
     if (!ln1_done)
         FG_TRY(launch_layernorm(xh, bls, h1, (const __half*)w->ln1_g, (const __half*)w->ln1_b, a, st));
     FG_TRY(lin(w, 0, a, bls, h1, 3 * h1, 0, nullptr, qkv, part, pb, st));
-    FG_TRY(launch_attn_decode(qkv, qkv + h1, qkv + 2 * h1, 3 * h1, kv, (int32_t)bls, d, pos, 1, o, st));
+    FG_TRY(launch_attn_decode(qkv, qkv + h1, qkv + 2 * h1, 3 * h1, kv, (int32_t)bls, d, pos, 1, o, st,
+                              topk));
     FG_TRY(lin(w, 1, o, bls, h1, h1, 0, xh, xh, part, pb, st, w->ln2_g, w->ln2_b, a));
     FG_TRY(lin(w, 2, a, bls, h1, h2, 1, nullptr, f, part, pb, st));
     if (next)   // the next layer's first LayerNorm, fused with this residual sum
@@ -207,10 +220,10 @@ extern "C" size_t fg_workspace_bytes(const fg_dims* d, int64_t rows, int32_t fmt
 
 extern "C" int fg_layer_decode_block(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs,
                                      int32_t nb, int32_t pos, const fg_kv* kv, void* ws,
-                                     size_t ws_bytes, void* stream) {
+                                     size_t ws_bytes, void* stream, int32_t attn_topk_ppm) {
     fg::clear_error();
     return fg::layer_decode(d, w, x, gbs, nb, pos, kv, ws, ws_bytes, fg::as_stream(stream), false,
-                            false, nullptr);
+                            false, nullptr, attn_topk_ppm);
 }
 
 extern "C" int fg_layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs,

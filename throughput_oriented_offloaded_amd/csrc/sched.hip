@@ -204,7 +204,7 @@ extern "C" int fg_model_decode_step(fg_sched* sc, const fg_dims* d, int32_t n_la
                                     const fg_layer_w* w, const fg_tier_w* tier, const fg_kv* kv,
                                     void* x, int32_t gbs, int32_t nb, int32_t pos, void* ws,
                                     size_t ws_bytes, void* stream, void* copy_stream,
-                                    int32_t flags) {
+                                    int32_t flags, int32_t attn_topk_ppm) {
     using namespace fg;
     clear_error();
     FG_TRY(check_dims(d));
@@ -215,6 +215,7 @@ extern "C" int fg_model_decode_step(fg_sched* sc, const fg_dims* d, int32_t n_la
                           // each layer's input LayerNorm runs fused into the
                           // previous layer's last residual sum
                           return layer_decode(d, &wj, x, gbs, nb, pos, &kv[j], ws, ws_bytes, st, chk,
-                                              j > 0, j + 1 < n_layers ? &w[j + 1] : nullptr);
+                                              j > 0, j + 1 < n_layers ? &w[j + 1] : nullptr,
+                                              attn_topk_ppm);
                       });
 }

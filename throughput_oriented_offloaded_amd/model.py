@@ -138,8 +138,13 @@ class Model:
     with embed [vocab, h1], pos [max_pos, h1], lnf_g, lnf_b (fp16, device)."""
 
     def __init__(self, shape: Shape, layers, emb: dict, kv_fmt: int, n_seq: int, max_len: int,
-                 device="cuda", tier=None):
-        """tier: None, or one TierLayer (or None) per layer for weight tiering."""
+                 device="cuda", tier=None, attn_topk: float = 0.0):
+        """tier: None, or one TierLayer (or None) per layer for weight tiering.
+        attn_topk: 0 for dense decode attention, else the fraction of cached
+        positions whose V each decode step reads (Top-K sparse V; the pages
+        use 0.1), rounded up per step."""
+        assert 0.0 <= attn_topk <= 1.0
+        self.attn_topk_ppm = int(round(attn_topk * 1_000_000))
         self.shape, self.layers, self.emb = shape, layers, emb
         self.d = shape.dims
         self.n_seq, self.max_len = n_seq, max_len
@@ -224,7 +229,8 @@ class Model:
         ws = self.workspace(bls)
         sc, tier, cp, flags = self._sched_args()
         L.fg_model_decode_step(sc, self.d, self._w_arr, tier, self._kv_arr, x, gbs, nb, pos, ws,
-                               ws.numel(), stream=stream, copy_stream=cp, flags=flags)
+                               ws.numel(), stream=stream, copy_stream=cp, flags=flags,
+                               attn_topk_ppm=self.attn_topk_ppm)
         return self._head(x, stream)
 
     def embed_step(self, tok: torch.Tensor, pos: int, stream=None) -> torch.Tensor:
