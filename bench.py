@@ -101,8 +101,10 @@ def h2d_probe(src, reps: int = 5) -> float:
 def profile_layer(cfg, reps: int):
     """One decoder layer at the config's shape for hardware-counter runs: the
     prefill fills its cache to s, then `reps` decode steps of the whole block
-    (the launches the step times), then a plain 1 GiB device-to-device copy
-    (reads and writes 1 GiB: the calibration of the byte counters)."""
+    (the launches the step times), the same `reps` steps again with Top-K
+    sparse V at 10% (rewriting those cache rows), then a plain 1 GiB
+    device-to-device copy (reads and writes 1 GiB: the calibration of the
+    byte counters)."""
     import torch
     import synth
     from throughput_oriented_offloaded_amd import _lib as L
@@ -124,6 +126,9 @@ def profile_layer(cfg, reps: int):
     log(f"profile-layer: {cfg['workload']}, {reps} decode steps from position {s}")
     for r in range(reps):
         L.fg_layer_decode_block(d, lay.struct, xd, gbs, nb, s + r, kv.struct, ws, ws_b)
+    for r in range(reps):
+        L.fg_layer_decode_block(d, lay.struct, xd, gbs, nb, s + r, kv.struct, ws, ws_b,
+                                attn_topk_ppm=100000)
     torch.cuda.synchronize()
     src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
@@ -138,7 +143,8 @@ def profile_layer(cfg, reps: int):
 # of the measured kernel's sources; reported only while those are unchanged.
 TRAFFIC_FILES = {5: "opt175b_q4_decode_hbm_traffic.md"}
 KERNEL_SOURCES = {"gemm_q4": ["gemm_sk.hip", "gemm_sk32.hip", "gemm_common.h"],
-                  "attn_decode_q4": ["attn_decode.hip", "codec_dev.h"]}
+                  "attn_decode_q4": ["attn_decode.hip", "codec_dev.h"],
+                  "attn_topk_q4": ["attn_decode.hip", "codec_dev.h"]}
 
 
 def measured_traffic(config: int, kind: str):
@@ -209,7 +215,7 @@ def topk_attention(model, cfg, L, pos: int, frac: float = 0.1, reps: int = 10):
     tr = L.fg_trace_collect()
     L.fg_trace_enable(False)
     L.fg_trace_kinds(None)
-    r = roofline(tr, ks, "hbm")
+    r = roofline(tr, ks, "hbm", cfg.get("id"))
     if r:
         r.update({"pos": pos, "topk": topk, "dense_avg_launch_us": round(tr[kd]["ms"] * 1e3 / tr[kd]["count"], 2),
                   "definition": "softmax over every score; V of the topk highest-scoring cached "
@@ -245,6 +251,7 @@ def sparse_decode(model, cfg, L, tok1, steps: int, no_trace: bool, frac: float =
                        "ceil(frac * pos) top-scoring cached positions"}
     if kind in tr:
         r["attn_ms_per_step"] = round(tr[kind]["ms"] / steps, 3)
+        r["roofline_attn"] = roofline(tr, kind, "hbm", cfg.get("id"))
     log(f"sparse-V decode: {r['ms_per_step']} ms/step")
     return r
 
@@ -307,7 +314,7 @@ def main():
     from throughput_oriented_offloaded_amd.model import Model
     import synth
 
-    cfg = CONFIGS[args.config]
+    cfg = dict(CONFIGS[args.config], id=args.config)
     if args.profile_layer:
         profile_layer(cfg, args.profile_layer)
         return
