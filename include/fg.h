@@ -46,7 +46,8 @@ const char* fg_status_str(int status);
 /* Detail of the calling thread's last failing call ("" if none). */
 const char* fg_last_error(void);
 /* ABI version, bumped on any incompatible change of this header (2: the
- * block-decode entry points take attn_topk_ppm). */
+ * block-decode entry points take attn_topk_ppm; 3: the layer and model
+ * passes take a KV tier, fg_kv_tier). */
 int fg_abi_version(void);
 
 /* ----------------------------------------------------------------- formats */
@@ -210,6 +211,51 @@ int fg_embed(const int32_t* tok, const int32_t* pos, int64_t rows, const void* E
  * (lowest index on ties). */
 int fg_argmax(const void* logits, int64_t rows, int64_t n, int32_t* out, void* stream);
 
+/* --------------------------------------------------------------- KV tier */
+/*
+ * KV-cache tiering to pinned host memory ([P2] "三条关键数据通路如何重叠" and
+ * "一个层级流水的伪代码": the cache of GPU batch k+1 is loaded while batch k
+ * computes, and the new entries of a batch are stored back afterwards;
+ * [P1] §6.4 load_cache / store_cache).
+ *
+ * The block's GPU batches 0..nb_dev-1 keep their cache in the device cache
+ * `kv` of the layer calls; batches nb_dev..nb-1 keep theirs in `host[j]`, a
+ * cache of the same format in pinned host memory (hipHostMalloc) whose
+ * sequence i is block sequence nb_dev*gbs + i.  For every host batch of every
+ * layer the library copies its history (positions 0..pos-1; K, V and their
+ * metadata, as 2-D copies of the cache's rows) into one of two device slots,
+ * runs that batch's attention on the slot (appending position pos there), and
+ * copies the appended row back to `host[j]`; prefill writes positions
+ * 0..s-1 of the slot and copies them back.  All copies run on the copy stream
+ * given at creation, ordered by events, in the order load(u), load(u+1),
+ * store(u), load(u+2), store(u+1), ... over the call's host batches u (layer
+ * by layer), so the load of the next batch, also across a layer boundary,
+ * runs while the current one computes.
+ *
+ * slots: caller-owned device memory of 2 * slot_bytes (256-byte aligned);
+ * slot_bytes >= fg_kvtier_slot_bytes(d, gbs, max_len, fmt) of every call
+ * (max_len: the host caches').  copy_stream: a caller-owned stream other
+ * than the compute streams of the calls (default priority); it must stay
+ * valid until fg_kvtier_destroy.  One fg_kvtier serves one call at a time;
+ * its slots must not be touched while a call's work is in flight.
+ */
+typedef struct fg_kvtier fg_kvtier;   /* opaque: two slots, copy stream, events */
+
+size_t fg_kvtier_slot_bytes(const fg_dims* d, int32_t gbs, int32_t max_len, int32_t fmt);
+int fg_kvtier_create(fg_kvtier** out, void* slots, size_t slot_bytes, void* copy_stream);
+int fg_kvtier_destroy(fg_kvtier* kt);
+
+/* KV tier of one layer or model call.  host: one pinned host cache (layer
+ * calls) or n_layers of them (model calls), each with n_seq >=
+ * (nb - nb_dev) * gbs and max_len > the call's last position.  With a tier,
+ * the device cache `kv` needs n_seq >= nb_dev * gbs only.  NULL tier: every
+ * sequence in `kv`. */
+typedef struct {
+    fg_kvtier* pipe;
+    const fg_kv* host;
+    int32_t nb_dev;
+} fg_kv_tier;
+
 /* ---------------------------------------------------------------- layers */
 /*
  * Prefill one layer for a block of nb GPU batches of gbs sequences each
@@ -221,7 +267,8 @@ int fg_argmax(const void* logits, int64_t rows, int64_t n, int32_t* out, void* s
  * ws: ws_bytes >= fg_workspace_bytes(d, gbs * s, w->fmt).
  */
 int fg_layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, int32_t nb,
-                     int32_t s, const fg_kv* kv, void* ws, size_t ws_bytes, void* stream);
+                     int32_t s, const fg_kv* kv, void* ws, size_t ws_bytes, void* stream,
+                     const fg_kv_tier* kvt);
 
 /*
  * One decode step of one layer for the whole block (bls = gbs * nb new
@@ -238,10 +285,11 @@ int fg_layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs
  * 100000.  0, any value >= 1000000, and any step where that topk reaches pos
  * (e.g. pos = 0) run dense attention.  Negative: FG_ERR_INVALID.  A sparse
  * step with pos > 8192 returns FG_ERR_UNSUPPORTED before anything is enqueued.
+ * kvt: KV tier (see fg_kv_tier; kvt->host is this layer's host cache) or NULL.
  */
 int fg_layer_decode_block(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs,
                           int32_t nb, int32_t pos, const fg_kv* kv, void* ws, size_t ws_bytes,
-                          void* stream, int32_t attn_topk_ppm);
+                          void* stream, int32_t attn_topk_ppm, const fg_kv_tier* kvt);
 
 /* Device scratch needed by one layer pass over `rows` token rows
  * (decode: rows = bls; prefill: rows = gbs * s). */
@@ -279,6 +327,7 @@ size_t fg_workspace_bytes(const fg_dims* d, int64_t rows, int32_t fmt_w);
  * touched while a call's work is in flight.
  * attn_topk_ppm (decode): as in fg_layer_decode_block, for every layer; every
  * layer is checked before the first is enqueued.
+ * kvt: KV tier with kvt->host[j] the host cache of layer j, or NULL.
  */
 enum { FG_SCHED_FIRST_STAGED = 1, FG_SCHED_STAGE_NEXT = 2 };
 
@@ -302,11 +351,12 @@ int fg_sched_destroy(fg_sched* sc);
 int fg_model_prefill(fg_sched* sc, const fg_dims* d, int32_t n_layers, const fg_layer_w* w,
                      const fg_tier_w* tier, const fg_kv* kv, void* x, int32_t gbs, int32_t nb,
                      int32_t s, void* ws, size_t ws_bytes, void* stream, void* copy_stream,
-                     int32_t flags);
+                     int32_t flags, const fg_kv_tier* kvt);
 int fg_model_decode_step(fg_sched* sc, const fg_dims* d, int32_t n_layers, const fg_layer_w* w,
                          const fg_tier_w* tier, const fg_kv* kv, void* x, int32_t gbs,
                          int32_t nb, int32_t pos, void* ws, size_t ws_bytes, void* stream,
-                         void* copy_stream, int32_t flags, int32_t attn_topk_ppm);
+                         void* copy_stream, int32_t flags, int32_t attn_topk_ppm,
+                         const fg_kv_tier* kvt);
 
 /* --------------------------------------------------------------- sizes */
 /* Bytes of the six layer matrices of n_layers layers ([P2]: M_W =

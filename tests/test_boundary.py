@@ -22,7 +22,7 @@ def test_exports_every_declared_symbol(L):
     for name in ("fg_quant_group4", "fg_dequant_group4", "fg_layer_prefill",
                  "fg_layer_decode_block", "fg_kv_append_q4", "fg_attn_decode_q4"):
         assert name in declared
-    assert L.raw("fg_abi_version")() == 2
+    assert L.raw("fg_abi_version")() == 3
 
 
 def test_status_strings(L):
@@ -123,27 +123,27 @@ def test_layer_rejects_bad_arguments(L):
     need = L.fg_workspace_bytes(d, 4, 1)
     assert need > 0
     st = f(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(p), 2, 2, 3, ctypes.byref(kv),
-           ctypes.c_void_p(p), need - 1, None, 0)
+           ctypes.c_void_p(p), need - 1, None, 0, None)
     assert st == L.FG_ERR_CAPACITY
     st = f(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(p), 3, 2, 3, ctypes.byref(kv),
-           ctypes.c_void_p(p), need, None, 0)
+           ctypes.c_void_p(p), need, None, 0, None)
     assert st == L.FG_ERR_INVALID                     # 6 sequences > n_seq
     st = f(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(p), 2, 2, 3, ctypes.byref(kv),
-           ctypes.c_void_p(p), need, None, -1)
+           ctypes.c_void_p(p), need, None, -1, None)
     assert st == L.FG_ERR_INVALID                     # negative Top-K fraction
     long_kv = _kv(L, max_len=9000, n_seq=4)
     st = f(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(p), 2, 2, 8193, ctypes.byref(long_kv),
-           ctypes.c_void_p(p), need, None, 100000)
+           ctypes.c_void_p(p), need, None, 100000, None)
     assert st == L.FG_ERR_UNSUPPORTED                 # sparse history beyond the on-chip scores
     assert "Top-K" in L.last_error()
     w.m_o = None
     st = f(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(p), 2, 2, 3, ctypes.byref(kv),
-           ctypes.c_void_p(p), need, None, 0)
+           ctypes.c_void_p(p), need, None, 0, None)
     assert st == L.FG_ERR_INVALID
     g = L.raw("fg_layer_prefill")
     w.m_o = p
     st = g(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(p), 2, 2, 17, ctypes.byref(kv),
-           ctypes.c_void_p(p), 1 << 40, None)
+           ctypes.c_void_p(p), 1 << 40, None, None)
     assert st == L.FG_ERR_INVALID                     # s > max_len
 
 
@@ -176,22 +176,78 @@ def test_model_pass_rejects_bad_arguments(L):
     kvs = (L.KV * 2)(_kv(L, max_len=16, n_seq=4), _kv(L, max_len=16, n_seq=4))
     f = L.raw("fg_model_decode_step")
     V = ctypes.c_void_p
-    assert f(None, ctypes.byref(d), 0, w, None, kvs, V(p), 2, 2, 3, V(p), ws_need, None, None, 0, 0) \
+    assert f(None, ctypes.byref(d), 0, w, None, kvs, V(p), 2, 2, 3, V(p), ws_need, None, None, 0, 0, None) \
         == L.FG_ERR_INVALID                            # no layers
     w[1].m_o = None                                    # second layer broken: nothing may run
-    assert f(None, ctypes.byref(d), 2, w, None, kvs, V(p), 2, 2, 3, V(p), ws_need, None, None, 0, 0) \
+    assert f(None, ctypes.byref(d), 2, w, None, kvs, V(p), 2, 2, 3, V(p), ws_need, None, None, 0, 0, None) \
         == L.FG_ERR_INVALID
     assert "metadata" in L.last_error()
     w[1].m_o = p
     tier = (L.TierW * 2)(L.TierW(p, p, p), L.TierW())
-    assert f(None, ctypes.byref(d), 2, w, tier, kvs, V(p), 2, 2, 3, V(p), ws_need, None, None, 0, 0) \
+    assert f(None, ctypes.byref(d), 2, w, tier, kvs, V(p), 2, 2, 3, V(p), ws_need, None, None, 0, 0, None) \
         == L.FG_ERR_INVALID                            # tiering without a scheduler
     assert "scheduler" in L.last_error()
     long_kvs = (L.KV * 2)(_kv(L, max_len=9000, n_seq=4), _kv(L, max_len=9000, n_seq=4))
     assert f(None, ctypes.byref(d), 2, w, None, long_kvs, V(p), 2, 2, 8193, V(p), ws_need, None,
-             None, 0, 100000) == L.FG_ERR_UNSUPPORTED   # sparse step past the on-chip scores
+             None, 0, 100000, None) == L.FG_ERR_UNSUPPORTED   # sparse step past the on-chip scores
     g = L.raw("fg_model_prefill")
-    assert g(None, ctypes.byref(d), 2, w, None, kvs, V(p), 2, 2, 17, V(p), 1 << 40, None, None, 0) \
+    assert g(None, ctypes.byref(d), 2, w, None, kvs, V(p), 2, 2, 17, V(p), 1 << 40, None, None, 0, None) \
         == L.FG_ERR_INVALID                            # s > max_len
     assert L.raw("fg_sched_create")(None, V(p), 256) == L.FG_ERR_INVALID
     assert L.raw("fg_sched_destroy")(None) == L.FG_OK
+
+
+def test_kv_tier_slot_bytes_closed_form(L):
+    """Two K/V code tensors and (4-bit) two metadata tensors of gbs sequences,
+    each rounded up to 256 bytes."""
+    up = lambda n: -(-n // 256) * 256  # noqa: E731
+    for h1, nh, hd, gbs, ml in ((768, 12, 64, 4, 40), (7168, 56, 128, 48, 544), (256, 2, 128, 3, 17)):
+        d = L.dims(h1, 4 * h1, nh, hd)
+        rows = gbs * nh * ml
+        assert L.fg_kvtier_slot_bytes(d, gbs, ml, L.FG_FMT_Q4G64) == \
+            2 * up(rows * hd // 2) + 2 * up(rows * hd // 64 * 4)
+        assert L.fg_kvtier_slot_bytes(d, gbs, ml, L.FG_FMT_F16) == 2 * up(rows * hd * 2)
+    assert L.fg_kvtier_slot_bytes(L.dims(256, 1024, 2, 128), 0, 16, 1) == 0
+    assert L.raw("fg_kvtier_create")(None, ctypes.c_void_p(1 << 20), 256, ctypes.c_void_p(1)) \
+        == L.FG_ERR_INVALID
+    h = ctypes.c_void_p()
+    assert L.raw("fg_kvtier_create")(ctypes.byref(h), ctypes.c_void_p((1 << 20) + 8), 256,
+                                     ctypes.c_void_p(1)) == L.FG_ERR_INVALID   # misaligned
+    assert L.raw("fg_kvtier_destroy")(None) == L.FG_OK
+
+
+def test_kv_tier_rejects_bad_geometry(L):
+    """The host cache and nb_dev are checked before the tier object or any
+    device (fails on the host; no GPU needed)."""
+    p = 1 << 20
+    d = L.dims(256, 1024, 2, 128)
+    w = L.LayerW(1, *([p] * 16))
+    kv = _kv(L, max_len=16, n_seq=4)
+    f = L.raw("fg_layer_decode_block")
+    need = L.fg_workspace_bytes(d, 6, 1)
+    V = ctypes.c_void_p
+
+    def call(host, nb_dev, pos=3, pipe=None):
+        t = L.KvTier(pipe, ctypes.pointer(host), nb_dev)
+        return f(ctypes.byref(d), ctypes.byref(w), V(p), 2, 3, pos, ctypes.byref(kv), V(p), need,
+                 None, 0, ctypes.byref(t))
+
+    assert call(_kv(L, max_len=16, n_seq=4), 4) == L.FG_ERR_INVALID          # nb_dev > nb
+    assert "nb_dev" in L.last_error()
+    assert call(_kv(L, max_len=16, n_seq=3), 1) == L.FG_ERR_INVALID          # 4 host sequences needed
+    assert "sequences" in L.last_error()
+    assert call(_kv(L, fmt=0, max_len=16, n_seq=4), 1) == L.FG_ERR_INVALID   # format differs
+    assert call(_kv(L, max_len=3, n_seq=4), 1) == L.FG_ERR_INVALID           # pos 3 beyond host max_len
+    assert call(_kv(L, max_len=16, n_seq=4), 1) == L.FG_ERR_INVALID          # no tier object
+    assert "tier object" in L.last_error()
+    # every batch on the device: the host cache is not consulted
+    t = L.KvTier(None, None, 3)
+    kv6 = _kv(L, max_len=16, n_seq=6)
+    assert f(ctypes.byref(d), ctypes.byref(w), V(p), 2, 3, 3, ctypes.byref(kv6), V(p), need - 1,
+             None, 0, ctypes.byref(t)) == L.FG_ERR_CAPACITY
+    g = L.raw("fg_model_decode_step")
+    ws = (L.LayerW * 1)(w)
+    kvs = (L.KV * 1)(kv)
+    t = L.KvTier(None, None, 1)
+    assert g(None, ctypes.byref(d), 1, ws, None, kvs, V(p), 2, 3, 3, V(p), need, None, None, 0, 0,
+             ctypes.byref(t)) == L.FG_ERR_INVALID                        # no host cache array

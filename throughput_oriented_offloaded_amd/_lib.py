@@ -51,6 +51,11 @@ class KV(ctypes.Structure):
                 ("max_len", I32), ("n_seq", I32)]
 
 
+class KvTier(ctypes.Structure):
+    """fg_kv_tier: tier object, host cache(s), GPU batches kept on the device."""
+    _fields_ = [("pipe", P), ("host", ctypes.POINTER(KV)), ("nb_dev", I32)]
+
+
 class TierW(ctypes.Structure):
     _fields_ = [("qk_host", P), ("v_dev", P), ("w1_host", P)]
 
@@ -81,19 +86,23 @@ _PROTOS = {
     "fg_embed": (ctypes.c_int, [P, P, I64, P, I64, P, I64, I64, P, P]),
     "fg_argmax": (ctypes.c_int, [P, I64, I64, P, P]),
     "fg_layer_prefill": (ctypes.c_int, [ctypes.POINTER(Dims), ctypes.POINTER(LayerW), P, I32, I32, I32,
-                                        ctypes.POINTER(KV), P, SZ, P]),
+                                        ctypes.POINTER(KV), P, SZ, P, ctypes.POINTER(KvTier)]),
     "fg_layer_decode_block": (ctypes.c_int, [ctypes.POINTER(Dims), ctypes.POINTER(LayerW), P, I32, I32,
-                                             I32, ctypes.POINTER(KV), P, SZ, P, I32]),
+                                             I32, ctypes.POINTER(KV), P, SZ, P, I32,
+                                             ctypes.POINTER(KvTier)]),
     "fg_workspace_bytes": (SZ, [ctypes.POINTER(Dims), I64, I32]),
     "fg_stage_bytes": (SZ, [ctypes.POINTER(Dims)]),
     "fg_sched_create": (ctypes.c_int, [ctypes.POINTER(P), P, SZ]),
     "fg_sched_destroy": (ctypes.c_int, [P]),
     "fg_model_prefill": (ctypes.c_int, [P, ctypes.POINTER(Dims), I32, ctypes.POINTER(LayerW),
                                         ctypes.POINTER(TierW), ctypes.POINTER(KV), P, I32, I32, I32,
-                                        P, SZ, P, P, I32]),
+                                        P, SZ, P, P, I32, ctypes.POINTER(KvTier)]),
     "fg_model_decode_step": (ctypes.c_int, [P, ctypes.POINTER(Dims), I32, ctypes.POINTER(LayerW),
                                             ctypes.POINTER(TierW), ctypes.POINTER(KV), P, I32, I32,
-                                            I32, P, SZ, P, P, I32, I32]),
+                                            I32, P, SZ, P, P, I32, I32, ctypes.POINTER(KvTier)]),
+    "fg_kvtier_slot_bytes": (SZ, [ctypes.POINTER(Dims), I32, I32, I32]),
+    "fg_kvtier_create": (ctypes.c_int, [ctypes.POINTER(P), P, SZ, P]),
+    "fg_kvtier_destroy": (ctypes.c_int, [P]),
     "fg_weight_bytes": (I64, [ctypes.POINTER(Dims), I32, I32]),
     "fg_kv_bytes": (I64, [ctypes.POINTER(Dims), I32, I32, I32, I32, I32]),
     "fg_trace_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -227,18 +236,38 @@ def fg_argmax(logits, rows, n, out, stream=None):
     _check("fg_argmax", _L.fg_argmax(ptr(logits), rows, n, ptr(out), stream_ptr(stream)))
 
 
-def fg_layer_prefill(d: Dims, w: LayerW, x, gbs, nb, s, kv: KV, ws, ws_bytes, stream=None):
+def _kvt(kvt):
+    return ctypes.byref(kvt) if kvt is not None else None
+
+
+def fg_layer_prefill(d: Dims, w: LayerW, x, gbs, nb, s, kv: KV, ws, ws_bytes, stream=None, kvt=None):
     _check("fg_layer_prefill", _L.fg_layer_prefill(ctypes.byref(d), ctypes.byref(w), ptr(x), gbs, nb, s,
                                                    ctypes.byref(kv), ptr(ws), ws_bytes,
-                                                   stream_ptr(stream)))
+                                                   stream_ptr(stream), _kvt(kvt)))
 
 
 def fg_layer_decode_block(d: Dims, w: LayerW, x, gbs, nb, pos, kv: KV, ws, ws_bytes, stream=None,
-                          attn_topk_ppm=0):
+                          attn_topk_ppm=0, kvt=None):
     _check("fg_layer_decode_block", _L.fg_layer_decode_block(ctypes.byref(d), ctypes.byref(w), ptr(x),
                                                              gbs, nb, pos, ctypes.byref(kv), ptr(ws),
                                                              ws_bytes, stream_ptr(stream),
-                                                             attn_topk_ppm))
+                                                             attn_topk_ppm, _kvt(kvt)))
+
+
+def fg_kvtier_slot_bytes(d: Dims, gbs, max_len, fmt) -> int:
+    return _L.fg_kvtier_slot_bytes(ctypes.byref(d), gbs, max_len, fmt)
+
+
+def fg_kvtier_create(slots, slot_bytes, copy_stream) -> int:
+    """KV tier object over the caller's two slots (2 * slot_bytes) and copy stream."""
+    h = P()
+    _check("fg_kvtier_create", _L.fg_kvtier_create(ctypes.byref(h), ptr(slots), slot_bytes,
+                                                   copy_stream.cuda_stream))
+    return h.value
+
+
+def fg_kvtier_destroy(h):
+    _check("fg_kvtier_destroy", _L.fg_kvtier_destroy(h))
 
 
 def fg_stage_bytes(d: Dims) -> int:
@@ -261,22 +290,23 @@ def _arr(T, items):
 
 
 def fg_model_prefill(sched, d: Dims, layers, tier, kvs, x, gbs, nb, s, ws, ws_bytes, stream=None,
-                     copy_stream=None, flags=0):
+                     copy_stream=None, flags=0, kvt=None):
     """layers: ctypes array of LayerW; tier: array of TierW or None; kvs: array of KV."""
     _check("fg_model_prefill", _L.fg_model_prefill(sched, ctypes.byref(d), len(layers), layers, tier,
                                                    kvs, ptr(x), gbs, nb, s, ptr(ws), ws_bytes,
                                                    stream_ptr(stream),
                                                    copy_stream.cuda_stream if copy_stream else None,
-                                                   flags))
+                                                   flags, _kvt(kvt)))
 
 
 def fg_model_decode_step(sched, d: Dims, layers, tier, kvs, x, gbs, nb, pos, ws, ws_bytes,
-                         stream=None, copy_stream=None, flags=0, attn_topk_ppm=0):
+                         stream=None, copy_stream=None, flags=0, attn_topk_ppm=0, kvt=None):
     _check("fg_model_decode_step", _L.fg_model_decode_step(sched, ctypes.byref(d), len(layers),
                                                            layers, tier, kvs, ptr(x), gbs, nb, pos,
                                                            ptr(ws), ws_bytes, stream_ptr(stream),
                                                            copy_stream.cuda_stream if copy_stream
-                                                           else None, flags, attn_topk_ppm))
+                                                           else None, flags, attn_topk_ppm,
+                                                           _kvt(kvt)))
 
 
 def fg_workspace_bytes(d: Dims, rows, fmt_w) -> int:
@@ -297,7 +327,7 @@ def fg_trace_enable(on: bool):
 
 TRACE_KINDS = ["quant_g4", "dequant_g4", "gemm_q4", "gemm_f16", "splitk_reduce", "attn_decode_q4",
                "attn_decode_f16", "kv_store", "attn_prefill", "layernorm", "embed", "argmax",
-               "reduce_layernorm", "attn_topk_q4", "attn_topk_f16"]
+               "reduce_layernorm", "attn_topk_q4", "attn_topk_f16", "kv_h2d", "kv_d2h"]
 
 
 def fg_trace_kinds(names=None):

@@ -53,7 +53,7 @@ int check_dims(const fg_dims* d) {
 
 extern "C" {
 
-int fg_abi_version(void) { return 2; }
+int fg_abi_version(void) { return 3; }
 
 const char* fg_status_str(int status) {
     switch (status) {

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstddef>
 #include <cstdint>
+#include <vector>
 
 #include "../../include/fg.h"
 
@@ -96,6 +97,48 @@ int launch_linear(const LinearArgs& a, hipStream_t st);
 size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t fmt);
 // M rows take the data-parallel (prefill-shaped) GEMM schedule
 bool linear_is_dp(int64_t M);
+// KV tiering (kvtier.hip): validation of a tier against the device cache
+// `dev`, for n_host_seq host sequences of GPU batches of gbs and positions
+// below end_pos.
+int kvtier_check(const fg_kvtier* kt, const fg_dims* d, const fg_kv* dev, const fg_kv* host,
+                 int32_t gbs, int32_t n_host_seq, int32_t end_pos);
+// The host-resident GPU batches ("units") of one call, in execution order,
+// moved through the tier object's two slots.  begin(u): loads enqueued
+// through unit u + 1 (rows [0, load_rows) each), the compute stream made to
+// wait for unit u's, and u's slot returned as a cache of gbs sequences;
+// end(u, lo, hi): rows [lo, hi) of the slot copied back to the host after the
+// compute stream's work so far.  Units are begun and ended strictly in order,
+// each ended before the next is begun.
+class KvPipe {
+  public:
+    KvPipe(fg_kvtier* kt, const fg_dims* d, int32_t gbs, int32_t load_rows, hipStream_t st);
+    void add(const fg_kv* host, int32_t seq0);
+    int begin(int32_t u, fg_kv* slot);
+    int end(int32_t u, int32_t lo, int32_t hi);
+
+  private:
+    struct Unit {
+        const fg_kv* host;
+        int32_t seq0;
+    };
+    fg_kv slot(int32_t u) const;
+    int copy(int32_t u, int32_t lo, int32_t hi, bool to_host);
+    fg_kvtier* kt_;
+    const fg_dims* d_;
+    int32_t gbs_, load_rows_;
+    hipStream_t st_;
+    std::vector<Unit> unit_;
+    int32_t loaded_ = 0, begun_ = 0, stored_ = 0;
+};
+// KV tier of one layer pass: GPU batches nb_dev.. use host (their first is
+// unit u0 of pipe); pipe is null in check-only passes.
+struct KvTierCall {
+    KvPipe* pipe;
+    const fg_kvtier* kt;
+    const fg_kv* host;
+    int32_t nb_dev;
+    int32_t u0;
+};
 // One decoder layer (layer.hip): arguments validated, then (unless
 // check_only) enqueued on st.
 // ln1_done: the layer's input LayerNorm is already in the workspace (the
@@ -104,13 +147,14 @@ bool linear_is_dp(int64_t M);
 // over ceil(pos * ppm / 1e6) cached positions (0 or >= 1e6: dense).
 int layer_decode(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, int32_t nb,
                  int32_t pos, const fg_kv* kv, void* ws, size_t ws_bytes, hipStream_t st,
-                 bool check_only, bool ln1_done, const fg_layer_w* next, int32_t attn_topk_ppm);
+                 bool check_only, bool ln1_done, const fg_layer_w* next, int32_t attn_topk_ppm,
+                 const KvTierCall* kvt);
 // Top-K count of a decode step at position pos: -1 (dense) unless
 // 0 < ppm < 1e6 selects fewer than pos positions.
 int32_t attn_topk_count(int32_t pos, int32_t ppm);
 int layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, int32_t nb,
                   int32_t s, const fg_kv* kv, void* ws, size_t ws_bytes, hipStream_t st,
-                  bool check_only);
+                  bool check_only, const KvTierCall* kvt);
 size_t layer_ws_bytes(const fg_dims* d, int64_t rows, int32_t fmt);
 
 int launch_layernorm(const __half* x, int64_t rows, int64_t h, const __half* g, const __half* b,

@@ -1,0 +1,225 @@
+// KV-cache tiering: the cache of some GPU batches lives in pinned host memory
+// and passes through two device slots.
+//
+// Method ("FlexGen 完全拆解", sections "三条关键数据通路如何重叠" and "一个层级
+// 流水的伪代码"; bjbfmj.com walkthrough §6.4, load_cache / store_cache): while
+// GPU batch k computes, the cache of batch k+1 is loaded and the new entries
+// of the batch before are stored.  Here a "unit" is one host-resident GPU
+// batch of one layer; the units of a call are numbered in execution order
+// (layer by layer, batch by batch) and unit u uses slot u mod 2:
+//   copy stream:    load(u): rows [0, n) of every (sequence, head) of the
+//                   unit's K, V (and metadata), host -> slot, as 2-D copies;
+//                   record ready[u mod 2]
+//   compute stream: wait ready[u mod 2]; the unit's kernel on the slot;
+//                   record done[u mod 2]
+//   copy stream:    wait done[u mod 2]; store(u): the rows the kernel wrote,
+//                   slot -> host
+// The copy stream receives load(0), load(1), store(0), load(2), store(1), ...:
+// load(u+2) reuses the slot of u and follows store(u) in stream order, which
+// itself waited for unit u's kernel, so two loads are never more than one
+// unit ahead and a slot is never overwritten while read.  Across calls the
+// same order holds because every copy of a tier object runs on its one copy
+// stream.
+#include <new>
+
+#include "fg_internal.h"
+#include "fg_trace.h"
+
+struct fg_kvtier {
+    unsigned char* slot[2];
+    size_t slot_bytes;
+    hipStream_t cp;
+    hipEvent_t ready[2];
+    hipEvent_t done[2];
+    int device;
+};
+
+namespace fg {
+namespace {
+
+// One cache of `nseq` sequences: the four tensors' byte offsets (codes of K,
+// codes of V, metadata of K, of V), each 256-byte aligned, and their row sizes.
+struct SlotLayout {
+    size_t off[4];
+    size_t row[4];
+    size_t total;
+};
+
+SlotLayout slot_layout(const fg_dims* d, int32_t nseq, int32_t max_len, int32_t fmt) {
+    SlotLayout L{};
+    const size_t rows = (size_t)nseq * d->n_heads * max_len;
+    const bool q4 = fmt == FG_FMT_Q4G64;
+    const size_t code = q4 ? (size_t)d->head_dim / 2 : (size_t)d->head_dim * 2;
+    const size_t meta = q4 ? (size_t)d->head_dim / 64 * 4 : 0;
+    const size_t rs[4] = {code, code, meta, meta};
+    size_t at = 0;
+    for (int t = 0; t < 4; ++t) {
+        L.off[t] = at;
+        L.row[t] = rs[t];
+        at += align_up(rows * rs[t], 256);
+    }
+    L.total = at;
+    return L;
+}
+
+void* tensor_of(const fg_kv* kv, int t) {
+    return t == 0 ? kv->k : t == 1 ? kv->v : t == 2 ? kv->k_meta : kv->v_meta;
+}
+
+}  // namespace
+
+int kvtier_check(const fg_kvtier* kt, const fg_dims* d, const fg_kv* dev, const fg_kv* host,
+                 int32_t gbs, int32_t n_host_seq, int32_t end_pos) {
+    FG_CHECK_ARG(host, "KV tier: null host cache");
+    FG_CHECK_ARG(host->fmt == dev->fmt, "KV tier: host cache format %d differs from the device's %d",
+                 host->fmt, dev->fmt);
+    FG_CHECK_ARG(host->k && host->v && (host->fmt != FG_FMT_Q4G64 || (host->k_meta && host->v_meta)),
+                 "KV tier: null host cache tensors");
+    FG_CHECK_ARG(host->n_seq >= n_host_seq, "KV tier: host cache holds %d sequences, %d needed",
+                 host->n_seq, n_host_seq);
+    FG_CHECK_ARG(end_pos <= host->max_len, "KV tier: position %d beyond the host cache's max_len %d",
+                 end_pos - 1, host->max_len);
+    FG_CHECK_ARG(kt, "KV tier: null tier object (fg_kvtier_create)");
+    const size_t need = slot_layout(d, gbs, host->max_len, host->fmt).total;
+    if (need > kt->slot_bytes)
+        return set_error(FG_ERR_CAPACITY, "KV tier: slots of %zu bytes < %zu needed", kt->slot_bytes,
+                         need);
+    int cur = -1;
+    FG_HIP(hipGetDevice(&cur));
+    FG_CHECK_ARG(cur == kt->device, "KV tier created on device %d, called on %d", kt->device, cur);
+    const int nt = host->fmt == FG_FMT_Q4G64 ? 4 : 2;
+    for (int t = 0; t < nt; ++t) {
+        hipPointerAttribute_t at{};
+        if (hipPointerGetAttributes(&at, tensor_of(host, t)) != hipSuccess ||
+            at.type != hipMemoryTypeHost) {
+            (void)hipGetLastError();
+            return set_error(FG_ERR_INVALID, "KV tier: host cache must be pinned (hipHostMalloc)");
+        }
+    }
+    return FG_OK;
+}
+
+KvPipe::KvPipe(fg_kvtier* kt, const fg_dims* d, int32_t gbs, int32_t load_rows, hipStream_t st)
+    : kt_(kt), d_(d), gbs_(gbs), load_rows_(load_rows), st_(st) {}
+
+void KvPipe::add(const fg_kv* host, int32_t seq0) { unit_.push_back(Unit{host, seq0}); }
+
+fg_kv KvPipe::slot(int32_t u) const {
+    const fg_kv* h = unit_[u].host;
+    const SlotLayout L = slot_layout(d_, gbs_, h->max_len, h->fmt);
+    unsigned char* b = kt_->slot[u & 1];
+    fg_kv s{};
+    s.fmt = h->fmt;
+    s.k = b + L.off[0];
+    s.v = b + L.off[1];
+    s.k_meta = h->fmt == FG_FMT_Q4G64 ? b + L.off[2] : nullptr;
+    s.v_meta = h->fmt == FG_FMT_Q4G64 ? b + L.off[3] : nullptr;
+    s.max_len = h->max_len;
+    s.n_seq = gbs_;
+    return s;
+}
+
+// rows [lo, hi) of every (sequence, head) between unit u's host cache and its
+// slot, as one 2-D copy per tensor
+int KvPipe::copy(int32_t u, int32_t lo, int32_t hi, bool to_host) {
+    if (hi <= lo) return FG_OK;
+    const Unit& un = unit_[u];
+    const fg_kv* h = un.host;
+    const SlotLayout L = slot_layout(d_, gbs_, h->max_len, h->fmt);
+    const int nt = h->fmt == FG_FMT_Q4G64 ? 4 : 2;
+    const size_t height = (size_t)gbs_ * d_->n_heads;
+    double bytes = 0;
+    for (int t = 0; t < nt; ++t) bytes += (double)height * (hi - lo) * L.row[t];
+    TraceScope ts(to_host ? TK_KV_D2H : TK_KV_H2D, kt_->cp, 0.0, bytes);
+    for (int t = 0; t < nt; ++t) {
+        const size_t r = L.row[t], pitch = (size_t)h->max_len * r;
+        unsigned char* hp = static_cast<unsigned char*>(tensor_of(h, t)) +
+                            (size_t)un.seq0 * d_->n_heads * pitch + (size_t)lo * r;
+        unsigned char* dp = kt_->slot[u & 1] + L.off[t] + (size_t)lo * r;
+        const size_t width = (size_t)(hi - lo) * r;
+        if (to_host)
+            FG_HIP(hipMemcpy2DAsync(hp, pitch, dp, pitch, width, height, hipMemcpyDeviceToHost, kt_->cp));
+        else
+            FG_HIP(hipMemcpy2DAsync(dp, pitch, hp, pitch, width, height, hipMemcpyHostToDevice, kt_->cp));
+    }
+    return FG_OK;
+}
+
+int KvPipe::begin(int32_t u, fg_kv* slot_out) {
+    const int32_t n = (int32_t)unit_.size();
+    FG_CHECK_ARG(u >= 0 && u < n && u == begun_, "KV tier: unit %d out of order", u);
+    // loads through u + 1 (the next one runs while unit u computes); load(v)
+    // for v >= 2 follows store(v - 2), enqueued by end(v - 2)
+    while (loaded_ <= u + 1 && loaded_ < n) {
+        FG_CHECK_ARG(loaded_ < 2 || stored_ >= loaded_ - 1, "KV tier: slot of unit %d still in use",
+                     loaded_);
+        FG_TRY(copy(loaded_, 0, load_rows_, false));
+        FG_HIP(hipEventRecord(kt_->ready[loaded_ & 1], kt_->cp));
+        ++loaded_;
+    }
+    FG_HIP(hipStreamWaitEvent(st_, kt_->ready[u & 1], 0));
+    *slot_out = slot(u);
+    begun_ = u + 1;
+    return FG_OK;
+}
+
+int KvPipe::end(int32_t u, int32_t lo, int32_t hi) {
+    FG_CHECK_ARG(u == stored_ && u < begun_, "KV tier: unit %d ended out of order", u);
+    FG_HIP(hipEventRecord(kt_->done[u & 1], st_));
+    FG_HIP(hipStreamWaitEvent(kt_->cp, kt_->done[u & 1], 0));
+    FG_TRY(copy(u, lo, hi, true));
+    ++stored_;
+    return FG_OK;
+}
+
+}  // namespace fg
+
+// -------------------------------------------------------------------- C ABI
+extern "C" size_t fg_kvtier_slot_bytes(const fg_dims* d, int32_t gbs, int32_t max_len, int32_t fmt) {
+    if (fg::check_dims(d) != FG_OK || gbs < 1 || max_len < 1 ||
+        (fmt != FG_FMT_F16 && fmt != FG_FMT_Q4G64)) {
+        fg::clear_error();
+        return 0;
+    }
+    return fg::slot_layout(d, gbs, max_len, fmt).total;
+}
+
+extern "C" int fg_kvtier_create(fg_kvtier** out, void* slots, size_t slot_bytes, void* copy_stream) {
+    fg::clear_error();
+    FG_CHECK_ARG(out && slots && slot_bytes > 0, "null pointer or empty slots");
+    FG_CHECK_ARG((uintptr_t)slots % 256 == 0 && slot_bytes % 256 == 0,
+                 "slots must be 256-byte aligned and a multiple of 256 bytes");
+    FG_CHECK_ARG(copy_stream, "KV tier needs a copy stream (not the null stream)");
+    *out = nullptr;
+    fg_kvtier* kt = new (std::nothrow) fg_kvtier();
+    FG_CHECK_ARG(kt, "out of host memory");
+    kt->slot[0] = static_cast<unsigned char*>(slots);
+    kt->slot[1] = static_cast<unsigned char*>(slots) + slot_bytes;
+    kt->slot_bytes = slot_bytes;
+    kt->cp = fg::as_stream(copy_stream);
+    hipEvent_t* ev[4] = {&kt->ready[0], &kt->ready[1], &kt->done[0], &kt->done[1]};
+    int made = 0;
+    bool ok = hipGetDevice(&kt->device) == hipSuccess;
+    while (ok && made < 4) {
+        if (hipEventCreateWithFlags(ev[made], hipEventDisableTiming) != hipSuccess) ok = false;
+        else ++made;
+    }
+    if (!ok) {
+        for (int i = 0; i < made; ++i) (void)hipEventDestroy(*ev[i]);
+        delete kt;
+        return fg::set_error(FG_ERR_HIP, "fg_kvtier_create: %s", hipGetErrorString(hipGetLastError()));
+    }
+    *out = kt;
+    return FG_OK;
+}
+
+extern "C" int fg_kvtier_destroy(fg_kvtier* kt) {
+    fg::clear_error();
+    if (!kt) return FG_OK;
+    for (int i = 0; i < 2; ++i) {
+        (void)hipEventDestroy(kt->ready[i]);
+        (void)hipEventDestroy(kt->done[i]);
+    }
+    delete kt;
+    return FG_OK;
+}

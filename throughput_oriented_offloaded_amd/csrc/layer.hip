@@ -103,6 +103,25 @@ int lin(const fg_layer_w* w, int which, const __half* x, int64_t M, int64_t K, i
     return launch_linear(a, st);
 }
 
+// The block's sequences against the device cache and, with a KV tier, the
+// host cache; positions below end_pos must fit.
+int check_block(const fg_dims* d, const fg_kv* kv, int32_t gbs, int32_t nb, int32_t end_pos,
+                const KvTierCall* kvt) {
+    FG_CHECK_ARG(gbs >= 1 && nb >= 1, "block %d x %d is empty", gbs, nb);
+    const int32_t nd = kvt ? kvt->nb_dev : nb;
+    if (kvt) FG_CHECK_ARG(nd >= 0 && nd <= nb, "KV tier: nb_dev %d outside [0, nb %d]", nd, nb);
+    FG_CHECK_ARG(end_pos >= 1, "position %d is negative", end_pos - 1);
+    if (nd > 0) {   // the device cache is not read when every batch is on the host
+        FG_CHECK_ARG((int64_t)gbs * nd <= kv->n_seq,
+                     "block %d x %d exceeds the cache's %d sequences", gbs, nd, kv->n_seq);
+        FG_CHECK_ARG(end_pos <= kv->max_len, "position %d outside [0, max_len %d)", end_pos - 1,
+                     kv->max_len);
+    }
+    if (kvt && nd < nb)
+        FG_TRY(kvtier_check(kvt->kt, d, kv, kvt->host, gbs, (nb - nd) * gbs, end_pos));
+    return FG_OK;
+}
+
 }  // namespace
 
 // Positions whose V a sparse step reads: the fraction ppm / 1e6 of the
@@ -115,12 +134,10 @@ int32_t attn_topk_count(int32_t pos, int32_t ppm) {
 
 int layer_decode(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, int32_t nb,
                  int32_t pos, const fg_kv* kv, void* ws, size_t ws_bytes, hipStream_t st,
-                 bool check_only, bool ln1_done, const fg_layer_w* next, int32_t attn_topk_ppm) {
+                 bool check_only, bool ln1_done, const fg_layer_w* next, int32_t attn_topk_ppm,
+                 const KvTierCall* kvt) {
     FG_TRY(check_layer(d, w, x, kv, ws));
-    FG_CHECK_ARG(gbs >= 1 && nb >= 1 && (int64_t)gbs * nb <= kv->n_seq,
-                 "block %d x %d exceeds the cache's %d sequences", gbs, nb, kv->n_seq);
-    FG_CHECK_ARG(pos >= 0 && pos < kv->max_len, "pos %d outside [0, max_len %d)", pos,
-                 kv->max_len);
+    FG_TRY(check_block(d, kv, gbs, nb, pos + 1, kvt));
     FG_CHECK_ARG(attn_topk_ppm >= 0, "attn_topk_ppm %d is negative", attn_topk_ppm);
     const int32_t topk = attn_topk_count(pos, attn_topk_ppm);
     FG_CHECK_SUP(topk < 0 || pos <= kAttnTopkMaxPos, "Top-K attention: history %d longer than %d",
@@ -143,8 +160,21 @@ int layer_decode(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, in
     if (!ln1_done)
         FG_TRY(launch_layernorm(xh, bls, h1, (const __half*)w->ln1_g, (const __half*)w->ln1_b, a, st));
     FG_TRY(lin(w, 0, a, bls, h1, 3 * h1, 0, nullptr, qkv, part, pb, st));
-    FG_TRY(launch_attn_decode(qkv, qkv + h1, qkv + 2 * h1, 3 * h1, kv, (int32_t)bls, d, pos, 1, o, st,
+    // GPU batches with a device-resident cache in one launch; the others one
+    // by one on their slot of the KV tier (history loaded, row pos appended
+    // there and stored back)
+    const int32_t nd = kvt ? kvt->nb_dev : nb;
+    FG_TRY(launch_attn_decode(qkv, qkv + h1, qkv + 2 * h1, 3 * h1, kv, nd * gbs, d, pos, 1, o, st,
                               topk));
+    for (int32_t k = nd; k < nb; ++k) {
+        const int32_t u = kvt->u0 + (k - nd);
+        const __half* q = qkv + (int64_t)k * gbs * 3 * h1;
+        fg_kv slot;
+        FG_TRY(kvt->pipe->begin(u, &slot));
+        FG_TRY(launch_attn_decode(q, q + h1, q + 2 * h1, 3 * h1, &slot, gbs, d, pos, 1,
+                                  o + (int64_t)k * gbs * h1, st, topk));
+        FG_TRY(kvt->pipe->end(u, pos, pos + 1));
+    }
     FG_TRY(lin(w, 1, o, bls, h1, h1, 0, xh, xh, part, pb, st, w->ln2_g, w->ln2_b, a));
     FG_TRY(lin(w, 2, a, bls, h1, h2, 1, nullptr, f, part, pb, st));
     if (next)   // the next layer's first LayerNorm, fused with this residual sum
@@ -156,12 +186,10 @@ int layer_decode(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, in
 
 int layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, int32_t nb,
                   int32_t s, const fg_kv* kv, void* ws, size_t ws_bytes, hipStream_t st,
-                  bool check_only) {
+                  bool check_only, const KvTierCall* kvt) {
     FG_TRY(check_layer(d, w, x, kv, ws));
-    FG_CHECK_ARG(gbs >= 1 && nb >= 1 && (int64_t)gbs * nb <= kv->n_seq,
-                 "block %d x %d exceeds the cache's %d sequences", gbs, nb, kv->n_seq);
-    FG_CHECK_ARG(s >= 1 && s <= kv->max_len, "prompt length %d outside [1, max_len %d]", s,
-                 kv->max_len);
+    FG_CHECK_ARG(s >= 1, "prompt length %d < 1", s);
+    FG_TRY(check_block(d, kv, gbs, nb, s, kvt));
     const int64_t rows = (int64_t)gbs * s;
     const WsLayout L = layout(d, rows, w->fmt);
     if (ws_bytes < L.total)
@@ -201,7 +229,15 @@ int layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, i
         FG_TRY(launch_layernorm(xh, rows, h1, (const __half*)wl.ln1_g, (const __half*)wl.ln1_b, a, st));
         FG_TRY(lin(&wl, 0, a, rows, h1, 3 * h1, 0, nullptr, qkv, part, pb, st, nullptr, nullptr, nullptr, dq));
         FG_TRY(launch_attn_prefill(qkv, gbs, s, d, o, st));
-        FG_TRY(launch_kv_store(qkv + h1, qkv + 2 * h1, 3 * h1, kv, k * gbs, gbs, 0, s, d, st));
+        if (!kvt || k < kvt->nb_dev) {
+            FG_TRY(launch_kv_store(qkv + h1, qkv + 2 * h1, 3 * h1, kv, k * gbs, gbs, 0, s, d, st));
+        } else {   // written to the batch's slot, then stored to the host cache
+            const int32_t u = kvt->u0 + (k - kvt->nb_dev);
+            fg_kv slot;
+            FG_TRY(kvt->pipe->begin(u, &slot));
+            FG_TRY(launch_kv_store(qkv + h1, qkv + 2 * h1, 3 * h1, &slot, 0, gbs, 0, s, d, st));
+            FG_TRY(kvt->pipe->end(u, 0, s));
+        }
         FG_TRY(lin(&wl, 1, o, rows, h1, h1, 0, xh, xh, part, pb, st, wl.ln2_g, wl.ln2_b, a, dq));
         FG_TRY(lin(&wl, 2, a, rows, h1, h2, 1, nullptr, f, part, pb, st, nullptr, nullptr, nullptr, dq));
         FG_TRY(lin(&wl, 3, f, rows, h2, h1, 0, xh, xh, part, pb, st, nullptr, nullptr, nullptr, dq));
@@ -220,15 +256,39 @@ extern "C" size_t fg_workspace_bytes(const fg_dims* d, int64_t rows, int32_t fmt
 
 extern "C" int fg_layer_decode_block(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs,
                                      int32_t nb, int32_t pos, const fg_kv* kv, void* ws,
-                                     size_t ws_bytes, void* stream, int32_t attn_topk_ppm) {
+                                     size_t ws_bytes, void* stream, int32_t attn_topk_ppm,
+                                     const fg_kv_tier* kvt) {
     fg::clear_error();
+    fg::KvTierCall kc{};
+    if (kvt) {
+        kc = fg::KvTierCall{nullptr, kvt->pipe, kvt->host, kvt->nb_dev, 0};
+        FG_TRY(fg::layer_decode(d, w, x, gbs, nb, pos, kv, ws, ws_bytes, fg::as_stream(stream), true,
+                                false, nullptr, attn_topk_ppm, &kc));
+    }
+    fg::KvPipe pipe(kvt ? kvt->pipe : nullptr, d, gbs, pos, fg::as_stream(stream));
+    if (kvt) {
+        for (int32_t k = kvt->nb_dev; k < nb; ++k) pipe.add(kvt->host, (k - kvt->nb_dev) * gbs);
+        kc.pipe = &pipe;
+    }
     return fg::layer_decode(d, w, x, gbs, nb, pos, kv, ws, ws_bytes, fg::as_stream(stream), false,
-                            false, nullptr, attn_topk_ppm);
+                            false, nullptr, attn_topk_ppm, kvt ? &kc : nullptr);
 }
 
 extern "C" int fg_layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs,
                                 int32_t nb, int32_t s, const fg_kv* kv, void* ws, size_t ws_bytes,
-                                void* stream) {
+                                void* stream, const fg_kv_tier* kvt) {
     fg::clear_error();
-    return fg::layer_prefill(d, w, x, gbs, nb, s, kv, ws, ws_bytes, fg::as_stream(stream), false);
+    fg::KvTierCall kc{};
+    if (kvt) {
+        kc = fg::KvTierCall{nullptr, kvt->pipe, kvt->host, kvt->nb_dev, 0};
+        FG_TRY(fg::layer_prefill(d, w, x, gbs, nb, s, kv, ws, ws_bytes, fg::as_stream(stream), true,
+                                 &kc));
+    }
+    fg::KvPipe pipe(kvt ? kvt->pipe : nullptr, d, gbs, 0, fg::as_stream(stream));
+    if (kvt) {
+        for (int32_t k = kvt->nb_dev; k < nb; ++k) pipe.add(kvt->host, (k - kvt->nb_dev) * gbs);
+        kc.pipe = &pipe;
+    }
+    return fg::layer_prefill(d, w, x, gbs, nb, s, kv, ws, ws_bytes, fg::as_stream(stream), false,
+                             kvt ? &kc : nullptr);
 }

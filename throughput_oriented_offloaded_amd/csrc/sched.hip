@@ -137,6 +137,23 @@ int run_layers(fg_sched* sc, const fg_dims* d, int32_t n, const fg_layer_w* w,
     return FG_OK;
 }
 
+// The host batches of every layer of a KV-tiered call, in execution order:
+// layer j's batch k (k >= nb_dev) is unit j * (nb - nb_dev) + k - nb_dev.
+int kv_units(const fg_kv_tier* kvt, int32_t n_layers, int32_t gbs, int32_t nb, KvPipe& pipe) {
+    if (!kvt) return FG_OK;
+    FG_CHECK_ARG(kvt->host, "KV tier: null host cache array");
+    FG_CHECK_ARG(kvt->nb_dev >= 0 && kvt->nb_dev <= nb, "KV tier: nb_dev %d outside [0, nb %d]",
+                 kvt->nb_dev, nb);
+    for (int32_t j = 0; j < n_layers; ++j)
+        for (int32_t k = kvt->nb_dev; k < nb; ++k) pipe.add(&kvt->host[j], (k - kvt->nb_dev) * gbs);
+    return FG_OK;
+}
+
+KvTierCall kv_call(const fg_kv_tier* kvt, KvPipe* pipe, int32_t j, int32_t nb) {
+    if (!kvt) return KvTierCall{};
+    return KvTierCall{pipe, kvt->pipe, &kvt->host[j], kvt->nb_dev, j * (nb - kvt->nb_dev)};
+}
+
 }  // namespace
 }  // namespace fg
 
@@ -188,15 +205,20 @@ extern "C" int fg_sched_destroy(fg_sched* sc) {
 extern "C" int fg_model_prefill(fg_sched* sc, const fg_dims* d, int32_t n_layers,
                                 const fg_layer_w* w, const fg_tier_w* tier, const fg_kv* kv,
                                 void* x, int32_t gbs, int32_t nb, int32_t s, void* ws,
-                                size_t ws_bytes, void* stream, void* copy_stream, int32_t flags) {
+                                size_t ws_bytes, void* stream, void* copy_stream, int32_t flags,
+                                const fg_kv_tier* kvt) {
     using namespace fg;
     clear_error();
     FG_TRY(check_dims(d));
     FG_CHECK_ARG(n_layers >= 1 && w && kv, "need n_layers >= 1 and layer arrays");
     hipStream_t st = as_stream(stream);
+    KvPipe pipe(kvt ? kvt->pipe : nullptr, d, gbs, 0, st);
+    FG_TRY(kv_units(kvt, n_layers, gbs, nb, pipe));
     return run_layers(sc, d, n_layers, w, tier, st, as_stream(copy_stream), flags,
                       [&](int32_t j, const fg_layer_w& wj, bool chk) {
-                          return layer_prefill(d, &wj, x, gbs, nb, s, &kv[j], ws, ws_bytes, st, chk);
+                          const KvTierCall kc = kv_call(kvt, chk ? nullptr : &pipe, j, nb);
+                          return layer_prefill(d, &wj, x, gbs, nb, s, &kv[j], ws, ws_bytes, st, chk,
+                                               kvt ? &kc : nullptr);
                       });
 }
 
@@ -204,18 +226,21 @@ extern "C" int fg_model_decode_step(fg_sched* sc, const fg_dims* d, int32_t n_la
                                     const fg_layer_w* w, const fg_tier_w* tier, const fg_kv* kv,
                                     void* x, int32_t gbs, int32_t nb, int32_t pos, void* ws,
                                     size_t ws_bytes, void* stream, void* copy_stream,
-                                    int32_t flags, int32_t attn_topk_ppm) {
+                                    int32_t flags, int32_t attn_topk_ppm, const fg_kv_tier* kvt) {
     using namespace fg;
     clear_error();
     FG_TRY(check_dims(d));
     FG_CHECK_ARG(n_layers >= 1 && w && kv, "need n_layers >= 1 and layer arrays");
     hipStream_t st = as_stream(stream);
+    KvPipe pipe(kvt ? kvt->pipe : nullptr, d, gbs, pos, st);
+    FG_TRY(kv_units(kvt, n_layers, gbs, nb, pipe));
     return run_layers(sc, d, n_layers, w, tier, st, as_stream(copy_stream), flags,
                       [&](int32_t j, const fg_layer_w& wj, bool chk) {
                           // each layer's input LayerNorm runs fused into the
                           // previous layer's last residual sum
+                          const KvTierCall kc = kv_call(kvt, chk ? nullptr : &pipe, j, nb);
                           return layer_decode(d, &wj, x, gbs, nb, pos, &kv[j], ws, ws_bytes, st, chk,
                                               j > 0, j + 1 < n_layers ? &w[j + 1] : nullptr,
-                                              attn_topk_ppm);
+                                              attn_topk_ppm, kvt ? &kc : nullptr);
                       });
 }

@@ -112,19 +112,22 @@ class TierLayer:
 
 class DeviceKV:
     """One layer's cache: q4 codes [n_seq, nh, max_len, hd/2] + meta
-    [n_seq, nh, max_len, hd/64, 2], or fp16 [n_seq, nh, max_len, hd]."""
+    [n_seq, nh, max_len, hd/64, 2], or fp16 [n_seq, nh, max_len, hd].
+    device "pinned": in pinned host memory (a KV tier's host cache)."""
 
     def __init__(self, fmt: int, n_seq: int, n_heads: int, head_dim: int, max_len: int, device):
         self.fmt = fmt
         shp = (n_seq, n_heads, max_len)
+        pin = device == "pinned"
+        kw = dict(device="cpu", pin_memory=True) if pin else dict(device=device)
         if fmt == L.FG_FMT_Q4G64:
-            self.k = torch.zeros(shp + (head_dim // 2,), dtype=torch.uint8, device=device)
-            self.v = torch.zeros_like(self.k)
-            self.km = torch.zeros(shp + (head_dim // 64, 2), dtype=torch.float16, device=device)
-            self.vm = torch.zeros_like(self.km)
+            self.k = torch.zeros(shp + (head_dim // 2,), dtype=torch.uint8, **kw)
+            self.v = torch.zeros(shp + (head_dim // 2,), dtype=torch.uint8, **kw)
+            self.km = torch.zeros(shp + (head_dim // 64, 2), dtype=torch.float16, **kw)
+            self.vm = torch.zeros(shp + (head_dim // 64, 2), dtype=torch.float16, **kw)
         else:
-            self.k = torch.zeros(shp + (head_dim,), dtype=torch.float16, device=device)
-            self.v = torch.zeros_like(self.k)
+            self.k = torch.zeros(shp + (head_dim,), dtype=torch.float16, **kw)
+            self.v = torch.zeros(shp + (head_dim,), dtype=torch.float16, **kw)
             self.km = self.vm = None
         s = L.KV()
         s.fmt, s.k, s.v = fmt, L.ptr(self.k), L.ptr(self.v)
@@ -138,18 +141,27 @@ class Model:
     with embed [vocab, h1], pos [max_pos, h1], lnf_g, lnf_b (fp16, device)."""
 
     def __init__(self, shape: Shape, layers, emb: dict, kv_fmt: int, n_seq: int, max_len: int,
-                 device="cuda", tier=None, attn_topk: float = 0.0):
+                 device="cuda", tier=None, attn_topk: float = 0.0, kv_host_seqs: int = 0):
         """tier: None, or one TierLayer (or None) per layer for weight tiering.
         attn_topk: 0 for dense decode attention, else the fraction of cached
         positions whose V each decode step reads (Top-K sparse V; the pages
-        use 0.1), rounded up per step."""
+        use 0.1), rounded up per step.
+        kv_host_seqs: the last kv_host_seqs sequences keep their KV cache in
+        pinned host memory (KV tiering; a whole number of GPU batches at every
+        call), moved through two device slots by the library."""
         assert 0.0 <= attn_topk <= 1.0
         self.attn_topk_ppm = int(round(attn_topk * 1_000_000))
         self.shape, self.layers, self.emb = shape, layers, emb
         self.d = shape.dims
         self.n_seq, self.max_len = n_seq, max_len
-        self.kv = [DeviceKV(kv_fmt, n_seq, shape.n_heads, shape.head_dim, max_len, device)
+        assert 0 <= kv_host_seqs <= n_seq
+        self.kv_host_seqs = kv_host_seqs
+        n_dev = max(n_seq - kv_host_seqs, 1)   # the device cache is unused when every batch is on the host
+        self.kv = [DeviceKV(kv_fmt, n_dev, shape.n_heads, shape.head_dim, max_len, device)
                    for _ in layers]
+        self.kv_host = [DeviceKV(kv_fmt, kv_host_seqs, shape.n_heads, shape.head_dim, max_len, "pinned")
+                        for _ in layers] if kv_host_seqs else []
+        self._kvt = {}     # gbs -> (tier object, its slots, copy stream, host array)
         self.device = device
         self._ws = None
         n = len(layers)
@@ -173,6 +185,27 @@ class Model:
             torch.cuda.synchronize(self.device)
             L.fg_sched_destroy(self._sched)
             self._sched = None
+        if getattr(self, "_kvt", None):
+            torch.cuda.synchronize(self.device)
+            for kt in self._kvt.values():
+                L.fg_kvtier_destroy(kt[0])
+            self._kvt = {}
+
+    def kv_tier(self, gbs: int, nb: int):
+        """fg_kv_tier of a call with GPU batches of gbs sequences (None
+        without KV tiering): two slots of one GPU batch, a copy stream."""
+        if not self.kv_host_seqs:
+            return None
+        assert self.kv_host_seqs % gbs == 0 and gbs * nb == self.n_seq, \
+            "host-resident sequences must be whole GPU batches of the block"
+        if gbs not in self._kvt:
+            sb = L.fg_kvtier_slot_bytes(self.d, gbs, self.max_len, self.kv_host[0].fmt)
+            slots = torch.empty(2 * sb, dtype=torch.uint8, device=self.device)
+            cp = torch.cuda.Stream(device=self.device)
+            host = (L.KV * len(self.kv_host))(*[h.struct for h in self.kv_host])
+            self._kvt[gbs] = (L.fg_kvtier_create(slots, sb, cp), slots, cp, host)
+        kt, _, _, host = self._kvt[gbs]
+        return L.KvTier(kt, host, nb - self.kv_host_seqs // gbs)
 
     def _sched_args(self):
         """(sched, tier array, copy stream, flags) of the next pass; with tiering
@@ -217,7 +250,8 @@ class Model:
         ws = self.workspace(gbs * s)
         sc, tier, cp, flags = self._sched_args()
         L.fg_model_prefill(sc, self.d, self._w_arr, tier, self._kv_arr, x, gbs, nb, s, ws,
-                           ws.numel(), stream=stream, copy_stream=cp, flags=flags)
+                           ws.numel(), stream=stream, copy_stream=cp, flags=flags,
+                           kvt=self.kv_tier(gbs, nb))
         last = x.view(bls, s, sh.h1)[:, s - 1, :].contiguous()
         return self._head(last, stream)
 
@@ -230,7 +264,7 @@ class Model:
         sc, tier, cp, flags = self._sched_args()
         L.fg_model_decode_step(sc, self.d, self._w_arr, tier, self._kv_arr, x, gbs, nb, pos, ws,
                                ws.numel(), stream=stream, copy_stream=cp, flags=flags,
-                               attn_topk_ppm=self.attn_topk_ppm)
+                               attn_topk_ppm=self.attn_topk_ppm, kvt=self.kv_tier(gbs, nb))
         return self._head(x, stream)
 
     def embed_step(self, tok: torch.Tensor, pos: int, stream=None) -> torch.Tensor:
