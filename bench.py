@@ -43,6 +43,9 @@ CONFIGS = {
             tier=True),
     5: dict(workload="opt-175b-shape 4-bit block decode", l=96, h1=12288, h2=49152, nh=96,
             hd=128, w="q4", kv="q4", gbs=48, nb=3, s=512, n=32),
+    6: dict(workload="opt-30b-shape 4-bit block decode, KV cache of every GPU batch in pinned "
+                     "host memory", l=48, h1=7168, h2=28672, nh=56, hd=128, w="q4", kv="q4",
+            gbs=48, nb=3, s=512, n=32, kv_host_seqs=144),
 }
 
 
@@ -190,7 +193,7 @@ def topk_attention(model, cfg, L, pos: int, frac: float = 0.1, reps: int = 10):
     timed with the same HIP-event tracing, beside the dense kernel on the same
     cache.  Returns the sparse kernel's roofline plus both average durations."""
     import torch
-    sh, bls = model.shape, model.n_seq
+    sh, bls = model.shape, model.kv[0].struct.n_seq   # device-resident sequences
     h1 = sh.h1
     topk = min(pos, -(-int(round(frac * 1_000_000)) * pos // 1_000_000))
     g = torch.Generator(device="cuda").manual_seed(11)
@@ -326,7 +329,8 @@ def main():
     log(f"building {cfg['workload']} ({cfg['l']} layers, bls {bls})")
     sh, layers, tier, emb, host0, quant, fmt = build_model(cfg, want_cpu)
     max_len = s + max(n, K + 1, Wm + 1)
-    model = Model(sh, layers, emb, fmt(cfg["kv"]), bls, max_len, tier=tier)
+    model = Model(sh, layers, emb, fmt(cfg["kv"]), bls, max_len, tier=tier,
+                  kv_host_seqs=cfg.get("kv_host_seqs", 0))
     tokens = synth.tokens(bls, s, seed=0, device="cuda")
     torch.cuda.synchronize()
     log(f"built in {time.time() - t_build:.1f} s; prefill s={s} ...")
@@ -348,8 +352,10 @@ def main():
     torch.cuda.synchronize()
     tr_warm = L.fg_trace_collect() if not args.no_trace else {}
 
-    # timed steps: events only around the two roofline kernels
-    L.fg_trace_kinds([gemm_kind, attn_kind])
+    # timed steps: events only around the two roofline kernels (and, with KV
+    # tiering, the host <-> slot copies on the copy stream)
+    kvt_kinds = ["kv_h2d", "kv_d2h"] if cfg.get("kv_host_seqs") else []
+    L.fg_trace_kinds([gemm_kind, attn_kind] + kvt_kinds)
     L.fg_trace_enable(not args.no_trace)
     tok = tok1
     torch.cuda.synchronize()
@@ -390,7 +396,7 @@ def main():
                     for k, v in tr_warm.items()},
         "tokens_valid": ok,
     }
-    if not args.no_trace and s + K // 2 <= 8192:
+    if not args.no_trace and s + K // 2 <= 8192 and not cfg.get("kv_host_seqs"):
         out["roofline_attn_topk"] = topk_attention(model, cfg, L, s + K // 2)
     if s + K <= 8192:
         out["decode_attn_topk"] = sparse_decode(model, cfg, L, tok1, min(K, 8), args.no_trace)
@@ -407,6 +413,24 @@ def main():
             "kernel_s_per_step": round(kern_s, 4) if kern_s else None,
             "overlap_efficiency": round(max(hb / probe / 1e9, kern_s or 0.0) / step, 4),
             "definition": "overlap = max(copy time at probe rate, kernel time) / step time"}
+    if cfg.get("kv_host_seqs") and "kv_h2d" in tr:
+        # KV tiering: history bytes loaded per step and the copy stream's busy time
+        ld, st_ = tr["kv_h2d"], tr.get("kv_d2h", {"bytes": 0.0, "ms": 0.0})
+        step = t_dec / K
+        kern_s = (tr[gemm_kind]["ms"] + tr[attn_kind]["ms"]) / 1e3 / K
+        out["kv_tiering"] = {
+            "host_sequences": cfg["kv_host_seqs"], "load_bytes_per_step": round(ld["bytes"] / K),
+            "store_bytes_per_step": round(st_["bytes"] / K),
+            "h2d_GBs_while_copying": round(ld["bytes"] / (ld["ms"] / 1e3) / 1e9, 2),
+            "h2d_GBs_over_step": round(ld["bytes"] / K / step / 1e9, 2),
+            "load_s_per_step": round(ld["ms"] / 1e3 / K, 4),
+            "store_s_per_step": round(st_["ms"] / 1e3 / K, 4),
+            "gemm_attn_s_per_step": round(kern_s, 4), "step_s": round(step, 4),
+            "overlap_efficiency": round(max(ld["ms"] / 1e3 / K, kern_s) / step, 4),
+            "definition": "loads: 2-D copies of positions 0..pos-1 of every host batch's K, V and "
+                          "metadata into a device slot (copy stream); stores: the appended rows "
+                          "back (their own stream); overlap = max(load busy time, GEMM + "
+                          "attention time) / step time"}
     if quant:
         out["weight_quant"] = {"GB/s": round(quant["bytes"] / (quant["ms"] / 1e3) / 1e9, 1),
                                "frac": round(quant["bytes"] / (quant["ms"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4),

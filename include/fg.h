@@ -226,11 +226,13 @@ int fg_argmax(const void* logits, int64_t rows, int64_t n, int32_t* out, void* s
  * metadata, as 2-D copies of the cache's rows) into one of two device slots,
  * runs that batch's attention on the slot (appending position pos there), and
  * copies the appended row back to `host[j]`; prefill writes positions
- * 0..s-1 of the slot and copies them back.  All copies run on the copy stream
- * given at creation, ordered by events, in the order load(u), load(u+1),
- * store(u), load(u+2), store(u+1), ... over the call's host batches u (layer
- * by layer), so the load of the next batch, also across a layer boundary,
- * runs while the current one computes.
+ * 0..s-1 of the slot and copies them back.  Loads run on the copy stream
+ * given at creation and stores on a stream the tier object creates, ordered
+ * by events: over the call's host batches u (layer by layer), load(u+1) is
+ * issued before store(u), so the load of the next batch, also across a layer
+ * boundary, runs while the current one computes, and load(u+2) waits for
+ * store(u) to have read the slot.  A call's loads wait for all stores of
+ * earlier calls; a caller reading the host caches synchronizes the device.
  *
  * slots: caller-owned device memory of 2 * slot_bytes (256-byte aligned);
  * slot_bytes >= fg_kvtier_slot_bytes(d, gbs, max_len, fmt) of every call

@@ -7,19 +7,21 @@
 // of the batch before are stored.  Here a "unit" is one host-resident GPU
 // batch of one layer; the units of a call are numbered in execution order
 // (layer by layer, batch by batch) and unit u uses slot u mod 2:
-//   copy stream:    load(u): rows [0, n) of every (sequence, head) of the
-//                   unit's K, V (and metadata), host -> slot, as 2-D copies;
-//                   record ready[u mod 2]
+//   copy stream:    [u >= 2: wait stored[u mod 2]] load(u): rows [0, n) of
+//                   every (sequence, head) of the unit's K, V (and metadata),
+//                   host -> slot, as 2-D copies; record ready[u mod 2]
 //   compute stream: wait ready[u mod 2]; the unit's kernel on the slot;
 //                   record done[u mod 2]
-//   copy stream:    wait done[u mod 2]; store(u): the rows the kernel wrote,
-//                   slot -> host
-// The copy stream receives load(0), load(1), store(0), load(2), store(1), ...:
-// load(u+2) reuses the slot of u and follows store(u) in stream order, which
-// itself waited for unit u's kernel, so two loads are never more than one
-// unit ahead and a slot is never overwritten while read.  Across calls the
-// same order holds because every copy of a tier object runs on its one copy
-// stream.
+//   store stream:   wait done[u mod 2]; store(u): the rows the kernel wrote,
+//                   slot -> host; record stored[u mod 2]
+// Loads are enqueued one unit ahead (load(u+1) before store(u)), so the copy
+// stream moves the next batch's history while the current one computes;
+// load(u+2) reuses the slot of u and waits until store(u), which itself
+// waited for unit u's kernel, has read it.  Stores run on a stream of their
+// own (device -> host traffic does not hold up the loads).  A call's first
+// loads wait for every store of the calls before it (the store stream runs
+// in order, so its latest two records cover them), which also orders each
+// history load after the store of that history's last row.
 #include <new>
 
 #include "fg_internal.h"
@@ -28,9 +30,11 @@
 struct fg_kvtier {
     unsigned char* slot[2];
     size_t slot_bytes;
-    hipStream_t cp;
+    hipStream_t cp;       // loads (the caller's copy stream)
+    hipStream_t sp;       // stores (created here, default priority)
     hipEvent_t ready[2];
     hipEvent_t done[2];
+    hipEvent_t stored[2];
     int device;
 };
 
@@ -130,7 +134,8 @@ int KvPipe::copy(int32_t u, int32_t lo, int32_t hi, bool to_host) {
     const size_t height = (size_t)gbs_ * d_->n_heads;
     double bytes = 0;
     for (int t = 0; t < nt; ++t) bytes += (double)height * (hi - lo) * L.row[t];
-    TraceScope ts(to_host ? TK_KV_D2H : TK_KV_H2D, kt_->cp, 0.0, bytes);
+    hipStream_t cs = to_host ? kt_->sp : kt_->cp;
+    TraceScope ts(to_host ? TK_KV_D2H : TK_KV_H2D, cs, 0.0, bytes);
     for (int t = 0; t < nt; ++t) {
         const size_t r = L.row[t], pitch = (size_t)h->max_len * r;
         unsigned char* hp = static_cast<unsigned char*>(tensor_of(h, t)) +
@@ -138,9 +143,9 @@ int KvPipe::copy(int32_t u, int32_t lo, int32_t hi, bool to_host) {
         unsigned char* dp = kt_->slot[u & 1] + L.off[t] + (size_t)lo * r;
         const size_t width = (size_t)(hi - lo) * r;
         if (to_host)
-            FG_HIP(hipMemcpy2DAsync(hp, pitch, dp, pitch, width, height, hipMemcpyDeviceToHost, kt_->cp));
+            FG_HIP(hipMemcpy2DAsync(hp, pitch, dp, pitch, width, height, hipMemcpyDeviceToHost, cs));
         else
-            FG_HIP(hipMemcpy2DAsync(dp, pitch, hp, pitch, width, height, hipMemcpyHostToDevice, kt_->cp));
+            FG_HIP(hipMemcpy2DAsync(dp, pitch, hp, pitch, width, height, hipMemcpyHostToDevice, cs));
     }
     return FG_OK;
 }
@@ -150,9 +155,14 @@ int KvPipe::begin(int32_t u, fg_kv* slot_out) {
     FG_CHECK_ARG(u >= 0 && u < n && u == begun_, "KV tier: unit %d out of order", u);
     // loads through u + 1 (the next one runs while unit u computes); load(v)
     // for v >= 2 follows store(v - 2), enqueued by end(v - 2)
+    if (loaded_ == 0) {   // every store of earlier calls before this call's loads
+        FG_HIP(hipStreamWaitEvent(kt_->cp, kt_->stored[0], 0));
+        FG_HIP(hipStreamWaitEvent(kt_->cp, kt_->stored[1], 0));
+    }
     while (loaded_ <= u + 1 && loaded_ < n) {
         FG_CHECK_ARG(loaded_ < 2 || stored_ >= loaded_ - 1, "KV tier: slot of unit %d still in use",
                      loaded_);
+        if (loaded_ >= 2) FG_HIP(hipStreamWaitEvent(kt_->cp, kt_->stored[loaded_ & 1], 0));
         FG_TRY(copy(loaded_, 0, load_rows_, false));
         FG_HIP(hipEventRecord(kt_->ready[loaded_ & 1], kt_->cp));
         ++loaded_;
@@ -166,8 +176,9 @@ int KvPipe::begin(int32_t u, fg_kv* slot_out) {
 int KvPipe::end(int32_t u, int32_t lo, int32_t hi) {
     FG_CHECK_ARG(u == stored_ && u < begun_, "KV tier: unit %d ended out of order", u);
     FG_HIP(hipEventRecord(kt_->done[u & 1], st_));
-    FG_HIP(hipStreamWaitEvent(kt_->cp, kt_->done[u & 1], 0));
+    FG_HIP(hipStreamWaitEvent(kt_->sp, kt_->done[u & 1], 0));
     FG_TRY(copy(u, lo, hi, true));
+    FG_HIP(hipEventRecord(kt_->stored[u & 1], kt_->sp));
     ++stored_;
     return FG_OK;
 }
@@ -197,14 +208,22 @@ extern "C" int fg_kvtier_create(fg_kvtier** out, void* slots, size_t slot_bytes,
     kt->slot[1] = static_cast<unsigned char*>(slots) + slot_bytes;
     kt->slot_bytes = slot_bytes;
     kt->cp = fg::as_stream(copy_stream);
-    hipEvent_t* ev[4] = {&kt->ready[0], &kt->ready[1], &kt->done[0], &kt->done[1]};
+    hipEvent_t* ev[6] = {&kt->ready[0], &kt->ready[1], &kt->done[0],
+                         &kt->done[1], &kt->stored[0], &kt->stored[1]};
     int made = 0;
     bool ok = hipGetDevice(&kt->device) == hipSuccess;
-    while (ok && made < 4) {
+    while (ok && made < 6) {
         if (hipEventCreateWithFlags(ev[made], hipEventDisableTiming) != hipSuccess) ok = false;
         else ++made;
     }
-    if (!ok) {
+    bool have_sp = ok && hipStreamCreateWithFlags(&kt->sp, hipStreamNonBlocking) == hipSuccess;
+    // the first call's loads wait for these (complete at once)
+    if (have_sp && (hipEventRecord(kt->stored[0], kt->sp) != hipSuccess ||
+                    hipEventRecord(kt->stored[1], kt->sp) != hipSuccess)) {
+        (void)hipStreamDestroy(kt->sp);
+        have_sp = false;
+    }
+    if (!have_sp) {
         for (int i = 0; i < made; ++i) (void)hipEventDestroy(*ev[i]);
         delete kt;
         return fg::set_error(FG_ERR_HIP, "fg_kvtier_create: %s", hipGetErrorString(hipGetLastError()));
@@ -216,9 +235,12 @@ extern "C" int fg_kvtier_create(fg_kvtier** out, void* slots, size_t slot_bytes,
 extern "C" int fg_kvtier_destroy(fg_kvtier* kt) {
     fg::clear_error();
     if (!kt) return FG_OK;
+    (void)hipStreamSynchronize(kt->sp);
+    (void)hipStreamDestroy(kt->sp);
     for (int i = 0; i < 2; ++i) {
         (void)hipEventDestroy(kt->ready[i]);
         (void)hipEventDestroy(kt->done[i]);
+        (void)hipEventDestroy(kt->stored[i]);
     }
     delete kt;
     return FG_OK;
