@@ -1,0 +1,193 @@
+"""Cost model and policy search ("FlexGen 完全拆解", sections "用线性规划搜索
+卸载策略", "从硬件画像得到每层时间", "为什么固定批量后能变成线性规划").
+
+The oracle (oracle.cost) is pinned to figures the pages print; the product
+(throughput_oriented_offloaded_amd.policy: the same model assembled as a
+linear program) is held to the oracle: equal path times and peak memory for
+arbitrary placements, and LP solutions that are feasible under the oracle's
+own test, score what the LP claims, and are beaten by no grid placement and
+no random feasible placement (the objective is convex in the shares)."""
+import numpy as np
+import pytest
+
+from oracle import cost as oc
+
+GIB = 2.0 ** 30
+OPT175 = dict(l=96, h1=12288, h2=49152)
+
+
+def _hw(**kw):
+    base = dict(bw_c2g=12e9, bw_g2c=12e9, bw_d2c=2e9, bw_c2d=1e9, gemm_flops=50e12,
+                prefill_flops=60e12, attn_bw=250e9, hbm_bw=300e9, cap_g=16e9, cap_c=208e9,
+                cap_d=1.5e12)
+    base.update(kw)
+    return oc.Hardware(**base)
+
+
+# ------------------------------------------------------------ oracle pins
+def _pin_weights():
+    """[P2] "FlexGen 统一调度权重、激活与 KV Cache": OPT-175B fp16 weights are
+    about 325 GB (the figure is in binary units: 350e9 parameter bytes less
+    the embeddings)."""
+    m = oc.Model(s=512, n=32, **OPT175)
+    total = m.l * oc.layer_weight_bytes(m)
+    assert abs(total / GIB - 325) / 325 < 0.005
+    return total
+
+
+def _pin_kv_peak():
+    """Same passage: at b = 512, s = 512, n = 32 the KV cache peaks near
+    1.2 TB, 3.8 times the weights."""
+    m = oc.Model(s=512, n=32, **OPT175)
+    kv = m.l * oc.cache_bytes(m, 512, m.s + m.n)
+    assert abs(kv / 2.0 ** 40 - 1.2) / 1.2 < 0.01
+    assert abs(kv / _pin_weights() - 3.8) / 3.8 < 0.01
+
+
+def test_pages_weight_bytes():
+    _pin_weights()
+
+
+def test_pages_kv_peak():
+    _pin_kv_peak()
+
+
+def test_pages_ssd_weight_read():
+    """[P2] "SSD 不是更慢的显存": reading all 325 GB of fp16 weights from a
+    2 GB/s SSD takes about 162.5 s per decode step: l disk -> CPU weight terms
+    at the disk's rate."""
+    m = oc.Model(s=512, n=32, **OPT175)
+    hw = _hw(bw_d2c=2 * GIB)
+    p = dict(wg=0, wc=0, wd=1, hg=1, hc=0, hd=0, cg=1, cc=0, cd=0)
+    t = m.l * oc.path_times(m, hw, 144, p, "gen")["d2c"]
+    assert abs(t - 162.5) / 162.5 < 0.005
+
+
+def test_one_token_is_all_prefill():
+    """T = l T_pre + l (n - 1) T_gen: with n = 1 the run is its prefill, and
+    every further token adds the same l T_gen."""
+    hw = _hw()
+    p = dict(wg=0.3, wc=0.7, wd=0, hg=1, hc=0, hd=0, cg=0.2, cc=0.8, cd=0)
+    m1 = oc.Model(l=4, h1=256, h2=1024, s=64, n=1)
+    t_pre = max(oc.path_times(m1, hw, 32, p, "pre").values())
+    assert oc.total_time(m1, hw, 32, p) == pytest.approx(4 * t_pre, rel=1e-12)
+    # the mean decode cache length moves with n, so compare at the same n
+    m9 = oc.Model(l=4, h1=256, h2=1024, s=64, n=9)
+    t_gen = max(oc.path_times(m9, hw, 32, p, "gen").values())
+    assert oc.total_time(m9, hw, 32, p) == pytest.approx(4 * t_pre + 4 * 8 * t_gen, rel=1e-12)
+
+
+def test_slowest_path_sets_the_time():
+    """With compute and all but one link made free, T_gen is that link's
+    bytes over its bandwidth: moving a share of the weights from GPU to CPU
+    adds exactly share x W / bandwidth to CPU -> GPU."""
+    m = oc.Model(s=128, n=8, l=2, h1=512, h2=2048)
+    fast = 1e30
+    hw = _hw(bw_g2c=fast, bw_d2c=fast, bw_c2d=fast, gemm_flops=fast, prefill_flops=fast,
+             attn_bw=fast, hbm_bw=fast)
+    base = dict(wg=1, wc=0, wd=0, hg=1, hc=0, hd=0, cg=1, cc=0, cd=0)
+    moved = dict(base, wg=0.75, wc=0.25)
+    t0 = oc.path_times(m, hw, 16, base, "gen")
+    t1 = oc.path_times(m, hw, 16, moved, "gen")
+    assert t0["c2g"] == 0.0
+    assert t1["c2g"] == pytest.approx(0.25 * oc.layer_weight_bytes(m) / hw.bw_c2g, rel=1e-12)
+    assert max(t1.values()) == t1["c2g"]
+
+
+def test_planted_cache_mistake_is_caught(monkeypatch):
+    """A cache term that forgets V (2 bytes per element instead of 4 for K
+    and V) fails the pages' KV-peak pin."""
+    monkeypatch.setattr(oc, "cache_bytes", lambda m, bls, length: 2 * bls * length * m.h1 * m.c_ratio)
+    with pytest.raises(AssertionError):
+        _pin_kv_peak()
+
+
+# ------------------------------------------------------ product vs oracle
+@pytest.fixture(scope="module")
+def pol():
+    from throughput_oriented_offloaded_amd import policy
+    return policy
+
+
+def _pair(pol, wl_kw, hw_kw):
+    m = oc.Model(**wl_kw)
+    hw = _hw(**hw_kw)
+    wl = pol.Workload(**wl_kw)
+    mc = pol.Machine(**{k: getattr(hw, k) for k in pol.Machine.__dataclass_fields__})
+    return m, hw, wl, mc
+
+
+CASES = [
+    (dict(l=48, h1=7168, h2=28672, s=512, n=32), {}),                                # 30B fp16, T4-like
+    (dict(l=96, h1=12288, h2=49152, s=512, n=32, w_ratio=9 / 32, c_ratio=9 / 32),   # 175B 4-bit, MI355X-like
+     dict(bw_c2g=55.9e9, bw_g2c=55.9e9, gemm_flops=961e12, prefill_flops=1.09e15, attn_bw=5.63e12,
+          hbm_bw=5.6e12, cap_g=288e9, cap_c=1e12, cap_d=0.0, alpha_g=1.1)),
+    (dict(l=24, h1=2048, h2=8192, s=256, n=64), dict(cap_g=2e9, cap_c=20e9, cap_d=0.0)),
+]
+
+
+@pytest.mark.parametrize("wl_kw,hw_kw", CASES)
+def test_estimate_matches_oracle(pol, wl_kw, hw_kw):
+    m, hw, wl, mc = _pair(pol, wl_kw, hw_kw)
+    rng = np.random.default_rng(0)
+    for _ in range(20):
+        f = [rng.dirichlet(np.ones(3)) for _ in range(3)]
+        p = dict(zip(pol.SHARES, np.concatenate(f).tolist()))
+        bls, gbs = int(rng.integers(1, 64)) * 8, 8
+        got = pol.estimate(wl, mc, bls, gbs, p)
+        for ph in ("pre", "gen"):
+            want = oc.path_times(m, hw, bls, p, ph)
+            for k in oc.PATHS:
+                assert got["paths_" + ph][k] == pytest.approx(want[k], rel=1e-12, abs=1e-18)
+        pk = oc.peak_memory(m, bls, gbs, p)
+        for t in "gcd":
+            assert got["peak"][t] == pytest.approx(pk[t], rel=1e-12, abs=1e-3)
+        assert got["T"] == pytest.approx(oc.total_time(m, hw, bls, p), rel=1e-12)
+
+
+LP_CASES = [
+    # 30B fp16 on a 16 GB GPU with 208 GB DRAM and a disk: weights and cache must leave the GPU
+    (dict(l=48, h1=7168, h2=28672, s=512, n=32), {}, 144, 48, 0.1),
+    # 1.3B-shape with tight GPU and host memory, no disk
+    (dict(l=24, h1=2048, h2=8192, s=256, n=64), dict(cap_g=2e9, cap_c=20e9, cap_d=0.0), 256, 32, 0.05),
+    # 175B 4-bit on MI355X-like constants at a block whose cache exceeds HBM
+    (dict(l=96, h1=12288, h2=49152, s=512, n=32, w_ratio=9 / 32, c_ratio=9 / 32),
+     dict(bw_c2g=55.9e9, bw_g2c=55.9e9, gemm_flops=961e12, prefill_flops=1.09e15, attn_bw=5.63e12,
+          hbm_bw=5.6e12, cap_g=288e9, cap_c=1e12, cap_d=0.0, alpha_g=1.1), 512, 64, 0.05),
+]
+
+
+@pytest.mark.parametrize("wl_kw,hw_kw,bls,gbs,step", LP_CASES)
+def test_lp_optimum_against_oracle_search(pol, wl_kw, hw_kw, bls, gbs, step):
+    m, hw, wl, mc = _pair(pol, wl_kw, hw_kw)
+    shares, v = pol.solve(wl, mc, bls, gbs)
+    assert shares is not None
+    assert oc.feasible(m, hw, bls, gbs, shares, tol=1e-7)
+    assert oc.objective(m, hw, bls, shares) == pytest.approx(v, rel=1e-6)
+    _, grid_v = oc.grid_search(m, hw, bls, gbs, step)
+    assert v <= grid_v * (1 + 1e-9)
+    rng = np.random.default_rng(1)
+    no_disk = hw.cap_d == 0
+    beaten = 0
+    for _ in range(3000):
+        f = [rng.dirichlet(np.ones(2 if no_disk else 3)) for _ in range(3)]
+        if no_disk:
+            f = [np.append(x, 0.0) for x in f]
+        p = dict(zip(pol.SHARES, np.concatenate(f).tolist()))
+        if oc.feasible(m, hw, bls, gbs, p):
+            beaten += oc.objective(m, hw, bls, p) < v * (1 - 1e-9)
+    assert beaten == 0
+
+
+def test_lp_infeasible_block_reports_none(pol):
+    """A block whose cache fits in no tier has no policy."""
+    _, _, wl, mc = _pair(pol, dict(l=24, h1=2048, h2=8192, s=256, n=64),
+                         dict(cap_g=2e9, cap_c=2e9, cap_d=0.0))
+    shares, v = pol.solve(wl, mc, 4096, 64)
+    assert shares is None and v == float("inf")
+
+
+def test_search_cli_runs(pol, capsys):
+    pol.main(["--model", "opt-30b", "--percent", "100", "0", "0", "100", "100", "0"])
+    out = capsys.readouterr().out
+    assert '"tokens_per_s"' in out

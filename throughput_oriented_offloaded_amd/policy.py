@@ -1,0 +1,241 @@
+"""Offloading policy search: the pages' cost model and linear program, with
+hardware constants fitted to one MI355X.
+
+"FlexGen 完全拆解" (pinghaoyang.com.cn), sections "用线性规划搜索卸载策略",
+"从硬件画像得到每层时间" and "为什么固定批量后能变成线性规划"; bjbfmj.com
+walkthrough §6.2 (cost_model.py: search a policy under GPU / CPU / disk
+capacities, or estimate a given one, with hardware constants re-fitted per
+machine).
+
+A policy is (bls, gbs) and the shares of weights (w), activations (h) and KV
+cache (c) on GPU, CPU and disk.  For fixed (bls, gbs) every transfer time,
+the compute time and every tier's peak memory are affine in the nine shares,
+so the best shares solve a linear program: minimize
+(l z_pre + l (n - 1) z_gen) / bls with z_pre, z_gen at least each path's time
+in their phase, peak memory x alpha within each capacity, and each tensor
+class's shares summing to one.  The search solves it for every (gbs, number
+of GPU batches) on a grid and keeps the best.
+
+Per-layer bytes: weights (8 h1^2 + 4 h1 h2) x compression, cache
+4 bls L h1 x compression, activations 2 bls h1 per token.  Off-GPU data crosses
+CPU -> GPU (disk data through the CPU); new cache entries and outputs go back.
+Decode uses the mean cache length s + n/2.  Compute on MI355X: a projection
+costs the larger of its flops at the GEMM rate and its weight bytes at HBM
+bandwidth (small batches read weights faster than they multiply them);
+decode attention reads the cache at the attention kernel's bandwidth;
+prefill runs its flops (projections and causal attention) at the prompt
+GEMM rate.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+from dataclasses import asdict, dataclass
+
+import numpy as np
+
+SHARES = ("wg", "wc", "wd", "hg", "hc", "hd", "cg", "cc", "cd")
+PATHS = ("c2g", "g2c", "d2c", "c2d", "comp")
+Q4G64 = 9.0 / 32.0          # 4-bit codes + fp16 (min, scale) per 64, over fp16
+
+
+@dataclass(frozen=True)
+class Workload:
+    l: int
+    h1: int
+    h2: int
+    s: int
+    n: int
+    w_ratio: float = 1.0
+    c_ratio: float = 1.0
+
+
+@dataclass(frozen=True)
+class Machine:
+    bw_c2g: float            # bytes/s, pinned host -> device
+    bw_g2c: float
+    bw_d2c: float
+    bw_c2d: float
+    gemm_flops: float        # decode-shaped projections, flop/s
+    prefill_flops: float     # prompt-shaped projections and attention, flop/s
+    hbm_bw: float            # weight reads of small-batch projections, bytes/s
+    attn_bw: float           # cache reads of decode attention, bytes/s
+    cap_g: float             # bytes
+    cap_c: float
+    cap_d: float
+    alpha_g: float = 1.0     # peak-memory multipliers (fragmentation, runtime)
+    alpha_c: float = 1.0
+    alpha_d: float = 1.0
+
+
+def mi355x(host_bytes: float = 1.0e12, disk_bytes: float = 0.0, disk_bw: float = 2.0e9) -> Machine:
+    """One MI355X, constants measured by this package's benchmark:
+    pinned host -> device 55.9 GB/s (KV history loads while copying; the
+    reverse direction assumed equal), 4-bit decode GEMM 961 TFLOP/s at
+    M = 144, prompt-shaped GEMMs and attention 1.09 PFLOP/s effective (OPT-175B
+    prefill), decode attention 5.63 TB/s, weight streaming at 5.6 TB/s of the
+    8 TB/s HBM.  288 GB of HBM with 10% held back (alpha_g 1.1).  Host memory
+    and disk are machine-specific arguments (no disk tier by default)."""
+    return Machine(bw_c2g=55.9e9, bw_g2c=55.9e9, bw_d2c=disk_bw, bw_c2d=disk_bw / 2,
+                   gemm_flops=961e12, prefill_flops=1.09e15, hbm_bw=5.6e12, attn_bw=5.63e12,
+                   cap_g=288e9, cap_c=host_bytes, cap_d=disk_bytes, alpha_g=1.1)
+
+
+MODELS = {   # OPT shapes: layers, h1, h2
+    "opt-1.3b": (24, 2048, 8192), "opt-6.7b": (32, 4096, 16384), "opt-13b": (40, 5120, 20480),
+    "opt-30b": (48, 7168, 28672), "opt-66b": (64, 9216, 36864), "opt-175b": (96, 12288, 49152),
+}
+
+
+def _affine(wl: Workload, mc: Machine, bls: int, gbs: int):
+    """Coefficients of the nine shares: path times T[phase] = A f + b (5 x 9,
+    5) for phase "pre" and "gen", and peak memory M = P f + q (3 x 9, 3)
+    for tiers g, c, d."""
+    h1, h2 = wl.h1, wl.h2
+    W = (8 * h1 * h1 + 4 * h1 * h2) * wl.w_ratio
+    mats = 8 * h1 * h1 + 4 * h1 * h2
+    i = {k: j for j, k in enumerate(SHARES)}
+    out = {}
+    for ph in ("pre", "gen"):
+        if ph == "gen":
+            L = wl.s + wl.n / 2
+            c_in, c_out, act = 4 * bls * L * h1 * wl.c_ratio, 4 * bls * h1 * wl.c_ratio, 2 * bls * h1
+            comp = max(bls * mats / mc.gemm_flops, W / mc.hbm_bw) + c_in / mc.attn_bw
+        else:
+            c_in, c_out, act = 0.0, 4 * bls * wl.s * h1 * wl.c_ratio, 2 * bls * wl.s * h1
+            comp = (bls * wl.s * mats + 2 * bls * wl.s * wl.s * h1) / mc.prefill_flops
+        A = np.zeros((5, 9))
+        b = np.zeros(5)
+        # CPU -> GPU: every off-GPU share of the layer's inputs
+        for k, v in (("wc", W), ("wd", W), ("cc", c_in), ("cd", c_in), ("hc", act), ("hd", act)):
+            A[0, i[k]] += v / mc.bw_c2g
+        # GPU -> CPU: new cache entries and outputs of the off-GPU shares
+        for k, v in (("cc", c_out), ("cd", c_out), ("hc", act), ("hd", act)):
+            A[1, i[k]] += v / mc.bw_g2c
+        for k, v in (("wd", W), ("cd", c_in), ("hd", act)):
+            A[2, i[k]] += v / mc.bw_d2c
+        for k, v in (("cd", c_out), ("hd", act)):
+            A[3, i[k]] += v / mc.bw_c2d
+        b[4] = comp
+        out[ph] = (A, b)
+    kv_all = wl.l * 4 * bls * (wl.s + wl.n) * h1 * wl.c_ratio
+    act_all = 2 * bls * wl.s * h1
+    P = np.zeros((3, 9))
+    q = np.zeros(3)
+    for t, tier in enumerate("gcd"):
+        P[t, i["w" + tier]] += wl.l * W
+        P[t, i["c" + tier]] += kv_all
+        P[t, i["h" + tier]] += act_all
+    # GPU extras: a batch's working set, double buffers of the off-GPU
+    # weight share (2 layers) and cache share (2 GPU batches)
+    stage_c = 2 * 4 * gbs * (wl.s + wl.n) * h1 * wl.c_ratio
+    q[0] = 2 * gbs * wl.s * (5 * h1 + h2) + 2 * W + stage_c
+    P[0, i["wg"]] -= 2 * W
+    P[0, i["cg"]] -= stage_c
+    out["mem"] = (P, q)
+    return out
+
+
+def estimate(wl: Workload, mc: Machine, bls: int, gbs: int, shares: dict) -> dict:
+    """Times, throughput and peak memory of one policy."""
+    f = np.array([shares[k] for k in SHARES], dtype=np.float64)
+    co = _affine(wl, mc, bls, gbs)
+    res = {}
+    for ph in ("pre", "gen"):
+        A, b = co[ph]
+        res["paths_" + ph] = dict(zip(PATHS, (A @ f + b).tolist()))
+        res["T_" + ph] = float(np.max(A @ f + b))
+    P, q = co["mem"]
+    res["peak"] = dict(zip("gcd", (P @ f + q).tolist()))
+    res["T"] = wl.l * res["T_pre"] + wl.l * (wl.n - 1) * res["T_gen"]
+    res["tokens_per_s"] = bls * wl.n / res["T"]
+    res["decode_tokens_per_s"] = bls / (wl.l * res["T_gen"])
+    return res
+
+
+def solve(wl: Workload, mc: Machine, bls: int, gbs: int):
+    """Best shares for fixed (bls, gbs): (shares, T / bls) or (None, inf)."""
+    from scipy.optimize import linprog
+    co = _affine(wl, mc, bls, gbs)
+    nv = 11                                   # nine shares, z_pre, z_gen
+    rows, rhs = [], []
+    for zi, ph in ((9, "pre"), (10, "gen")):
+        A, b = co[ph]
+        for r in range(5):                    # A f + b <= z
+            row = np.zeros(nv)
+            row[:9] = A[r]
+            row[zi] = -1.0
+            rows.append(row)
+            rhs.append(-b[r])
+    P, q = co["mem"]
+    for t, (cap, alpha) in enumerate(((mc.cap_g, mc.alpha_g), (mc.cap_c, mc.alpha_c),
+                                      (mc.cap_d, mc.alpha_d))):
+        row = np.zeros(nv)                    # alpha (P f + q) <= cap
+        row[:9] = alpha * P[t]
+        rows.append(row)
+        rhs.append(cap - alpha * q[t])
+    A_eq = np.zeros((3, nv))
+    for c in range(3):
+        A_eq[c, 3 * c:3 * c + 3] = 1.0
+    cost = np.zeros(nv)
+    cost[9] = wl.l / bls
+    cost[10] = wl.l * (wl.n - 1) / bls
+    r = linprog(cost, A_ub=np.array(rows), b_ub=np.array(rhs), A_eq=A_eq, b_eq=np.ones(3),
+                bounds=[(0, 1)] * 9 + [(0, None)] * 2, method="highs")
+    if r.status != 0:
+        return None, float("inf")
+    f = np.clip(r.x[:9], 0.0, 1.0)
+    for c in range(3):                        # renormalize solver round-off
+        f[3 * c:3 * c + 3] /= f[3 * c:3 * c + 3].sum()
+    return dict(zip(SHARES, f.tolist())), float(r.fun)
+
+
+def search(wl: Workload, mc: Machine, gbs_list=(8, 16, 24, 32, 48, 64, 96, 128, 192, 256),
+           nb_max: int = 64):
+    """The (gbs, nb, shares) of least T / bls over gbs_list x 1..nb_max."""
+    best = None
+    for gbs in gbs_list:
+        for nb in range(1, nb_max + 1):
+            shares, v = solve(wl, mc, gbs * nb, gbs)
+            if shares is not None and (best is None or v < best[3]):
+                best = (gbs, nb, shares, v)
+    if best is None:
+        return None
+    gbs, nb, shares, v = best
+    return {"gbs": gbs, "num_gpu_batches": nb, "bls": gbs * nb, "shares": shares,
+            "seconds_per_sequence": v, **estimate(wl, mc, gbs * nb, gbs, shares)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description="offloading policy search / estimate on one MI355X")
+    ap.add_argument("--model", default="opt-175b", choices=sorted(MODELS))
+    ap.add_argument("--prompt-len", type=int, default=512)
+    ap.add_argument("--gen-len", type=int, default=32)
+    ap.add_argument("--cpu-mem", type=float, default=1000.0, help="GB of host memory")
+    ap.add_argument("--disk-mem", type=float, default=0.0, help="GB of disk")
+    ap.add_argument("--compress", choices=("none", "w", "wc"), default="wc",
+                    help="4-bit group-64 compression of weights (w) and cache (c)")
+    ap.add_argument("--gpu-batch-size", type=int)
+    ap.add_argument("--num-gpu-batches", type=int)
+    ap.add_argument("--percent", type=float, nargs=6,
+                    help="wg wc cg cc hg hc in percent (disk = the rest): estimate this policy")
+    a = ap.parse_args(argv)
+    l, h1, h2 = MODELS[a.model]
+    wl = Workload(l, h1, h2, a.prompt_len, a.gen_len,
+                  w_ratio=Q4G64 if a.compress in ("w", "wc") else 1.0,
+                  c_ratio=Q4G64 if a.compress == "wc" else 1.0)
+    mc = mi355x(a.cpu_mem * 1e9, a.disk_mem * 1e9)
+    if a.percent:
+        wg, wc, cg, cc, hg, hc = (x / 100 for x in a.percent)
+        sh = {"wg": wg, "wc": wc, "wd": 1 - wg - wc, "cg": cg, "cc": cc, "cd": 1 - cg - cc,
+              "hg": hg, "hc": hc, "hd": 1 - hg - hc}
+        gbs, nb = a.gpu_batch_size or 48, a.num_gpu_batches or 3
+        out = {"gbs": gbs, "num_gpu_batches": nb, "shares": sh,
+               **estimate(wl, mc, gbs * nb, gbs, sh)}
+    else:
+        out = search(wl, mc)
+    print(json.dumps({"workload": asdict(wl), "policy": out}, indent=1))
+
+
+if __name__ == "__main__":
+    main()
