@@ -184,7 +184,7 @@ def solve(wl: Workload, mc: Machine, bls: int, gbs: int):
                 bounds=[(0, 1)] * 9 + [(0, None)] * 2, method="highs")
     if r.status != 0:
         return None, float("inf")
-    f = np.clip(r.x[:9], 0.0, 1.0)
+    f = np.clip(r.x[:9], 0.0, 1.0) + 0.0      # (+ 0.0: no negative zeros)
     for c in range(3):                        # renormalize solver round-off
         f[3 * c:3 * c + 3] /= f[3 * c:3 * c + 3].sum()
     return dict(zip(SHARES, f.tolist())), float(r.fun)
