@@ -309,7 +309,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the block decode is measured on a single "
-              "MI355X (sharding across GPUs is not part of this build)", file=sys.stderr)
+              "MI355X (sharding across GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch
