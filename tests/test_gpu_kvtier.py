@@ -144,13 +144,15 @@ def test_layer_decode_kv_tier_matches_oracle(L):
     assert np.array_equal(host.k[:, :, :P].numpy(), oc.k[gbs:, :, :P])
 
 
-@pytest.mark.parametrize("kv_host_seqs,gbs,nb", [(4, 2, 3), (6, 2, 3), (3, 3, 2)])
-def test_model_generation_kv_tier_bit_exact(L, kv_host_seqs, gbs, nb):
+@pytest.mark.parametrize("kv_host_seqs,gbs,nb,topk", [(4, 2, 3, 0.0), (6, 2, 3, 0.0), (3, 3, 2, 0.0),
+                                                       (4, 2, 3, 0.1)])
+def test_model_generation_kv_tier_bit_exact(L, kv_host_seqs, gbs, nb, topk):
     """2-layer OPT-125m-shape model, prefill s = 20 and 5 decode steps, with
     the last kv_host_seqs sequences' caches in pinned host memory: tokens,
     every step's logits and the caches equal the all-device model's.  The
     loads cross layer boundaries (one host batch of layer 0 is followed by
-    layer 1's) and the slots are reused across calls."""
+    layer 1's) and the slots are reused across calls.  topk: the same with
+    Top-K sparse V at that fraction on both models."""
     import torch
     from throughput_oriented_offloaded_amd.model import DeviceLayer, Model, Shape
     sh = Shape(n_layers=2, h1=768, h2=3072, n_heads=12, head_dim=64)
@@ -160,8 +162,9 @@ def test_model_generation_kv_tier_bit_exact(L, kv_host_seqs, gbs, nb):
     toks = synth.tokens(bls, s, seed=3).cuda()
     layers = [DeviceLayer.from_fp16({k: v.cuda() for k, v in W.items()}, L.FG_FMT_Q4G64) for W in Ws]
     embd = {k: v.cuda() for k, v in emb.items()}
-    ref = Model(sh, layers, embd, L.FG_FMT_Q4G64, bls, s + n)
-    tr = Model(sh, layers, embd, L.FG_FMT_Q4G64, bls, s + n, kv_host_seqs=kv_host_seqs)
+    ref = Model(sh, layers, embd, L.FG_FMT_Q4G64, bls, s + n, attn_topk=topk)
+    tr = Model(sh, layers, embd, L.FG_FMT_Q4G64, bls, s + n, kv_host_seqs=kv_host_seqs,
+               attn_topk=topk)
     out_r, lg_r = ref.generate(toks, n, gbs=gbs, nb=nb)
     out_t, lg_t = tr.generate(toks, n, gbs=gbs, nb=nb)
     torch.cuda.synchronize()
