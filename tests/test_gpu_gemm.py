@@ -162,3 +162,50 @@ def test_linear_shared_tiles_any_workspace(L, M, N, K):
         assert torch.equal(yi, ys[0]), f"call {i} differs bitwise"
     ref_o = oracle.linear(x, oracle.dequant_weight(rc[:128], rm[:4], 256, K), None)
     assert_close(np16(y_o), ref_o, "q4 first 256 columns")
+
+
+OPT175_PROJ = [  # N, K, act, residual: QKV, out-projection, FC1 (ReLU), FC2
+    (3 * 12288, 12288, 0, False), (12288, 12288, 0, True), (49152, 12288, 1, False),
+    (12288, 49152, 0, True)]
+
+
+@pytest.mark.parametrize("N,K,act,res", OPT175_PROJ)
+def test_linear_q4_opt175b_shapes_sampled(L, N, K, act, res):
+    """The decode GEMM at the OPT-175B block (M = 144) on full weights,
+    quantized on the device in one call, through the stream-K path the
+    benchmark times.  The oracle quantizes the sampled 64-row groups itself
+    from the same fp16 weights (the device's codes must equal them) and
+    computes the sampled outputs from its own dequantized rows."""
+    import torch
+    import synth
+    M = 144
+    lay = N // 1024 + K // 1024          # distinct seeds per shape
+    w = synth.normal_f16((N, K), synth.tensor_seed(7, lay, "w_1"), "cuda", std=0.02)
+    x = synth.normal_f16((M, K), synth.tensor_seed(7, lay, "x"), "cuda")
+    b = synth.normal_f16((N,), synth.tensor_seed(7, lay, "b_1"), "cuda", std=0.02)
+    r = synth.normal_f16((M, N), synth.tensor_seed(7, lay, "vhist"), "cuda") if res else None
+    codes = torch.empty((N // 2, K), dtype=torch.uint8, device="cuda")
+    meta = torch.empty((N // 64, 2, K), dtype=torch.float16, device="cuda")
+    L.fg_quant_group4(w, 1, N, K, codes, meta)
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    wsb = L.fg_linear_workspace_bytes(M, N, K)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    L.fg_linear(x, M, K, L.FG_FMT_Q4G64, codes, meta, N, b, act, r, y, ws, wsb)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(N + K)
+    groups = sorted(set(rng.integers(0, N // 64, size=3).tolist()) | {0, N // 64 - 1})
+    rows = np.sort(rng.choice(M, size=6, replace=False))
+    xs = np16(x)[rows]
+    ys = np16(y)[rows]
+    rs = np16(r)[rows] if res else None
+    bh = np16(b)
+    for g in groups:
+        wg = np16(w[g * 64:(g + 1) * 64])
+        rc, rm = oracle.quant_weight(wg)
+        assert np.array_equal(codes[g * 32:(g + 1) * 32].cpu().numpy(), rc), f"codes of group {g}"
+        assert np.array_equal(np16(meta[g:g + 1]), rm), f"meta of group {g}"
+        w_ref = oracle.dequant_weight(rc, rm, 64, K)
+        resid = np.ascontiguousarray(rs[:, g * 64:(g + 1) * 64]) if res else None
+        ref = oracle.linear(xs, w_ref, bh[g * 64:(g + 1) * 64], relu=bool(act), residual=resid)
+        got = ys[:, g * 64:(g + 1) * 64]
+        assert_close(got, ref, f"M=144 N={N} K={K} group {g}")
