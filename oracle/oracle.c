@@ -135,7 +135,7 @@ void or_quant_g4(const uint16_t* x, int64_t outer, int64_t axis, int64_t inner,
 void or_dequant_g4(const uint8_t* codes, const uint16_t* meta, int64_t outer,
                    int64_t axis, int64_t inner, int32_t group, uint16_t* y) {
     const int64_t ngroups = axis / group;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for collapse(2) schedule(static)
     for (int64_t o = 0; o < outer; ++o) {
         for (int64_t a = 0; a < axis; ++a) {
             const int64_t g = a / group;

@@ -293,3 +293,43 @@ def test_model_attn_topk_option(L):
         assert torch.equal(a, b)
     assert torch.equal(runs[0.0][0], runs[0.1][0])
     assert not torch.equal(runs[0.0][1], runs[0.1][1])
+
+
+def test_decode_block_opt175b_shape_sampled(L):
+    """One OPT-175B-shape layer (4-bit weights and cache, random LayerNorms)
+    decoding the benchmark's block: gbs 48 x 3, history of 528 positions,
+    the same launches as a benchmark step (stream-K GEMMs, split-k sums fused
+    with LayerNorm, one-wavefront attention per (sequence, head)).  The
+    library's weight codes equal the oracle's; three sampled sequences (first,
+    middle and last GPU batch) are checked against the oracle's layer."""
+    import torch
+    from throughput_oriented_offloaded_amd.model import DeviceKV, DeviceLayer
+    h1, h2, nh, hd = 12288, 49152, 96, 128
+    gbs, nb, P = 48, 3, 528
+    bls, lmax = gbs * nb, P + 16
+    W = synth.layer_weights(h1, h2, 0, seed=3, device="cuda", random_ln=True)
+    dl = DeviceLayer.from_fp16(W, L.FG_FMT_Q4G64)
+    od = oracle.Dims(h1, h2, nh, hd)
+    Wq = oracle.quant_layer(od, {k: np16(v) for k, v in W.items()})
+    del W
+    for name in ("qkv", "o", "1", "2"):
+        assert np.array_equal(dl.t["w_" + name].cpu().numpy(), Wq["c_" + name]), name
+        assert np.array_equal(np16(dl.t["m_" + name]), Wq["m_" + name]), name
+    Wd = oracle.dequant_layer(od, Wq)
+    del Wq
+    d = L.dims(h1, h2, nh, hd)
+    kv = DeviceKV(L.FG_FMT_Q4G64, bls, nh, hd, lmax, "cuda")
+    kh, vh = synth.kv_history(bls, nh, P, hd, seed=4, device="cuda")
+    for p in range(P):
+        L.fg_kv_append_q4(kh[:, p].contiguous(), vh[:, p].contiguous(), h1, kv.struct, bls, d, p)
+    sample = np.array([0, 70, bls - 1])
+    oc = oracle.KVCache("q4", len(sample), nh, hd, lmax)
+    oc.store(np16(kh[sample]), np16(vh[sample]), 0)
+    del kh, vh
+    x = synth.activations(bls, h1, seed=5, device="cuda")
+    x0 = np16(x)[sample]
+    ws = torch.empty(L.fg_workspace_bytes(d, bls, dl.fmt), dtype=torch.uint8, device="cuda")
+    L.fg_layer_decode_block(d, dl.struct, x, gbs, nb, P, kv.struct, ws, ws.numel())
+    torch.cuda.synchronize()
+    ref, _, _ = oracle.layer_decode(od, Wd, x0, P, oc)
+    assert_close(np16(x)[sample], ref, "OPT-175B-shape decode block, sampled sequences")
