@@ -192,7 +192,6 @@ void tile_kernel(Params p, int64_t tiles_m, int64_t tiles_n, int64_t grid) {
     }
     // drain the reloads past the end before the workgroup exits; the MFMA
     // results are read by VALU below (an XDL write needs up to 11 wait states)
-    // drain the reloads past the end before the workgroup exits
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
     asm volatile("s_nop 7\n\ts_nop 7");
 
