@@ -75,3 +75,32 @@ def test_tiering_rejects_pageable_host_memory(L):
     with pytest.raises(L.FgError) as e:
         tiered.generate(toks, 2, gbs=4, nb=1)
     assert e.value.status == L.FG_ERR_INVALID and "pinned" in str(e.value)
+
+
+def test_weight_and_kv_tiering_together(L):
+    """Weight tiering (host halves of layers 0 and 2) and KV tiering (the last
+    GPU batch's cache in pinned host memory) in one model, each on its own
+    copy stream: tokens and logits equal the fully resident model's."""
+    import torch
+    from throughput_oriented_offloaded_amd.model import DeviceLayer, Model, Shape, TierLayer
+    res, _, toks, n, bls = _models(L, (1, 0, 1))
+    sh = res.shape
+    s = toks.shape[1]
+    Ws = [{k: v.cuda() for k, v in synth.layer_weights(sh.h1, sh.h2, j, seed=3).items()}
+          for j in range(sh.n_layers)]
+    layers, tier = [], []
+    for j, W in enumerate(Ws):
+        if j != 1:
+            dl, tl = TierLayer.split(W, L.FG_FMT_F16)
+            layers.append(dl)
+            tier.append(tl)
+        else:
+            layers.append(DeviceLayer.from_fp16(W, L.FG_FMT_F16))
+            tier.append(None)
+    both = Model(sh, layers, res.emb, L.FG_FMT_Q4G64, bls, s + n, tier=tier, kv_host_seqs=2)
+    out_r, lg_r = res.generate(toks, n, gbs=2, nb=2)
+    out_b, lg_b = both.generate(toks, n, gbs=2, nb=2)
+    torch.cuda.synchronize()
+    assert torch.equal(out_r, out_b)
+    for a, b in zip(lg_r, lg_b):
+        assert torch.equal(a, b)
