@@ -191,3 +191,21 @@ def test_search_cli_runs(pol, capsys):
     pol.main(["--model", "opt-30b", "--percent", "100", "0", "0", "100", "100", "0"])
     out = capsys.readouterr().out
     assert '"tokens_per_s"' in out
+
+
+def test_search_picks_a_feasible_best_policy(pol):
+    """The (gbs, nb) search on MI355X-like constants: the chosen policy is
+    feasible under the oracle and no other grid point's LP optimum beats it;
+    175B fp16 weights (348 GB) cannot all stay in 288 GB of HBM."""
+    wl = pol.Workload(96, 12288, 49152, 512, 32)
+    mc = pol.mi355x(1e12)
+    best = pol.search(wl, mc, gbs_list=(16, 48), nb_max=8)
+    assert best is not None
+    m = oc.Model(l=96, h1=12288, h2=49152, s=512, n=32)
+    hw = oc.Hardware(**{k: getattr(mc, k) for k in oc.Hardware.__dataclass_fields__})
+    assert oc.feasible(m, hw, best["bls"], best["gbs"], best["shares"], tol=1e-7)
+    assert best["shares"]["wg"] < 1.0
+    for gbs in (16, 48):
+        for nb in range(1, 9):
+            _, v = pol.solve(wl, mc, gbs * nb, gbs)
+            assert best["seconds_per_sequence"] <= v * (1 + 1e-9)
