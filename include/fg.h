@@ -379,8 +379,11 @@ int64_t fg_kv_bytes(const fg_dims* d, int32_t n_layers, int32_t bls, int32_t s, 
  * (on != 0) or stops recording.  fg_trace_collect waits for the recorded
  * events and fills, per kind k < n_kinds, the launch count, summed duration
  * (ms), summed flops and summed bytes; it returns the number of kinds (or a
- * negative status).  fg_trace_kind_name names a kind.  Recording adds two
- * event records per launch; it is off by default.
+ * negative status).  A record whose events cannot be waited on or timed is
+ * left out of the sums; the others are still summed, and the first such
+ * failure is then returned as FG_ERR_HIP.  A launch whose events cannot be
+ * created or recorded is not recorded.  fg_trace_kind_name names a kind.
+ * Recording adds two event records per launch; it is off by default.
  */
 int fg_trace_enable(int on);
 /* Bit k of mask selects kind k for recording while tracing is on (default:

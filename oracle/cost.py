@@ -111,24 +111,42 @@ def path_times(m: Model, hw: Hardware, bls: int, p: dict, phase: str) -> dict:
     }
 
 
-def peak_memory(m: Model, bls: int, gbs: int, p: dict) -> dict:
-    """Bytes held per tier at the peak: each tier's share of all layers'
-    weights, of the block's cache at full length s + n and of the block's
-    prompt activations; the GPU also holds two layers' worth of the
-    off-GPU weight share and two GPU batches' worth of the off-GPU cache
-    share (the double buffers the transfers fill) and one GPU batch's
-    working set (QKV, attention output, MLP hidden)."""
+def phase_memory(m: Model, bls: int, gbs: int, p: dict, phase: str) -> dict:
+    """Bytes held per tier during phase "pre" (the prompt: cache at s
+    positions, activations of s tokens per sequence) or "gen" (a decode step:
+    cache at its full length s + n, activations of one token per sequence).
+
+    Each tier holds its share of all layers' weights, of the block's cache and
+    of the block's activations.  The GPU also holds two layers' worth of the
+    off-GPU weight share and two GPU batches' worth of the off-GPU cache share
+    (the double buffers the transfers fill) and one GPU batch's working set
+    (QKV, attention output, MLP hidden) for the phase's tokens.
+
+    [P2] "FlexGen 的核心:计算图分块与张量生命周期" gives the decode-phase peak
+    of a tier that holds one layer's weights, the activations and the whole
+    block's cache as w + 2 h1 bls + 4 h1 bls l (s + n): with a weight share
+    of 1/l and the whole cache and activation shares on that tier, the "gen"
+    figure here is exactly that sum."""
     W = layer_weight_bytes(m)
-    kv_all = m.l * cache_bytes(m, bls, m.s + m.n)
-    act = act_bytes(m, bls, m.s)
-    work = 2 * gbs * m.s * (5 * m.h1 + m.h2)
+    length, tokens = (m.s + m.n, 1) if phase == "gen" else (m.s, m.s)
+    kv_all = m.l * cache_bytes(m, bls, length)
+    act = act_bytes(m, bls, tokens)
+    work = 2 * gbs * tokens * (5 * m.h1 + m.h2)
     stage_w = 2 * W * (1 - p["wg"])
-    stage_c = 2 * cache_bytes(m, gbs, m.s + m.n) * (1 - p["cg"])
+    stage_c = 2 * cache_bytes(m, gbs, length) * (1 - p["cg"])
     return {
         "g": p["wg"] * m.l * W + p["cg"] * kv_all + p["hg"] * act + work + stage_w + stage_c,
         "c": p["wc"] * m.l * W + p["cc"] * kv_all + p["hc"] * act,
         "d": p["wd"] * m.l * W + p["cd"] * kv_all + p["hd"] * act,
     }
+
+
+def peak_memory(m: Model, bls: int, gbs: int, p: dict) -> dict:
+    """Bytes held per tier at the peak of the run: the larger of the prompt
+    phase and a decode step at full cache length."""
+    pre = phase_memory(m, bls, gbs, p, "pre")
+    gen = phase_memory(m, bls, gbs, p, "gen")
+    return {t: max(pre[t], gen[t]) for t in "gcd"}
 
 
 def total_time(m: Model, hw: Hardware, bls: int, p: dict) -> float:

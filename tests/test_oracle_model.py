@@ -55,6 +55,66 @@ def test_layernorm_moments_and_affine():
     assert np.allclose(z2, z, atol=2e-3)
 
 
+def _pin_layernorm(ln):
+    """Rows alternating +a, -a over h = 64 have mean 0 and (biased) variance
+    a^2 exactly, so LayerNorm with unit gain and zero shift gives
+    +-a / sqrt(a^2 + eps), eps = 1e-5 inside the square root.  Small a makes
+    eps matter (a = 2^-8: a^2 = 1.5e-5); a = 1 separates the biased variance
+    (divide by h) from the unbiased one (h - 1), about 16 fp16 steps apart."""
+    h = 64
+    one, zero = np.ones(h, F16), np.zeros(h, F16)
+    for a in (2.0 ** -8, 2.0 ** -6, 2.0 ** -3, 1.0, 3.0):
+        x = f16(np.tile([a, -a], h // 2))[None].repeat(3, 0)
+        y = ln(x, one, zero)
+        v = a / math.sqrt(a * a + 1e-5)
+        want = f16(np.tile([v, -v], h // 2))[None].repeat(3, 0)
+        assert np.array_equal(oracle.to_f16(y).view(np.uint16), want.view(np.uint16)), a
+
+
+def test_layernorm_alternating_rows_closed_form():
+    _pin_layernorm(oracle.layernorm)
+
+
+def _ln_unbiased(x, g, b):
+    x = oracle.to_f16(x).astype(np.float64)
+    z = (x - x.mean(1, keepdims=True)) / np.sqrt(x.var(1, ddof=1, keepdims=True) + 1e-5)
+    return f16(z * g.astype(np.float64) + b.astype(np.float64))
+
+
+def _ln_eps_outside(x, g, b):
+    x = oracle.to_f16(x).astype(np.float64)
+    z = (x - x.mean(1, keepdims=True)) / (np.sqrt(x.var(1, keepdims=True)) + 1e-5)
+    return f16(z * g.astype(np.float64) + b.astype(np.float64))
+
+
+def _ln_no_eps(x, g, b):
+    x = oracle.to_f16(x).astype(np.float64)
+    z = (x - x.mean(1, keepdims=True)) / np.sqrt(x.var(1, keepdims=True))
+    return f16(z * g.astype(np.float64) + b.astype(np.float64))
+
+
+@pytest.mark.parametrize("planted", [_ln_unbiased, _ln_eps_outside, _ln_no_eps])
+def test_layernorm_pin_catches_planted_conventions(planted):
+    with pytest.raises(AssertionError):
+        _pin_layernorm(planted)
+
+
+def test_layernorm_matches_torch_float64():
+    """A library routine: torch's layer_norm (biased variance, eps inside the
+    square root, elementwise affine) in float64, rounded once to fp16."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(21)
+    for h, scale in ((64, 0.01), (768, 1.0), (1000, 30.0)):
+        x = rnd(rng, (6, h), scale)
+        g, b = rnd(rng, h), rnd(rng, h)
+        ref = torch.nn.functional.layer_norm(
+            torch.from_numpy(x.astype(np.float64)), (h,), torch.from_numpy(g.astype(np.float64)),
+            torch.from_numpy(b.astype(np.float64)), eps=1e-5).numpy()
+        got = as64(oracle.layernorm(x, g, b))
+        ulp = np.abs(np.spacing(f16(ref))).astype(np.float64)
+        assert np.max(np.abs(got - f16(ref).astype(np.float64)) / ulp) <= 1.0
+
+
 # -------------------------------------------------------------------- linear
 def test_linear_matches_numpy_matmul():
     rng = np.random.default_rng(2)
@@ -314,6 +374,58 @@ def test_model_greedy_is_consistent():
     m2 = oracle.Model(d, layers, E, P, g, be, "f16", s + n, b)
     lg_ref, _ = m2.prefill(np.concatenate([toks, t1[:, None]], 1))
     assert np.array_equal(lg2, lg_ref)
+
+
+def _pin_lm_head(head):
+    """The head is the final LayerNorm followed by the tied embedding
+    (logits = LN_f(x) E^T).  With zero gain the LayerNorm returns its shift
+    beta for every row, so the logits are beta E^T whatever x is; a one-hot
+    beta = c e_j picks c times column j of E."""
+    rng = np.random.default_rng(22)
+    V, h = 50, 64
+    E = rnd(rng, (V, h), 0.5)
+    x = rnd(rng, (4, h), 2.0)
+    zero = np.zeros(h, F16)
+    beta = rnd(rng, h)
+    lg = as64(head(x, zero, beta, E))
+    want = f16(np.tile(E.astype(np.float64) @ beta.astype(np.float64), (4, 1))).astype(np.float64)
+    assert lg.shape == (4, V) and np.array_equal(lg, want)
+    onehot = np.zeros(h, F16)
+    onehot[7] = F16(0.75)
+    lg = as64(head(x, zero, onehot, E))
+    assert np.array_equal(lg, np.tile(f16(0.75 * E[:, 7].astype(np.float64)).astype(np.float64), (4, 1)))
+
+
+def test_lm_head_is_final_layernorm_then_tied_embedding():
+    _pin_lm_head(oracle.lm_head)
+
+
+@pytest.mark.parametrize("planted", [
+    lambda x, g, b, E: oracle.linear(x, E),                                   # final LN skipped
+    lambda x, g, b, E: oracle.linear(oracle.layernorm(x, np.ones_like(g), b), E),   # gain ignored
+    lambda x, g, b, E: oracle.linear(oracle.layernorm(x, g, b), E, bias=E[:, 0].copy()),  # stray bias
+])
+def test_lm_head_pin_catches_planted_mistakes(planted):
+    with pytest.raises(AssertionError):
+        _pin_lm_head(planted)
+
+
+def test_model_logits_come_from_the_head():
+    """Whole-model bookkeeping: with a zero-gain final LayerNorm every
+    sequence's logits are beta E^T after the prefill and after a decode step,
+    whatever the layers computed."""
+    rng = np.random.default_rng(23)
+    d = oracle.Dims(h1=64, h2=256, nh=1, hd=64)
+    layers = [_layer(rng, d) for _ in range(2)]
+    V, b, s, n = 40, 2, 4, 2
+    E, P = rnd(rng, (V, d.h1)), rnd(rng, (s + n, d.h1))
+    beta = rnd(rng, d.h1)
+    m = oracle.Model(d, layers, E, P, np.zeros(d.h1, F16), beta, "q4", s + n, b)
+    want = f16(np.tile(E.astype(np.float64) @ beta.astype(np.float64), (b, 1))).view(np.uint16)
+    lg, tok = m.prefill(rng.integers(0, V, (b, s)))
+    assert np.array_equal(lg, want)
+    lg2, _ = m.decode(tok, s)
+    assert np.array_equal(lg2, want)
 
 
 # --------------------------------------------------------------- closed forms

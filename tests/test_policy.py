@@ -102,6 +102,52 @@ def test_planted_cache_mistake_is_caught(monkeypatch):
         _pin_kv_peak()
 
 
+def _pin_decode_peak():
+    """[P2] "FlexGen 的核心:计算图分块与张量生命周期": a tier that holds the
+    current layer's weights w, the block's activations and the whole block's
+    KV cache peaks at w + 2 h1 bls + 4 h1 bls l (s + n) bytes (fp16), which
+    bounds the block by bls <= (M_C - w) / (2 h1 + 4 h1 l (s + n)).  In the
+    oracle's terms that tier is the CPU with a weight share of one layer
+    (1/l), the whole cache and the whole activation share."""
+    m = oc.Model(s=512, n=32, **OPT175)
+    w = oc.layer_weight_bytes(m)
+    p = dict(wg=1 - 1 / m.l, wc=1 / m.l, wd=0, hg=0, hc=1, hd=0, cg=0, cc=1, cd=0)
+    for bls in (1, 48, 144, 512):
+        want = w + 2 * m.h1 * bls + 4 * m.h1 * bls * m.l * (m.s + m.n)
+        got = oc.phase_memory(m, bls, 8, p, "gen")["c"]
+        assert got == pytest.approx(want, rel=1e-12)
+        # the decode step is the run's peak there (2 l n >= s - 1)
+        assert oc.peak_memory(m, bls, 8, p)["c"] == pytest.approx(want, rel=1e-12)
+    # the block-size bound: the largest bls whose placement fits M_C
+    M_C = 208e9
+    hw = _hw(cap_g=1e30, cap_c=M_C, cap_d=0.0)
+    bound = int((M_C - w) // (2 * m.h1 + 4 * m.h1 * m.l * (m.s + m.n)))
+    assert bound >= 1
+    assert oc.feasible(m, hw, bound, 1, p)
+    assert not oc.feasible(m, hw, bound + 1, 1, p)
+
+
+def test_pages_decode_peak_and_block_bound():
+    _pin_decode_peak()
+
+
+@pytest.mark.parametrize("mistake", ["prompt_acts_in_decode", "cache_at_prompt_length", "no_layers"])
+def test_planted_peak_mistakes_are_caught(monkeypatch, mistake):
+    """Peak-memory terms that hold the prompt's activations during decode,
+    count the cache at s instead of s + n positions, or drop the l layers of
+    cache each fail the decode-peak pin."""
+    real = oc.phase_memory
+    if mistake == "prompt_acts_in_decode":
+        monkeypatch.setattr(oc, "act_bytes", lambda m, bls, tokens: 2 * bls * m.s * m.h1)
+    elif mistake == "cache_at_prompt_length":
+        monkeypatch.setattr(oc, "phase_memory",
+                            lambda m, bls, gbs, p, phase: real(m, bls, gbs, p, "pre" if phase == "gen" else phase))
+    else:
+        monkeypatch.setattr(oc, "cache_bytes", lambda m, bls, length: 4 * bls * length * m.h1 * m.c_ratio / m.l)
+    with pytest.raises(AssertionError):
+        _pin_decode_peak()
+
+
 # ------------------------------------------------------ product vs oracle
 @pytest.fixture(scope="module")
 def pol():

@@ -24,6 +24,10 @@ uint64_t g_mask = ~0ull;          // kinds that are recorded while tracing is on
 std::vector<Rec> g_recs;
 std::vector<hipEvent_t> g_pool;   // free events
 
+void give(hipEvent_t e) {
+    if (e) g_pool.push_back(e);
+}
+
 hipEvent_t take() {
     if (!g_pool.empty()) {
         hipEvent_t e = g_pool.back();
@@ -49,8 +53,13 @@ TraceScope::TraceScope(int kind, hipStream_t st, double flops, double bytes) {
     std::lock_guard<std::mutex> lk(g_mu);
     if (!g_on) return;
     Rec r{kind, take(), take(), flops, bytes};
-    if (!r.a || !r.b) return;
-    if (hipEventRecord(r.a, st) != hipSuccess) return;
+    // a launch that cannot be traced is simply not recorded; its events go
+    // back to the pool
+    if (!r.a || !r.b || hipEventRecord(r.a, st) != hipSuccess) {
+        give(r.a);
+        give(r.b);
+        return;
+    }
     st_ = st;
     idx_ = (long)g_recs.size();
     g_recs.push_back(r);
@@ -92,14 +101,29 @@ extern "C" int fg_trace_collect(int32_t n_kinds, int64_t* count, double* ms, dou
     FG_CHECK_ARG(n_kinds >= fg::TK_COUNT, "need room for %d kinds", (int)fg::TK_COUNT);
     for (int k = 0; k < n_kinds; ++k) { count[k] = 0; ms[k] = flops[k] = bytes[k] = 0.0; }
     std::lock_guard<std::mutex> lk(fg::g_mu);
+    // every record is visited: one that cannot be timed is left out of the
+    // sums and the first such failure is reported after the rest are summed
+    hipError_t first = hipSuccess;
+    const char* what = "";
     for (auto& r : fg::g_recs) {
-        FG_HIP(hipEventSynchronize(r.b));
+        hipError_t e = hipEventSynchronize(r.b);
         float t = 0.f;
-        FG_HIP(hipEventElapsedTime(&t, r.a, r.b));
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+        else what = "hipEventSynchronize";
+        if (e != hipSuccess) {
+            if (first == hipSuccess) {
+                first = e;
+                if (!*what) what = "hipEventElapsedTime";
+            }
+            continue;
+        }
         count[r.kind] += 1;
         ms[r.kind] += t;
         flops[r.kind] += r.flops;
         bytes[r.kind] += r.bytes;
     }
+    if (first != hipSuccess)
+        return fg::set_error(FG_ERR_HIP, "%s failed: %s (records that could be timed are summed)", what,
+                             hipGetErrorString(first));
     return fg::TK_COUNT;
 }

@@ -89,8 +89,8 @@ MODELS = {   # OPT shapes: layers, h1, h2
 
 def _affine(wl: Workload, mc: Machine, bls: int, gbs: int):
     """Coefficients of the nine shares: path times T[phase] = A f + b (5 x 9,
-    5) for phase "pre" and "gen", and peak memory M = P f + q (3 x 9, 3)
-    for tiers g, c, d."""
+    5) for phase "pre" and "gen", and memory held M = P f + q (3 x 9, 3) for
+    tiers g, c, d in each phase ("mem_pre", "mem_gen")."""
     h1, h2 = wl.h1, wl.h2
     W = (8 * h1 * h1 + 4 * h1 * h2) * wl.w_ratio
     mats = 8 * h1 * h1 + 4 * h1 * h2
@@ -118,21 +118,25 @@ def _affine(wl: Workload, mc: Machine, bls: int, gbs: int):
             A[3, i[k]] += v / mc.bw_c2d
         b[4] = comp
         out[ph] = (A, b)
-    kv_all = wl.l * 4 * bls * (wl.s + wl.n) * h1 * wl.c_ratio
-    act_all = 2 * bls * wl.s * h1
-    P = np.zeros((3, 9))
-    q = np.zeros(3)
-    for t, tier in enumerate("gcd"):
-        P[t, i["w" + tier]] += wl.l * W
-        P[t, i["c" + tier]] += kv_all
-        P[t, i["h" + tier]] += act_all
-    # GPU extras: a batch's working set, double buffers of the off-GPU
-    # weight share (2 layers) and cache share (2 GPU batches)
-    stage_c = 2 * 4 * gbs * (wl.s + wl.n) * h1 * wl.c_ratio
-    q[0] = 2 * gbs * wl.s * (5 * h1 + h2) + 2 * W + stage_c
-    P[0, i["wg"]] -= 2 * W
-    P[0, i["cg"]] -= stage_c
-    out["mem"] = (P, q)
+    # peak memory per phase: the prompt (cache at s, activations of s tokens
+    # per sequence) and a decode step (cache at s + n, one token); each
+    # tier's peak is the larger of the two, so the LP bounds both
+    for ph, length, tokens in (("pre", wl.s, wl.s), ("gen", wl.s + wl.n, 1)):
+        kv_all = wl.l * 4 * bls * length * h1 * wl.c_ratio
+        act_all = 2 * bls * tokens * h1
+        P = np.zeros((3, 9))
+        q = np.zeros(3)
+        for t, tier in enumerate("gcd"):
+            P[t, i["w" + tier]] += wl.l * W
+            P[t, i["c" + tier]] += kv_all
+            P[t, i["h" + tier]] += act_all
+        # GPU extras: a batch's working set, double buffers of the off-GPU
+        # weight share (2 layers) and cache share (2 GPU batches)
+        stage_c = 2 * 4 * gbs * length * h1 * wl.c_ratio
+        q[0] = 2 * gbs * tokens * (5 * h1 + h2) + 2 * W + stage_c
+        P[0, i["wg"]] -= 2 * W
+        P[0, i["cg"]] -= stage_c
+        out["mem_" + ph] = (P, q)
     return out
 
 
@@ -145,8 +149,8 @@ def estimate(wl: Workload, mc: Machine, bls: int, gbs: int, shares: dict) -> dic
         A, b = co[ph]
         res["paths_" + ph] = dict(zip(PATHS, (A @ f + b).tolist()))
         res["T_" + ph] = float(np.max(A @ f + b))
-    P, q = co["mem"]
-    res["peak"] = dict(zip("gcd", (P @ f + q).tolist()))
+    held = [co["mem_" + ph][0] @ f + co["mem_" + ph][1] for ph in ("pre", "gen")]
+    res["peak"] = dict(zip("gcd", np.maximum(held[0], held[1]).tolist()))
     res["T"] = wl.l * res["T_pre"] + wl.l * (wl.n - 1) * res["T_gen"]
     res["tokens_per_s"] = bls * wl.n / res["T"]
     res["decode_tokens_per_s"] = bls / (wl.l * res["T_gen"])
@@ -167,13 +171,14 @@ def solve(wl: Workload, mc: Machine, bls: int, gbs: int):
             row[zi] = -1.0
             rows.append(row)
             rhs.append(-b[r])
-    P, q = co["mem"]
-    for t, (cap, alpha) in enumerate(((mc.cap_g, mc.alpha_g), (mc.cap_c, mc.alpha_c),
-                                      (mc.cap_d, mc.alpha_d))):
-        row = np.zeros(nv)                    # alpha (P f + q) <= cap
-        row[:9] = alpha * P[t]
-        rows.append(row)
-        rhs.append(cap - alpha * q[t])
+    for ph in ("pre", "gen"):
+        P, q = co["mem_" + ph]
+        for t, (cap, alpha) in enumerate(((mc.cap_g, mc.alpha_g), (mc.cap_c, mc.alpha_c),
+                                          (mc.cap_d, mc.alpha_d))):
+            row = np.zeros(nv)                # alpha (P f + q) <= cap in both phases
+            row[:9] = alpha * P[t]
+            rows.append(row)
+            rhs.append(cap - alpha * q[t])
     A_eq = np.zeros((3, nv))
     for c in range(3):
         A_eq[c, 3 * c:3 * c + 3] = 1.0
