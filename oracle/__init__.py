@@ -70,12 +70,23 @@ def lib():
             L.or_attn_decode_topk.argtypes = [P, P, P, I64, I64, I64, I64, P, P, I64, I64, I64, P]
             L.or_embed.argtypes = [P, P, I64, P, P, I64, P]
             L.or_argmax.argtypes = [P, I64, I64, P]
+            L.or_set_threads.argtypes, L.or_set_threads.restype = [I32], None
+            L.or_get_threads.argtypes, L.or_get_threads.restype = [], I32
             for f in ("or_quant_g4", "or_dequant_g4", "or_layernorm", "or_linear",
                       "or_attn_prefill", "or_attn_decode", "or_attn_decode_topk", "or_embed",
                       "or_argmax"):
                 getattr(L, f).restype = None
             _lib = L
     return _lib
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of the C primitives (timing only; results do not depend on it)."""
+    lib().or_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(lib().or_get_threads())
 
 
 def _u16(a) -> np.ndarray:

@@ -15,8 +15,15 @@
 #include "oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdlib.h>
+
+/* ------------------------------------------------------------- threading */
+/* Number of OpenMP threads the parallel loops below use (timing of the CPU
+ * baseline at one thread and at all cores); no effect on any result. */
+void or_set_threads(int32_t n) { omp_set_num_threads(n > 0 ? n : 1); }
+int32_t or_get_threads(void) { return (int32_t)omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- binary16 */
 /* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.

@@ -29,6 +29,12 @@
 extern "C" {
 #endif
 
+/* OpenMP threads used by the parallel loops (timing only; results do not
+ * depend on it). */
+void or_set_threads(int32_t n);
+int32_t or_get_threads(void);
+
+
 /* binary16 <-> double.  or_d2h rounds once, to nearest, ties to even. */
 double   or_h2d(uint16_t h);
 uint16_t or_d2h(double x);

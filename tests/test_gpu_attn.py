@@ -231,6 +231,66 @@ def test_decode_attention_topk(L, fmt, bls, nh, hd, pos, topk):
     _cache_equal(kv, oc, pos + 1)
 
 
+LONG_SPARSE_CASES = [  # fmt, bls, nh, hd, pos, topk
+    # one wavefront per (sequence, head): keys held in registers up to 640
+    # positions, counted from LDS beyond
+    ("q4", 16, 128, 64, 640, 64), ("q4", 16, 128, 64, 1000, 100),
+    # four wavefronts: registers up to 2560 positions, LDS beyond
+    ("q4", 1, 2, 128, 2560, 256), ("q4", 1, 2, 128, 3000, 300), ("f16", 2, 3, 64, 2561, 257),
+    # the longest history a Top-K launch takes (one chunk of 8192 scores)
+    ("q4", 1, 2, 128, 8192, 820), ("f16", 1, 2, 64, 8192, 820), ("f16", 1, 2, 128, 8192, 8191),
+]
+
+
+@pytest.mark.parametrize("fmt,bls,nh,hd,pos,topk", LONG_SPARSE_CASES)
+def test_decode_attention_topk_long_history(L, fmt, bls, nh, hd, pos, topk):
+    """Histories past the register-held selection (640 positions with one
+    wavefront per (sequence, head), 2560 with four) up to the 8192-position
+    limit.  Keys c_p u (u a +-1 vector per head, no noise) take 256 evenly
+    spaced values c, each on a run of positions: positions of one value have
+    identical rows, so their scores tie exactly on both sides and the
+    selection inside a run goes to the lower positions; distinct values are
+    far apart in score.  The topk counts cut through runs."""
+    import torch
+    from throughput_oriented_offloaded_amd.model import DeviceKV
+    rng = np.random.default_rng(pos + topk + nh)
+    h1 = nh * hd
+    lmax = pos + 3
+    d = L.dims(h1, 4 * h1, nh, hd)
+    fmt_id = L.FG_FMT_Q4G64 if fmt == "q4" else L.FG_FMT_F16
+    kv = DeviceKV(fmt_id, bls, nh, hd, lmax, "cuda")
+    u = rng.choice([-1.0, 1.0], size=(bls, nh, hd))
+    grid = np.arange(256) * (3.0 / 256) - 1.5          # multiples of 2^-8: exact in fp16
+    rep = -(-pos // 256)
+    c = np.stack([grid[rng.permutation(pos) // rep] for _ in range(bls * nh)]).reshape(bls, nh, pos)
+    k = c[..., None] * u[:, :, None, :]
+    kx = k.transpose(0, 2, 1, 3).reshape(bls, pos, h1).astype(np.float16)
+    vx = (rng.standard_normal((bls, pos, h1)) * 2).astype(np.float16)
+    append = L.fg_kv_append_q4 if fmt == "q4" else L.fg_kv_append_f16
+    kd, vd = dev16(kx), dev16(vx)
+    for p in range(pos):
+        append(kd[:, p].contiguous(), vd[:, p].contiguous(), h1, kv.struct, bls, d, p)
+    oc = oracle.KVCache(fmt, bls, nh, hd, lmax)
+    oc.store(kx, vx, 0)
+    qkv = (rng.standard_normal((bls, 3 * h1)) * 2).astype(np.float16)
+    qkv[:, :h1] = (u.reshape(bls, h1) * 0.5).astype(np.float16)
+    buf = dev16(qkv)
+    out = torch.empty((bls, h1), dtype=torch.float16, device="cuda")
+    fn = L.fg_attn_decode_topk_q4 if fmt == "q4" else L.fg_attn_decode_topk_f16
+    fn(buf, buf[:, h1:], buf[:, 2 * h1:], 3 * h1, kv.struct, bls, d, pos, topk, 1, out)
+    torch.cuda.synchronize()
+    kh, vh = oc.history()
+    ref = oracle.attn_decode_topk(qkv, bls, nh, hd, kh, vh, lmax, pos, topk)
+    assert_close(np16(out), ref, f"{fmt} top-{topk} attention pos {pos}")
+    dense = oracle.attn_decode(qkv, bls, nh, hd, kh, vh, lmax, pos)
+    if topk < pos - rep:
+        err = np.abs(oracle.to_f16(np16(out)).astype(np.float32) - oracle.to_f16(dense).astype(np.float32)).max()
+        assert err > 1e-2 * np.abs(oracle.to_f16(dense).astype(np.float32)).max() + 1e-3
+    q3 = qkv.reshape(bls, 1, 3, h1)
+    oc.store(q3[:, :, 1], q3[:, :, 2], pos)
+    _cache_equal(kv, oc, pos + 1)
+
+
 @pytest.mark.parametrize("fmt", ["q4", "f16"])
 def test_decode_attention_topk_ties_take_lowest_positions(L, fmt):
     """Zero keys: every score is equal, and the selection must be the lowest

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import assert_close, dev16, np16
+from helpers import assert_close, dev16, np16, ranked_kv
 
 pytestmark = pytest.mark.gpu
 
@@ -78,20 +78,12 @@ def test_decode_block_matches_oracle(L, fmt, kvfmt, P):
 
 
 def _ranked_history(L, kvfmt, q, bls, P, lmax, seed):
-    """Cache of P positions whose keys are c_p sign(q_h) r_h per (sequence,
-    head): c_p a random permutation of evenly spaced values in [-1.5, 1.5) and
-    r_h = sqrt(hd) / |q_h|_1, so the head's scores are c_p (spaced 3 / P).  The
-    rows are two-level, which the 4-bit codec keeps exactly, and the selection
-    does not hinge on either side's rounding of q.  q: float [bls, nh, hd]."""
+    """Device cache and oracle cache of P positions with evenly spread scores
+    against q (helpers.ranked_kv).  q: float [bls, nh, hd]."""
     from throughput_oriented_offloaded_amd.model import DeviceKV
     bls_, nh, hd = q.shape
     h1 = nh * hd
-    rng = np.random.default_rng(seed)
-    c = np.stack([rng.permutation(P) for _ in range(bls * nh)]).reshape(bls, nh, P) * (3.0 / P) - 1.5
-    sg = np.where(q >= 0, 1.0, -1.0) * (np.sqrt(hd) / np.abs(q).sum(-1))[..., None]
-    k = c[..., None] * sg[:, :, None, :]
-    kx = k.transpose(0, 2, 1, 3).reshape(bls, P, h1).astype(np.float16)
-    vx = (rng.standard_normal((bls, P, h1)) * 2).astype(np.float16)
+    kx, vx = ranked_kv(q, P, seed)
     kv = DeviceKV(L.FG_FMT_Q4G64 if kvfmt == "q4" else L.FG_FMT_F16, bls, nh, hd, lmax, "cuda")
     d = L.dims(h1, OPT125["h2"], nh, hd)
     app = L.fg_kv_append_q4 if kvfmt == "q4" else L.fg_kv_append_f16

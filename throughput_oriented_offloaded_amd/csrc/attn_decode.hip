@@ -287,11 +287,13 @@ __device__ __forceinline__ void attn_decode_body(
     float* sL = sFix + NW * ROWS * LPP;                 // [NW*ROWS]
     float* sMax = sL + NW * ROWS;                       // [NW]
     // Top-K: per-wave counts, (selected count, normalizer over all scores),
-    // selected positions in index order
+    // selected positions in index order (16 bits each: a Top-K history is one
+    // chunk of at most 8192 positions, which keeps the launch under 64 KB of
+    // LDS with four wavefronts)
     int* sCnt = reinterpret_cast<int*>(sMax + NW);      // [NW]
     int* sSel = sCnt + NW;                              // [1]
     float* sLall = reinterpret_cast<float*>(sSel + 1);  // [1]
-    int* sIdx = sSel + 2;                               // [chunk]
+    unsigned short* sIdx = reinterpret_cast<unsigned short*>(sSel + 2);   // [chunk]
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -511,7 +513,7 @@ __device__ __forceinline__ void attn_decode_body(
                     const uint64_t sm = __ballot(sel);
                     const int off = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(sm >> 32),
                                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)sm, 0u));
-                    if (sel) sIdx[cnt + off] = p;
+                    if (sel) sIdx[cnt + off] = (unsigned short)p;
                     cnt += (int)__builtin_popcountll(sm);
                     if (valid) lsum += exp2f(sp - M);
                 }
@@ -791,7 +793,12 @@ int launch_attn_decode(const __half* q, const __half* k_new, const __half* v_new
     const int chunk = multi ? kAttnChunk : (int)std::max<int64_t>(cdiv(pos, 64) * 64, 64);
     const int lpp = d->head_dim / 32;
     const size_t lds = sizeof(float) * ((size_t)chunk + nw * 4 * lpp * 33 + nw * 4 + nw) +
-                       (sparse ? sizeof(int) * ((size_t)nw + 2 + chunk) : 0);
+                       (sparse ? sizeof(int) * ((size_t)nw + 2) + sizeof(uint16_t) * chunk : 0);
+    static_assert(kAttnTopkMaxPos <= 65536, "Top-K positions are listed in 16 bits");
+    // every launch stays within 64 KB of dynamic LDS (the largest: Top-K over
+    // 8192 positions with four wavefronts of head_dim 128, 57.7 KB)
+    if (lds > 65536)
+        return set_error(FG_ERR_UNSUPPORTED, "decode attention needs %zu bytes of LDS", lds);
 #define FG_ATTN(HD_, Q_, NW_, MU_)                                                           \
     (sparse ? attn_decode_topk_kernel<HD_, Q_, NW_>                                          \
             : (MU_ ? attn_decode_multi_kernel<HD_, Q_, NW_> : attn_decode_kernel<HD_, Q_, NW_>)) \

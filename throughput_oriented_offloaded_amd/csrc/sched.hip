@@ -20,6 +20,7 @@
 #include <vector>
 
 #include "fg_internal.h"
+#include "fg_trace.h"
 
 struct fg_sched {
     unsigned char* stage[2];
@@ -100,9 +101,14 @@ int run_layers(fg_sched* sc, const fg_dims* d, int32_t n, const fg_layer_w* w,
         const fg_tier_w& tw = tier[tl[t]];
         unsigned char* base = sc->stage[b];
         FG_HIP(hipStreamWaitEvent(cp, sc->released[b], 0));
-        FG_HIP(hipMemcpyAsync(base, tw.qk_host, qk_bytes, hipMemcpyHostToDevice, cp));
-        FG_HIP(hipMemcpyAsync(base + qk_bytes, tw.v_dev, v_bytes, hipMemcpyDeviceToDevice, cp));
-        FG_HIP(hipMemcpyAsync(base + qkv_b, tw.w1_host, w1_bytes, hipMemcpyHostToDevice, cp));
+        {
+            // traced as host -> device bytes (the device-resident W_V rows
+            // moved beside them are a few percent of the time)
+            TraceScope ts(TK_W_H2D, cp, 0.0, (double)(qk_bytes + w1_bytes));
+            FG_HIP(hipMemcpyAsync(base, tw.qk_host, qk_bytes, hipMemcpyHostToDevice, cp));
+            FG_HIP(hipMemcpyAsync(base + qk_bytes, tw.v_dev, v_bytes, hipMemcpyDeviceToDevice, cp));
+            FG_HIP(hipMemcpyAsync(base + qkv_b, tw.w1_host, w1_bytes, hipMemcpyHostToDevice, cp));
+        }
         FG_HIP(hipEventRecord(sc->staged[b], cp));
         return FG_OK;
     };

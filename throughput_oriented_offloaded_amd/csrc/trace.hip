@@ -42,7 +42,7 @@ hipEvent_t take() {
 const char* kNames[TK_COUNT] = {
     "quant_g4", "dequant_g4", "gemm_q4", "gemm_f16", "splitk_reduce", "attn_decode_q4",
     "attn_decode_f16", "kv_store", "attn_prefill", "layernorm", "embed", "argmax",
-    "reduce_layernorm", "attn_topk_q4", "attn_topk_f16", "kv_h2d", "kv_d2h"};
+    "reduce_layernorm", "attn_topk_q4", "attn_topk_f16", "kv_h2d", "kv_d2h", "w_h2d"};
 
 }  // namespace
 
