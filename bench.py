@@ -71,16 +71,23 @@ def build_model(cfg, keep_layer0_host: bool):
 
     fmt = lambda f: L.FG_FMT_Q4G64 if f == "q4" else L.FG_FMT_F16  # noqa: E731
     sh = Shape(n_layers=cfg["l"], h1=cfg["h1"], h2=cfg["h2"], n_heads=cfg["nh"], head_dim=cfg["hd"])
-    layers, tier, host0 = [], ([] if cfg.get("tier") else None), None
+    tiered = cfg.get("tier_layers")
+    if tiered is None and cfg.get("tier"):
+        tiered = range(cfg["l"])
+    tiered = set(tiered or ())
+    layers, tier, host0 = [], ([] if tiered else None), None
     L.fg_trace_enable(True)            # time the weight quantizer (init, not in the step)
     for j in range(sh.n_layers):
         W = synth.layer_weights(sh.h1, sh.h2, j, seed=0, device="cuda")
         if j == 0 and keep_layer0_host:
             host0 = {k: v.cpu() for k, v in W.items()}
-        if tier is not None:           # half of the fp16 weights to pinned host memory
+        if j in tiered:                # half of the layer's fp16 weights to pinned host memory
             dl, tl = TierLayer.split(W, fmt(cfg["w"]))
             layers.append(dl)
             tier.append(tl)
+        elif tier is not None:
+            layers.append(DeviceLayer.from_fp16(W, fmt(cfg["w"])))
+            tier.append(None)
         else:
             layers.append(DeviceLayer.from_fp16(W, fmt(cfg["w"])))
         del W
@@ -253,40 +260,217 @@ def sparse_decode(model, cfg, L, tok1, steps: int, no_trace: bool, frac: float =
     return r
 
 
-def cpu_baseline(cfg, host0, emb, budget_s: float = 15.0):
-    """The oracle (as it is) on the host cores: one decoder layer's decode step
-    for a sample of sequences at context s + n/2, plus the LM head for them;
-    decode tokens/s = rows / (l * t_layer + t_head)."""
+def host_cpu():
+    """The host's CPU model, logical CPUs, the CPUs this process may run on and
+    the physical cores among them (sysfs topology), and the thread count of
+    the all-cores runs: those physical cores, capped by OMP_NUM_THREADS."""
+    import subprocess
+    model = None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        model = next((ln.split(":", 1)[1].strip() for ln in out.splitlines()
+                      if ln.startswith("Model name")), None)
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if model is None and os.path.exists("/proc/cpuinfo"):
+        model = next((ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo")
+                      if ln.startswith("model name")), None)
+    aff = sorted(os.sched_getaffinity(0))
+    cores = set()
+    for c in aff:
+        try:
+            base = f"/sys/devices/system/cpu/cpu{c}/topology/"
+            cores.add((open(base + "physical_package_id").read().strip(),
+                       open(base + "core_id").read().strip()))
+        except OSError:
+            cores.add(("cpu", str(c)))
+    cap = int(os.environ.get("OMP_NUM_THREADS", len(cores)) or len(cores))
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": len(aff),
+            "usable_physical_cores": len(cores), "threads_all_cores": max(1, min(len(cores), cap))}
+
+
+def gpu_config1():
+    """Seconds of the config-1 generation on the GPU (prefill s = 32 and 7
+    decode steps of a 2-layer OPT-125m-shape decoder, 4-bit weights and KV,
+    bls 4): the second of two runs."""
+    import torch
+    import synth
+    from throughput_oriented_offloaded_amd import _lib as L
+    from throughput_oriented_offloaded_amd.model import DeviceLayer, Model, Shape
+    c = CONFIGS[1]
+    sh = Shape(n_layers=c["l"], h1=c["h1"], h2=c["h2"], n_heads=c["nh"], head_dim=c["hd"])
+    layers = [DeviceLayer.from_fp16(synth.layer_weights(sh.h1, sh.h2, j, seed=0, device="cuda"),
+                                    L.FG_FMT_Q4G64) for j in range(sh.n_layers)]
+    emb = synth.embeddings(sh.h1, c["s"] + c["n"], seed=0, device="cuda")
+    toks = synth.tokens(c["gbs"], c["s"], seed=0, device="cuda")
+    m = Model(sh, layers, emb, L.FG_FMT_Q4G64, c["gbs"], c["s"] + c["n"])
+    dt = 0.0
+    for _ in range(2):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        m.generate(toks, c["n"], gbs=c["gbs"], nb=c["nb"])
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t
+    return dt
+
+
+def cpu_baseline(cfg, host0, emb, gpu: dict):
+    """The oracle (as it is) on the host's cores, on the five units of the
+    measurement plan, each at 1 thread and at all usable physical cores and
+    each beside the GPU's time for the same unit.  Units at the benchmark's
+    shape run on a bounded sample (a few rows, a slice of one matrix, two
+    prompt tokens) and are scaled to the whole unit; the scale is stated per
+    unit.  The oracle's cost does not depend on the weight values, so the
+    layer's fp16 weights stand in for their dequantized copies.
+    value: the oracle's decode tokens/s for the whole block at all cores,
+    bls / (l * t_layer + t_head)."""
     import numpy as np
     import oracle
     import synth
+    hc = host_cpu()
+    n_all = hc["threads_all_cores"]
     d = oracle.Dims(cfg["h1"], cfg["h2"], cfg["nh"], cfg["hd"])
-    rows, pos = 4, cfg["s"] + cfg["n"] // 2
+    h1, l, bls, s = cfg["h1"], cfg["l"], cfg["gbs"] * cfg["nb"], cfg["s"]
+    ctx = s + cfg["n"] // 2
     Wn = {k: v.numpy().view(np.uint16) for k, v in host0.items()}
-    if cfg["w"] == "q4":
-        Wn = oracle.dequant_layer(d, oracle.quant_layer(d, Wn))
-    kh, vh = synth.kv_history(rows, cfg["nh"], pos, cfg["hd"], seed=7)
-    x = synth.activations(rows, cfg["h1"], seed=8).numpy().view(np.uint16)
+    kh, vh = synth.kv_history(4, cfg["nh"], ctx, cfg["hd"], seed=7)
+    kh, vh = kh.numpy().view(np.uint16), vh.numpy().view(np.uint16)
+    x = synth.activations(4, h1, seed=8).numpy().view(np.uint16)
+    qkv = synth.activations(4, 3 * h1, seed=9).numpy().view(np.uint16)
+    xp = synth.activations(2 * 2, h1, seed=10).numpy().view(np.uint16)
     E = emb["embed"].cpu().numpy().view(np.uint16)
     g, b = emb["lnf_g"].cpu().numpy().view(np.uint16), emb["lnf_b"].cpu().numpy().view(np.uint16)
-    t_layer, reps, t0 = 0.0, 0, time.time()
-    while reps == 0 or (time.time() - t0 < budget_s and reps < 200):
-        cache = oracle.KVCache(cfg["kv"], rows, cfg["nh"], cfg["hd"], pos + 1)
-        cache.store(kh.numpy().view(np.uint16), vh.numpy().view(np.uint16), 0)
+
+    def cache(rows):
+        c = oracle.KVCache(cfg["kv"], rows, cfg["nh"], cfg["hd"], ctx + 1)
+        c.store(kh[:rows], vh[:rows], 0)
+        return c
+
+    def clock(fn):
         t = time.perf_counter()
-        oracle.layer_decode(d, Wn, x, pos, cache)
-        t_layer += time.perf_counter() - t
-        reps += 1
-    t_layer /= reps
-    t = time.perf_counter()
-    oracle.lm_head(x, g, b, E)
-    t_head = time.perf_counter() - t
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    tps = rows / (cfg["l"] * t_layer + t_head)
-    return {"value": round(tps, 5), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} sequences x 1 decode layer at context {pos} ({reps} reps, "
-                      f"{t_layer:.2f} s/layer) + LM head ({t_head:.2f} s); scaled to "
-                      f"{cfg['l']} layers"}
+        fn()
+        return time.perf_counter() - t
+
+    # config 1 end to end (the whole unit, no scaling)
+    c1 = CONFIGS[1]
+    d1 = oracle.Dims(c1["h1"], c1["h2"], c1["nh"], c1["hd"])
+    W1 = [oracle.dequant_layer(d1, oracle.quant_layer(d1, {k: v.numpy().view(np.uint16) for k, v in
+                               synth.layer_weights(c1["h1"], c1["h2"], j, seed=0).items()}))
+          for j in range(c1["l"])]
+    e1 = {k: v.numpy().view(np.uint16) for k, v in synth.embeddings(c1["h1"], c1["s"] + c1["n"], seed=0).items()}
+    t1 = synth.tokens(c1["gbs"], c1["s"], seed=0).numpy()
+
+    def config1():
+        om = oracle.Model(d1, W1, e1["embed"], e1["pos"], e1["lnf_g"], e1["lnf_b"], "q4",
+                          c1["s"] + c1["n"], c1["gbs"])
+        _, tok = om.prefill(t1)
+        for i in range(1, c1["n"]):
+            _, tok = om.decode(tok, c1["s"] + i - 1)
+
+    quant_rows = 1024
+    elems_layer = 8 * h1 * h1 + 4 * h1 * cfg["h2"]
+    units = {
+        "config1_end_to_end": dict(
+            sample="the whole unit: prefill s=32 and 7 decode steps of the 2-layer OPT-125m-shape "
+                   "4-bit decoder, bls 4", scale=1.0, gpu_s=gpu.get("config1_s"),
+            run={1: config1, n_all: config1}),
+        "quantize_one_layer": dict(
+            sample=f"{quant_rows} rows ({quant_rows // 64} groups) of W_1, scaled to the layer's "
+                   f"{elems_layer / 2:.4g} elements",
+            scale=elems_layer / 2 / (quant_rows * h1), gpu_s=gpu.get("quant_layer_s"),
+            run={th: (lambda: oracle.quant_weight(Wn["w_1"][:quant_rows])) for th in (1, n_all)}),
+        "decode_attention_one_layer": dict(
+            sample=f"1 sequence (1 thread) / 4 sequences (all cores) at context {ctx}: the "
+                   f"oracle's cache dequantization and attention, scaled to bls {bls}",
+            scale={1: bls / 1, n_all: bls / 4}, gpu_s=gpu.get("attn_layer_s"),
+            run={1: None, n_all: None}),
+        "decode_layer_block": dict(
+            sample=f"1 sequence (1 thread) / 4 sequences (all cores) through one decoder layer "
+                   f"at context {ctx}, scaled to bls {bls}",
+            scale={1: bls / 1, n_all: bls / 4}, gpu_s=gpu.get("layer_decode_s"),
+            run={1: None, n_all: None}),
+        "prefill_one_layer_2_sequences": dict(
+            sample=f"2 sequences x 2 prompt tokens through one decoder layer, scaled linearly to "
+                   f"s = {s} (the projections are over 99% of the work)",
+            scale=s / 2, gpu_s=gpu.get("prefill_layer_2seq_s"),
+            run={th: (lambda: oracle.layer_prefill(d, Wn, xp, 2, 2, oracle.KVCache(cfg["kv"], 2, cfg["nh"],
+                                                                                      cfg["hd"], 2)))
+                 for th in (1, n_all)}),
+    }
+    out_units = {}
+    t_head = None
+    for name, u in units.items():
+        res = {"sample": u["sample"]}
+        for th in sorted({1, n_all}):
+            oracle.set_threads(th)
+            if name == "decode_attention_one_layer":
+                rows = 1 if th == 1 else 4
+                c = cache(rows)
+                meas = clock(lambda: oracle.attn_decode(qkv[:rows], rows, cfg["nh"], cfg["hd"],
+                                                        *c.history(), ctx + 1, ctx))
+            elif name == "decode_layer_block":
+                rows = 1 if th == 1 else 4
+                c = cache(rows)
+                meas = clock(lambda: oracle.layer_decode(d, Wn, x[:rows], ctx, c))
+            else:
+                meas = clock(u["run"][th])
+            sc = u["scale"][th] if isinstance(u["scale"], dict) else u["scale"]
+            key = "1_thread" if th == 1 else "all_cores"
+            res["cpu_s_" + key] = round(meas * sc, 4)
+            res["measured_s_" + key] = round(meas, 4)
+            res["scale_" + key] = round(sc, 3)
+        if u["gpu_s"]:
+            res["gpu_s"] = round(u["gpu_s"], 6)
+            res["gpu_speedup_vs_all_cores"] = round(res["cpu_s_all_cores"] / u["gpu_s"], 1)
+        out_units[name] = res
+    oracle.set_threads(n_all)
+    t_head = clock(lambda: oracle.lm_head(x, g, b, E)) * bls / 4
+    t_layer = out_units["decode_layer_block"]["cpu_s_all_cores"]
+    tps = bls / (l * t_layer + t_head)
+    return {"value": round(tps, 5), "unit": "tokens/s", "cores": n_all, "kind": "oracle",
+            "sample": f"decode tokens/s of the whole block (bls {bls}) from the decode_layer_block "
+                      f"unit at all cores ({t_layer:.1f} s per layer) times {l} layers plus the LM "
+                      f"head ({t_head:.1f} s, 4 rows scaled to {bls}); every unit below at 1 thread "
+                      f"and at all cores",
+            "host": hc, "threads": {"one": 1, "all_cores": n_all}, "units": out_units}
+
+
+def plan_policy(cfg, gpu_gb: float, host_gb: float):
+    """The pages' cost model and LP search ("FlexGen 完全拆解", sections
+    "用线性规划搜索卸载策略" and "为什么固定批量后能变成线性规划") choose gbs,
+    the number of GPU batches and the shares of weights and cache off the GPU
+    for the config's model under the given HBM and host-memory budgets, over
+    gbs in {16, 32, 48, 64} x 1..8 GPU batches, within what this executor
+    realizes (activations on the GPU, at most half of an fp16 layer's weights
+    off it); the shares are then rounded up to whole tiered layers and whole
+    host-resident GPU batches, and the cost model predicts that placement."""
+    from throughput_oriented_offloaded_amd import policy as P
+    q4 = P.Q4G64
+    wl = P.Workload(cfg["l"], cfg["h1"], cfg["h2"], cfg["s"], cfg["n"],
+                    w_ratio=q4 if cfg["w"] == "q4" else 1.0, c_ratio=q4 if cfg["kv"] == "q4" else 1.0)
+    base = P.mi355x(host_gb * 1e9)
+    mc = P.Machine(**{**base.__dict__, "cap_g": gpu_gb * 1e9})
+    best = P.search(wl, mc, gbs_list=(16, 32, 48, 64), nb_max=8,
+                    limits=P.executor_limits(cfg["w"] == "f16"))
+    if best is None:
+        raise SystemExit(f"policy: no placement of {cfg['workload']} fits {gpu_gb} GB of HBM and "
+                         f"{host_gb} GB of host memory")
+    gbs, nb = best["gbs"], best["num_gpu_batches"]
+    r = P.realize(wl, best["shares"], nb)
+    est = P.estimate(wl, mc, gbs * nb, gbs, r["shares"])
+    fits = est["peak"]["g"] * mc.alpha_g <= mc.cap_g and est["peak"]["c"] <= mc.cap_c
+    block = {"gpu_mem_gb": gpu_gb, "host_mem_gb": host_gb, "search": "gbs {16,32,48,64} x nb 1..8",
+             "gbs": gbs, "num_gpu_batches": nb, "bls": gbs * nb,
+             "lp_shares": {k: round(v, 4) for k, v in best["shares"].items()},
+             "realized_shares": {k: round(v, 4) for k, v in r["shares"].items()},
+             "tiered_layers": r["n_tiered"], "kv_host_gpu_batches": r["kv_host_batches"],
+             "realized_fits_budgets": bool(fits),
+             "predicted_ms_per_step": round(est["T_gen"] * wl.l * 1e3, 2),
+             "predicted_prefill_s": round(est["T_pre"] * wl.l, 3),
+             "predicted_peak_gb": {k: round(v / 1e9, 2) for k, v in est["peak"].items()}}
+    over = dict(gbs=gbs, nb=nb, tier_layers=r["tiered_layers"], tier=False,
+                kv_host_seqs=r["kv_host_batches"] * gbs)
+    return over, block
 
 
 def main():
@@ -297,6 +481,11 @@ def main():
     ap.add_argument("--config", type=int, default=5, choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true", help="time without per-kernel events")
+    ap.add_argument("--policy", choices=("auto",), default=None,
+                    help="choose gbs, GPU batches and host shares with the cost model's LP search")
+    ap.add_argument("--gpu-mem-gb", type=float, default=288.0, help="HBM budget of --policy auto")
+    ap.add_argument("--host-mem-gb", type=float, default=64.0,
+                    help="pinned host memory budget of --policy auto")
     ap.add_argument("--profile-layer", type=int, default=0, metavar="R",
                     help="counter-collection driver: one layer of the config (prefilled to s), "
                          "R decode steps, then a 1 GiB device copy that calibrates byte counters")
@@ -320,13 +509,30 @@ def main():
         profile_layer(cfg, args.profile_layer)
         return
     K, Wm = args.steps, args.warmup
+    policy_block = None
+    if args.policy:
+        over, policy_block = plan_policy(cfg, args.gpu_mem_gb, args.host_mem_gb)
+        cfg.update(over)
+        cfg["workload"] += (f", placement chosen by the policy search for {args.gpu_mem_gb:g} GB of "
+                            f"HBM and {args.host_mem_gb:g} GB of host memory")
+        log(f"policy: {json.dumps(policy_block)}")
     bls, s, n = cfg["gbs"] * cfg["nb"], cfg["s"], cfg["n"]
     torch.cuda.set_device(0)
+    # capacity pre-check before anything of the model is allocated: the
+    # policy's HBM budget, else the device's free memory
+    n_tiered = len(set(cfg.get("tier_layers") or ())) if cfg.get("tier_layers") is not None else \
+        (cfg["l"] if cfg.get("tier") else 0)
+    fmt_of = lambda f: L.FG_FMT_Q4G64 if f == "q4" else L.FG_FMT_F16  # noqa: E731
+    max_len = s + max(n, K + 1, Wm + 1)
+    kv_host = cfg.get("kv_host_seqs", 0)
+    L.fg_check_capacity(L.dims(cfg["h1"], cfg["h2"], cfg["nh"], cfg["hd"]),
+                        L.plan(cfg["l"], fmt_of(cfg["w"]), fmt_of(cfg["kv"]), max_len, bls - kv_host,
+                               cfg["gbs"], s, synth.VOCAB, n_tiered=n_tiered, bls_host=kv_host),
+                        int(args.gpu_mem_gb * 1e9) if args.policy else 0)
     want_cpu = not args.no_cpu_baseline
     t_build = time.time()
     log(f"building {cfg['workload']} ({cfg['l']} layers, bls {bls})")
     sh, layers, tier, emb, host0, quant, fmt = build_model(cfg, want_cpu)
-    max_len = s + max(n, K + 1, Wm + 1)
     model = Model(sh, layers, emb, fmt(cfg["kv"]), bls, max_len, tier=tier,
                   kv_host_seqs=cfg.get("kv_host_seqs", 0))
     tokens = synth.tokens(bls, s, seed=0, device="cuda")
@@ -441,6 +647,11 @@ def main():
                           "metadata into a device slot (copy stream); stores: the appended rows "
                           "back (their own stream); overlap = max(load busy time, GEMM + "
                           "attention time) / step time"}
+    if policy_block is not None:
+        policy_block["measured_ms_per_step"] = out["ms_per_step"]
+        policy_block["measured_prefill_s"] = round(t_prefill, 3)
+        policy_block["measured_over_predicted"] = round(out["ms_per_step"] / policy_block["predicted_ms_per_step"], 3)
+        out["policy"] = policy_block
     if quant:
         out["weight_quant"] = {"GB/s": round(quant["bytes"] / (quant["ms"] / 1e3) / 1e9, 1),
                                "frac": round(quant["bytes"] / (quant["ms"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -448,8 +659,15 @@ def main():
     if want_cpu:
         del model, layers, tier
         torch.cuda.empty_cache()
+        gpu_units = {
+            "config1_s": gpu_config1(),
+            "quant_layer_s": quant["ms"] / 1e3 / cfg["l"] if quant else None,
+            "attn_layer_s": (tr[attn_kind]["ms"] / tr[attn_kind]["count"] / 1e3) if attn_kind in tr else None,
+            "layer_decode_s": t_dec / K / cfg["l"],
+            "prefill_layer_2seq_s": t_prefill / cfg["l"] * 2 / bls,
+        }
         log("cpu baseline (oracle) ...")
-        out["cpu_baseline"] = cpu_baseline(cfg, host0, emb)
+        out["cpu_baseline"] = cpu_baseline(cfg, host0, emb, gpu_units)
     print(json.dumps(out), flush=True)
 
 

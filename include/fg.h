@@ -369,6 +369,40 @@ int64_t fg_weight_bytes(const fg_dims* d, int32_t n_layers, int32_t fmt);
 int64_t fg_kv_bytes(const fg_dims* d, int32_t n_layers, int32_t bls, int32_t s, int32_t n,
                     int32_t fmt);
 
+/* ------------------------------------------------------------ capacity */
+/*
+ * Placement of a whole model on one GPU, for the capacity pre-check.  The
+ * block schedule keeps every layer's weights and the whole block's KV cache
+ * alive for the run, so the block is bounded by memory ([P2] "FlexGen 的核心:
+ * 计算图分块与张量生命周期": the peak holds the weights in use, the block's
+ * activations and the block's cache at s + n positions, which bounds bls).
+ *   n_layers, fmt_w:  the decoder's layers and their weight format;
+ *   n_tiered:         fp16 layers whose W_Q, W_K rows and W_1 live in pinned
+ *                     host memory (staged through two device stage buffers);
+ *   fmt_kv, max_len:  cache format and positions allocated per sequence;
+ *   bls_dev:          sequences whose cache is in HBM;
+ *   bls_host, gbs:    sequences whose cache is in pinned host memory (whole
+ *                     GPU batches of gbs, moved through two device slots);
+ *                     gbs also sizes the prefill's workspace;
+ *   s:                prompt length (the block's prompt activations);
+ *   vocab:            rows of the tied embedding (and the LM head's logits).
+ */
+typedef struct {
+    int32_t n_layers, fmt_w, n_tiered, fmt_kv, max_len, bls_dev, bls_host, gbs, s;
+    int64_t vocab;
+} fg_plan;
+/* Device bytes the plan keeps in HBM: device-resident weights, biases and
+ * LayerNorms, stage buffers, the device cache, KV tier slots, the larger of
+ * the prefill and decode workspaces (with the LM head's), the embeddings, the
+ * block's prompt activations and the logits.  -1 on an invalid plan (detail
+ * in fg_last_error). */
+int64_t fg_plan_device_bytes(const fg_dims* d, const fg_plan* p);
+/* FG_OK if fg_plan_device_bytes fits budget_bytes, or the device's free
+ * memory (hipMemGetInfo on the current device) when budget_bytes is 0;
+ * FG_ERR_CAPACITY otherwise, with the byte breakdown in fg_last_error.  Meant
+ * to run before anything of the model is allocated; it allocates nothing. */
+int fg_check_capacity(const fg_dims* d, const fg_plan* p, int64_t budget_bytes);
+
 /* --------------------------------------------------------------- tracing */
 /*
  * Per-kernel timing for roofline reports.  While enabled, each kernel launch

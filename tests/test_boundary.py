@@ -251,3 +251,71 @@ def test_kv_tier_rejects_bad_geometry(L):
     t = L.KvTier(None, None, 1)
     assert g(None, ctypes.byref(d), 1, ws, None, kvs, V(p), 2, 3, 3, V(p), need, None, None, 0, 0,
              ctypes.byref(t)) == L.FG_ERR_INVALID                        # no host cache array
+
+
+# ------------------------------------------------------------ capacity
+def _plan175(L, bls_dev=144, **kw):
+    args = dict(n_layers=96, fmt_w=L.FG_FMT_Q4G64, fmt_kv=L.FG_FMT_Q4G64, max_len=544,
+                bls_dev=bls_dev, gbs=48, s=512, vocab=50272)
+    args.update(kw)
+    return L.dims(12288, 49152, 96, 128), L.plan(**args)
+
+
+def test_plan_bytes_add_up(L):
+    """The plan's device bytes are the closed-form weights and cache plus the
+    stated extras: weight tiering moves 2 h1^2 + h1 h2 fp16 elements per
+    tiered layer to the host and adds two stage buffers; host-resident GPU
+    batches leave the device cache and add two slots."""
+    d, p = _plan175(L)
+    total = L.fg_plan_device_bytes(d, p)
+    w = L.fg_weight_bytes(d, 96, L.FG_FMT_Q4G64)
+    kv = L.fg_kv_bytes(d, 96, 144, 544, 0, L.FG_FMT_Q4G64)
+    assert w + kv < total < w + kv + 16e9             # workspaces, embeddings, activations
+    # more sequences cost at least their cache
+    d, p2 = _plan175(L, bls_dev=145)
+    assert L.fg_plan_device_bytes(d, p2) - total >= kv // 144
+    # fp16, tiering of 40 of 96 layers
+    f16 = dict(fmt_w=L.FG_FMT_F16)
+    d, pa = _plan175(L, **f16)
+    d, pb = _plan175(L, n_tiered=40, **f16)
+    h1, h2 = 12288, 49152
+    assert L.fg_plan_device_bytes(d, pa) - L.fg_plan_device_bytes(d, pb) == \
+        40 * 2 * (2 * h1 * h1 + h1 * h2) - 2 * L.fg_stage_bytes(d)
+    # one of three GPU batches' cache on the host
+    d, pc = _plan175(L, bls_dev=96, bls_host=48)
+    assert L.fg_plan_device_bytes(d, p) - L.fg_plan_device_bytes(d, pc) == \
+        kv // 3 - 2 * L.fg_kvtier_slot_bytes(d, 48, 544, L.FG_FMT_Q4G64)
+
+
+def test_capacity_check_rejects_before_allocating(L):
+    """The OPT-175B-shape 4-bit block (bls 48 x 3) fits 288 GB of HBM; with
+    fp16 weights (348 GB) it does not, and neither does a 4-bit block of
+    bls 512 (its 370 GB of cache); the refusal names the breakdown."""
+    d, p = _plan175(L)
+    L.fg_check_capacity(d, p, int(288e9))
+    d, pf = _plan175(L, fmt_w=L.FG_FMT_F16)
+    with pytest.raises(L.FgError) as e:
+        L.fg_check_capacity(d, pf, int(288e9))
+    assert e.value.status == L.FG_ERR_CAPACITY and "weights" in str(e.value)
+    d, pb = _plan175(L, bls_dev=512)
+    with pytest.raises(L.FgError) as e:
+        L.fg_check_capacity(d, pb, int(288e9))
+    assert e.value.status == L.FG_ERR_CAPACITY and "KV" in str(e.value)
+    # fp16 with every layer's host half in pinned memory still misses by a few
+    # GB; one of the three GPU batches' cache on the host as well fits
+    d, pt = _plan175(L, fmt_w=L.FG_FMT_F16, n_tiered=96)
+    with pytest.raises(L.FgError):
+        L.fg_check_capacity(d, pt, int(288e9))
+    d, pt = _plan175(L, fmt_w=L.FG_FMT_F16, n_tiered=96, bls_dev=96, bls_host=48)
+    L.fg_check_capacity(d, pt, int(288e9))
+
+
+def test_capacity_check_rejects_bad_plans(L):
+    d, p = _plan175(L, fmt_w=L.FG_FMT_Q4G64, n_tiered=2)
+    with pytest.raises(L.FgError) as e:
+        L.fg_check_capacity(d, p, int(288e9))
+    assert e.value.status == L.FG_ERR_INVALID and "fp16" in str(e.value)
+    d, p = _plan175(L, bls_dev=100, bls_host=20)
+    with pytest.raises(L.FgError) as e:
+        L.fg_check_capacity(d, p, int(288e9))
+    assert e.value.status == L.FG_ERR_INVALID and "whole GPU batches" in str(e.value)

@@ -255,3 +255,34 @@ def test_search_picks_a_feasible_best_policy(pol):
         for nb in range(1, 9):
             _, v = pol.solve(wl, mc, gbs * nb, gbs)
             assert best["seconds_per_sequence"] <= v * (1 + 1e-9)
+
+
+def test_executor_realization_rounds_up_and_stays_feasible(pol):
+    """The LP under the executor's limits (activations on the GPU, at most
+    half of an fp16 layer off it) and its realization: whole tiered layers
+    and whole host-resident GPU batches, rounded up from the LP's shares, so
+    the GPU holds no more than the LP placed there; the realized placement
+    costs at least the LP optimum."""
+    wl = pol.Workload(48, 7168, 28672, 512, 32, w_ratio=1.0, c_ratio=pol.Q4G64)
+    base = pol.mi355x(32e9)
+    mc = pol.Machine(**{**base.__dict__, "cap_g": 56e9})
+    best = pol.search(wl, mc, gbs_list=(16, 32), nb_max=6, limits=pol.executor_limits(True))
+    assert best is not None
+    sh = best["shares"]
+    assert sh["hg"] == pytest.approx(1.0) and sh["wc"] <= 0.5 + 1e-9 and sh["wd"] == pytest.approx(0.0)
+    nb = best["num_gpu_batches"]
+    r = pol.realize(wl, sh, nb)
+    rs = r["shares"]
+    assert rs["wc"] >= sh["wc"] - 1e-9 and rs["cc"] >= sh["cc"] - 1e-9
+    assert r["n_tiered"] == len(r["tiered_layers"]) and rs["wc"] == r["n_tiered"] / (2 * wl.l)
+    assert rs["cc"] == r["kv_host_batches"] / nb
+    gaps = np.diff(r["tiered_layers"])
+    assert len(gaps) == 0 or gaps.max() - gaps.min() <= 1          # evenly spaced
+    est = pol.estimate(wl, mc, best["bls"], best["gbs"], rs)
+    assert est["T"] / best["bls"] >= best["seconds_per_sequence"] * (1 - 1e-9)
+    lp = pol.estimate(wl, mc, best["bls"], best["gbs"], sh)
+    assert est["peak"]["g"] <= lp["peak"]["g"] + 1e-3
+    # 4-bit weights never leave the GPU under the executor's limits
+    wq = pol.Workload(48, 7168, 28672, 512, 32, w_ratio=pol.Q4G64, c_ratio=pol.Q4G64)
+    bq = pol.search(wq, mc, gbs_list=(16,), nb_max=4, limits=pol.executor_limits(False))
+    assert bq is not None and bq["shares"]["wc"] == pytest.approx(0.0)

@@ -60,6 +60,12 @@ class TierW(ctypes.Structure):
     _fields_ = [("qk_host", P), ("v_dev", P), ("w1_host", P)]
 
 
+class Plan(ctypes.Structure):
+    """fg_plan: a model's placement on one GPU (capacity pre-check)."""
+    _fields_ = [(n, I32) for n in ("n_layers", "fmt_w", "n_tiered", "fmt_kv", "max_len", "bls_dev",
+                                   "bls_host", "gbs", "s")] + [("vocab", I64)]
+
+
 FG_SCHED_FIRST_STAGED, FG_SCHED_STAGE_NEXT = 1, 2
 
 
@@ -105,6 +111,8 @@ _PROTOS = {
     "fg_kvtier_destroy": (ctypes.c_int, [P]),
     "fg_weight_bytes": (I64, [ctypes.POINTER(Dims), I32, I32]),
     "fg_kv_bytes": (I64, [ctypes.POINTER(Dims), I32, I32, I32, I32, I32]),
+    "fg_plan_device_bytes": (I64, [ctypes.POINTER(Dims), ctypes.POINTER(Plan)]),
+    "fg_check_capacity": (ctypes.c_int, [ctypes.POINTER(Dims), ctypes.POINTER(Plan), I64]),
     "fg_trace_enable": (ctypes.c_int, [ctypes.c_int]),
     "fg_trace_kinds": (ctypes.c_int, [ctypes.c_uint64]),
     "fg_trace_collect": (ctypes.c_int, [I32, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_double),
@@ -321,13 +329,31 @@ def fg_kv_bytes(d: Dims, n_layers, bls, s, n, fmt) -> int:
     return _L.fg_kv_bytes(ctypes.byref(d), n_layers, bls, s, n, fmt)
 
 
+def plan(n_layers, fmt_w, fmt_kv, max_len, bls_dev, gbs, s, vocab, n_tiered=0, bls_host=0) -> Plan:
+    return Plan(n_layers, fmt_w, n_tiered, fmt_kv, max_len, bls_dev, bls_host, gbs, s, vocab)
+
+
+def fg_plan_device_bytes(d: Dims, p: Plan) -> int:
+    v = _L.fg_plan_device_bytes(ctypes.byref(d), ctypes.byref(p))
+    if v < 0:
+        raise FgError("fg_plan_device_bytes", FG_ERR_INVALID, last_error())
+    return v
+
+
+def fg_check_capacity(d: Dims, p: Plan, budget_bytes: int = 0):
+    """Raises FgError (FG_ERR_CAPACITY) when the plan does not fit the budget
+    (0: the device's free memory)."""
+    _check("fg_check_capacity", _L.fg_check_capacity(ctypes.byref(d), ctypes.byref(p), int(budget_bytes)))
+
+
 def fg_trace_enable(on: bool):
     _check("fg_trace_enable", _L.fg_trace_enable(int(on)))
 
 
 TRACE_KINDS = ["quant_g4", "dequant_g4", "gemm_q4", "gemm_f16", "splitk_reduce", "attn_decode_q4",
                "attn_decode_f16", "kv_store", "attn_prefill", "layernorm", "embed", "argmax",
-               "reduce_layernorm", "attn_topk_q4", "attn_topk_f16", "kv_h2d", "kv_d2h", "w_h2d"]
+               "reduce_layernorm", "attn_topk_q4", "attn_topk_f16", "kv_h2d", "kv_d2h", "w_h2d",
+               "proj_qkv", "proj_out", "proj_fc1", "proj_fc2"]
 
 
 def fg_trace_kinds(names=None):

@@ -92,6 +92,9 @@ struct LinearArgs {
     const __half* ln_g;
     const __half* ln_b;
     __half* ln_y;
+    // optional: which projection of a decoder layer this is (1 QKV, 2 out,
+    // 3 FC1, 4 FC2; 0 none), traced as a kind of its own beside the GEMM's
+    int32_t proj;
 };
 int launch_linear(const LinearArgs& a, hipStream_t st);
 size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t fmt);

@@ -10,7 +10,8 @@ namespace fg {
 enum TraceKind {
     TK_QUANT = 0, TK_DEQUANT, TK_GEMM_Q4, TK_GEMM_F16, TK_SPLITK_REDUCE, TK_ATTN_DECODE_Q4,
     TK_ATTN_DECODE_F16, TK_KV_STORE, TK_ATTN_PREFILL, TK_LAYERNORM, TK_EMBED, TK_ARGMAX,
-    TK_REDUCE_LN, TK_ATTN_TOPK_Q4, TK_ATTN_TOPK_F16, TK_KV_H2D, TK_KV_D2H, TK_W_H2D, TK_COUNT
+    TK_REDUCE_LN, TK_ATTN_TOPK_Q4, TK_ATTN_TOPK_F16, TK_KV_H2D, TK_KV_D2H, TK_W_H2D,
+    TK_PROJ_QKV, TK_PROJ_OUT, TK_PROJ_FC1, TK_PROJ_FC2, TK_COUNT
 };
 
 bool trace_on();

@@ -65,6 +65,7 @@ int launch_linear(const LinearArgs& a, hipStream_t st) {
     if (sc.slots > 1) FG_TRY(need_ws((size_t)sc.slots * a.M * a.N * sizeof(float)));
     {
         TraceScope ts(q4 ? TK_GEMM_Q4 : TK_GEMM_F16, st, 2 * Md * Nd * Kd, gbytes);
+        TraceScope tp(a.proj >= 1 && a.proj <= 4 ? TK_PROJ_QKV + a.proj - 1 : -1, st, 2 * Md * Nd * Kd, gbytes);
         FG_TRY(launch_sk(p, sc, q4, st));
     }
     if (sc.slots > 1 && a.ln_y) {

@@ -94,6 +94,7 @@ int lin(const fg_layer_w* w, int which, const __half* x, int64_t M, int64_t K, i
     if (dq & (1 << which)) a.fmt = FG_FMT_F16;   // restored to fp16 for this call
     a.residual = res; a.y = y; a.ldy = N; a.ws = part; a.ws_bytes = part_bytes;
     a.ln_g = (const __half*)ln_g; a.ln_b = (const __half*)ln_b; a.ln_y = ln_y;
+    a.proj = which + 1;
     switch (which) {
         case 0: a.w = w->w_qkv; a.meta = (const __half*)w->m_qkv; a.bias = (const __half*)w->b_qkv; break;
         case 1: a.w = w->w_o; a.meta = (const __half*)w->m_o; a.bias = (const __half*)w->b_o; break;

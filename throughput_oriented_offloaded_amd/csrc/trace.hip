@@ -42,14 +42,15 @@ hipEvent_t take() {
 const char* kNames[TK_COUNT] = {
     "quant_g4", "dequant_g4", "gemm_q4", "gemm_f16", "splitk_reduce", "attn_decode_q4",
     "attn_decode_f16", "kv_store", "attn_prefill", "layernorm", "embed", "argmax",
-    "reduce_layernorm", "attn_topk_q4", "attn_topk_f16", "kv_h2d", "kv_d2h", "w_h2d"};
+    "reduce_layernorm", "attn_topk_q4", "attn_topk_f16", "kv_h2d", "kv_d2h", "w_h2d",
+    "proj_qkv", "proj_out", "proj_fc1", "proj_fc2"};
 
 }  // namespace
 
 bool trace_on() { return g_on; }
 
 TraceScope::TraceScope(int kind, hipStream_t st, double flops, double bytes) {
-    if (!g_on || !((g_mask >> kind) & 1ull)) return;
+    if (kind < 0 || kind >= TK_COUNT || !g_on || !((g_mask >> kind) & 1ull)) return;
     std::lock_guard<std::mutex> lk(g_mu);
     if (!g_on) return;
     Rec r{kind, take(), take(), flops, bytes};

@@ -157,8 +157,11 @@ def estimate(wl: Workload, mc: Machine, bls: int, gbs: int, shares: dict) -> dic
     return res
 
 
-def solve(wl: Workload, mc: Machine, bls: int, gbs: int):
-    """Best shares for fixed (bls, gbs): (shares, T / bls) or (None, inf)."""
+def solve(wl: Workload, mc: Machine, bls: int, gbs: int, limits: dict | None = None):
+    """Best shares for fixed (bls, gbs): (shares, T / bls) or (None, inf).
+    limits: optional {share: (low, high)} bounds, e.g. what an executor can
+    realize (activations kept on the GPU, at most half of a layer's weights
+    off it)."""
     from scipy.optimize import linprog
     co = _affine(wl, mc, bls, gbs)
     nv = 11                                   # nine shares, z_pre, z_gen
@@ -185,8 +188,11 @@ def solve(wl: Workload, mc: Machine, bls: int, gbs: int):
     cost = np.zeros(nv)
     cost[9] = wl.l / bls
     cost[10] = wl.l * (wl.n - 1) / bls
+    bounds = [(0.0, 1.0)] * 9 + [(0, None)] * 2
+    for k, (lo, hi) in (limits or {}).items():
+        bounds[SHARES.index(k)] = (lo, hi)
     r = linprog(cost, A_ub=np.array(rows), b_ub=np.array(rhs), A_eq=A_eq, b_eq=np.ones(3),
-                bounds=[(0, 1)] * 9 + [(0, None)] * 2, method="highs")
+                bounds=bounds, method="highs")
     if r.status != 0:
         return None, float("inf")
     f = np.clip(r.x[:9], 0.0, 1.0) + 0.0      # (+ 0.0: no negative zeros)
@@ -196,12 +202,12 @@ def solve(wl: Workload, mc: Machine, bls: int, gbs: int):
 
 
 def search(wl: Workload, mc: Machine, gbs_list=(8, 16, 24, 32, 48, 64, 96, 128, 192, 256),
-           nb_max: int = 64):
+           nb_max: int = 64, limits: dict | None = None):
     """The (gbs, nb, shares) of least T / bls over gbs_list x 1..nb_max."""
     best = None
     for gbs in gbs_list:
         for nb in range(1, nb_max + 1):
-            shares, v = solve(wl, mc, gbs * nb, gbs)
+            shares, v = solve(wl, mc, gbs * nb, gbs, limits)
             if shares is not None and (best is None or v < best[3]):
                 best = (gbs, nb, shares, v)
     if best is None:
@@ -209,6 +215,30 @@ def search(wl: Workload, mc: Machine, gbs_list=(8, 16, 24, 32, 48, 64, 96, 128, 
     gbs, nb, shares, v = best
     return {"gbs": gbs, "num_gpu_batches": nb, "bls": gbs * nb, "shares": shares,
             "seconds_per_sequence": v, **estimate(wl, mc, gbs * nb, gbs, shares)}
+
+
+def executor_limits(fp16_weights: bool) -> dict:
+    """Shares this package's executor can realize on one GPU: activations stay
+    in HBM; weights go to pinned host memory only for fp16 layers and only
+    their W_Q, W_K rows and W_1 (half of a layer); no disk tier."""
+    lim = {"hg": (1.0, 1.0), "hc": (0.0, 0.0), "hd": (0.0, 0.0), "wd": (0.0, 0.0), "cd": (0.0, 0.0)}
+    lim["wc"] = (0.0, 0.5) if fp16_weights else (0.0, 0.0)
+    return lim
+
+
+def realize(wl: Workload, shares: dict, nb: int) -> dict:
+    """The executor's placement nearest above an LP solution: the weight share
+    off the GPU rounded up to whole tiered layers (each moves half a layer),
+    the cache share rounded up to whole GPU batches.  Returns the number of
+    tiered layers, the layers themselves (evenly spaced), the host-resident
+    GPU batches and the realized shares."""
+    n_tiered = min(wl.l, int(np.ceil(shares["wc"] * 2 * wl.l - 1e-9)))
+    nb_host = min(nb, int(np.ceil(shares["cc"] * nb - 1e-9)))
+    layers = [j for j in range(wl.l) if (j + 1) * n_tiered // wl.l > j * n_tiered // wl.l]
+    sh = {"wg": 1 - n_tiered / (2 * wl.l), "wc": n_tiered / (2 * wl.l), "wd": 0.0,
+          "hg": 1.0, "hc": 0.0, "hd": 0.0,
+          "cg": 1 - nb_host / nb, "cc": nb_host / nb, "cd": 0.0}
+    return {"n_tiered": n_tiered, "tiered_layers": layers, "kv_host_batches": nb_host, "shares": sh}
 
 
 def main(argv=None):
