@@ -196,6 +196,25 @@ int fg_linear(const void* x, int64_t M, int64_t K, int32_t fmt, const void* w, c
               void* ws, size_t ws_bytes, void* stream);
 size_t fg_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+/*
+ * fg_linear without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, layout, results and errors as
+ * fg_linear minus ws / ws_bytes.  The split-k partials live in a device
+ * array of fg_linear_noalloc_max_bytes() (96 MiB) that the library holds on
+ * each GPU it runs on until the process ends; shapes whose partials
+ * (fg_linear_workspace_bytes) exceed it are refused with
+ * FG_ERR_UNSUPPORTED.  No part of the array needs to start at zero: every
+ * partial a call reads was written earlier in the same call.  All calls on
+ * one GPU share its array, so calls that overlap on that GPU (concurrent
+ * streams, threads) race; calls ordered on one stream do not.  Allocates
+ * nothing on the host or the device.
+ */
+size_t fg_linear_noalloc_max_bytes(void);
+int fg_linear_noalloc(const void* x, int64_t M, int64_t K, int32_t fmt, const void* w, const void* m,
+                      int64_t N, const void* bias, int32_t act, const void* residual, void* y,
+                      void* stream);
+
 /* Row LayerNorm over the last dim h (biased variance, eps 1e-5):
  * y = (x - mean) / sqrt(var + eps) * gamma + beta.  x, y fp16 [rows, h]. */
 int fg_layernorm(const void* x, int64_t rows, int64_t h, const void* gamma, const void* beta,

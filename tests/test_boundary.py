@@ -319,3 +319,18 @@ def test_capacity_check_rejects_bad_plans(L):
     with pytest.raises(L.FgError) as e:
         L.fg_check_capacity(d, p, int(288e9))
     assert e.value.status == L.FG_ERR_INVALID and "whole GPU batches" in str(e.value)
+
+
+def test_linear_noalloc_refuses_shapes_beyond_its_array(L):
+    """fg_linear_noalloc keeps its split-k partials in a device array of
+    fg_linear_noalloc_max_bytes(); a shape needing more is refused on the
+    host, before any launch (the pointers are never dereferenced)."""
+    M, N, K = 144, 98304, 12288
+    cap = L._L.fg_linear_noalloc_max_bytes()
+    assert cap == 96 << 20
+    assert L.fg_linear_workspace_bytes(M, N, K) > cap
+    p = ctypes.c_void_p(1 << 20)
+    st, msg = _bad(L, "fg_linear_noalloc", p, M, K, L.FG_FMT_Q4G64, p, p, N, None, 0, None, p, None)
+    assert st == L.FG_ERR_UNSUPPORTED and "scratch" in msg
+    st, msg = _bad(L, "fg_linear_noalloc", None, M, K, L.FG_FMT_Q4G64, p, p, N, None, 0, None, p, None)
+    assert st == L.FG_ERR_INVALID

@@ -88,6 +88,8 @@ _PROTOS = {
     "fg_attn_prefill": (ctypes.c_int, [P, I32, I32, ctypes.POINTER(Dims), P, P]),
     "fg_linear": (ctypes.c_int, [P, I64, I64, I32, P, P, I64, P, I32, P, P, P, SZ, P]),
     "fg_linear_workspace_bytes": (SZ, [I64, I64, I64]),
+    "fg_linear_noalloc": (ctypes.c_int, [P, I64, I64, I32, P, P, I64, P, I32, P, P, P]),
+    "fg_linear_noalloc_max_bytes": (SZ, []),
     "fg_layernorm": (ctypes.c_int, [P, I64, I64, P, P, P, P]),
     "fg_embed": (ctypes.c_int, [P, P, I64, P, I64, P, I64, I64, P, P]),
     "fg_argmax": (ctypes.c_int, [P, I64, I64, P, P]),
@@ -228,6 +230,12 @@ def fg_linear_workspace_bytes(M, N, K) -> int:
 def fg_linear(x, M, K, fmt, w, m, N, bias, act, residual, y, ws=None, ws_bytes=0, stream=None):
     _check("fg_linear", _L.fg_linear(ptr(x), M, K, fmt, ptr(w), ptr(m), N, ptr(bias), act,
                                      ptr(residual), ptr(y), ptr(ws), ws_bytes, stream_ptr(stream)))
+
+
+def fg_linear_noalloc(x, M, K, fmt, w, m, N, bias, act, residual, y, stream=None):
+    """fg_linear with its partials in the library's own device array (no workspace)."""
+    _check("fg_linear_noalloc", _L.fg_linear_noalloc(ptr(x), M, K, fmt, ptr(w), ptr(m), N, ptr(bias), act,
+                                                     ptr(residual), ptr(y), stream_ptr(stream)))
 
 
 def fg_layernorm(x, rows, h, gamma, beta, y, stream=None):
