@@ -62,6 +62,8 @@ int launch_linear(const LinearArgs& a, hipStream_t st) {
         return a.ln_y ? launch_layernorm(a.y, a.M, a.N, a.ln_g, a.ln_b, a.ln_y, st) : FG_OK;
     }
     const SkSched sc = sk_schedule(a.M, a.N, a.K);
+    if (!sc.dp && sc.T >= (1ll << 31))
+        return set_error(FG_ERR_UNSUPPORTED, "decode GEMM: %lld (tile, k-step) iterations", (long long)sc.T);
     if (sc.slots > 1) FG_TRY(need_ws((size_t)sc.slots * a.M * a.N * sizeof(float)));
     {
         TraceScope ts(q4 ? TK_GEMM_Q4 : TK_GEMM_F16, st, 2 * Md * Nd * Kd, gbytes);

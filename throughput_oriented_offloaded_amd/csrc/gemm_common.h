@@ -143,7 +143,8 @@ __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, const vo
 #pragma clang diagnostic pop
 
 // Stream-K schedule of the decode-shaped kernel (gemm_sk.hip): T = tiles x nk
-// iterations (tile, 64-wide k-step) split evenly over G workgroups.
+// iterations (tile, 64-wide k-step) split over G workgroups, workgroup g
+// taking the contiguous range [bnd[g], bnd[g+1]).
 constexpr int kSkGroups = 256;   // one workgroup per CU of the 256-CU part
 constexpr int64_t kSkDpRows = 576;   // above: data-parallel whole tiles (prefill shapes)
 struct SkSched {
@@ -154,6 +155,16 @@ struct SkSched {
     int32_t dp;           // 1: data-parallel, whole tiles g, g + G, ... (large M)
     int64_t tiles, mt;    // output tiles; M tiles
     int64_t band;         // dp: M tiles per band of the tile order
+    // stream-K: iteration ranges balanced by time rather than by count: a
+    // workgroup pays a fixed cost per segment (tile) it touches (pipeline
+    // fill, the merge of the k-halves, the tile's stores) on top of its
+    // k-steps, so ranges that cross a tile boundary are made shorter; empty
+    // ranges are allowed
+    int32_t bnd[kSkGroups + 1];
+    // partial slot of workgroup g's first segment (g minus the owner of that
+    // tile's first iteration); every later segment starts at its tile's
+    // first k-step and takes slot 0
+    int16_t slot0[kSkGroups];
 };
 
 // Output tile of linear index `tile`.  Stream-K: row-major (tm, tn).  Data-
@@ -175,9 +186,22 @@ __device__ __host__ __forceinline__ void sk_tile_coords(const SkSched& sc, int64
     tn = r / gm;
 }
 
-// workgroup holding iteration x of T split over G: ceil((x + 1) G / T) - 1
-__device__ __host__ __forceinline__ int64_t sk_owner(int64_t x, int64_t T, int64_t G) {
-    return ((x + 1) * G + T - 1) / T - 1;
+// workgroup holding iteration x < T: the g with bnd[g] <= x < bnd[g + 1]
+// (the last g with bnd[g] <= x, which skips empty ranges)
+__device__ __host__ __forceinline__ int32_t sk_owner_in(const int32_t* bnd, int32_t G, int64_t x) {
+    int32_t lo = 0, hi = G;   // bnd[lo] <= x < bnd[hi]
+    while (hi - lo > 1) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (bnd[mid] <= x) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+inline int32_t sk_owner(const SkSched& sc, int64_t x) { return sk_owner_in(sc.bnd, (int32_t)sc.G, x); }
+// Kernels search a copy of the boundaries in LDS: read from the kernel
+// arguments, each step of the search would be a dependent memory load.
+__device__ __forceinline__ void sk_bnd_to_lds(const SkSched& sc, int32_t* s_bnd) {
+    for (int i = threadIdx.x; i <= (int)sc.G; i += blockDim.x) s_bnd[i] = sc.bnd[i];
 }
 SkSched sk_schedule(int64_t M, int64_t N, int64_t K);
 int launch_sk(const Params& p, const SkSched& sc, bool q4, hipStream_t st);

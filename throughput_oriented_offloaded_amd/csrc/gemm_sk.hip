@@ -37,6 +37,9 @@
 //    covered by one workgroup is written with its epilogue; a tile shared by
 //    several leaves fp32 partials in per-segment slots, summed in segment order
 //    (deterministic) by sk_reduce_kernel.
+#include <mutex>
+#include <unordered_map>
+
 #include "gemm_common.h"
 #include "rowops.h"
 
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(C::NT) void sk_kernel(Params p, SkSched sc) {
     const int r16 = lane & 15, q = lane >> 4;
     const uint32_t shn = (uint32_t)(r16 & 1) * 4u;   // nibble of this lane's weight row
     const int64_t g = blockIdx.x;
-    const int64_t it_beg = g * sc.T / sc.G, it_end = (g + 1) * sc.T / sc.G;
+    const int64_t it_beg = sc.dp ? 0 : sc.bnd[g], it_end = sc.dp ? 0 : sc.bnd[g + 1];
 
     int64_t it = it_beg, next_tile = g;
     for (;;) {
@@ -342,10 +345,17 @@ __global__ __launch_bounds__(C::NT) void sk_kernel(Params p, SkSched sc) {
             Dq S;
             uint32_t wa[4][4], wb[4][4];
             h8 xc[PD];
-#pragma unroll
-            for (int st = 0; st < C::NS; ++st) issue(buf(st), st);
-            __builtin_amdgcn_s_waitcnt(vmcnt_wait(C::LWL * (C::NS - 2)));
+            // stages 0 and 1 first (step 0 computes on 0 and dequantizes 1):
+            // every workgroup of a launch fills its pipeline at once, and
+            // requesting the later stages only after these have landed lets
+            // the first MFMAs start sooner; the loop's waits are unchanged
+            // (the stages are still issued in order)
+            issue(buf(0), 0);
+            issue(buf(1), 1);
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
             __builtin_amdgcn_s_barrier();
+#pragma unroll
+            for (int st = 2; st < C::NS; ++st) issue(buf(st), st);
             {
                 const unsigned char* b0 = buf(0);
                 const uint2 c0[2] = {read_cp(b0, 0), read_cp(b0, 1)};
@@ -452,10 +462,9 @@ __global__ __launch_bounds__(C::NT) void sk_kernel(Params p, SkSched sc) {
         __builtin_amdgcn_s_barrier();
 
         // add the two k-halves (kh = 1 -> LDS -> kh = 0), two fragments per round
-        const int64_t gf = sk_owner(tile * sc.nk, sc.T, sc.G);
-        const int64_t gl = sk_owner((tile + 1) * sc.nk - 1, sc.T, sc.G);
-        const bool full = sc.dp || gf == gl;
-        const int slot = (int)(g - gf);
+        // the whole tile in this segment: final outputs; else its partial slot
+        const bool full = sc.dp || (kb == 0 && ke == (int)sc.nk);
+        const int slot = (sc.dp || kb == 0) ? 0 : (int)sc.slot0[g];
         const int nq = q * 4;
 #pragma unroll
         for (int rd = 0; rd < 2; ++rd) {
@@ -528,12 +537,15 @@ __global__ __launch_bounds__(C::NT) void sk_kernel(Params p, SkSched sc) {
 // ReLU / residual.  Tiles written whole by one workgroup are skipped.
 // Generic form (64-bit indices): any shape.
 __global__ __launch_bounds__(256) void sk_reduce64_kernel(Params p, SkSched sc) {
+    __shared__ int32_t s_bnd[kSkGroups + 1];
+    sk_bnd_to_lds(sc, s_bnd);
+    __syncthreads();
     const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;   // element (m, n..n+3)
     if (idx >= p.M * p.N) return;
     const int64_t m = idx / p.N, n = idx % p.N;
     const int64_t tile = (m / sc.bm) * sc.ntn + n / sc.bn;
-    const int64_t gf = sk_owner(tile * sc.nk, sc.T, sc.G);
-    const int64_t gl = sk_owner((tile + 1) * sc.nk - 1, sc.T, sc.G);
+    const int64_t gf = sk_owner_in(s_bnd, (int32_t)sc.G, tile * sc.nk);
+    const int64_t gl = sk_owner_in(s_bnd, (int32_t)sc.G, (tile + 1) * sc.nk - 1);
     if (gf == gl) return;
     float o[4] = {0.f, 0.f, 0.f, 0.f};
     for (int64_t s = 0; s <= gl - gf; ++s) {
@@ -566,10 +578,13 @@ __global__ __launch_bounds__(256) void sk_reduce_kernel(Params p, SkSched sc) {
     const int m = blockIdx.y;
     const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (n >= p.N) return;
-    const uint32_t T = (uint32_t)sc.T, G = (uint32_t)sc.G, nk = (uint32_t)sc.nk;
-    const uint32_t tile = (uint32_t)(m / (int)sc.bm) * (uint32_t)sc.ntn + (uint32_t)(n >> 8);
-    const uint32_t gf = ((tile * nk + 1) * G + T - 1) / T - 1;           // owner of the tile's first step
-    const uint32_t gl = ((tile + 1) * nk * G + T - 1) / T - 1;           // owner of its last step
+    // one 256-column tile per wavefront: the owner search runs on wave-uniform
+    // values (scalar loads of the boundaries)
+    const uint32_t nk = (uint32_t)sc.nk;
+    const uint32_t tile = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)((uint32_t)(m / (int)sc.bm) * (uint32_t)sc.ntn + (uint32_t)(n >> 8)));
+    const int32_t gf = __builtin_amdgcn_readfirstlane(sk_owner_in(sc.bnd, (int32_t)sc.G, (int64_t)(tile * nk)));
+    const int32_t gl = __builtin_amdgcn_readfirstlane(sk_owner_in(sc.bnd, (int32_t)sc.G, (int64_t)((tile + 1) * nk - 1)));
     if (gf == gl) return;
     const int ns = (int)(gl - gf + 1);
     const int64_t MN = p.M * p.N;
@@ -615,11 +630,15 @@ __global__ __launch_bounds__(kLnThreads) void sk_reduce_ln_kernel(Params p, SkSc
     constexpr int NT = kLnThreads;
     __shared__ float sh[NT / 64];
     __shared__ int s_ns[kLnTiles];   // segments of each column tile of this row
+    __shared__ int32_t s_bnd[kSkGroups + 1];
+    sk_bnd_to_lds(sc, s_bnd);
+    __syncthreads();
     const int64_t m = blockIdx.x;
     const int64_t tm = m / sc.bm;
     for (int t = threadIdx.x; t < sc.ntn; t += NT) {
         const int64_t tile = tm * sc.ntn + t;
-        s_ns[t] = (int)(sk_owner((tile + 1) * sc.nk - 1, sc.T, sc.G) - sk_owner(tile * sc.nk, sc.T, sc.G) + 1);
+        s_ns[t] = (int)(sk_owner_in(s_bnd, (int32_t)sc.G, (tile + 1) * sc.nk - 1) -
+                        sk_owner_in(s_bnd, (int32_t)sc.G, tile * sc.nk) + 1);
     }
     __syncthreads();
     const int nu = (int)(p.N / 4);
@@ -722,6 +741,69 @@ int64_t sk_rows_for(int64_t M, int32_t& wide) {
     return best.bm;
 }
 
+namespace {
+
+// Fills bnd[0..G] so that every workgroup's estimated time, its k-steps plus
+// R k-steps per segment (tile) it touches, is at most tau; false if the T
+// iterations do not fit in G workgroups that way.
+bool sk_fill(SkSched& sc, double tau, double R) {
+    int64_t x = 0;
+    sc.bnd[0] = 0;
+    for (int64_t g = 0; g < sc.G; ++g) {
+        double budget = tau;
+        const int64_t start = x;
+        while (x < sc.T) {
+            const int64_t tile_end = (x / sc.nk + 1) * sc.nk;
+            const double avail = budget - R;   // entering a segment
+            if (avail < 1.0) break;
+            const int64_t take = std::min<int64_t>(tile_end - x, (int64_t)avail);
+            x += take;
+            budget = avail - (double)take;
+            if (x < tile_end) break;           // budget spent inside the tile
+        }
+        if (x == start && x < sc.T && budget == tau) return false;   // not even one k-step fits
+        sc.bnd[g + 1] = (int32_t)x;
+    }
+    return x >= sc.T;
+}
+
+// Time-balanced stream-K ranges: the least tau (bisection) for which the
+// greedy fill covers every iteration.  R, the fixed cost of a segment in
+// k-steps, was measured on gfx950 for 144-row tiles of 4-bit weights (about
+// 13 us of pipeline fill, k-half merge and stores against about 1 us per
+// k-step); tiles of fewer rows have cheaper k-steps, so R grows as 144 / bm.
+void sk_balance(SkSched& sc) {
+    const double R = std::min(48.0, 12.0 * 144.0 / (double)sc.bm);
+    double lo = (double)sc.T / (double)sc.G, hi = (double)sc.T / (double)sc.G + 4.0 * R + (double)sc.nk;
+    while (!sk_fill(sc, hi, R)) hi *= 2.0;
+    for (int i = 0; i < 40 && hi - lo > 0.25; ++i) {
+        const double mid = 0.5 * (lo + hi);
+        if (sk_fill(sc, mid, R)) hi = mid;
+        else lo = mid;
+    }
+    sk_fill(sc, hi, R);
+    // most segments any tile is cut into (1: every workgroup covers whole tiles)
+    sc.slots = 1;
+    for (int64_t t = 0; t < sc.tiles; ++t)
+        sc.slots = std::max<int64_t>(sc.slots, sk_owner(sc, (t + 1) * sc.nk - 1) - sk_owner(sc, t * sc.nk) + 1);
+    for (int64_t g = 0; g < sc.G; ++g) {
+        const int64_t b = sc.bnd[g];
+        sc.slot0[g] = (b >= sc.T || b % sc.nk == 0) ? 0 : (int16_t)(g - sk_owner(sc, b - b % sc.nk));
+    }
+}
+
+struct SkKey {
+    int64_t M, N, K;
+    bool operator==(const SkKey& o) const { return M == o.M && N == o.N && K == o.K; }
+};
+struct SkKeyHash {
+    size_t operator()(const SkKey& k) const {
+        return std::hash<int64_t>()(k.M * 1000003 + k.N * 10007 + k.K);
+    }
+};
+
+}  // namespace
+
 SkSched sk_schedule(int64_t M, int64_t N, int64_t K) {
     SkSched sc{};
     sc.bn = 256;
@@ -740,6 +822,15 @@ SkSched sk_schedule(int64_t M, int64_t N, int64_t K) {
         sc.slots = 1;
         return sc;
     }
+    // the balanced ranges are a pure function of the shape: computed once
+    static std::mutex mu;
+    static std::unordered_map<SkKey, SkSched, SkKeyHash> cache;
+    const SkKey key{M, N, K};
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        auto it = cache.find(key);
+        if (it != cache.end()) return it->second;
+    }
     sc.bm = sk_rows_for(M, sc.wide);
     sc.mt = cdiv(M, sc.bm);
     sc.tiles = sc.mt * sc.ntn;
@@ -747,9 +838,10 @@ SkSched sk_schedule(int64_t M, int64_t N, int64_t K) {
     // one workgroup per CU of the 256-CU part (a constant, so the schedule and
     // its workspace depend on the shape only), at least 4 k-steps each
     sc.G = std::max<int64_t>(1, std::min<int64_t>(kSkGroups, sc.T / 4));
-    // most segments any tile is cut into (1 when every workgroup covers whole tiles)
-    const int64_t per = sc.T / sc.G;   // each workgroup takes per or per + 1 iterations
-    sc.slots = (sc.T % sc.G == 0 && per % sc.nk == 0) ? 1 : cdiv(sc.nk, per) + 1;
+    if (sc.T >= (1ll << 31)) return sc;   // refused by the caller (ranges are 32-bit)
+    sk_balance(sc);
+    std::lock_guard<std::mutex> lk(mu);
+    cache.emplace(key, sc);
     return sc;
 }
 
@@ -775,8 +867,7 @@ int launch_sk(const Params& p, const SkSched& sc, bool q4, hipStream_t st) {
 }
 
 int launch_sk_reduce(const Params& p, const SkSched& sc, hipStream_t st) {
-    const bool fits32 = sc.bn == 256 && p.M <= 65535 && p.N % 4 == 0 &&
-                        ((uint64_t)sc.T + 1) * (uint64_t)sc.G + (uint64_t)sc.T < (1ull << 32);
+    const bool fits32 = sc.bn == 256 && p.M <= 65535 && p.N % 4 == 0 && sc.T < (1ll << 31);
     if (!fits32) {
         const int64_t n4 = p.M * p.N / 4;
         sk_reduce64_kernel<<<(unsigned)cdiv(n4, 256), 256, 0, st>>>(p, sc);

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(C::NT) void sk32_kernel(Params p, SkSched sc) {
     const int r32 = lane & 31, hl = lane >> 5;    // operand row, 8-k half of a k-step
     const uint32_t shn = (uint32_t)(r32 & 1) * 4u;   // nibble of this lane's weight row
     const int64_t g = blockIdx.x;
-    const int64_t it_beg = g * sc.T / sc.G, it_end = (g + 1) * sc.T / sc.G;
+    const int64_t it_beg = sc.bnd[g], it_end = sc.bnd[g + 1];
 
     for (int64_t it = it_beg; it < it_end;) {
         const int64_t tile = it / sc.nk;
@@ -290,10 +290,9 @@ __global__ __launch_bounds__(C::NT) void sk32_kernel(Params p, SkSched sc) {
         __builtin_amdgcn_s_barrier();
 
         // add the two k-halves (kh = 1 -> LDS -> kh = 0), one column block per round
-        const int64_t gf = sk_owner(tile * sc.nk, sc.T, sc.G);
-        const int64_t gl = sk_owner((tile + 1) * sc.nk - 1, sc.T, sc.G);
-        const bool full = gf == gl;
-        const int slot = (int)(g - gf);
+        // the whole tile in this segment: final outputs; else its partial slot
+        const bool full = kb == 0 && ke == (int)sc.nk;
+        const int slot = kb == 0 ? 0 : (int)sc.slot0[g];
         float4* reg = reinterpret_cast<float4*>(buf(wc / C::PER_BUF) + (wc % C::PER_BUF) * C::MERGE);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
