@@ -28,7 +28,7 @@ bool linear_is_dp(int64_t M) { return M > gemm::kSkDpRows; }
 
 size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t) {
     const gemm::SkSched sc = gemm::sk_schedule(M, N, K);
-    return sc.slots > 1 ? (size_t)sc.slots * M * N * sizeof(float) : 0;
+    return gemm::sk_ws_bytes(sc, M, N);
 }
 
 int launch_linear(const LinearArgs& a, hipStream_t st) {
@@ -42,6 +42,7 @@ int launch_linear(const LinearArgs& a, hipStream_t st) {
     p.bias = a.bias; p.act = a.act; p.residual = a.residual;
     p.y = a.y; p.ldy = a.ldy;
     p.part = nullptr;
+    p.tile_ns = nullptr;
     // algorithmic work: 2MNK flops; weights once, activations in, outputs out
     const double Md = (double)p.M, Nd = (double)p.N, Kd = (double)p.K;
     const double wbytes = q4 ? Nd * Kd / 2 + Nd / 64 * Kd * 4 : Nd * Kd * 2;
@@ -50,7 +51,6 @@ int launch_linear(const LinearArgs& a, hipStream_t st) {
         if (!a.ws || a.ws_bytes < need)
             return set_error(FG_ERR_CAPACITY, "linear needs %zu workspace bytes, got %zu", need,
                              a.ws ? a.ws_bytes : (size_t)0);
-        p.part = static_cast<float*>(a.ws);
         return FG_OK;
     };
 
@@ -64,7 +64,11 @@ int launch_linear(const LinearArgs& a, hipStream_t st) {
     const SkSched sc = sk_schedule(a.M, a.N, a.K);
     if (!sc.dp && sc.T >= (1ll << 31))
         return set_error(FG_ERR_UNSUPPORTED, "decode GEMM: %lld (tile, k-step) iterations", (long long)sc.T);
-    if (sc.slots > 1) FG_TRY(need_ws((size_t)sc.slots * a.M * a.N * sizeof(float)));
+    if (sc.slots > 1) {
+        FG_TRY(need_ws(sk_ws_bytes(sc, a.M, a.N)));
+        p.part = static_cast<float*>(a.ws);
+        p.tile_ns = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(a.ws) + sk_part_bytes(sc, a.M, a.N));
+    }
     {
         TraceScope ts(q4 ? TK_GEMM_Q4 : TK_GEMM_F16, st, 2 * Md * Nd * Kd, gbytes);
         TraceScope tp(a.proj >= 1 && a.proj <= 4 ? TK_PROJ_QKV + a.proj - 1 : -1, st, 2 * Md * Nd * Kd, gbytes);

@@ -24,6 +24,8 @@ struct Params {
     __half* y;
     int64_t ldy;
     float* part;         // stream-K partials [slots][M][N] or null
+    int32_t* tile_ns;    // stream-K with partials: segments of each tile [tiles],
+                         // written by the workgroup that ends the tile
 };
 
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
@@ -188,7 +190,7 @@ __device__ __host__ __forceinline__ void sk_tile_coords(const SkSched& sc, int64
 
 // workgroup holding iteration x < T: the g with bnd[g] <= x < bnd[g + 1]
 // (the last g with bnd[g] <= x, which skips empty ranges)
-__device__ __host__ __forceinline__ int32_t sk_owner_in(const int32_t* bnd, int32_t G, int64_t x) {
+inline int32_t sk_owner_in(const int32_t* bnd, int32_t G, int64_t x) {
     int32_t lo = 0, hi = G;   // bnd[lo] <= x < bnd[hi]
     while (hi - lo > 1) {
         const int32_t mid = (lo + hi) >> 1;
@@ -198,10 +200,13 @@ __device__ __host__ __forceinline__ int32_t sk_owner_in(const int32_t* bnd, int3
     return lo;
 }
 inline int32_t sk_owner(const SkSched& sc, int64_t x) { return sk_owner_in(sc.bnd, (int32_t)sc.G, x); }
-// Kernels search a copy of the boundaries in LDS: read from the kernel
-// arguments, each step of the search would be a dependent memory load.
-__device__ __forceinline__ void sk_bnd_to_lds(const SkSched& sc, int32_t* s_bnd) {
-    for (int i = threadIdx.x; i <= (int)sc.G; i += blockDim.x) s_bnd[i] = sc.bnd[i];
+// Bytes of a stream-K launch's workspace: the partials, then (256-byte
+// aligned) the segment count of every tile.
+inline size_t sk_part_bytes(const SkSched& sc, int64_t M, int64_t N) {
+    return (sc.slots * M * N * sizeof(float) + 255) / 256 * 256;
+}
+inline size_t sk_ws_bytes(const SkSched& sc, int64_t M, int64_t N) {
+    return sc.slots > 1 ? sk_part_bytes(sc, M, N) + (size_t)sc.tiles * sizeof(int32_t) : 0;
 }
 SkSched sk_schedule(int64_t M, int64_t N, int64_t K);
 int launch_sk(const Params& p, const SkSched& sc, bool q4, hipStream_t st);

@@ -465,6 +465,8 @@ __global__ __launch_bounds__(C::NT) void sk_kernel(Params p, SkSched sc) {
         // the whole tile in this segment: final outputs; else its partial slot
         const bool full = sc.dp || (kb == 0 && ke == (int)sc.nk);
         const int slot = (sc.dp || kb == 0) ? 0 : (int)sc.slot0[g];
+        // the workgroup that ends a tile records how many segments it has
+        if (p.tile_ns && ke == (int)sc.nk && tid == 0) p.tile_ns[tile] = slot + 1;
         const int nq = q * 4;
 #pragma unroll
         for (int rd = 0; rd < 2; ++rd) {
@@ -537,18 +539,14 @@ __global__ __launch_bounds__(C::NT) void sk_kernel(Params p, SkSched sc) {
 // ReLU / residual.  Tiles written whole by one workgroup are skipped.
 // Generic form (64-bit indices): any shape.
 __global__ __launch_bounds__(256) void sk_reduce64_kernel(Params p, SkSched sc) {
-    __shared__ int32_t s_bnd[kSkGroups + 1];
-    sk_bnd_to_lds(sc, s_bnd);
-    __syncthreads();
     const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;   // element (m, n..n+3)
     if (idx >= p.M * p.N) return;
     const int64_t m = idx / p.N, n = idx % p.N;
     const int64_t tile = (m / sc.bm) * sc.ntn + n / sc.bn;
-    const int64_t gf = sk_owner_in(s_bnd, (int32_t)sc.G, tile * sc.nk);
-    const int64_t gl = sk_owner_in(s_bnd, (int32_t)sc.G, (tile + 1) * sc.nk - 1);
-    if (gf == gl) return;
+    const int ns = p.tile_ns[tile];
+    if (ns == 1) return;                 // whole tile written by one workgroup
     float o[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t s = 0; s <= gl - gf; ++s) {
+    for (int64_t s = 0; s < ns; ++s) {
         const float4 v = *reinterpret_cast<const float4*>(p.part + (s * p.M + m) * p.N + n);
         o[0] += v.x; o[1] += v.y; o[2] += v.z; o[3] += v.w;
     }
@@ -578,15 +576,9 @@ __global__ __launch_bounds__(256) void sk_reduce_kernel(Params p, SkSched sc) {
     const int m = blockIdx.y;
     const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (n >= p.N) return;
-    // one 256-column tile per wavefront: the owner search runs on wave-uniform
-    // values (scalar loads of the boundaries)
-    const uint32_t nk = (uint32_t)sc.nk;
-    const uint32_t tile = (uint32_t)__builtin_amdgcn_readfirstlane(
-        (int)((uint32_t)(m / (int)sc.bm) * (uint32_t)sc.ntn + (uint32_t)(n >> 8)));
-    const int32_t gf = __builtin_amdgcn_readfirstlane(sk_owner_in(sc.bnd, (int32_t)sc.G, (int64_t)(tile * nk)));
-    const int32_t gl = __builtin_amdgcn_readfirstlane(sk_owner_in(sc.bnd, (int32_t)sc.G, (int64_t)((tile + 1) * nk - 1)));
-    if (gf == gl) return;
-    const int ns = (int)(gl - gf + 1);
+    const uint32_t tile = (uint32_t)(m / (int)sc.bm) * (uint32_t)sc.ntn + (uint32_t)(n >> 8);
+    const int ns = p.tile_ns[tile];
+    if (ns == 1) return;                 // whole tile written by one workgroup
     const int64_t MN = p.M * p.N;
     const float* pr = p.part + (int64_t)m * p.N + n;
     f4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -630,16 +622,9 @@ __global__ __launch_bounds__(kLnThreads) void sk_reduce_ln_kernel(Params p, SkSc
     constexpr int NT = kLnThreads;
     __shared__ float sh[NT / 64];
     __shared__ int s_ns[kLnTiles];   // segments of each column tile of this row
-    __shared__ int32_t s_bnd[kSkGroups + 1];
-    sk_bnd_to_lds(sc, s_bnd);
-    __syncthreads();
     const int64_t m = blockIdx.x;
     const int64_t tm = m / sc.bm;
-    for (int t = threadIdx.x; t < sc.ntn; t += NT) {
-        const int64_t tile = tm * sc.ntn + t;
-        s_ns[t] = (int)(sk_owner_in(s_bnd, (int32_t)sc.G, (tile + 1) * sc.nk - 1) -
-                        sk_owner_in(s_bnd, (int32_t)sc.G, tile * sc.nk) + 1);
-    }
+    for (int t = threadIdx.x; t < sc.ntn; t += NT) s_ns[t] = p.tile_ns[tm * sc.ntn + t];
     __syncthreads();
     const int nu = (int)(p.N / 4);
     const int64_t MN = p.M * p.N;

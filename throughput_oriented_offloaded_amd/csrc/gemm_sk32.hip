@@ -293,6 +293,8 @@ __global__ __launch_bounds__(C::NT) void sk32_kernel(Params p, SkSched sc) {
         // the whole tile in this segment: final outputs; else its partial slot
         const bool full = kb == 0 && ke == (int)sc.nk;
         const int slot = kb == 0 ? 0 : (int)sc.slot0[g];
+        // the workgroup that ends a tile records how many segments it has
+        if (p.tile_ns && ke == (int)sc.nk && tid == 0) p.tile_ns[tile] = slot + 1;
         float4* reg = reinterpret_cast<float4*>(buf(wc / C::PER_BUF) + (wc % C::PER_BUF) * C::MERGE);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
