@@ -135,10 +135,11 @@ def test_decode_attention_full_shape_sampled(L):
     _sampled_check(L, "q4", 144, 96, 128, 528, 544, seed=5)
 
 
-@pytest.mark.parametrize("fmt,pos", [("q4", 0), ("q4", 37), ("f16", 61), ("q4", 8300)])
+@pytest.mark.parametrize("fmt,pos", [("q4", 0), ("q4", 37), ("f16", 61), ("q4", 8300), ("f16", 8300),
+                                     ("q4", 1)])
 def test_decode_attention_one_wave_per_head(L, fmt, pos):
-    """2048 (sequence, head) pairs: the launch with one wavefront per pair,
-    short, ragged and multi-chunk histories."""
+    """2048 (sequence, head) pairs: the launch with two wavefronts per pair for
+    the 4-bit cache and one for fp16; short, ragged and multi-chunk histories."""
     _sampled_check(L, fmt, 32, 64, 64, pos, pos + 2, seed=11 + pos)
 
 
