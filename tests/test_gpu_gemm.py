@@ -209,3 +209,11 @@ def test_linear_q4_opt175b_shapes_sampled(L, N, K, act, res):
         ref = oracle.linear(xs, w_ref, bh[g * 64:(g + 1) * 64], relu=bool(act), residual=resid)
         got = ys[:, g * 64:(g + 1) * 64]
         assert_close(got, ref, f"M=144 N={N} K={K} group {g}")
+    # every tile here is shared (up to 6 segments): the fixed summation order
+    # gives the same bits on every call, whatever order the segments finish in
+    y2 = torch.empty_like(y)
+    for i in range(12):
+        L.fg_linear(x, M, K, L.FG_FMT_Q4G64, codes, meta, N, b, act, r, y2, ws, wsb)
+        torch.cuda.synchronize()
+        assert torch.equal(y2, y), f"repeat {i} differs bitwise"
+

@@ -567,6 +567,53 @@ __global__ __launch_bounds__(256) void sk_reduce64_kernel(Params p, SkSched sc) 
     *reinterpret_cast<uint2*>(p.y + m * p.ldy + n) = make_uint2(pack_h2(o[0], o[1]), pack_h2(o[2], o[3]));
 }
 
+// acc += the ns >= 1 slots at pr, pr + MN, ... in slot order, in two steps:
+// slot_load issues the first SMAX loads together (clamped addresses, so they
+// are always valid), slot_add adds them, slots past the first through a
+// select.  A load whose use sits under `if (q < ns)` is sunk into that branch
+// by the compiler, which then waits for each slot's round trip to memory
+// before requesting the next.
+template <int SMAX>
+__device__ __forceinline__ void slot_load(f4 (&o)[SMAX], const float* pr, int64_t MN, int ns) {
+#pragma unroll
+    for (int q = 0; q < SMAX; ++q) o[q] = *reinterpret_cast<const f4*>(pr + min(q, ns - 1) * MN);
+}
+template <int SMAX>
+__device__ __forceinline__ void slot_add(f4& acc, const f4 (&o)[SMAX], const float* pr, int64_t MN, int ns) {
+    acc += o[0];
+#pragma unroll
+    for (int q = 1; q < SMAX; ++q) {
+        const f4 t = acc + o[q];
+        acc = q < ns ? t : acc;
+    }
+    // only the widest instantiation serves schedules with more slots (a loop
+    // here splits the caller into blocks the scheduler does not cross)
+    if constexpr (SMAX >= 8)
+        for (int q = SMAX; q < ns; ++q) acc += *reinterpret_cast<const f4*>(pr + q * MN);
+}
+template <int SMAX>
+__device__ __forceinline__ void slot_sum(f4& acc, const float* pr, int64_t MN, int ns) {
+    f4 o[SMAX];
+    slot_load<SMAX>(o, pr, MN, ns);
+    slot_add<SMAX>(acc, o, pr, MN, ns);
+}
+
+// Epilogue of 4 summed columns without branches: + bias, ReLU, + residual
+// (each applied through a select when present; the same operations in the
+// same order as the GEMM's own epilogue).
+__device__ __forceinline__ void epi4(f4& acc, uint2 bb, uint2 rr, bool has_b, bool relu, bool has_r) {
+    const float b4[4] = {h2f(bb.x), h2f(bb.x >> 16), h2f(bb.y), h2f(bb.y >> 16)};
+    const float r4[4] = {h2f(rr.x), h2f(rr.x >> 16), h2f(rr.y), h2f(rr.y >> 16)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float v = acc[j];
+        v = has_b ? v + b4[j] : v;
+        v = relu ? fmaxf(v, 0.f) : v;
+        v = has_r ? v + r4[j] : v;
+        acc[j] = v;
+    }
+}
+
 // Decode shapes (the host checks that the schedule fits 32-bit arithmetic):
 // one workgroup per (row, 1024 columns), so no index division per element;
 // the segments of a 256-column tile from two 32-bit divisions; the slot
@@ -581,27 +628,15 @@ __global__ __launch_bounds__(256) void sk_reduce_kernel(Params p, SkSched sc) {
     if (ns == 1) return;                 // whole tile written by one workgroup
     const int64_t MN = p.M * p.N;
     const float* pr = p.part + (int64_t)m * p.N + n;
+    // bias and residual requested with the slots (from a valid stand-in
+    // address when absent, the value then unused), so that no branch sinks
+    // their loads behind the sum
+    const uint2 bb = *reinterpret_cast<const uint2*>(p.bias ? p.bias + n : p.y + (int64_t)m * p.ldy + n);
+    const uint2 rr = *reinterpret_cast<const uint2*>(p.residual ? p.residual + (int64_t)m * p.ldy + n
+                                                                : p.y + (int64_t)m * p.ldy + n);
     f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int q = 0; q < SMAX; ++q) {
-        const f4 o = *reinterpret_cast<const f4*>(pr + min(q, ns - 1) * MN);
-        if (q < ns) acc += o;
-    }
-    for (int q = SMAX; q < ns; ++q) acc += *reinterpret_cast<const f4*>(pr + q * MN);
-    if (p.bias) {
-        const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n);
-        acc[0] += h2f(bb.x); acc[1] += h2f(bb.x >> 16);
-        acc[2] += h2f(bb.y); acc[3] += h2f(bb.y >> 16);
-    }
-    if (p.act == 1) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = fmaxf(acc[i], 0.f);
-    }
-    if (p.residual) {
-        const uint2 rr = *reinterpret_cast<const uint2*>(p.residual + (int64_t)m * p.ldy + n);
-        acc[0] += h2f(rr.x); acc[1] += h2f(rr.x >> 16);
-        acc[2] += h2f(rr.y); acc[3] += h2f(rr.y >> 16);
-    }
+    slot_sum<SMAX>(acc, pr, MN, ns);
+    epi4(acc, bb, rr, p.bias != nullptr, p.act == 1, p.residual != nullptr);
     *reinterpret_cast<uint2*>(p.y + (int64_t)m * p.ldy + n) =
         make_uint2(pack_h2(acc[0], acc[1]), pack_h2(acc[2], acc[3]));
 }
@@ -632,39 +667,63 @@ __global__ __launch_bounds__(kLnThreads) void sk_reduce_ln_kernel(Params p, SkSc
     const __half* rr = p.residual ? p.residual + m * p.ldy : nullptr;
     const float* pr = p.part + m * p.N;
     float v[MAXU][4];
+    uint2 wr[MAXU];   // summed fp16 outputs, stored after the loads of every
+                      // unit (no store between two units' loads)
+    // LayerNorm gamma and beta, requested with the first loads where the
+    // registers allow (up to 4 units per thread), else at the end
+    constexpr bool early_gb = MAXU <= 4;
+    uint2 gg[MAXU], be[MAXU];
     float s = 0.f;
+    // units in groups of UG: every load of a group (its slots, the residual
+    // or the finished y, the bias) is requested before any of them is used,
+    // without branches (stand-in addresses in the row when one is absent)
+    constexpr int UG = (24 / (SMAX + 2)) < 1 ? 1 : ((24 / (SMAX + 2)) > MAXU ? MAXU : 24 / (SMAX + 2));
+#pragma unroll
+    for (int i0 = 0; i0 < MAXU; i0 += UG) {
+        f4 o[UG][SMAX];
+        uint2 h16[UG], bb[UG];
+        int nsu[UG];
+#pragma unroll
+        for (int j = 0; j < UG; ++j) {
+            const int i = i0 + j;
+            if (i < MAXU) {
+                const int u = min((int)threadIdx.x + i * NT, nu - 1);   // clamped: loads stay in the row
+                const int64_t n = (int64_t)u * 4;
+                const int ns = s_ns[n >> 8];   // 256-column tiles
+                nsu[j] = ns;
+                slot_load<SMAX>(o[j], pr + n, MN, ns);
+                // whole tile: y is final; shared tile: partials + bias /
+                // ReLU / residual
+                h16[j] = *reinterpret_cast<const uint2*>(ns == 1 || !rr ? yr + n : rr + n);
+                bb[j] = *reinterpret_cast<const uint2*>(p.bias ? p.bias + n : yr + n);
+                if constexpr (early_gb) {
+                    gg[i] = *reinterpret_cast<const uint2*>(g + n);
+                    be[i] = *reinterpret_cast<const uint2*>(b + n);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < UG; ++j) {
+            const int i = i0 + j;
+            if (i < MAXU) {
+                const int u = min((int)threadIdx.x + i * NT, nu - 1);
+                const int ns = nsu[j];
+                f4 acc = {0.f, 0.f, 0.f, 0.f};
+                slot_add<SMAX>(acc, o[j], pr + (int64_t)u * 4, MN, ns);
+                epi4(acc, bb[j], h16[j], p.bias != nullptr, p.act == 1, rr != nullptr);
+                const uint2 w = ns == 1 ? h16[j] : make_uint2(pack_h2(acc[0], acc[1]), pack_h2(acc[2], acc[3]));
+                const bool mine = (int)threadIdx.x + i * NT < nu;
+                wr[i] = w;
+                // the LayerNorm sees the row as stored (fp16)
+                v[i][0] = h2f(w.x); v[i][1] = h2f(w.x >> 16); v[i][2] = h2f(w.y); v[i][3] = h2f(w.y >> 16);
+                if (mine) s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+            }
+        }
+    }
 #pragma unroll
     for (int i = 0; i < MAXU; ++i) {
-        const int u = min((int)threadIdx.x + i * NT, nu - 1);   // clamped: loads stay in the row
-        const int64_t n = (int64_t)u * 4;
-        const int ns = s_ns[n >> 8];   // 256-column tiles
-        // whole tile: y is final; shared tile: partials + bias / ReLU / residual
-        const __half* src16 = ns == 1 ? yr + n : (rr ? rr + n : nullptr);
-        const uint2 h16 = src16 ? *reinterpret_cast<const uint2*>(src16) : make_uint2(0u, 0u);
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q = 0; q < SMAX; ++q) {
-            const f4 o = *reinterpret_cast<const f4*>(pr + min(q, ns - 1) * MN + n);
-            if (q < ns) acc += o;
-        }
-        for (int q = SMAX; q < ns; ++q) acc += *reinterpret_cast<const f4*>(pr + q * MN + n);
-        if (p.bias) {
-            const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n);
-            acc[0] += h2f(bb.x); acc[1] += h2f(bb.x >> 16); acc[2] += h2f(bb.y); acc[3] += h2f(bb.y >> 16);
-        }
-        if (p.act == 1) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] = fmaxf(acc[j], 0.f);
-        }
-        if (rr) {
-            acc[0] += h2f(h16.x); acc[1] += h2f(h16.x >> 16); acc[2] += h2f(h16.y); acc[3] += h2f(h16.y >> 16);
-        }
-        const uint2 w = ns == 1 ? h16 : make_uint2(pack_h2(acc[0], acc[1]), pack_h2(acc[2], acc[3]));
-        const bool mine = (int)threadIdx.x + i * NT < nu;
-        if (mine && ns > 1) *reinterpret_cast<uint2*>(yr + n) = w;
-        // the LayerNorm sees the row as stored (fp16)
-        v[i][0] = h2f(w.x); v[i][1] = h2f(w.x >> 16); v[i][2] = h2f(w.y); v[i][3] = h2f(w.y >> 16);
-        if (mine) s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+        const int u = (int)threadIdx.x + i * NT;
+        if (u < nu && s_ns[(u * 4) >> 8] > 1) *reinterpret_cast<uint2*>(yr + (int64_t)u * 4) = wr[i];
     }
     const float mean = row::block_sum<NT>(s, sh) / (float)p.N;
     float qs = 0.f;
@@ -685,10 +744,12 @@ __global__ __launch_bounds__(kLnThreads) void sk_reduce_ln_kernel(Params p, SkSc
     for (int i = 0; i < MAXU; ++i) {
         const int u = (int)threadIdx.x + i * NT;
         if (u < nu) {
-            const uint2 gg = *reinterpret_cast<const uint2*>(g + u * 4);
-            const uint2 be = *reinterpret_cast<const uint2*>(b + u * 4);
-            const float gv[4] = {h2f(gg.x), h2f(gg.x >> 16), h2f(gg.y), h2f(gg.y >> 16)};
-            const float bv[4] = {h2f(be.x), h2f(be.x >> 16), h2f(be.y), h2f(be.y >> 16)};
+            if constexpr (!early_gb) {
+                gg[i] = *reinterpret_cast<const uint2*>(g + u * 4);
+                be[i] = *reinterpret_cast<const uint2*>(b + u * 4);
+            }
+            const float gv[4] = {h2f(gg[i].x), h2f(gg[i].x >> 16), h2f(gg[i].y), h2f(gg[i].y >> 16)};
+            const float bv[4] = {h2f(be[i].x), h2f(be[i].x >> 16), h2f(be[i].y), h2f(be[i].y >> 16)};
             *reinterpret_cast<uint2*>(out + u * 4) =
                 make_uint2(pack_h2((v[i][0] - mean) * rstd * gv[0] + bv[0], (v[i][1] - mean) * rstd * gv[1] + bv[1]),
                            pack_h2((v[i][2] - mean) * rstd * gv[2] + bv[2], (v[i][3] - mean) * rstd * gv[3] + bv[3]));
@@ -861,7 +922,9 @@ int launch_sk_reduce(const Params& p, const SkSched& sc, hipStream_t st) {
     }
     const dim3 grid((unsigned)cdiv(p.N, 1024), (unsigned)p.M);
     if (sc.slots <= 2) sk_reduce_kernel<2><<<grid, 256, 0, st>>>(p, sc);
+    else if (sc.slots <= 3) sk_reduce_kernel<3><<<grid, 256, 0, st>>>(p, sc);
     else if (sc.slots <= 4) sk_reduce_kernel<4><<<grid, 256, 0, st>>>(p, sc);
+    else if (sc.slots <= 6) sk_reduce_kernel<6><<<grid, 256, 0, st>>>(p, sc);
     else sk_reduce_kernel<8><<<grid, 256, 0, st>>>(p, sc);
     FG_LAUNCHED("sk_reduce_kernel");
     return FG_OK;
@@ -873,14 +936,17 @@ int launch_sk_reduce_ln(const Params& p, const SkSched& sc, const __half* g, con
     if (p.N % 8 != 0 || p.ldy != p.N || sc.bn != 256 || sc.ntn > kLnTiles || nu > kLnThreads * 8)
         return set_error(FG_ERR_UNSUPPORTED, "fused reduce + layernorm: width %lld", (long long)p.N);
     const unsigned rows = (unsigned)p.M;
-    const int mu = nu <= kLnThreads ? 1 : (nu <= 2 * kLnThreads ? 2 : (nu <= 4 * kLnThreads ? 4 : 8));
-    const int sm = sc.slots <= 2 ? 2 : (sc.slots <= 4 ? 4 : 8);
+    const int64_t need = cdiv(nu, (int64_t)kLnThreads);   // units per thread
+    const int mu = need <= 4 ? (int)need : (need <= 6 ? 6 : 8);
+    const int sm = sc.slots <= 2 ? 2 : (sc.slots <= 4 ? 4 : (sc.slots <= 6 ? 6 : 8));
 #define FG_RLN(U, S) sk_reduce_ln_kernel<U, S><<<rows, kLnThreads, 0, st>>>(p, sc, g, b, ln_y)
-#define FG_RLN_S(U) (sm == 2 ? FG_RLN(U, 2) : (sm == 4 ? FG_RLN(U, 4) : FG_RLN(U, 8)))
+#define FG_RLN_S(U) (sm == 2 ? FG_RLN(U, 2) : (sm == 4 ? FG_RLN(U, 4) : (sm == 6 ? FG_RLN(U, 6) : FG_RLN(U, 8))))
     switch (mu) {
         case 1: FG_RLN_S(1); break;
         case 2: FG_RLN_S(2); break;
+        case 3: FG_RLN_S(3); break;
         case 4: FG_RLN_S(4); break;
+        case 6: FG_RLN_S(6); break;
         default: FG_RLN_S(8); break;
     }
 #undef FG_RLN_S
