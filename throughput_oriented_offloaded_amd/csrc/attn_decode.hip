@@ -743,6 +743,59 @@ __global__ __launch_bounds__(256) void kv_store_kernel(const __half* __restrict_
 
 }  // namespace
 
+// One position (the decode step's append): the slots of a wavefront take
+// SLOTS different (sequence, head) units, one position each.  With the
+// many-position kernel above a wavefront would quantize the same row in
+// every slot, and the exact codec's divisions make that kernel VALU-bound
+// (24 us for the OPT-175B block against about 3 here).
+template <int HD, bool Q4>
+__global__ __launch_bounds__(256) void kv_append_kernel(const __half* __restrict__ k,
+                                                        const __half* __restrict__ v, int64_t ld,
+                                                        void* __restrict__ kc, __half* __restrict__ km,
+                                                        void* __restrict__ vc, __half* __restrict__ vm,
+                                                        int32_t lmax, int32_t nh, int32_t seq0,
+                                                        int32_t nseq, int32_t t0) {
+    constexpr int LPP = HD / 32;
+    constexpr int SLOTS = 64 / LPP;
+    constexpr int GPH = HD / 64;
+    const int lane = threadIdx.x & 63;
+    const int64_t units = (int64_t)nseq * nh;
+    const int64_t u0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * SLOTS;
+    if (u0 >= units) return;                     // whole wavefront
+    const int qi = lane % LPP, slot = lane / LPP, g = (qi * 32) / 64;
+    const int64_t unit = u0 + slot;
+    const bool ok = unit < units;                // whole 4- or 2-lane groups agree
+    const int64_t uu = ok ? unit : units - 1;
+    const int64_t bl = uu / nh;                  // sequence within this call
+    const int h = (int)(uu - bl * nh);
+    const __half* ks = k + bl * ld + h * HD + qi * 32;
+    const __half* vs = v + bl * ld + h * HD + qi * 32;
+    const int64_t row = ((seq0 + bl) * (int64_t)nh + h) * lmax + t0;
+    if constexpr (Q4) {
+        uint4 kv[4], vv[4];
+        load32p(ks, kv);
+        load32p(vs, vv);
+        uint32_t kmb, vmb;
+        const uint4 kq = quant_half_group(kv, kmb);   // every lane: the group's halves meet by shuffle
+        const uint4 vq = quant_half_group(vv, vmb);
+        if (ok) {
+            *reinterpret_cast<uint4*>((uint8_t*)kc + row * (HD / 2) + qi * 16) = kq;
+            *reinterpret_cast<uint4*>((uint8_t*)vc + row * (HD / 2) + qi * 16) = vq;
+            if ((qi & 1) == 0) {
+                *reinterpret_cast<uint32_t*>(km + (row * GPH + g) * 2) = kmb;
+                *reinterpret_cast<uint32_t*>(vm + (row * GPH + g) * 2) = vmb;
+            }
+        }
+    } else if (ok) {
+        const uint4* k4 = reinterpret_cast<const uint4*>(ks);
+        const uint4* v4 = reinterpret_cast<const uint4*>(vs);
+        uint4* kd = reinterpret_cast<uint4*>((__half*)kc + row * HD + qi * 32);
+        uint4* vd = reinterpret_cast<uint4*>((__half*)vc + row * HD + qi * 32);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { kd[j] = k4[j]; vd[j] = v4[j]; }
+    }
+}
+
 int launch_kv_store(const __half* k, const __half* v, int64_t ld, const fg_kv* kv, int32_t seq0,
                     int32_t nseq, int32_t t0, int32_t nt, const fg_dims* d, hipStream_t st) {
     if (nseq == 0 || nt == 0) return FG_OK;
@@ -751,6 +804,22 @@ int launch_kv_store(const __half* k, const __half* v, int64_t ld, const fg_kv* k
     const bool q4 = kv->fmt == FG_FMT_Q4G64;
     const double ne = (double)nseq * nt * d->h1 * 2;       // K and V elements
     TraceScope ts(TK_KV_STORE, st, 0.0, ne * 2 + (q4 ? ne / 2 + ne / 64 * 4 : ne * 2));
+    if (nt == 1) {
+        const int slots = 64 / (d->head_dim / 32);
+        const unsigned g1 = (unsigned)cdiv(units, 4 * (int64_t)slots);
+#define FG_KV_APPEND(HD_, Q_)                                                                  \
+    kv_append_kernel<HD_, Q_><<<g1, 256, 0, st>>>(k, v, ld, kv->k, (__half*)kv->k_meta, kv->v,   \
+                                                  (__half*)kv->v_meta, kv->max_len, d->n_heads,  \
+                                                  seq0, nseq, t0)
+        if (d->head_dim == 128) {
+            if (q4) FG_KV_APPEND(128, true); else FG_KV_APPEND(128, false);
+        } else {
+            if (q4) FG_KV_APPEND(64, true); else FG_KV_APPEND(64, false);
+        }
+#undef FG_KV_APPEND
+        FG_LAUNCHED("kv_append_kernel");
+        return FG_OK;
+    }
 #define FG_KV_STORE(HD_, Q_)                                                                 \
     kv_store_kernel<HD_, Q_><<<grid, 256, 0, st>>>(k, v, ld, kv->k, (__half*)kv->k_meta, kv->v, \
                                                    (__half*)kv->v_meta, kv->max_len, d->n_heads, \
