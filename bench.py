@@ -2,8 +2,8 @@
 4-bit KV cache on one MI355X.
 
 A step is one decode step of the whole model for the whole block: embed, every
-layer (LN1, QKV dequant-GEMM, decode attention over the 4-bit cache with the
-fused append, out-proj, LN2, FC1, FC2), final LN, LM head and greedy pick, for
+layer (LN1, QKV dequant-GEMM, decode attention over the 4-bit cache, the new
+token's K/V append, out-proj, LN2, FC1, FC2), final LN, LM head and greedy pick, for
 bls = gbs x nb sequences at once.  Before the timed region the prompt (s
 tokens per sequence) is prefilled and W warm-up steps run; the K timed steps
 then generate positions s .. s+K-1 again from the prefill's first token, so

@@ -1,6 +1,8 @@
 // Internal tracing hooks (see trace.hip).  A TraceScope placed around a kernel
 // launch records one event before and one after it on the same stream when
-// tracing is enabled; otherwise it does nothing.
+// tracing is enabled; otherwise it does nothing.  A second kind (kind2 >= 0)
+// credits the same bracket to that kind too (a decoder projection beside the
+// GEMM kind), so no bracket is ever nested inside another and timed with it.
 #pragma once
 
 #include "fg_internal.h"
@@ -18,7 +20,7 @@ bool trace_on();
 
 class TraceScope {
   public:
-    TraceScope(int kind, hipStream_t st, double flops, double bytes);
+    TraceScope(int kind, hipStream_t st, double flops, double bytes, int kind2 = -1);
     ~TraceScope();
     TraceScope(const TraceScope&) = delete;
     TraceScope& operator=(const TraceScope&) = delete;

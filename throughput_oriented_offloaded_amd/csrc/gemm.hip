@@ -70,8 +70,8 @@ int launch_linear(const LinearArgs& a, hipStream_t st) {
         p.tile_ns = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(a.ws) + sk_part_bytes(sc, a.M, a.N));
     }
     {
-        TraceScope ts(q4 ? TK_GEMM_Q4 : TK_GEMM_F16, st, 2 * Md * Nd * Kd, gbytes);
-        TraceScope tp(a.proj >= 1 && a.proj <= 4 ? TK_PROJ_QKV + a.proj - 1 : -1, st, 2 * Md * Nd * Kd, gbytes);
+        TraceScope ts(q4 ? TK_GEMM_Q4 : TK_GEMM_F16, st, 2 * Md * Nd * Kd, gbytes,
+                      a.proj >= 1 && a.proj <= 4 ? TK_PROJ_QKV + a.proj - 1 : -1);
         FG_TRY(launch_sk(p, sc, q4, st));
     }
     if (sc.slots > 1 && a.ln_y) {

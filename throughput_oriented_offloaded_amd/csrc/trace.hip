@@ -13,7 +13,7 @@ namespace fg {
 namespace {
 
 struct Rec {
-    int kind;
+    int kind, kind2;   // kinds credited with the bracket (-1: none)
     hipEvent_t a, b;
     double flops, bytes;
 };
@@ -34,8 +34,12 @@ hipEvent_t take() {
         g_pool.pop_back();
         return e;
     }
+    // timing-only events: no system-scope fence on record (the cache
+    // write-back and invalidation it implies would be timed with the kernel
+    // and slow the work that follows); collection waits on them and reads
+    // elapsed times only
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     return e;
 }
 
@@ -49,11 +53,14 @@ const char* kNames[TK_COUNT] = {
 
 bool trace_on() { return g_on; }
 
-TraceScope::TraceScope(int kind, hipStream_t st, double flops, double bytes) {
-    if (kind < 0 || kind >= TK_COUNT || !g_on || !((g_mask >> kind) & 1ull)) return;
+TraceScope::TraceScope(int kind, hipStream_t st, double flops, double bytes, int kind2) {
+    if (!g_on) return;
     std::lock_guard<std::mutex> lk(g_mu);
     if (!g_on) return;
-    Rec r{kind, take(), take(), flops, bytes};
+    auto wanted = [](int k) { return k >= 0 && k < TK_COUNT && ((g_mask >> k) & 1ull) ? k : -1; };
+    const int k1 = wanted(kind), k2 = wanted(kind2);
+    if (k1 < 0 && k2 < 0) return;
+    Rec r{k1, k2, take(), take(), flops, bytes};
     // a launch that cannot be traced is simply not recorded; its events go
     // back to the pool
     if (!r.a || !r.b || hipEventRecord(r.a, st) != hipSuccess) {
@@ -118,10 +125,13 @@ extern "C" int fg_trace_collect(int32_t n_kinds, int64_t* count, double* ms, dou
             }
             continue;
         }
-        count[r.kind] += 1;
-        ms[r.kind] += t;
-        flops[r.kind] += r.flops;
-        bytes[r.kind] += r.bytes;
+        for (const int k : {r.kind, r.kind2}) {
+            if (k < 0) continue;
+            count[k] += 1;
+            ms[k] += t;
+            flops[k] += r.flops;
+            bytes[k] += r.bytes;
+        }
     }
     if (first != hipSuccess)
         return fg::set_error(FG_ERR_HIP, "%s failed: %s (records that could be timed are summed)", what,
