@@ -145,7 +145,7 @@ def profile_layer(cfg, reps: int):
 # calibrated on a copy of known size), committed per workload with the sha256
 # of the measured kernel's sources; reported only while those are unchanged.
 TRAFFIC_FILES = {5: "opt175b_q4_decode_hbm_traffic.md"}
-TRACE_EVERY = 4     # timed steps between the ones whose roofline kernels carry events
+TRACE_EVERY = 8     # timed steps between the ones whose roofline kernels carry events
 KERNEL_SOURCES = {"gemm_q4": ["gemm_sk.hip", "gemm_sk32.hip", "gemm_common.h"],
                   "attn_decode_q4": ["attn_decode.hip", "codec_dev.h"],
                   "attn_topk_q4": ["attn_decode.hip", "codec_dev.h"]}
@@ -556,11 +556,14 @@ def main():
     torch.cuda.synchronize()
     tr_warm = L.fg_trace_collect() if not args.no_trace else {}
 
-    # timed steps: events only around the two roofline kernels (and, with KV
+    # timed steps: events only for the two roofline kernels (and, with KV
     # tiering, the host <-> slot copies on the copy stream), and only on every
-    # TRACE_EVERY-th step: an event pair per launch costs about 2.7% of a step,
-    # the sampled steps still hold hundreds of launches of each kernel, and the
-    # kind mask pauses recording without discarding what was recorded
+    # TRACE_EVERY-th step.  The roofline kernels' events are recorded by their
+    # own launches (hipExtLaunchKernelGGL: the kernel's start and end, no event
+    # packets between kernels); a traced step still takes about 2.7 ms longer
+    # than an untraced one at config 5 (0.7 ms per step when every 4th was
+    # traced), the sampled steps hold over a thousand decode GEMM launches, and
+    # the kind mask pauses recording without discarding what was recorded
     kvt_kinds = ["kv_h2d", "kv_d2h"] if cfg.get("kv_host_seqs") else []
     if tier is not None:
         kvt_kinds.append("w_h2d")

@@ -37,6 +37,8 @@
 //
 // Reading of the current token (stated in fg.h): positions < pos come from the
 // cache; position pos uses the fresh fp16 k, v.
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 
 #include "codec_dev.h"
@@ -852,8 +854,9 @@ int launch_attn_decode(const __half* q, const __half* k_new, const __half* v_new
     const double bytes = (double)bls * (pos + vrows) * d->h1 * per_elem +
                          (double)bls * d->h1 * 2 * 4 + (fuse ? 2.0 * bls * d->h1 * per_elem : 0.0);
     const double flops = 2.0 * bls * (pos + 1) * (double)d->h1 + 2.0 * bls * (vrows + 1) * (double)d->h1;
-    TraceScope ts(sparse ? (q4 ? TK_ATTN_TOPK_Q4 : TK_ATTN_TOPK_F16)
-                         : (q4 ? TK_ATTN_DECODE_Q4 : TK_ATTN_DECODE_F16),
+    // the launch below records the trace events itself
+    TraceScope ts(kExtLaunch, sparse ? (q4 ? TK_ATTN_TOPK_Q4 : TK_ATTN_TOPK_F16)
+                                     : (q4 ? TK_ATTN_DECODE_Q4 : TK_ATTN_DECODE_F16),
                   st, flops, bytes);
     // with enough (sequence, head) pairs to fill the chip: two wavefronts per
     // pair for the 4-bit cache (a launch at the OPT-175B block shape, 13824
@@ -871,10 +874,13 @@ int launch_attn_decode(const __half* q, const __half* k_new, const __half* v_new
     // 8192 positions with four wavefronts of head_dim 128, 57.7 KB)
     if (lds > 65536)
         return set_error(FG_ERR_UNSUPPORTED, "decode attention needs %zu bytes of LDS", lds);
+    hipEvent_t ea, eb;
+    trace_take_ext(&ea, &eb);
 #define FG_ATTN(HD_, Q_, NW_, MU_)                                                           \
-    (sparse ? attn_decode_topk_kernel<HD_, Q_, NW_>                                          \
-            : (MU_ ? attn_decode_multi_kernel<HD_, Q_, NW_> : attn_decode_kernel<HD_, Q_, NW_>)) \
-        <<<(unsigned)units, NW_ * 64, lds, st>>>(                                            \
+    hipExtLaunchKernelGGL(                                                                   \
+        (sparse ? attn_decode_topk_kernel<HD_, Q_, NW_>                                      \
+                : (MU_ ? attn_decode_multi_kernel<HD_, Q_, NW_> : attn_decode_kernel<HD_, Q_, NW_>)), \
+        dim3((unsigned)units), dim3(NW_ * 64), (uint32_t)lds, st, ea, eb, 0u,                \
         q, k_new, v_new, ld, kv->k, (__half*)kv->k_meta, kv->v, (__half*)kv->v_meta,         \
         kv->max_len, d->n_heads, pos, chunk, fuse, topk, out)
 #define FG_ATTN_NW(HD_, Q_, MU_)                        \

@@ -18,9 +18,19 @@ enum TraceKind {
 
 bool trace_on();
 
+// Marks a TraceScope whose launch records the two events itself: the kernel is
+// launched with hipExtLaunchKernelGGL and the events that trace_take_ext hands
+// out, so they hold the kernel's own start and end, and no event packet sits
+// between it and its neighbours (an event pair recorded around a launch drains
+// the queue before and after it: about 5 us of idle time per pair).  A scope
+// in this mode whose events no launch takes is dropped.
+struct ExtLaunch {};
+constexpr ExtLaunch kExtLaunch{};
+
 class TraceScope {
   public:
     TraceScope(int kind, hipStream_t st, double flops, double bytes, int kind2 = -1);
+    TraceScope(ExtLaunch, int kind, hipStream_t st, double flops, double bytes, int kind2 = -1);
     ~TraceScope();
     TraceScope(const TraceScope&) = delete;
     TraceScope& operator=(const TraceScope&) = delete;
@@ -28,6 +38,12 @@ class TraceScope {
   private:
     hipStream_t st_ = nullptr;
     long idx_ = -1;
+    bool ext_ = false;
 };
+
+// The events of this thread's innermost pending launch-recorded scope (and
+// that scope is then no longer pending); null events when there is none, in
+// which case hipExtLaunchKernelGGL launches without timing.
+void trace_take_ext(hipEvent_t* start, hipEvent_t* stop);
 
 }  // namespace fg

@@ -70,7 +70,8 @@ int launch_linear(const LinearArgs& a, hipStream_t st) {
         p.tile_ns = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(a.ws) + sk_part_bytes(sc, a.M, a.N));
     }
     {
-        TraceScope ts(q4 ? TK_GEMM_Q4 : TK_GEMM_F16, st, 2 * Md * Nd * Kd, gbytes,
+        // the stream-K launch records the trace events itself
+        TraceScope ts(kExtLaunch, q4 ? TK_GEMM_Q4 : TK_GEMM_F16, st, 2 * Md * Nd * Kd, gbytes,
                       a.proj >= 1 && a.proj <= 4 ? TK_PROJ_QKV + a.proj - 1 : -1);
         FG_TRY(launch_sk(p, sc, q4, st));
     }

@@ -40,6 +40,9 @@
 #include <mutex>
 #include <unordered_map>
 
+#include <hip/hip_ext.h>
+
+#include "fg_trace.h"
 #include "gemm_common.h"
 #include "rowops.h"
 
@@ -759,7 +762,9 @@ __global__ __launch_bounds__(kLnThreads) void sk_reduce_ln_kernel(Params p, SkSc
 
 template <class C>
 int run(const Params& p, const SkSched& sc, hipStream_t st) {
-    sk_kernel<C><<<(unsigned)sc.G, C::NT, 0, st>>>(p, sc);
+    hipEvent_t ea, eb;   // the enclosing trace scope's events, if any
+    trace_take_ext(&ea, &eb);
+    hipExtLaunchKernelGGL(sk_kernel<C>, dim3((unsigned)sc.G), dim3(C::NT), 0, st, ea, eb, 0u, p, sc);
     FG_LAUNCHED("sk_kernel");
     return FG_OK;
 }

@@ -25,6 +25,9 @@
 //    swizzles; each k-half of a stage is two MFMA k-steps of 16, and the next
 //    step's weight fragments are dequantized while the current step's MFMAs
 //    issue.
+#include <hip/hip_ext.h>
+
+#include "fg_trace.h"
 #include "gemm_common.h"
 
 namespace fg {
@@ -336,7 +339,9 @@ __global__ __launch_bounds__(C::NT) void sk32_kernel(Params p, SkSched sc) {
 
 template <class C>
 int run32(const Params& p, const SkSched& sc, hipStream_t st) {
-    sk32_kernel<C><<<(unsigned)sc.G, C::NT, 0, st>>>(p, sc);
+    hipEvent_t ea, eb;   // the enclosing trace scope's events, if any
+    trace_take_ext(&ea, &eb);
+    hipExtLaunchKernelGGL(sk32_kernel<C>, dim3((unsigned)sc.G), dim3(C::NT), 0, st, ea, eb, 0u, p, sc);
     FG_LAUNCHED("sk32_kernel");
     return FG_OK;
 }

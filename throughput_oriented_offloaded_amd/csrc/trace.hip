@@ -16,7 +16,10 @@ struct Rec {
     int kind, kind2;   // kinds credited with the bracket (-1: none)
     hipEvent_t a, b;
     double flops, bytes;
+    bool dropped;      // launch-recorded scope whose events no launch took
 };
+
+thread_local long t_ext_pending = -1;   // record index of this thread's pending ext scope
 
 std::mutex g_mu;
 bool g_on = false;
@@ -60,7 +63,7 @@ TraceScope::TraceScope(int kind, hipStream_t st, double flops, double bytes, int
     auto wanted = [](int k) { return k >= 0 && k < TK_COUNT && ((g_mask >> k) & 1ull) ? k : -1; };
     const int k1 = wanted(kind), k2 = wanted(kind2);
     if (k1 < 0 && k2 < 0) return;
-    Rec r{k1, k2, take(), take(), flops, bytes};
+    Rec r{k1, k2, take(), take(), flops, bytes, false};
     // a launch that cannot be traced is simply not recorded; its events go
     // back to the pool
     if (!r.a || !r.b || hipEventRecord(r.a, st) != hipSuccess) {
@@ -73,10 +76,49 @@ TraceScope::TraceScope(int kind, hipStream_t st, double flops, double bytes, int
     g_recs.push_back(r);
 }
 
+TraceScope::TraceScope(ExtLaunch, int kind, hipStream_t st, double flops, double bytes, int kind2) {
+    ext_ = true;
+    if (!g_on) return;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_on) return;
+    auto wanted = [](int k) { return k >= 0 && k < TK_COUNT && ((g_mask >> k) & 1ull) ? k : -1; };
+    const int k1 = wanted(kind), k2 = wanted(kind2);
+    if (k1 < 0 && k2 < 0) return;
+    Rec r{k1, k2, take(), take(), flops, bytes, false};
+    if (!r.a || !r.b) {
+        give(r.a);
+        give(r.b);
+        return;
+    }
+    st_ = st;
+    idx_ = (long)g_recs.size();
+    g_recs.push_back(r);
+    t_ext_pending = idx_;
+}
+
 TraceScope::~TraceScope() {
     if (idx_ < 0) return;
     std::lock_guard<std::mutex> lk(g_mu);
-    if (idx_ < (long)g_recs.size()) (void)hipEventRecord(g_recs[idx_].b, st_);
+    if (idx_ >= (long)g_recs.size()) return;   // tracing was reset meanwhile
+    if (!ext_) {
+        (void)hipEventRecord(g_recs[idx_].b, st_);
+        return;
+    }
+    if (t_ext_pending == idx_) {               // no launch took the events
+        t_ext_pending = -1;
+        g_recs[idx_].dropped = true;
+    }
+}
+
+void trace_take_ext(hipEvent_t* start, hipEvent_t* stop) {
+    *start = *stop = nullptr;
+    if (t_ext_pending < 0) return;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (t_ext_pending < (long)g_recs.size()) {
+        *start = g_recs[t_ext_pending].a;
+        *stop = g_recs[t_ext_pending].b;
+    }
+    t_ext_pending = -1;
 }
 
 }  // namespace fg
@@ -114,6 +156,7 @@ extern "C" int fg_trace_collect(int32_t n_kinds, int64_t* count, double* ms, dou
     hipError_t first = hipSuccess;
     const char* what = "";
     for (auto& r : fg::g_recs) {
+        if (r.dropped) continue;
         hipError_t e = hipEventSynchronize(r.b);
         float t = 0.f;
         if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
