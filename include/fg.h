@@ -379,6 +379,20 @@ int fg_model_decode_step(fg_sched* sc, const fg_dims* d, int32_t n_layers, const
                          void* copy_stream, int32_t flags, int32_t attn_topk_ppm,
                          const fg_kv_tier* kvt);
 
+/* One host -> device copy of the tiering path, for callers that run their
+ * own layer-ahead schedule ([P2] "三条关键数据通路如何重叠": the next layer's
+ * weights move over PCIe while the current layer computes; fg_model_* issue
+ * the same copies themselves).  Enqueues `bytes` from src_pinned (pinned
+ * host memory: hipHostMalloc, torch pin_memory) to dst_dev (device memory)
+ * on copy_stream, then records `done` (a hipEvent_t, or NULL) on that stream
+ * so that the compute stream can wait for it.  bytes == 0 records only the
+ * event.  Errors: null pointers with bytes > 0, pageable or device source, or
+ * a destination that is not device memory: FG_ERR_INVALID, nothing enqueued.
+ * Allocates nothing; the caller owns both buffers and keeps them alive until
+ * the copy is done.  Traced as kind "w_h2d". */
+int fg_prefetch(void* dst_dev, const void* src_pinned, size_t bytes, void* copy_stream,
+                void* done);
+
 /* --------------------------------------------------------------- sizes */
 /* Bytes of the six layer matrices of n_layers layers ([P2]: M_W =
  * l (8 h1^2 + 4 h1 h2) in fp16; 4-bit: codes + 4 bytes of meta per 64). */

@@ -197,6 +197,16 @@ def test_model_pass_rejects_bad_arguments(L):
     assert L.raw("fg_sched_destroy")(None) == L.FG_OK
 
 
+def test_prefetch_rejects_null_pointers(L):
+    """fg_prefetch checks its pointers before any HIP call; with nothing to
+    copy and no event it enqueues nothing."""
+    f = L.raw("fg_prefetch")
+    assert f(None, None, 64, None, None) == L.FG_ERR_INVALID
+    assert "null" in L.last_error()
+    assert f(ctypes.c_void_p(1 << 20), None, 64, None, None) == L.FG_ERR_INVALID
+    assert f(None, None, 0, None, None) == L.FG_OK
+
+
 def test_kv_tier_slot_bytes_closed_form(L):
     """Two K/V code tensors and (4-bit) two metadata tensors of gbs sequences,
     each rounded up to 256 bytes."""

@@ -79,6 +79,32 @@ def test_tiering_rejects_pageable_host_memory(L):
     assert e.value.status == L.FG_ERR_INVALID and "pinned" in str(e.value)
 
 
+def test_prefetch_copies_a_pinned_block_and_records_its_event(L):
+    """fg_prefetch: a pinned host block reaches device memory on a side
+    stream, and the compute stream that waits for the recorded event sees all
+    of it; pageable and device sources are refused before anything is
+    enqueued."""
+    import torch
+    n = 3 << 20
+    src = torch.empty(n, dtype=torch.int32, pin_memory=True)
+    src.copy_(torch.arange(n, dtype=torch.int32) * 7 - 5)
+    dst = torch.zeros(n, dtype=torch.int32, device="cuda")
+    cp = torch.cuda.Stream()
+    done = torch.cuda.Event()
+    L.fg_prefetch(dst, src, n * 4, cp, done)
+    torch.cuda.current_stream().wait_event(done)
+    got = dst.clone()
+    torch.cuda.synchronize()
+    assert torch.equal(got.cpu(), src)
+    with pytest.raises(L.FgError) as e:
+        L.fg_prefetch(dst, torch.arange(16, dtype=torch.int32), 64, cp)
+    assert e.value.status == L.FG_ERR_INVALID and "pinned" in str(e.value)
+    with pytest.raises(L.FgError) as e:
+        L.fg_prefetch(dst, dst, 64, cp)
+    assert e.value.status == L.FG_ERR_INVALID
+    torch.cuda.synchronize()
+
+
 def test_weight_and_kv_tiering_together(L):
     """Weight tiering (host halves of layers 0 and 2) and KV tiering (the last
     GPU batch's cache in pinned host memory) in one model, each on its own

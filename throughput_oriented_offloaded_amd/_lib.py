@@ -102,6 +102,7 @@ _PROTOS = {
     "fg_stage_bytes": (SZ, [ctypes.POINTER(Dims)]),
     "fg_sched_create": (ctypes.c_int, [ctypes.POINTER(P), P, SZ]),
     "fg_sched_destroy": (ctypes.c_int, [P]),
+    "fg_prefetch": (ctypes.c_int, [P, P, SZ, P, P]),
     "fg_model_prefill": (ctypes.c_int, [P, ctypes.POINTER(Dims), I32, ctypes.POINTER(LayerW),
                                         ctypes.POINTER(TierW), ctypes.POINTER(KV), P, I32, I32, I32,
                                         P, SZ, P, P, I32, ctypes.POINTER(KvTier)]),
@@ -299,6 +300,18 @@ def fg_sched_create(stage, stage_bytes) -> int:
 
 def fg_sched_destroy(h):
     _check("fg_sched_destroy", _L.fg_sched_destroy(h))
+
+
+def fg_prefetch(dst, src, nbytes, copy_stream=None, done=None):
+    """Copy nbytes from pinned host memory src to device memory dst on
+    copy_stream (a torch stream, or None for the current one), then record
+    done (a torch.cuda.Event, or None) there."""
+    ev = None
+    if done is not None:
+        if done.cuda_event == 0:          # torch creates its events on first record
+            done.record(copy_stream) if copy_stream is not None else done.record()
+        ev = done.cuda_event
+    _check("fg_prefetch", _L.fg_prefetch(ptr(dst), ptr(src), nbytes, stream_ptr(copy_stream), ev))
 
 
 def _arr(T, items):

@@ -250,3 +250,26 @@ extern "C" int fg_model_decode_step(fg_sched* sc, const fg_dims* d, int32_t n_la
                                               attn_topk_ppm, kvt ? &kc : nullptr);
                       });
 }
+
+extern "C" int fg_prefetch(void* dst_dev, const void* src_pinned, size_t bytes, void* copy_stream,
+                           void* done) {
+    using namespace fg;
+    clear_error();
+    FG_CHECK_ARG(bytes == 0 || (dst_dev && src_pinned), "null pointer argument");
+    hipStream_t cp = as_stream(copy_stream);
+    if (bytes > 0) {
+        hipPointerAttribute_t as{}, ad{};
+        if (hipPointerGetAttributes(&as, src_pinned) != hipSuccess || as.type != hipMemoryTypeHost) {
+            (void)hipGetLastError();
+            return set_error(FG_ERR_INVALID, "fg_prefetch: the source must be pinned host memory (hipHostMalloc)");
+        }
+        if (hipPointerGetAttributes(&ad, dst_dev) != hipSuccess || ad.type != hipMemoryTypeDevice) {
+            (void)hipGetLastError();
+            return set_error(FG_ERR_INVALID, "fg_prefetch: the destination must be device memory");
+        }
+        TraceScope ts(TK_W_H2D, cp, 0.0, (double)bytes);
+        FG_HIP(hipMemcpyAsync(dst_dev, src_pinned, bytes, hipMemcpyHostToDevice, cp));
+    }
+    if (done) FG_HIP(hipEventRecord(static_cast<hipEvent_t>(done), cp));
+    return FG_OK;
+}
