@@ -59,6 +59,34 @@ CASES = [  # fmt, bls, nh, hd, pos
 ]
 
 
+@pytest.mark.parametrize("fmt,bls,nh,hd,pos", [("q4", 7, 11, 128, 5), ("q4", 9, 15, 64, 2),
+                                                 ("f16", 7, 11, 128, 3), ("f16", 5, 13, 64, 0)])
+def test_append_one_position_over_many_workgroups(L, fmt, bls, nh, hd, pos):
+    """The one-position append takes 16 (head_dim 128) or 32 (64) (sequence,
+    head) units per wavefront: with 77 / 135 / 65 units the last workgroup is
+    partly empty and its last wavefront ragged.  Row pos of every unit equals
+    the oracle's codec bit for bit, and the rows around it keep their
+    contents."""
+    from throughput_oriented_offloaded_amd.model import DeviceKV
+    rng = np.random.default_rng(bls * 100 + nh)
+    h1 = nh * hd
+    d = L.dims(h1, 4 * h1, nh, hd)
+    fmt_id = L.FG_FMT_Q4G64 if fmt == "q4" else L.FG_FMT_F16
+    lmax = pos + 2
+    kv = DeviceKV(fmt_id, bls, nh, hd, lmax, "cuda")
+    oc = oracle.KVCache(fmt, bls, nh, hd, lmax)
+    kx = (rng.standard_normal((bls, 1, h1)) * 3).astype(np.float16)
+    vx = (rng.standard_normal((bls, 1, h1)) * 3).astype(np.float16)
+    append = L.fg_kv_append_q4 if fmt == "q4" else L.fg_kv_append_f16
+    # k and v rows inside one wider buffer (row stride 3 h1), as the layer passes them
+    qkv = np.zeros((bls, 3 * h1), np.float16)
+    qkv[:, h1:2 * h1], qkv[:, 2 * h1:] = kx[:, 0], vx[:, 0]
+    buf = dev16(qkv)
+    append(buf[:, h1:], buf[:, 2 * h1:], 3 * h1, kv.struct, bls, d, pos)
+    oc.store(kx, vx, pos)
+    _cache_equal(kv, oc, lmax)          # row pos as the oracle; every other row still zero
+
+
 @pytest.mark.parametrize("fmt,bls,nh,hd,pos", CASES)
 def test_decode_attention_and_append(L, fmt, bls, nh, hd, pos):
     import torch
