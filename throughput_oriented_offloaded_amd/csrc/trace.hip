@@ -1,9 +1,10 @@
-// Kernel tracing: when enabled, every launch of the library is bracketed by two
-// HIP events recorded on the launch stream, tagged with its kind and the
-// algorithmic work of that launch (flops, HBM bytes).  fg_trace_collect waits
-// for the events and returns, per kind, the launch count, the summed
-// durations and the summed work, from which a caller derives achieved
-// TFLOP/s or GB/s per kernel.
+// Kernel tracing: when enabled, every launch of the library gets two HIP
+// events on its stream, tagged with its kind and the algorithmic work of that
+// launch (flops, HBM bytes): recorded around the launch, or, for the launches
+// that take them (hipExtLaunchKernelGGL), recorded by the launch itself at
+// the kernel's start and end.  fg_trace_collect waits for the events and
+// returns, per kind, the launch count, the summed durations and the summed
+// work, from which a caller derives achieved TFLOP/s or GB/s per kernel.
 #include <mutex>
 #include <vector>
 
@@ -56,44 +57,49 @@ const char* kNames[TK_COUNT] = {
 
 bool trace_on() { return g_on; }
 
+// The record of a new scope (its events taken from the pool), or -1 when
+// tracing is off, neither kind is wanted or no event can be had.  Called with
+// g_mu held.
+static long open_record(int kind, int kind2, double flops, double bytes) {
+    auto wanted = [](int k) { return k >= 0 && k < TK_COUNT && ((g_mask >> k) & 1ull) ? k : -1; };
+    const int k1 = wanted(kind), k2 = wanted(kind2);
+    if (!g_on || (k1 < 0 && k2 < 0)) return -1;
+    Rec r{k1, k2, take(), take(), flops, bytes, false};
+    if (!r.a || !r.b) {
+        give(r.a);
+        give(r.b);
+        return -1;
+    }
+    g_recs.push_back(r);
+    return (long)g_recs.size() - 1;
+}
+
 TraceScope::TraceScope(int kind, hipStream_t st, double flops, double bytes, int kind2) {
     if (!g_on) return;
     std::lock_guard<std::mutex> lk(g_mu);
-    if (!g_on) return;
-    auto wanted = [](int k) { return k >= 0 && k < TK_COUNT && ((g_mask >> k) & 1ull) ? k : -1; };
-    const int k1 = wanted(kind), k2 = wanted(kind2);
-    if (k1 < 0 && k2 < 0) return;
-    Rec r{k1, k2, take(), take(), flops, bytes, false};
+    const long i = open_record(kind, kind2, flops, bytes);
+    if (i < 0) return;
     // a launch that cannot be traced is simply not recorded; its events go
     // back to the pool
-    if (!r.a || !r.b || hipEventRecord(r.a, st) != hipSuccess) {
-        give(r.a);
-        give(r.b);
+    if (hipEventRecord(g_recs[i].a, st) != hipSuccess) {
+        give(g_recs[i].a);
+        give(g_recs[i].b);
+        g_recs.pop_back();
         return;
     }
     st_ = st;
-    idx_ = (long)g_recs.size();
-    g_recs.push_back(r);
+    idx_ = i;
 }
 
 TraceScope::TraceScope(ExtLaunch, int kind, hipStream_t st, double flops, double bytes, int kind2) {
     ext_ = true;
     if (!g_on) return;
     std::lock_guard<std::mutex> lk(g_mu);
-    if (!g_on) return;
-    auto wanted = [](int k) { return k >= 0 && k < TK_COUNT && ((g_mask >> k) & 1ull) ? k : -1; };
-    const int k1 = wanted(kind), k2 = wanted(kind2);
-    if (k1 < 0 && k2 < 0) return;
-    Rec r{k1, k2, take(), take(), flops, bytes, false};
-    if (!r.a || !r.b) {
-        give(r.a);
-        give(r.b);
-        return;
-    }
+    const long i = open_record(kind, kind2, flops, bytes);
+    if (i < 0) return;
     st_ = st;
-    idx_ = (long)g_recs.size();
-    g_recs.push_back(r);
-    t_ext_pending = idx_;
+    idx_ = i;
+    t_ext_pending = i;
 }
 
 TraceScope::~TraceScope() {
