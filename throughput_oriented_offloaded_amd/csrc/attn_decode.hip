@@ -283,17 +283,18 @@ __device__ __forceinline__ void attn_decode_body(
     constexpr int U1 = Q4 ? 4 : 2;         // steps per batch of loads, pass 1
     constexpr int U2 = Q4 ? 2 : 1;         // pairs of steps per batch, pass 2
     extern __shared__ float smem[];
-    float* sS = smem;                                   // [chunk] scores (log2 units)
-    float* sRed = smem + chunk;                         // [NW*ROWS*LPP][32]
+    float* sVn = smem;                                  // Top-K: [HD] the current token's v (fp32)
+    float* sS = smem + (SPARSE ? HD : 0);               // [chunk] scores (log2 units)
+    float* sRed = sS + chunk;                           // [NW*ROWS*LPP][32]
     float* sFix = sRed + NW * ROWS * LPP * 32;          // [NW*ROWS*LPP]
     float* sL = sFix + NW * ROWS * LPP;                 // [NW*ROWS]
     float* sMax = sL + NW * ROWS;                       // [NW]
-    // Top-K: per-wave counts, (selected count, normalizer over all scores),
-    // selected positions in index order (16 bits each: a Top-K history is one
-    // chunk of at most 8192 positions, which keeps the launch under 64 KB of
-    // LDS with four wavefronts)
-    int* sCnt = reinterpret_cast<int*>(sMax + NW);      // [NW]
-    int* sSel = sCnt + NW;                              // [1]
+    // Top-K: per-wave counts (two alternating sets), (selected count,
+    // normalizer over all scores), selected positions in index order (16 bits
+    // each: a Top-K history is one chunk of at most 8192 positions, which
+    // keeps the launch under 64 KB of LDS with four wavefronts)
+    int* sCnt = reinterpret_cast<int*>(sMax + NW);      // [2][NW]
+    int* sSel = sCnt + 2 * NW;                          // [1]
     float* sLall = reinterpret_cast<float*>(sSel + 1);  // [1]
     unsigned short* sIdx = reinterpret_cast<unsigned short*>(sSel + 2);   // [chunk]
 
@@ -314,6 +315,21 @@ __device__ __forceinline__ void attn_decode_body(
     const float qscale = LOG2E / sqrtf((float)HD);      // scores in log2 units
     const h2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
 
+    // Top-K: the current token's v for the output, requested first and
+    // parked in LDS once q has arrived, so that its load latency is not
+    // exposed after the selection and the gathered pass (measured: the
+    // output phase of a workgroup 2.1 -> 1.0 us at the OPT-175B shape; the
+    // dense kernel gains nothing from it)
+    constexpr int OD = (HD + NW * 64 - 1) / (NW * 64);
+    float vnd[OD];
+    if constexpr (SPARSE) {
+#pragma unroll
+        for (int i = 0; i < OD; ++i) {
+            const int d = threadIdx.x + i * NW * 64;
+            vnd[i] = d < HD ? __half2float(v_new[b * ld + h * HD + d]) : 0.f;
+        }
+    }
+
     h2 qp[16];
     load_q<Q4>(q + b * ld + h * HD + qi * 32, qp);
     float qsum = 0.f;
@@ -322,6 +338,13 @@ __device__ __forceinline__ void attn_decode_body(
         for (int i = 0; i < 16; ++i) qsum = __builtin_amdgcn_fdot2(qp[i], one2, qsum, false);
     }
     const float qoff = -1024.0f * qsum;
+    if constexpr (SPARSE) {
+#pragma unroll
+        for (int i = 0; i < OD; ++i) {
+            const int d = threadIdx.x + i * NW * 64;
+            if (d < HD) sVn[d] = vnd[i];
+        }
+    }
 
     // score of the current token (fresh fp16 k, same pair order as qp)
     float snew;
@@ -437,17 +460,24 @@ __device__ __forceinline__ void attn_decode_body(
             // >= topk), then wave 0 lists the positions in index order with
             // key > tau, and the first topk - count(key > tau) with key == tau
             // counts are wave ballots (a scalar popcount per key slot), summed
-            // over the wavefronts through LDS
+            // over the wavefronts through LDS.  The search stops as soon as
+            // exactly topk keys are >= the candidate: those are then the topk
+            // highest, with no tie at the threshold (the next key is lower)
+            // one barrier per count: the two sets of sCnt alternate, so a wave
+            // that runs ahead writes the set that every wave had finished
+            // reading before the barrier it has just passed
+            int cset = 0;
             auto block_count = [&](int c) -> int {
                 if constexpr (NW == 1) {
                     return c;
                 } else {
-                    if (lane == 0) sCnt[wv] = c;
+                    int* cnt = sCnt + cset * NW;
+                    cset ^= 1;
+                    if (lane == 0) cnt[wv] = c;
                     __syncthreads();
                     int t = 0;
 #pragma unroll
-                    for (int w = 0; w < NW; ++w) t += sCnt[w];
-                    __syncthreads();
+                    for (int w = 0; w < NW; ++w) t += cnt[w];
                     return t;
                 }
             };
@@ -455,6 +485,21 @@ __device__ __forceinline__ void attn_decode_body(
             const int kk = topk < n ? topk : n;
             uint32_t tau = 0;
             int n_gt = 0;
+            auto search = [&](auto count_ge) {
+                for (int bit = 31; bit >= 0; --bit) {
+                    const uint32_t cand = tau | (1u << bit);
+                    const int c = block_count(count_ge(cand));
+                    if (c >= kk) {
+                        tau = cand;
+                        if (c == kk) {          // key > cand - 1 selects exactly kk
+                            tau = cand - 1u;
+                            n_gt = kk;
+                            return;
+                        }
+                    }
+                }
+                n_gt = block_count(count_ge(tau + 1u));
+            };
             if (kk > 0 && kk < n) {
                 if (n <= KR * NW * 64) {
                     uint32_t kr[KR];
@@ -469,11 +514,7 @@ __device__ __forceinline__ void attn_decode_body(
                         for (int i = 0; i < KR; ++i) t += (int)__builtin_popcountll(__ballot(kr[i] >= c));
                         return t;
                     };
-                    for (int bit = 31; bit >= 0; --bit) {
-                        const uint32_t cand = tau | (1u << bit);
-                        if (block_count(count_ge(cand)) >= kk) tau = cand;
-                    }
-                    n_gt = block_count(count_ge(tau + 1u));
+                    search(count_ge);
                 } else {
                     auto count_ge = [&](uint32_t c) -> int {
                         int t = 0;
@@ -483,11 +524,7 @@ __device__ __forceinline__ void attn_decode_body(
                         }
                         return t;
                     };
-                    for (int bit = 31; bit >= 0; --bit) {
-                        const uint32_t cand = tau | (1u << bit);
-                        if (block_count(count_ge(cand)) >= kk) tau = cand;
-                    }
-                    n_gt = block_count(count_ge(tau + 1u));
+                    search(count_ge);
                 }
             }
             if (wv == 0) {
@@ -503,7 +540,7 @@ __device__ __forceinline__ void attn_decode_body(
                         sel = valid;
                     } else if (kk == 0) {
                         sel = false;
-                    } else {
+                    } else if (need_eq > 0) {
                         const uint32_t key = score_key(sp);
                         const bool eq = valid && key == tau;
                         const uint64_t eqm = __ballot(eq);
@@ -511,6 +548,8 @@ __device__ __forceinline__ void attn_decode_body(
                             (uint32_t)(eqm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eqm, 0u));
                         eq_seen += (int)__builtin_popcountll(eqm);
                         sel = (valid && key > tau) || (eq && rank < need_eq);
+                    } else {
+                        sel = valid && score_key(sp) > tau;
                     }
                     const uint64_t sm = __ballot(sel);
                     const int off = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(sm >> 32),
@@ -617,7 +656,15 @@ __device__ __forceinline__ void attn_decode_body(
     }
     __syncthreads();
     const float wn = exp2f(snew - M);
-    for (int d = threadIdx.x; d < HD; d += NW * 64) {
+    // Top-K: the thread index afresh (an opaque copy); otherwise the compiler
+    // keeps the prologue's LDS address of sVn alive through the passes, and
+    // may spill it
+    int tx = (int)threadIdx.x;
+    if constexpr (SPARSE) asm("" : "+v"(tx));
+#pragma unroll
+    for (int i = 0; i < OD; ++i) {
+        const int d = tx + i * NW * 64;
+        if (d >= HD) break;
         const int dq = d >> 5, e = d & 31;
         float s = 0.f, L = 0.f;
 #pragma unroll
@@ -626,8 +673,8 @@ __device__ __forceinline__ void attn_decode_body(
             L += sL[r];
         }
         if constexpr (SPARSE) L = pos > 0 ? sLall[0] : 0.f;   // every score's weight
-        const float vnd = __half2float(v_new[b * ld + h * HD + d]);
-        out[b * (int64_t)nh * HD + h * HD + d] = __float2half_rn((s + wn * vnd) / (L + wn));
+        const float vnd_d = SPARSE ? sVn[d] : __half2float(v_new[b * ld + h * HD + d]);
+        out[b * (int64_t)nh * HD + h * HD + d] = __float2half_rn((s + wn * vnd_d) / (L + wn));
     }
 
     // append the current token at row pos (the passes above read rows < pos
@@ -868,10 +915,12 @@ int launch_attn_decode(const __half* q, const __half* k_new, const __half* v_new
     const int chunk = multi ? kAttnChunk : (int)std::max<int64_t>(cdiv(pos, 64) * 64, 64);
     const int lpp = d->head_dim / 32;
     const size_t lds = sizeof(float) * ((size_t)chunk + nw * 4 * lpp * 33 + nw * 4 + nw) +
-                       (sparse ? sizeof(int) * ((size_t)nw + 2) + sizeof(uint16_t) * chunk : 0);
+                       (sparse ? sizeof(float) * d->head_dim + sizeof(int) * (2 * (size_t)nw + 2) +
+                                     sizeof(uint16_t) * chunk
+                               : 0);
     static_assert(kAttnTopkMaxPos <= 65536, "Top-K positions are listed in 16 bits");
     // every launch stays within 64 KB of dynamic LDS (the largest: Top-K over
-    // 8192 positions with four wavefronts of head_dim 128, 57.7 KB)
+    // 8192 positions with four wavefronts of head_dim 128, 58.2 KB)
     if (lds > 65536)
         return set_error(FG_ERR_UNSUPPORTED, "decode attention needs %zu bytes of LDS", lds);
     hipEvent_t ea, eb;
