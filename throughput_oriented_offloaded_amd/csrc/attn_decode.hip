@@ -289,14 +289,15 @@ __device__ __forceinline__ void attn_decode_body(
     float* sFix = sRed + NW * ROWS * LPP * 32;          // [NW*ROWS*LPP]
     float* sL = sFix + NW * ROWS * LPP;                 // [NW*ROWS]
     float* sMax = sL + NW * ROWS;                       // [NW]
-    // Top-K: per-wave counts (two alternating sets), (selected count,
-    // normalizer over all scores), selected positions in index order (16 bits
-    // each: a Top-K history is one chunk of at most 8192 positions, which
-    // keeps the launch under 64 KB of LDS with four wavefronts)
+    // Top-K: per-wave counts (two alternating sets), the selected count, the
+    // per-wave parts of the normalizer over all scores, the selected
+    // positions in index order (16 bits each: a Top-K history is one chunk of
+    // at most 8192 positions, which keeps the launch under 64 KB of LDS with
+    // four wavefronts)
     int* sCnt = reinterpret_cast<int*>(sMax + NW);      // [2][NW]
     int* sSel = sCnt + 2 * NW;                          // [1]
-    float* sLall = reinterpret_cast<float*>(sSel + 1);  // [1]
-    unsigned short* sIdx = reinterpret_cast<unsigned short*>(sSel + 2);   // [chunk]
+    float* sLw = reinterpret_cast<float*>(sSel + 1);    // [NW] per-wave normalizer parts
+    unsigned short* sIdx = reinterpret_cast<unsigned short*>(sSel + 1 + NW);   // [chunk]
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -458,14 +459,15 @@ __device__ __forceinline__ void attn_decode_body(
             // the topk positions of highest score, ties to the lower position:
             // tau = the topk-th largest key (bitwise search: count(key >= tau)
             // >= topk), then wave 0 lists the positions in index order with
-            // key > tau, and the first topk - count(key > tau) with key == tau
-            // counts are wave ballots (a scalar popcount per key slot), summed
+            // key > tau, and the first topk - count(key > tau) with key == tau.
+            // Counts are wave ballots (a scalar popcount per key slot), summed
             // over the wavefronts through LDS.  The search stops as soon as
             // exactly topk keys are >= the candidate: those are then the topk
-            // highest, with no tie at the threshold (the next key is lower)
-            // one barrier per count: the two sets of sCnt alternate, so a wave
+            // highest, with no tie at the threshold (the next key is lower).
+            //
+            // One barrier per count: the two sets of sCnt alternate, so a wave
             // that runs ahead writes the set that every wave had finished
-            // reading before the barrier it has just passed
+            // reading before the barrier it has just passed.
             int cset = 0;
             auto block_count = [&](int c) -> int {
                 if constexpr (NW == 1) {
@@ -483,6 +485,26 @@ __device__ __forceinline__ void attn_decode_body(
             };
             constexpr int KR = 10;                      // keys held per lane
             const int kk = topk < n ? topk : n;
+            const bool search_needed = kk > 0 && kk < n;
+            // a history of up to KR * NW * 64 positions is held as keys in
+            // registers (0: below every real key) while every thread adds up
+            // its positions' softmax weights; a longer one is read from LDS
+            const bool in_regs = n <= KR * NW * 64;
+            uint32_t kr[KR];
+            float lpart = 0.f;
+            if (in_regs) {
+#pragma unroll
+                for (int i = 0; i < KR; ++i) {
+                    const int p = threadIdx.x + i * NW * 64;
+                    const float sp = p < n ? sS[p] : 0.f;
+                    kr[i] = p < n ? score_key(sp) : 0u;
+                    if (p < n) lpart += exp2f(sp - M);
+                }
+            } else {
+                for (int p = threadIdx.x; p < n; p += NW * 64) lpart += exp2f(sS[p] - M);
+            }
+            lpart = wave_fsum(lpart);
+            if (lane == 0) sLw[wv] = lpart;            // summed after the barrier below
             uint32_t tau = 0;
             int n_gt = 0;
             auto search = [&](auto count_ge) {
@@ -500,48 +522,38 @@ __device__ __forceinline__ void attn_decode_body(
                 }
                 n_gt = block_count(count_ge(tau + 1u));
             };
-            if (kk > 0 && kk < n) {
-                if (n <= KR * NW * 64) {
-                    uint32_t kr[KR];
-#pragma unroll
-                    for (int i = 0; i < KR; ++i) {
-                        const int p = threadIdx.x + i * NW * 64;
-                        kr[i] = p < n ? score_key(sS[p]) : 0u;   // 0: below every real key
-                    }
-                    auto count_ge = [&](uint32_t c) -> int {
+            if (search_needed) {
+                if (in_regs) {
+                    search([&](uint32_t c) -> int {
                         int t = 0;
 #pragma unroll
                         for (int i = 0; i < KR; ++i) t += (int)__builtin_popcountll(__ballot(kr[i] >= c));
                         return t;
-                    };
-                    search(count_ge);
+                    });
                 } else {
-                    auto count_ge = [&](uint32_t c) -> int {
+                    search([&](uint32_t c) -> int {
                         int t = 0;
                         for (int p0 = 0; p0 < n; p0 += NW * 64) {
                             const int p = p0 + threadIdx.x;
                             t += (int)__builtin_popcountll(__ballot(p < n && score_key(sS[p < n ? p : 0]) >= c));
                         }
                         return t;
-                    };
-                    search(count_ge);
+                    });
                 }
             }
             if (wv == 0) {
                 const int need_eq = kk - n_gt;
                 int cnt = 0, eq_seen = 0;
-                float lsum = 0.f;
-                for (int base = 0; base < n; base += 64) {
-                    const int p = base + lane;
+                // one 64-position block of the listing; key: the score key of
+                // position p (only read when a search ran)
+                auto list64 = [&](int p, uint32_t key) {
                     const bool valid = p < n;
-                    const float sp = valid ? sS[p] : 0.f;
                     bool sel;
                     if (kk >= n) {
                         sel = valid;
                     } else if (kk == 0) {
                         sel = false;
                     } else if (need_eq > 0) {
-                        const uint32_t key = score_key(sp);
                         const bool eq = valid && key == tau;
                         const uint64_t eqm = __ballot(eq);
                         const int rank = eq_seen + (int)__builtin_amdgcn_mbcnt_hi(
@@ -549,20 +561,28 @@ __device__ __forceinline__ void attn_decode_body(
                         eq_seen += (int)__builtin_popcountll(eqm);
                         sel = (valid && key > tau) || (eq && rank < need_eq);
                     } else {
-                        sel = valid && score_key(sp) > tau;
+                        sel = valid && key > tau;
                     }
                     const uint64_t sm = __ballot(sel);
                     const int off = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(sm >> 32),
                                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)sm, 0u));
                     if (sel) sIdx[cnt + off] = (unsigned short)p;
                     cnt += (int)__builtin_popcountll(sm);
-                    if (valid) lsum += exp2f(sp - M);
+                };
+                if (NW == 1 && in_regs && search_needed) {
+                    // one wavefront: key slot i of lane l is position 64 i + l
+#pragma unroll
+                    for (int i = 0; i < KR; ++i) {
+                        if (i * 64 >= n) break;
+                        list64(i * 64 + lane, kr[i]);
+                    }
+                } else {
+                    for (int base = 0; base < n; base += 64) {
+                        const int p = base + lane;
+                        list64(p, search_needed && p < n ? score_key(sS[p]) : 0u);
+                    }
                 }
-                lsum = wave_fsum(lsum);
-                if (lane == 0) {
-                    sSel[0] = cnt;
-                    sLall[0] = lsum;
-                }
+                if (lane == 0) sSel[0] = cnt;
             }
             __syncthreads();
             const int nsel = sSel[0];
@@ -672,7 +692,12 @@ __device__ __forceinline__ void attn_decode_body(
             s += sRed[(r * LPP + dq) * 32 + e] + sFix[r * LPP + dq];
             L += sL[r];
         }
-        if constexpr (SPARSE) L = pos > 0 ? sLall[0] : 0.f;   // every score's weight
+        if constexpr (SPARSE) {                         // every score's weight
+            L = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) L += sLw[w];
+            if (pos == 0) L = 0.f;
+        }
         const float vnd_d = SPARSE ? sVn[d] : __half2float(v_new[b * ld + h * HD + d]);
         out[b * (int64_t)nh * HD + h * HD + d] = __float2half_rn((s + wn * vnd_d) / (L + wn));
     }
@@ -915,7 +940,7 @@ int launch_attn_decode(const __half* q, const __half* k_new, const __half* v_new
     const int chunk = multi ? kAttnChunk : (int)std::max<int64_t>(cdiv(pos, 64) * 64, 64);
     const int lpp = d->head_dim / 32;
     const size_t lds = sizeof(float) * ((size_t)chunk + nw * 4 * lpp * 33 + nw * 4 + nw) +
-                       (sparse ? sizeof(float) * d->head_dim + sizeof(int) * (2 * (size_t)nw + 2) +
+                       (sparse ? sizeof(float) * d->head_dim + sizeof(int) * (3 * (size_t)nw + 1) +
                                      sizeof(uint16_t) * chunk
                                : 0);
     static_assert(kAttnTopkMaxPos <= 65536, "Top-K positions are listed in 16 bits");
