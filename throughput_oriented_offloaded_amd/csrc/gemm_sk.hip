@@ -619,14 +619,17 @@ __device__ __forceinline__ void epi4(f4& acc, uint2 bb, uint2 rr, bool has_b, bo
 
 // Decode shapes (the host checks that the schedule fits 32-bit arithmetic):
 // one workgroup per (row, 1024 columns), so no index division per element;
-// the segments of a 256-column tile from two 32-bit divisions; the slot
-// loads unrolled up to SMAX with clamped addresses, all in flight at once.
+// a wavefront's 256 columns are one tile, whose segment count is a scalar
+// load (the scalar cache serves it, instead of a vector round trip before
+// the slot loads can be addressed); the slot loads unrolled up to SMAX with
+// clamped addresses, all in flight at once.
 template <int SMAX>
 __global__ __launch_bounds__(256) void sk_reduce_kernel(Params p, SkSched sc) {
     const int m = blockIdx.y;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const uint32_t tile = (uint32_t)(m / (int)sc.bm) * (uint32_t)sc.ntn + (uint32_t)(blockIdx.x * 4 + wave);
     const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (n >= p.N) return;
-    const uint32_t tile = (uint32_t)(m / (int)sc.bm) * (uint32_t)sc.ntn + (uint32_t)(n >> 8);
     const int ns = p.tile_ns[tile];
     if (ns == 1) return;                 // whole tile written by one workgroup
     const int64_t MN = p.M * p.N;
@@ -659,12 +662,17 @@ __global__ __launch_bounds__(kLnThreads) void sk_reduce_ln_kernel(Params p, SkSc
                                                                  __half* __restrict__ ln_y) {
     constexpr int NT = kLnThreads;
     __shared__ float sh[NT / 64];
-    __shared__ int s_ns[kLnTiles];   // segments of each column tile of this row
     const int64_t m = blockIdx.x;
     const int64_t tm = m / sc.bm;
-    for (int t = threadIdx.x; t < sc.ntn; t += NT) s_ns[t] = p.tile_ns[tm * sc.ntn + t];
-    __syncthreads();
     const int nu = (int)(p.N / 4);
+    // unit i of a wavefront is the 256-column tile wave + 16 i (or, past the
+    // row's end, the last one, which the clamped units read): its segment
+    // count is one scalar load
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int* nsp = p.tile_ns + tm * sc.ntn;
+    int nsw[MAXU];
+#pragma unroll
+    for (int i = 0; i < MAXU; ++i) nsw[i] = nsp[min(wave + (NT / 64) * i, (nu - 1) >> 6)];
     const int64_t MN = p.M * p.N;
     __half* yr = p.y + m * p.ldy;
     const __half* rr = p.residual ? p.residual + m * p.ldy : nullptr;
@@ -692,7 +700,7 @@ __global__ __launch_bounds__(kLnThreads) void sk_reduce_ln_kernel(Params p, SkSc
             if (i < MAXU) {
                 const int u = min((int)threadIdx.x + i * NT, nu - 1);   // clamped: loads stay in the row
                 const int64_t n = (int64_t)u * 4;
-                const int ns = s_ns[n >> 8];   // 256-column tiles
+                const int ns = nsw[i];
                 nsu[j] = ns;
                 slot_load<SMAX>(o[j], pr + n, MN, ns);
                 // whole tile: y is final; shared tile: partials + bias /
@@ -726,7 +734,7 @@ __global__ __launch_bounds__(kLnThreads) void sk_reduce_ln_kernel(Params p, SkSc
 #pragma unroll
     for (int i = 0; i < MAXU; ++i) {
         const int u = (int)threadIdx.x + i * NT;
-        if (u < nu && s_ns[(u * 4) >> 8] > 1) *reinterpret_cast<uint2*>(yr + (int64_t)u * 4) = wr[i];
+        if (u < nu && nsw[i] > 1) *reinterpret_cast<uint2*>(yr + (int64_t)u * 4) = wr[i];
     }
     const float mean = row::block_sum<NT>(s, sh) / (float)p.N;
     float qs = 0.f;
