@@ -145,10 +145,18 @@ def profile_layer(cfg, reps: int):
 # calibrated on a copy of known size), committed per workload with the sha256
 # of the measured kernel's sources; reported only while those are unchanged.
 TRAFFIC_FILES = {5: "opt175b_q4_decode_hbm_traffic.md"}
-TRACE_EVERY = 8     # timed steps between the ones whose roofline kernels carry events
+TRACE_EVERY = 16    # timed steps between the ones whose roofline kernels carry events
+TRACE_FIRST = 8     # the first of them (away from the start of the timed region)
 KERNEL_SOURCES = {"gemm_q4": ["gemm_sk.hip", "gemm_sk32.hip", "gemm_common.h"],
                   "attn_decode_q4": ["attn_decode.hip", "codec_dev.h"],
                   "attn_topk_q4": ["attn_decode.hip", "codec_dev.h"]}
+
+
+def traced_steps(K: int) -> int:
+    """Timed steps that carry events: every TRACE_EVERY-th from TRACE_FIRST,
+    or the first one when the run is shorter than that."""
+    n = len(range(TRACE_FIRST, K, TRACE_EVERY))
+    return n if n else 1
 
 
 def measured_traffic(config: int, kind: str):
@@ -558,12 +566,12 @@ def main():
 
     # timed steps: events only for the two roofline kernels (and, with KV
     # tiering, the host <-> slot copies on the copy stream), and only on every
-    # TRACE_EVERY-th step.  The roofline kernels' events are recorded by their
-    # own launches (hipExtLaunchKernelGGL: the kernel's start and end, no event
-    # packets between kernels); a traced step still takes about 2.7 ms longer
-    # than an untraced one at config 5 (0.7 ms per step when every 4th was
-    # traced), the sampled steps hold over a thousand decode GEMM launches, and
-    # the kind mask pauses recording without discarding what was recorded
+    # TRACE_EVERY-th step from TRACE_FIRST.  The roofline kernels' events are
+    # recorded by their own launches (hipExtLaunchKernelGGL: the kernel's start
+    # and end, no event packets between kernels); a traced step still takes
+    # about 2.7 ms longer than an untraced one at config 5, the sampled steps
+    # of the default run hold 768 decode GEMM launches, and the kind mask
+    # pauses recording without discarding what was recorded
     kvt_kinds = ["kv_h2d", "kv_d2h"] if cfg.get("kv_host_seqs") else []
     if tier is not None:
         kvt_kinds.append("w_h2d")
@@ -573,7 +581,8 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        L.fg_trace_kinds([gemm_kind, attn_kind] + kvt_kinds if i % TRACE_EVERY == 0 else [])
+        traced = i % TRACE_EVERY == TRACE_FIRST % TRACE_EVERY or K <= TRACE_FIRST and i == 0
+        L.fg_trace_kinds([gemm_kind, attn_kind] + kvt_kinds if traced else [])
         _, tok = model.decode_step(tok, s + i, cfg["gbs"], cfg["nb"])
     torch.cuda.synchronize()
     t_dec = time.perf_counter() - t0
@@ -618,7 +627,7 @@ def main():
         # time (HIP events around the scheduler's own copies, traced steps)
         wc = tr["w_h2d"]
         step = t_dec / K
-        ns = len(range(0, K, TRACE_EVERY))      # traced steps
+        ns = traced_steps(K)
         kern_s = (tr[gemm_kind]["ms"] + tr[attn_kind]["ms"]) / 1e3 / ns
         busy = wc["ms"] / 1e3 / ns
         out["tiering"] = {
@@ -635,7 +644,7 @@ def main():
         # KV tiering: history bytes loaded per step and the copy stream's busy time
         ld, st_ = tr["kv_h2d"], tr.get("kv_d2h", {"bytes": 0.0, "ms": 0.0})
         step = t_dec / K
-        ns = len(range(0, K, TRACE_EVERY))      # traced steps
+        ns = traced_steps(K)
         kern_s = (tr[gemm_kind]["ms"] + tr[attn_kind]["ms"]) / 1e3 / ns
         out["kv_tiering"] = {
             "host_sequences": cfg["kv_host_seqs"], "load_bytes_per_step": round(ld["bytes"] / ns),
