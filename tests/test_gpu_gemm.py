@@ -78,6 +78,29 @@ def test_linear_f16_large_m(L, M, N, K):
     assert_close(got, ref, f"f16 {M}x{N}x{K}")
 
 
+# whole 8 x 4 blocks of 256 x 256 tiles (M = 2048, N = 8192: 256 tiles), the
+# order the XCDs take the blocks in: along the tile-rows for K <= 16384,
+# along the tile-columns beyond
+@pytest.mark.parametrize("K", [320, 16448])
+def test_linear_f16_large_m_block_orders(L, K):
+    """Every output tile is computed once, wherever the block order sends it:
+    three rows of every tile-row against the oracle over all columns."""
+    import torch
+    M, N = 2048, 8192
+    rng = np.random.default_rng(K)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    b = (rng.standard_normal(N) * 0.02).astype(np.float16)
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    wsb = L.fg_linear_workspace_bytes(M, N, K)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    L.fg_linear(dev16(x), M, K, L.FG_FMT_F16, dev16(w), None, N, dev16(b), 0, None, y, ws, wsb)
+    torch.cuda.synchronize()
+    rows = np.array([t * 256 + o for t in range(M // 256) for o in (0, 137, 255)])
+    ref = oracle.linear(np.ascontiguousarray(x[rows]), w, b)
+    assert_close(np16(y)[rows], ref, f"f16 {M}x{N}x{K} sampled rows")
+
+
 def test_linear_large_m_epilogues(L):
     got, ref = _run(L, "f16", 1000, 512, 1024, act=1)
     assert_close(got, ref, "relu")

@@ -24,10 +24,12 @@
 //    issue, and the one barrier per stage sits after the first four MFMAs of
 //    the last sub-step; the stage is a fixed sequence (MFMAs as volatile asm)
 //    with the LDS reads and the direct-to-LDS requests placed between MFMAs;
-//  * tiles are taken in groups of 8 tile-rows (column-major inside a group),
-//    with block ids remapped so that the 32 workgroups an XCD runs at once
-//    cover an 8 x 4 block of tiles and share its activation and weight
-//    panels in that XCD's L2.
+//  * the 32 workgroups an XCD runs at once cover an aligned 8 x 4 block of
+//    tiles and share its activation and weight panels in that XCD's L2; the
+//    blocks are dealt to the 8 XCDs round-robin along the tile-rows (K up to
+//    16384: the XCDs share activation panels through the infinity cache) or
+//    along the tile-columns (longer K: they share weight panels), measured
+//    2-4% faster than giving each XCD a contiguous range of its own.
 #include "gemm_common.h"
 #include "fg_trace.h"
 
@@ -63,16 +65,39 @@ void tile_kernel(Params p, int64_t tiles_m, int64_t tiles_n, int64_t grid) {
     __shared__ __align__(16) unsigned char sb1[T_STAGE];
     auto buf = [&](int s) -> unsigned char* { return s == 0 ? sb0 : sb1; };
 
-    // block id -> tile: consecutive ids of one XCD (ids are dealt to the 8
-    // XCDs round-robin), then grouped order
+    // block id -> tile (ids are dealt to the 8 XCDs round-robin, so id b
+    // runs on XCD b mod 8 as slot b / 8 of that XCD's sequence)
     const int64_t b = blockIdx.x;
-    const int64_t t = (b % 8) * (grid / 8) + b / 8;
-    if (t >= tiles_m * tiles_n) return;   // whole workgroup: before any barrier
-    const int64_t per_group = T_GM * tiles_n;
-    const int64_t first_m = (t / per_group) * T_GM;
-    const int64_t gm = min((int64_t)T_GM, tiles_m - first_m);
-    const int64_t wi = t % per_group;
-    const int64_t m0 = (first_m + wi % gm) * TB, n0 = (wi / gm) * TB;
+    int64_t m0, n0;
+    if (tiles_m % T_GM == 0 && tiles_n % 4 == 0 && (tiles_m * tiles_n) % 256 == 0) {
+        // 8 x 4 blocks of tiles: slot s of XCD x is tile s mod 32 of block
+        // 8 (s / 32) + x, taken down the block's 8 tile-rows, then across its
+        // 4 tile-columns; blocks in order along the tile-rows (K <= 16384) or
+        // along the tile-columns
+        const int64_t x = b % 8, sl = b / 8;
+        const int64_t gb = (sl / 32) * 8 + x, inner = sl % 32;
+        int64_t rb, cb;
+        if (p.K <= 16384) {
+            rb = gb / (tiles_n / 4);
+            cb = gb % (tiles_n / 4);
+        } else {
+            rb = gb % (tiles_m / T_GM);
+            cb = gb / (tiles_m / T_GM);
+        }
+        m0 = (rb * T_GM + inner % T_GM) * TB;
+        n0 = (cb * 4 + inner / T_GM) * TB;
+    } else {
+        // consecutive ids of one XCD, then groups of 8 tile-rows
+        // (column-major inside a group)
+        const int64_t t = (b % 8) * (grid / 8) + b / 8;
+        if (t >= tiles_m * tiles_n) return;   // whole workgroup: before any barrier
+        const int64_t per_group = T_GM * tiles_n;
+        const int64_t first_m = (t / per_group) * T_GM;
+        const int64_t gm = min((int64_t)T_GM, tiles_m - first_m);
+        const int64_t wi = t % per_group;
+        m0 = (first_m + wi % gm) * TB;
+        n0 = (wi / gm) * TB;
+    }
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
