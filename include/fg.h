@@ -266,6 +266,50 @@ size_t fg_kvtier_slot_bytes(const fg_dims* d, int32_t gbs, int32_t max_len, int3
 int fg_kvtier_create(fg_kvtier** out, void* slots, size_t slot_bytes, void* copy_stream);
 int fg_kvtier_destroy(fg_kvtier* kt);
 
+/*
+ * Decode attention on the host CPU for host-resident GPU batches ([P2]
+ * "为什么有时应该在 CPU 上算注意力": when a batch's cache is on the CPU side and
+ * the link is the bottleneck, the CPU computes that batch's attention, and
+ * only the current token's q, k, v (3·h1 values per sequence) go down the
+ * link and its attention row (h1 values) comes back, instead of the whole
+ * history).  The pages turn this off with 4-bit compression; here it takes
+ * fp16 caches only (FG_ERR_UNSUPPORTED for 4-bit ones at the layer calls).
+ *
+ * After fg_kvtier_host_attention(kt, stage, stage_bytes, n_threads) with a
+ * non-NULL stage, the decode calls of that tier (fg_layer_decode_block,
+ * fg_model_decode_step) no longer move host batches' histories through the
+ * slots.  Per layer they copy the host batches' q, k, v rows into `stage`
+ * on the call's stream, wait on the host until they have arrived (the
+ * device batches' attention is enqueued first and runs meanwhile), compute
+ * the host batches' attention with n_threads CPU threads, append their k, v
+ * at row pos of the host cache directly, and copy the attention rows back on
+ * the stream; the calls therefore return only after the GPU has reached
+ * each layer's attention.  Prefill calls keep using the slots.  stage:
+ * caller-owned pinned host memory of stage_bytes >=
+ * fg_kvtier_host_stage_bytes(d, n_host_seq), n_host_seq the host-resident
+ * sequences of a call ((nb - nb_dev) * gbs); it must not be touched while a
+ * call's work is in flight.  n_threads <= 0: all hardware threads.  stage
+ * NULL: back to the slots.
+ */
+size_t fg_kvtier_host_stage_bytes(const fg_dims* d, int32_t n_host_seq);
+int fg_kvtier_host_attention(fg_kvtier* kt, void* stage, size_t stage_bytes, int32_t n_threads);
+
+/*
+ * The host-CPU attention itself, on host memory only (no GPU involved): for
+ * sequences seq0 .. seq0+nseq-1 of the fp16 cache `kv` (host pointers) at
+ * position pos, the history rows < pos from the cache and the current token
+ * from its fresh k, v.  qkv: fp16 [nseq, ld] rows, q at column 0, k at h1, v
+ * at 2*h1 (ld >= 3*h1).  out: fp16 [nseq, h1].  append != 0: also store k, v
+ * at row pos of the cache.  Scores, softmax and the V sum in fp32, one fp16
+ * rounding per output.  Runs on n_threads threads (<= 0: all hardware
+ * threads) and returns when done.  FG_ERR_UNSUPPORTED for a 4-bit cache;
+ * FG_ERR_INVALID for sequences or pos outside the cache, ld < 3*h1, null
+ * pointers or bad dims.
+ */
+int fg_attn_decode_host_f16(const void* qkv, int64_t ld, const fg_kv* kv, int32_t seq0, int32_t nseq,
+                            const fg_dims* d, int32_t pos, int32_t append, void* out,
+                            int32_t n_threads);
+
 /* KV tier of one layer or model call.  host: one pinned host cache (layer
  * calls) or n_layers of them (model calls), each with n_seq >=
  * (nb - nb_dev) * gbs and max_len > the call's last position.  With a tier,

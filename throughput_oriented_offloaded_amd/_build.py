@@ -1,7 +1,8 @@
 """Build libfg.so (HIP, gfx950) in-tree with hipcc.
 
-Each csrc/*.hip file is compiled to an object under _build/ (in parallel),
-then linked into throughput_oriented_offloaded_amd/libfg.so.
+Each csrc/*.hip file is compiled to an object under _build/ (in parallel) by
+hipcc, each csrc/*.cpp file (host-only code) by the host compiler, then all
+are linked into throughput_oriented_offloaded_amd/libfg.so.
 """
 from __future__ import annotations
 
@@ -35,13 +36,27 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libfg.so)")
 
 
+# host-only sources (no HIP): the ROCm clang as a plain C++ compiler
+HOST_FLAGS = ["-O3", "-fPIC", "-std=c++17", "-pthread", f"-I{os.path.join(ROOT, 'include')}"]
+
+
+def host_cxx() -> str:
+    for c in (os.environ.get("FG_HOST_CXX"), "/opt/rocm/llvm/bin/clang++", shutil.which("clang++")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("clang++ not found (ROCm is required to build libfg.so)")
+
+
 def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [host_cxx(), *HOST_FLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -56,7 +71,7 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = OUT + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

@@ -112,6 +112,10 @@ _PROTOS = {
     "fg_kvtier_slot_bytes": (SZ, [ctypes.POINTER(Dims), I32, I32, I32]),
     "fg_kvtier_create": (ctypes.c_int, [ctypes.POINTER(P), P, SZ, P]),
     "fg_kvtier_destroy": (ctypes.c_int, [P]),
+    "fg_kvtier_host_stage_bytes": (SZ, [ctypes.POINTER(Dims), I32]),
+    "fg_kvtier_host_attention": (ctypes.c_int, [P, P, SZ, I32]),
+    "fg_attn_decode_host_f16": (ctypes.c_int, [P, I64, ctypes.POINTER(KV), I32, I32, ctypes.POINTER(Dims),
+                                               I32, I32, P, I32]),
     "fg_weight_bytes": (I64, [ctypes.POINTER(Dims), I32, I32]),
     "fg_kv_bytes": (I64, [ctypes.POINTER(Dims), I32, I32, I32, I32, I32]),
     "fg_plan_device_bytes": (I64, [ctypes.POINTER(Dims), ctypes.POINTER(Plan)]),
@@ -285,6 +289,22 @@ def fg_kvtier_create(slots, slot_bytes, copy_stream) -> int:
 
 def fg_kvtier_destroy(h):
     _check("fg_kvtier_destroy", _L.fg_kvtier_destroy(h))
+
+
+def fg_kvtier_host_stage_bytes(d: Dims, n_host_seq) -> int:
+    return _L.fg_kvtier_host_stage_bytes(ctypes.byref(d), n_host_seq)
+
+
+def fg_kvtier_host_attention(h, stage, stage_bytes, n_threads=0):
+    """Decode attention of the tier's host batches on the host CPU (stage:
+    pinned host memory), or back to the device slots (stage None)."""
+    _check("fg_kvtier_host_attention", _L.fg_kvtier_host_attention(h, ptr(stage), stage_bytes, n_threads))
+
+
+def fg_attn_decode_host_f16(qkv, ld, kv: KV, seq0, nseq, d: Dims, pos, append, out, n_threads=0):
+    _check("fg_attn_decode_host_f16", _L.fg_attn_decode_host_f16(ptr(qkv), ld, ctypes.byref(kv), seq0, nseq,
+                                                                 ctypes.byref(d), pos, int(append), ptr(out),
+                                                                 n_threads))
 
 
 def fg_stage_bytes(d: Dims) -> int:

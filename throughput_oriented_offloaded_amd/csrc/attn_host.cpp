@@ -1,0 +1,334 @@
+// Decode attention on the host CPU for sequences whose fp16 KV cache lives in
+// host memory.
+//
+// Method ("FlexGen 完全拆解", section "为什么有时应该在 CPU 上算注意力"): when a
+// GPU batch's cache already sits on the CPU side and the link is the
+// bottleneck, computing that batch's single-query attention on the CPU moves
+// only the current token's activations across the link (about 4·b·h1 bytes)
+// instead of the cache (about 4·b·s·h1 bytes).  With 4-bit compression the
+// pages switch this delegation off (the CPU's dequantization costs what the
+// smaller transfer saves), and so does this library: fp16 caches only.
+//
+// Arithmetic (the attention the GPU kernels compute, with roundings of its
+// own): scores q·k / sqrt(head_dim) in fp32 from fp16 q and cache rows,
+// softmax over the history and the current token, weighted V sum in fp32,
+// one rounding to fp16 per output element.  Work items are (sequence, head) pairs; each item's
+// arithmetic does not depend on which thread runs it, so results do not
+// depend on the thread count.
+//
+// Host code only: built with the host compiler; AVX2 + FMA + F16C where the
+// CPU has them (checked at run time), plain C++ otherwise.
+#include <immintrin.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <condition_variable>
+#include <cstring>
+#include <limits>
+#include <mutex>
+#include <new>
+#include <system_error>
+#include <thread>
+#include <vector>
+
+#include "host_attn.h"
+
+namespace fg {
+
+// ------------------------------------------------------------ thread pool
+struct HostPool::State {
+    std::vector<std::thread> th;
+    std::mutex mu;
+    std::condition_variable cv_work, cv_done;
+    const std::function<void(int64_t, int64_t)>* f = nullptr;
+    int64_t items = 0, chunk = 1;
+    std::atomic<int64_t> next{0};
+    int pending = 0;      // workers not yet done with the current loop
+    uint64_t gen = 0;     // loop number
+    bool stop = false;
+
+    void work(const std::function<void(int64_t, int64_t)>* fn, int64_t n, int64_t c) {
+        for (;;) {
+            const int64_t b = next.fetch_add(c);
+            if (b >= n) return;
+            (*fn)(b, std::min(b + c, n));
+        }
+    }
+    void worker() {
+        uint64_t seen = 0;
+        for (;;) {
+            std::unique_lock<std::mutex> lk(mu);
+            cv_work.wait(lk, [&] { return stop || gen != seen; });
+            if (stop) return;
+            seen = gen;
+            const auto* fn = f;
+            const int64_t n = items, c = chunk;
+            lk.unlock();
+            work(fn, n, c);
+            lk.lock();
+            if (--pending == 0) cv_done.notify_one();
+        }
+    }
+};
+
+HostPool::HostPool(int n) : s_(new State), nthreads_(1) {
+    if (n <= 0) n = (int)std::max(1u, std::thread::hardware_concurrency());
+    for (int i = 1; i < n; ++i) {
+        try {
+            s_->th.emplace_back([this] { s_->worker(); });
+        } catch (const std::system_error&) {
+            break;   // fewer workers: the loops still run, on fewer threads
+        }
+    }
+    nthreads_ = 1 + (int)s_->th.size();
+}
+
+HostPool::~HostPool() {
+    {
+        std::lock_guard<std::mutex> lk(s_->mu);
+        s_->stop = true;
+    }
+    s_->cv_work.notify_all();
+    for (auto& t : s_->th) t.join();
+    delete s_;
+}
+
+void HostPool::run(int64_t items, const std::function<void(int64_t, int64_t)>& f) {
+    if (items <= 0) return;
+    const int64_t chunk = std::max<int64_t>(1, items / ((int64_t)nthreads_ * 8));
+    if (s_->th.empty()) {
+        f(0, items);
+        return;
+    }
+    {
+        std::lock_guard<std::mutex> lk(s_->mu);
+        s_->f = &f;
+        s_->items = items;
+        s_->chunk = chunk;
+        s_->next.store(0);
+        s_->pending = (int)s_->th.size();
+        ++s_->gen;
+    }
+    s_->cv_work.notify_all();
+    s_->work(&f, items, chunk);
+    std::unique_lock<std::mutex> lk(s_->mu);
+    s_->cv_done.wait(lk, [&] { return s_->pending == 0; });
+}
+
+namespace {
+
+// ------------------------------------------------------- one (seq, head)
+// Inputs of one work item: the fresh q, k, v of the head, its cache rows
+// (row p at K + p * hd), the output slot, and the cache row to append at.
+struct Item {
+    const uint16_t* q;
+    const uint16_t* kn;
+    const uint16_t* vn;
+    uint16_t* K;
+    uint16_t* V;
+    uint16_t* out;
+};
+
+inline float h2f(uint16_t h) {
+    _Float16 v;
+    std::memcpy(&v, &h, 2);
+    return (float)v;
+}
+inline uint16_t f2h(float f) {
+    const _Float16 v = (_Float16)f;   // round to nearest even
+    uint16_t h;
+    std::memcpy(&h, &v, 2);
+    return h;
+}
+
+void item_scalar(const Item& it, int hd, int pos, float* s) {
+    float qf[256];
+    const float scale = 1.0f / std::sqrt((float)hd);
+    for (int d = 0; d < hd; ++d) qf[d] = h2f(it.q[d]) * scale;
+    auto dot = [&](const uint16_t* r) {
+        float a = 0.f;
+        for (int d = 0; d < hd; ++d) a += qf[d] * h2f(r[d]);
+        return a;
+    };
+    const float snew = dot(it.kn);
+    float m = snew;
+    for (int p = 0; p < pos; ++p) {
+        s[p] = dot(it.K + (int64_t)p * hd);
+        m = std::max(m, s[p]);
+    }
+    float l = 0.f;
+    for (int p = 0; p < pos; ++p) {
+        s[p] = std::exp(s[p] - m);
+        l += s[p];
+    }
+    const float en = std::exp(snew - m);
+    float acc[256];
+    for (int d = 0; d < hd; ++d) acc[d] = 0.f;
+    for (int p = 0; p < pos; ++p) {
+        const uint16_t* r = it.V + (int64_t)p * hd;
+        for (int d = 0; d < hd; ++d) acc[d] += s[p] * h2f(r[d]);
+    }
+    const float inv = 1.0f / (l + en);
+    for (int d = 0; d < hd; ++d) it.out[d] = f2h((acc[d] + en * h2f(it.vn[d])) * inv);
+}
+
+#define FG_AVX2 __attribute__((target("avx2,fma,f16c")))
+
+FG_AVX2 inline __m256 ld8(const uint16_t* p) {
+    return _mm256_cvtph_ps(_mm_loadu_si128(reinterpret_cast<const __m128i*>(p)));
+}
+FG_AVX2 inline float hsum(__m256 v) {
+    __m128 a = _mm_add_ps(_mm256_castps256_ps128(v), _mm256_extractf128_ps(v, 1));
+    a = _mm_hadd_ps(a, a);
+    a = _mm_hadd_ps(a, a);
+    return _mm_cvtss_f32(a);
+}
+// e^x for x <= 0: x log2(e) = n + f with n = floor, f in [0, 1); 2^f =
+// e^(f ln 2) from its Taylor series to degree 7 (relative error below
+// 1.4e-6 on [0, ln 2)); 2^n added to the exponent field.  Inputs below -87
+// are clamped there (e^-87 is about 1.6e-38, just above the smallest normal
+// float), which keeps 2^n normal.
+FG_AVX2 inline __m256 exp8(__m256 x) {
+    x = _mm256_max_ps(x, _mm256_set1_ps(-87.0f));
+    const __m256 t = _mm256_mul_ps(x, _mm256_set1_ps(1.44269504089f));
+    const __m256 n = _mm256_floor_ps(t);
+    const __m256 g = _mm256_mul_ps(_mm256_sub_ps(t, n), _mm256_set1_ps(0.69314718056f));
+    __m256 p = _mm256_set1_ps(1.0f / 5040.0f);
+    p = _mm256_fmadd_ps(p, g, _mm256_set1_ps(1.0f / 720.0f));
+    p = _mm256_fmadd_ps(p, g, _mm256_set1_ps(1.0f / 120.0f));
+    p = _mm256_fmadd_ps(p, g, _mm256_set1_ps(1.0f / 24.0f));
+    p = _mm256_fmadd_ps(p, g, _mm256_set1_ps(1.0f / 6.0f));
+    p = _mm256_fmadd_ps(p, g, _mm256_set1_ps(0.5f));
+    p = _mm256_fmadd_ps(p, g, _mm256_set1_ps(1.0f));
+    p = _mm256_fmadd_ps(p, g, _mm256_set1_ps(1.0f));
+    const __m256i e = _mm256_slli_epi32(_mm256_cvtps_epi32(n), 23);
+    return _mm256_castsi256_ps(_mm256_add_epi32(_mm256_castps_si256(p), e));
+}
+
+// q (scaled, NV x 8 floats) . one row of fp16
+template <int NV>
+FG_AVX2 inline float dotq(const __m256* qv, const uint16_t* r) {
+    __m256 a0 = _mm256_setzero_ps(), a1 = _mm256_setzero_ps();
+#pragma unroll
+    for (int i = 0; i < NV; i += 2) {
+        a0 = _mm256_fmadd_ps(ld8(r + 8 * i), qv[i], a0);
+        a1 = _mm256_fmadd_ps(ld8(r + 8 * i + 8), qv[i + 1], a1);
+    }
+    return hsum(_mm256_add_ps(a0, a1));
+}
+
+// s: room for pos rounded up to 8 scores
+template <int HD>
+FG_AVX2 void item_avx2(const Item& it, int pos, float* s) {
+    constexpr int NV = HD / 8;
+    const __m256 scale = _mm256_set1_ps(1.0f / std::sqrt((float)HD));
+    __m256 qv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) qv[i] = _mm256_mul_ps(ld8(it.q + 8 * i), scale);
+    auto dot = [&](const uint16_t* r) { return dotq<NV>(qv, r); };
+    const float snew = dot(it.kn);
+    float m = snew;
+    for (int p = 0; p < pos; ++p) {
+        s[p] = dot(it.K + (int64_t)p * HD);
+        m = std::max(m, s[p]);
+    }
+    const int pos8 = (pos + 7) & ~7;
+    for (int p = pos; p < pos8; ++p) s[p] = -std::numeric_limits<float>::infinity();
+    const __m256 mv = _mm256_set1_ps(m);
+    __m256 lv = _mm256_setzero_ps();
+    for (int p = 0; p < pos8; p += 8) {
+        const __m256 e = exp8(_mm256_sub_ps(_mm256_loadu_ps(s + p), mv));
+        _mm256_storeu_ps(s + p, e);
+        lv = _mm256_add_ps(lv, e);
+    }
+    const float en = _mm256_cvtss_f32(exp8(_mm256_set1_ps(snew - m)));
+    __m256 acc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[i] = _mm256_setzero_ps();
+    for (int p = 0; p < pos; ++p) {
+        const __m256 w = _mm256_set1_ps(s[p]);
+        const uint16_t* r = it.V + (int64_t)p * HD;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) acc[i] = _mm256_fmadd_ps(ld8(r + 8 * i), w, acc[i]);
+    }
+    const __m256 env = _mm256_set1_ps(en);
+    const __m256 inv = _mm256_set1_ps(1.0f / (hsum(lv) + en));
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const __m256 o = _mm256_mul_ps(_mm256_fmadd_ps(ld8(it.vn + 8 * i), env, acc[i]), inv);
+        _mm_storeu_si128(reinterpret_cast<__m128i*>(it.out + 8 * i),
+                         _mm256_cvtps_ph(o, _MM_FROUND_TO_NEAREST_INT | _MM_FROUND_NO_EXC));
+    }
+}
+
+bool have_avx2() {
+    static const bool ok = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma") &&
+                           __builtin_cpu_supports("f16c");
+    return ok;
+}
+
+}  // namespace
+
+int check_host_attn(const void* qkv, int64_t ld, const fg_kv* kv, int32_t seq0, int32_t nseq,
+                    const fg_dims* d, int32_t pos, const void* out) {
+    int st = check_dims(d);
+    if (st != FG_OK) return st;
+    if (!qkv || !kv || !out) return set_error(FG_ERR_INVALID, "null pointer argument");
+    if (kv->fmt != FG_FMT_F16)
+        return set_error(FG_ERR_UNSUPPORTED,
+                         "host attention needs the fp16 cache (4-bit caches are not delegated)");
+    if (!kv->k || !kv->v) return set_error(FG_ERR_INVALID, "null cache tensors");
+    if (seq0 < 0 || nseq < 0 || (int64_t)seq0 + nseq > kv->n_seq)
+        return set_error(FG_ERR_INVALID, "sequences [%d, %d) outside the cache's %d", seq0, seq0 + nseq,
+                         kv->n_seq);
+    if (pos < 0 || pos >= kv->max_len)
+        return set_error(FG_ERR_INVALID, "pos %d outside [0, max_len %d)", pos, kv->max_len);
+    if (ld < 3ll * d->h1) return set_error(FG_ERR_INVALID, "row stride %lld < 3 h1", (long long)ld);
+    return FG_OK;
+}
+
+void host_attn_decode_f16(const uint16_t* qkv, int64_t ld, const fg_kv* kv, int32_t seq0, int32_t nseq,
+                          const fg_dims* d, int32_t pos, bool append, uint16_t* out, HostPool& pool) {
+    const int nh = d->n_heads, hd = d->head_dim;
+    const int64_t h1 = d->h1, ml = kv->max_len;
+    uint16_t* kc = static_cast<uint16_t*>(kv->k);
+    uint16_t* vc = static_cast<uint16_t*>(kv->v);
+    const bool avx = have_avx2();
+    std::function<void(int64_t, int64_t)> f = [&](int64_t b, int64_t e) {
+        std::vector<float> s((size_t)((pos + 7) & ~7) + 8);
+        for (int64_t u = b; u < e; ++u) {
+            const int64_t sq = u / nh;
+            const int h = (int)(u - sq * nh);
+            const int64_t row0 = ((seq0 + sq) * nh + h) * ml * hd;
+            const uint16_t* r = qkv + sq * ld + (int64_t)h * hd;
+            Item it{r, r + h1, r + 2 * h1, kc + row0, vc + row0, out + sq * h1 + (int64_t)h * hd};
+            if (avx && hd == 64) item_avx2<64>(it, pos, s.data());
+            else if (avx && hd == 128) item_avx2<128>(it, pos, s.data());
+            else item_scalar(it, hd, pos, s.data());
+            if (append) {
+                std::memcpy(it.K + (int64_t)pos * hd, it.kn, (size_t)hd * 2);
+                std::memcpy(it.V + (int64_t)pos * hd, it.vn, (size_t)hd * 2);
+            }
+        }
+    };
+    pool.run((int64_t)nseq * nh, f);
+}
+
+}  // namespace fg
+
+extern "C" int fg_attn_decode_host_f16(const void* qkv, int64_t ld, const fg_kv* kv, int32_t seq0,
+                                       int32_t nseq, const fg_dims* d, int32_t pos, int32_t append,
+                                       void* out, int32_t n_threads) {
+    fg::clear_error();
+    int st = fg::check_host_attn(qkv, ld, kv, seq0, nseq, d, pos, out);
+    if (st != FG_OK) return st;
+    try {
+        fg::HostPool pool(n_threads);
+        fg::host_attn_decode_f16(static_cast<const uint16_t*>(qkv), ld, kv, seq0, nseq, d, pos, append != 0,
+                                 static_cast<uint16_t*>(out), pool);
+    } catch (const std::bad_alloc&) {
+        return fg::set_error(FG_ERR_CAPACITY, "host attention: out of host memory");
+    }
+    return FG_OK;
+}

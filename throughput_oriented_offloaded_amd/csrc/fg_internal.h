@@ -105,6 +105,18 @@ bool linear_is_dp(int64_t M);
 // below end_pos.
 int kvtier_check(const fg_kvtier* kt, const fg_dims* d, const fg_kv* dev, const fg_kv* host,
                  int32_t gbs, int32_t n_host_seq, int32_t end_pos);
+// Decode attention of the host-resident GPU batches on the host CPU
+// (kvtier.hip, attn_host.cpp), when the tier has a host stage: checks (fp16
+// host cache, dense attention, stage size for `rows` host sequences); send:
+// the rows' q, k, v to the stage and an event, on st; attend: wait for the
+// event on the host, compute the attention and append k, v at pos in the
+// host cache on the CPU, copy the attention rows to `out` on st.
+bool kvtier_host_attention_on(const fg_kvtier* kt);
+size_t host_stage_bytes(const fg_dims* d, int64_t rows);
+int kvtier_host_check(const fg_kvtier* kt, const fg_kv* host, const fg_dims* d, int64_t rows, int32_t topk);
+int kvtier_host_send(const fg_kvtier* kt, const __half* qkv, int64_t rows, int64_t h1, hipStream_t st);
+int kvtier_host_attend(const fg_kvtier* kt, const fg_kv* host, const fg_dims* d, int64_t rows, int32_t pos,
+                       __half* out, hipStream_t st);
 // The host-resident GPU batches ("units") of one call, in execution order,
 // moved through the tier object's two slots.  begin(u): loads enqueued
 // through unit u + 1 (rows [0, load_rows) each), the compute stream made to

@@ -26,6 +26,7 @@
 
 #include "fg_internal.h"
 #include "fg_trace.h"
+#include "host_attn.h"
 
 struct fg_kvtier {
     unsigned char* slot[2];
@@ -36,6 +37,13 @@ struct fg_kvtier {
     hipEvent_t done[2];
     hipEvent_t stored[2];
     int device;
+    // decode attention of the host batches on the host CPU (when hstage):
+    // pinned staging [rows, 3 h1] (q, k, v in) then [rows, h1] (attention
+    // out), the CPU threads, and the event that marks the rows' arrival
+    unsigned char* hstage = nullptr;
+    size_t hstage_bytes = 0;
+    fg::HostPool* pool = nullptr;
+    hipEvent_t hready = nullptr;
 };
 
 namespace fg {
@@ -183,6 +191,50 @@ int KvPipe::end(int32_t u, int32_t lo, int32_t hi) {
     return FG_OK;
 }
 
+// ------------------------------------------------ host-CPU attention path
+bool kvtier_host_attention_on(const fg_kvtier* kt) { return kt && kt->hstage; }
+
+size_t host_stage_bytes(const fg_dims* d, int64_t rows) {
+    return align_up((size_t)rows * 4 * (size_t)d->h1 * 2, 256);
+}
+
+int kvtier_host_check(const fg_kvtier* kt, const fg_kv* host, const fg_dims* d, int64_t rows,
+                      int32_t topk) {
+    FG_CHECK_SUP(host->fmt == FG_FMT_F16,
+                 "host attention: the host cache must be fp16 (4-bit caches are not delegated)");
+    FG_CHECK_SUP(topk < 0, "host attention computes dense attention only (no Top-K sparse V)");
+    const size_t need = host_stage_bytes(d, rows);
+    if (kt->hstage_bytes < need)
+        return set_error(FG_ERR_CAPACITY, "host attention: stage of %zu bytes < %zu needed", kt->hstage_bytes,
+                         need);
+    return FG_OK;
+}
+
+int kvtier_host_send(const fg_kvtier* kt, const __half* qkv, int64_t rows, int64_t h1, hipStream_t st) {
+    FG_HIP(hipMemcpyAsync(kt->hstage, qkv, (size_t)rows * 3 * h1 * 2, hipMemcpyDeviceToHost, st));
+    FG_HIP(hipEventRecord(kt->hready, st));
+    return FG_OK;
+}
+
+int kvtier_host_attend(const fg_kvtier* kt, const fg_kv* host, const fg_dims* d, int64_t rows, int32_t pos,
+                       __half* out, hipStream_t st) {
+    // the host cache's rows stored by earlier calls (the prefill's) and this
+    // layer's q, k, v rows must have landed before the CPU reads them
+    FG_HIP(hipEventSynchronize(kt->stored[0]));
+    FG_HIP(hipEventSynchronize(kt->stored[1]));
+    FG_HIP(hipEventSynchronize(kt->hready));
+    const int64_t h1 = d->h1;
+    const uint16_t* qkv = reinterpret_cast<const uint16_t*>(kt->hstage);
+    uint16_t* o = reinterpret_cast<uint16_t*>(kt->hstage) + rows * 3 * h1;
+    try {
+        host_attn_decode_f16(qkv, 3 * h1, host, 0, (int32_t)rows, d, pos, true, o, *kt->pool);
+    } catch (const std::bad_alloc&) {
+        return set_error(FG_ERR_CAPACITY, "host attention: out of host memory");
+    }
+    FG_HIP(hipMemcpyAsync(out, o, (size_t)rows * h1 * 2, hipMemcpyHostToDevice, st));
+    return FG_OK;
+}
+
 }  // namespace fg
 
 // -------------------------------------------------------------------- C ABI
@@ -232,9 +284,49 @@ extern "C" int fg_kvtier_create(fg_kvtier** out, void* slots, size_t slot_bytes,
     return FG_OK;
 }
 
+extern "C" size_t fg_kvtier_host_stage_bytes(const fg_dims* d, int32_t n_host_seq) {
+    if (fg::check_dims(d) != FG_OK || n_host_seq < 1) {
+        fg::clear_error();
+        return 0;
+    }
+    return fg::host_stage_bytes(d, n_host_seq);
+}
+
+extern "C" int fg_kvtier_host_attention(fg_kvtier* kt, void* stage, size_t stage_bytes, int32_t n_threads) {
+    fg::clear_error();
+    FG_CHECK_ARG(kt, "null tier object");
+    if (!stage) {
+        delete kt->pool;
+        kt->pool = nullptr;
+        kt->hstage = nullptr;
+        kt->hstage_bytes = 0;
+        return FG_OK;
+    }
+    FG_CHECK_ARG(stage_bytes > 0, "empty stage");
+    hipPointerAttribute_t at{};
+    if (hipPointerGetAttributes(&at, stage) != hipSuccess || at.type != hipMemoryTypeHost) {
+        (void)hipGetLastError();
+        return fg::set_error(FG_ERR_INVALID, "host attention: the stage must be pinned host memory");
+    }
+    if (!kt->hready) FG_HIP(hipEventCreateWithFlags(&kt->hready, hipEventDisableTiming));
+    fg::HostPool* pool = nullptr;
+    try {
+        pool = new fg::HostPool(n_threads);
+    } catch (const std::bad_alloc&) {
+        return fg::set_error(FG_ERR_CAPACITY, "host attention: out of host memory");
+    }
+    delete kt->pool;
+    kt->pool = pool;
+    kt->hstage = static_cast<unsigned char*>(stage);
+    kt->hstage_bytes = stage_bytes;
+    return FG_OK;
+}
+
 extern "C" int fg_kvtier_destroy(fg_kvtier* kt) {
     fg::clear_error();
     if (!kt) return FG_OK;
+    delete kt->pool;
+    if (kt->hready) (void)hipEventDestroy(kt->hready);
     (void)hipStreamSynchronize(kt->sp);
     (void)hipStreamDestroy(kt->sp);
     for (int i = 0; i < 2; ++i) {

@@ -144,6 +144,9 @@ int layer_decode(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, in
     FG_CHECK_SUP(topk < 0 || pos <= kAttnTopkMaxPos, "Top-K attention: history %d longer than %d",
                  pos, kAttnTopkMaxPos);
     const int64_t bls = (int64_t)gbs * nb;
+    // host batches' attention on the host CPU (the tier's choice)
+    const bool host_attn = kvt && kvt->nb_dev < nb && kvtier_host_attention_on(kvt->kt);
+    if (host_attn) FG_TRY(kvtier_host_check(kvt->kt, kvt->host, d, (int64_t)(nb - kvt->nb_dev) * gbs, topk));
     const WsLayout L = layout(d, bls, w->fmt);
     if (ws_bytes < L.total)
         return set_error(FG_ERR_CAPACITY, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
@@ -170,10 +173,17 @@ int layer_decode(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, in
     // cost about 14 us per OPT-175B layer on gfx950 (the attention alone: 189
     // against 172 us); after it, they drain during the next GEMM.
     const int32_t nd = kvt ? kvt->nb_dev : nb;
+    // With host attention, the host batches' q, k, v rows go to the host
+    // first, the device batches' attention runs while the CPU computes theirs,
+    // and their attention rows come back before the out-projection.
+    if (host_attn) FG_TRY(kvtier_host_send(kvt->kt, qkv + (int64_t)nd * gbs * 3 * h1, (int64_t)(nb - nd) * gbs, h1, st));
     FG_TRY(launch_attn_decode(qkv, qkv + h1, qkv + 2 * h1, 3 * h1, kv, nd * gbs, d, pos, 0, o, st,
                               topk));
     FG_TRY(launch_kv_store(qkv + h1, qkv + 2 * h1, 3 * h1, kv, 0, nd * gbs, pos, 1, d, st));
-    for (int32_t k = nd; k < nb; ++k) {
+    if (host_attn)
+        FG_TRY(kvtier_host_attend(kvt->kt, kvt->host, d, (int64_t)(nb - nd) * gbs, pos, o + (int64_t)nd * gbs * h1,
+                                  st));
+    for (int32_t k = host_attn ? nb : nd; k < nb; ++k) {
         const int32_t u = kvt->u0 + (k - nd);
         const __half* q = qkv + (int64_t)k * gbs * 3 * h1;
         fg_kv slot;
