@@ -177,3 +177,136 @@ def test_model_generation_kv_tier_bit_exact(L, kv_host_seqs, gbs, nb, topk):
             assert torch.equal(hh[:, :, :s + n - 1], a[n_dev:, :, :s + n - 1].cpu())
             if n_dev:
                 assert torch.equal(dd[:, :, :s + n - 1], a[:n_dev, :, :s + n - 1])
+
+
+# ------------------------------------------------ attention on the host CPU
+def _host_attn_tier(L, d, gbs, lmax, n_host_seq, threads=4):
+    """A tier whose decode calls compute the host batches' attention on the
+    CPU (fp16 cache), with its pinned stage."""
+    import torch
+    kt, slots, cp = _tier(L, d, gbs, lmax, "f16")
+    hb = L.fg_kvtier_host_stage_bytes(d, n_host_seq)
+    stage = torch.empty(hb, dtype=torch.uint8, pin_memory=True)
+    L.fg_kvtier_host_attention(kt, stage, hb, threads)
+    return kt, slots, cp, stage
+
+
+@pytest.mark.parametrize("nb_dev,P", [(0, 17), (1, 17), (2, 40), (1, 0)])
+def test_layer_decode_host_attention(L, nb_dev, P):
+    """fg_layer_decode_block with the host batches' attention on the CPU
+    ([P2] "为什么有时应该在 CPU 上算注意力"; fp16 cache): the layer output
+    against the oracle and against the all-device call (the CPU's roundings
+    differ, so within the tolerance), the device batches' rows bit for bit,
+    and the host cache: history untouched, row P the fresh k, v, bit for
+    bit equal to what the all-device call appended."""
+    import torch
+    from test_gpu_layer import _layer
+    gbs, nb, lmax = 2, 3, 48
+    bls = gbs * nb
+    dl, Wn, od = _layer(L, OPT125, "q4", seed=71)
+    kv, d, kh, vh = _filled_cache(L, "f16", bls, P, lmax, seed=72)
+    dev, host = _split(L, kv, "f16", nb_dev * gbs, bls, lmax)
+    x = synth.activations(bls, OPT125["h1"], seed=73)
+    ws = torch.empty(L.fg_workspace_bytes(d, bls, dl.fmt), dtype=torch.uint8, device="cuda")
+    x_ref = x.cuda()
+    L.fg_layer_decode_block(d, dl.struct, x_ref, gbs, nb, P, kv.struct, ws, ws.numel())
+    torch.cuda.synchronize()
+    kt, slots, cp, stage = _host_attn_tier(L, d, gbs, lmax, (nb - nb_dev) * gbs)
+    try:
+        x_h = x.cuda()
+        L.fg_layer_decode_block(d, dl.struct, x_h, gbs, nb, P, dev.struct, ws, ws.numel(),
+                                kvt=L.KvTier(kt, _ptr_kv(L, host), nb_dev))
+        torch.cuda.synchronize()
+    finally:
+        L.fg_kvtier_destroy(kt)
+    oc = oracle.KVCache("f16", bls, OPT125["nh"], OPT125["hd"], lmax)
+    if P:
+        oc.store(kh.numpy().view(np.uint16), vh.numpy().view(np.uint16), 0)
+    ref, _, _ = oracle.layer_decode(od, Wn, x.numpy().view(np.uint16), P, oc)
+    assert_close(np16(x_h), ref, "host-attention decode block vs oracle")
+    assert_close(np16(x_h), np16(x_ref), "host-attention decode block vs all-device")
+    n_dev = nb_dev * gbs
+    if n_dev:
+        assert torch.equal(x_h[:n_dev], x_ref[:n_dev])
+    for a, hh in zip(_tensors(kv), _tensors(host)):
+        assert torch.equal(hh[:, :, :P + 1], a[n_dev:, :, :P + 1].cpu())
+
+
+def test_model_decode_host_attention(L):
+    """2-layer OPT-125m-shape model, fp16 weights and cache, two of three GPU
+    batches' caches on the host: the prefill goes through the slots, the
+    decode steps' host attention runs on the CPU.  Teacher-forced on the
+    all-device model's tokens, every decode step's logits agree within the
+    tolerance and the host caches hold the same rows."""
+    import torch
+    from throughput_oriented_offloaded_amd.model import DeviceLayer, Model, Shape
+    sh = Shape(n_layers=2, h1=768, h2=3072, n_heads=12, head_dim=64)
+    gbs, nb, s, n = 2, 3, 20, 5
+    bls = gbs * nb
+    Ws = [synth.layer_weights(sh.h1, sh.h2, j, seed=0) for j in range(sh.n_layers)]
+    emb = synth.embeddings(sh.h1, s + n, seed=0)
+    toks = synth.tokens(bls, s, seed=5).cuda()
+    layers = [DeviceLayer.from_fp16({k: v.cuda() for k, v in W.items()}, L.FG_FMT_F16) for W in Ws]
+    embd = {k: v.cuda() for k, v in emb.items()}
+    ref = Model(sh, layers, embd, L.FG_FMT_F16, bls, s + n)
+    ha = Model(sh, layers, embd, L.FG_FMT_F16, bls, s + n, kv_host_seqs=2 * gbs, kv_host_attention=True,
+               host_threads=4)
+    lg_r, tok_r = ref.prefill(toks, gbs, nb)
+    lg_h, tok_h = ha.prefill(toks, gbs, nb)
+    assert torch.equal(lg_r, lg_h)
+    tok = tok_r
+    for i in range(n - 1):
+        lg_r, nxt = ref.decode_step(tok, s + i, gbs, nb)
+        lg_h, _ = ha.decode_step(tok, s + i, gbs, nb)
+        torch.cuda.synchronize()
+        assert_close(np16(lg_h), np16(lg_r), f"decode step {i} logits")
+        tok = nxt
+    n_dev = bls - 2 * gbs
+    for j in range(sh.n_layers):
+        for a, hh in zip(_tensors(ref.kv[j]), _tensors(ha.kv_host[j])):
+            assert torch.equal(hh[:, :, :s], a[n_dev:, :, :s].cpu())
+            got = hh[:, :, s:s + n - 1].float()
+            want = a[n_dev:, :, s:s + n - 1].float().cpu()
+            assert (got - want).abs().max() <= 1e-2 * want.abs().max() + 1e-3
+
+
+def test_host_attention_refusals(L):
+    """4-bit host cache, Top-K sparse V, a small stage, an unpinned stage:
+    refused on the host before anything is enqueued."""
+    import torch
+    from test_gpu_layer import _layer
+    gbs, nb, lmax, P = 2, 2, 24, 9
+    bls = gbs * nb
+    dl, _, _ = _layer(L, OPT125, "q4", seed=81)
+    d = L.dims(OPT125["h1"], OPT125["h2"], OPT125["nh"], OPT125["hd"])
+    x = synth.activations(bls, OPT125["h1"], seed=82).cuda()
+    ws = torch.empty(L.fg_workspace_bytes(d, bls, dl.fmt), dtype=torch.uint8, device="cuda")
+    kv16, _, _, _ = _filled_cache(L, "f16", bls, P, lmax, seed=83)
+    dev16_, host16 = _split(L, kv16, "f16", gbs, bls, lmax)
+    kvq, _, _, _ = _filled_cache(L, "q4", bls, P, lmax, seed=84)
+    devq, hostq = _split(L, kvq, "q4", gbs, bls, lmax)
+    x0 = x.clone()
+    kt, slots, cp, stage = _host_attn_tier(L, d, gbs, lmax, gbs)
+    try:
+        with pytest.raises(L.FgError) as e:
+            L.fg_layer_decode_block(d, dl.struct, x, gbs, nb, P, devq.struct, ws, ws.numel(),
+                                    kvt=L.KvTier(kt, _ptr_kv(L, hostq), 1))
+        assert e.value.status == L.FG_ERR_UNSUPPORTED
+        with pytest.raises(L.FgError) as e:
+            L.fg_layer_decode_block(d, dl.struct, x, gbs, nb, P, dev16_.struct, ws, ws.numel(),
+                                    attn_topk_ppm=100000, kvt=L.KvTier(kt, _ptr_kv(L, host16), 1))
+        assert e.value.status == L.FG_ERR_UNSUPPORTED
+        small = torch.empty(256, dtype=torch.uint8, pin_memory=True)
+        L.fg_kvtier_host_attention(kt, small, 256, 2)
+        with pytest.raises(L.FgError) as e:
+            L.fg_layer_decode_block(d, dl.struct, x, gbs, nb, P, dev16_.struct, ws, ws.numel(),
+                                    kvt=L.KvTier(kt, _ptr_kv(L, host16), 1))
+        assert e.value.status == L.FG_ERR_CAPACITY
+        plain = torch.empty(1 << 20, dtype=torch.uint8)
+        with pytest.raises(L.FgError) as e:
+            L.fg_kvtier_host_attention(kt, plain, plain.numel(), 2)
+        assert e.value.status == L.FG_ERR_INVALID
+        torch.cuda.synchronize()
+    finally:
+        L.fg_kvtier_destroy(kt)
+    assert torch.equal(x, x0), "refused calls must not touch x"

@@ -141,14 +141,18 @@ class Model:
     with embed [vocab, h1], pos [max_pos, h1], lnf_g, lnf_b (fp16, device)."""
 
     def __init__(self, shape: Shape, layers, emb: dict, kv_fmt: int, n_seq: int, max_len: int,
-                 device="cuda", tier=None, attn_topk: float = 0.0, kv_host_seqs: int = 0):
+                 device="cuda", tier=None, attn_topk: float = 0.0, kv_host_seqs: int = 0,
+                 kv_host_attention: bool = False, host_threads: int = 0):
         """tier: None, or one TierLayer (or None) per layer for weight tiering.
         attn_topk: 0 for dense decode attention, else the fraction of cached
         positions whose V each decode step reads (Top-K sparse V; the pages
         use 0.1), rounded up per step.
         kv_host_seqs: the last kv_host_seqs sequences keep their KV cache in
         pinned host memory (KV tiering; a whole number of GPU batches at every
-        call), moved through two device slots by the library."""
+        call), moved through two device slots by the library.
+        kv_host_attention: with an fp16 cache, the decode steps compute the
+        host-resident batches' attention on the host CPU (host_threads
+        threads, 0: all) instead of moving their history to the device."""
         assert 0.0 <= attn_topk <= 1.0
         self.attn_topk_ppm = int(round(attn_topk * 1_000_000))
         self.shape, self.layers, self.emb = shape, layers, emb
@@ -156,6 +160,9 @@ class Model:
         self.n_seq, self.max_len = n_seq, max_len
         assert 0 <= kv_host_seqs <= n_seq
         self.kv_host_seqs = kv_host_seqs
+        assert not kv_host_attention or (kv_host_seqs and kv_fmt == L.FG_FMT_F16), \
+            "host attention needs host-resident sequences and the fp16 cache"
+        self.kv_host_attention, self.host_threads = kv_host_attention, host_threads
         n_dev = max(n_seq - kv_host_seqs, 1)   # the device cache is unused when every batch is on the host
         self.kv = [DeviceKV(kv_fmt, n_dev, shape.n_heads, shape.head_dim, max_len, device)
                    for _ in layers]
@@ -203,8 +210,14 @@ class Model:
             slots = torch.empty(2 * sb, dtype=torch.uint8, device=self.device)
             cp = torch.cuda.Stream(device=self.device)
             host = (L.KV * len(self.kv_host))(*[h.struct for h in self.kv_host])
-            self._kvt[gbs] = (L.fg_kvtier_create(slots, sb, cp), slots, cp, host)
-        kt, _, _, host = self._kvt[gbs]
+            kt = L.fg_kvtier_create(slots, sb, cp)
+            stage = None
+            if self.kv_host_attention:
+                hb = L.fg_kvtier_host_stage_bytes(self.d, self.kv_host_seqs)
+                stage = torch.empty(hb, dtype=torch.uint8, pin_memory=True)
+                L.fg_kvtier_host_attention(kt, stage, hb, self.host_threads)
+            self._kvt[gbs] = (kt, slots, cp, host, stage)
+        kt, _, _, host, _ = self._kvt[gbs]
         return L.KvTier(kt, host, nb - self.kv_host_seqs // gbs)
 
     def _sched_args(self):
