@@ -50,6 +50,17 @@ CONFIGS = {
     7: dict(workload="opt-30b-shape fp16 block decode, 50% of weights in pinned host memory",
             l=48, h1=7168, h2=28672, nh=56, hd=128, w="f16", kv="q4", gbs=32, nb=8, s=512, n=32,
             tier=True),
+    # the pages' CPU delegation of attention: the same fp16 cache placement,
+    # with the host batches' history moved to the device (8) or their
+    # attention computed on the host CPU (9)
+    8: dict(workload="opt-1.3b-shape fp16 block decode, fp16 KV cache of two of four GPU batches in "
+                     "pinned host memory, moved through the device slots",
+            l=24, h1=2048, h2=8192, nh=32, hd=64, w="f16", kv="f16", gbs=32, nb=4, s=512, n=32,
+            kv_host_seqs=64),
+    9: dict(workload="opt-1.3b-shape fp16 block decode, fp16 KV cache of two of four GPU batches in "
+                     "pinned host memory, their attention on the host CPU",
+            l=24, h1=2048, h2=8192, nh=32, hd=64, w="f16", kv="f16", gbs=32, nb=4, s=512, n=32,
+            kv_host_seqs=64, kv_host_attention=True),
 }
 # Workloads that are not run: an earlier version of the OPT-66B-shape tiered run
 # ended in a host segmentation fault after its timed decode, and the cause has
@@ -61,6 +72,13 @@ REFUSED = {4: "the OPT-66B-shape weight-tiering run is not taken: an earlier ver
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def host_cpu_threads() -> int:
+    """CPU threads for host-side attention: the process's CPU share
+    (OMP_NUM_THREADS when set, else its affinity), at most 16."""
+    n = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    return max(1, min(16, n))
 
 
 def build_model(cfg, keep_layer0_host: bool):
@@ -541,8 +559,10 @@ def main():
     t_build = time.time()
     log(f"building {cfg['workload']} ({cfg['l']} layers, bls {bls})")
     sh, layers, tier, emb, host0, quant, fmt = build_model(cfg, want_cpu)
+    host_threads = host_cpu_threads()
     model = Model(sh, layers, emb, fmt(cfg["kv"]), bls, max_len, tier=tier,
-                  kv_host_seqs=cfg.get("kv_host_seqs", 0))
+                  kv_host_seqs=cfg.get("kv_host_seqs", 0),
+                  kv_host_attention=cfg.get("kv_host_attention", False), host_threads=host_threads)
     tokens = synth.tokens(bls, s, seed=0, device="cuda")
     torch.cuda.synchronize()
     log(f"built in {time.time() - t_build:.1f} s; prefill s={s} ...")
@@ -620,7 +640,7 @@ def main():
     }
     if not args.no_trace and s + K // 2 <= 8192 and not cfg.get("kv_host_seqs"):
         out["roofline_attn_topk"] = topk_attention(model, cfg, L, s + K // 2)
-    if s + K <= 8192:
+    if s + K <= 8192 and not cfg.get("kv_host_attention"):   # the host path is dense only
         out["decode_attn_topk"] = sparse_decode(model, cfg, L, tok1, min(K, 8), args.no_trace)
     if tier is not None and "w_h2d" in tr:
         # weight tiering: host bytes staged per step and the copy stream's busy
@@ -659,6 +679,22 @@ def main():
                           "metadata into a device slot (copy stream); stores: the appended rows "
                           "back (their own stream); overlap = max(load busy time, GEMM + "
                           "attention time) / step time"}
+    if cfg.get("kv_host_attention"):
+        # per step: the host batches' history the CPU reads (K and V rows of
+        # every layer, at the timed steps' mean position) against the rows
+        # that cross the link (q, k, v down, the attention row back)
+        step = t_dec / K
+        p_mean = s + Wm + (K - 1) / 2
+        hist = cfg["kv_host_seqs"] * cfg["l"] * p_mean * cfg["h1"] * 2 * 2
+        link = cfg["kv_host_seqs"] * cfg["l"] * 4 * cfg["h1"] * 2
+        out["host_attention"] = {
+            "host_sequences": cfg["kv_host_seqs"], "cpu_threads": host_threads,
+            "history_bytes_per_step": round(hist), "link_bytes_per_step": round(link),
+            "step_s": round(step, 4), "history_GBs_over_step": round(hist / step / 1e9, 2),
+            "definition": "the host batches' attention computed by the CPU over the fp16 host "
+                          "cache, only their q, k, v rows and attention rows crossing the link; "
+                          "history_GBs_over_step = history bytes read by the CPU per step / step "
+                          "time (a lower bound on the CPU's rate)"}
     if policy_block is not None:
         policy_block["measured_ms_per_step"] = out["ms_per_step"]
         policy_block["measured_prefill_s"] = round(t_prefill, 3)
