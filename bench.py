@@ -468,8 +468,10 @@ def plan_policy(cfg, gpu_gb: float, host_gb: float):
     for the config's model under the given HBM and host-memory budgets, over
     gbs in {16, 32, 48, 64} x 1..8 GPU batches, within what this executor
     realizes (activations on the GPU, at most half of an fp16 layer's weights
-    off it); the shares are then rounded up to whole tiered layers and whole
-    host-resident GPU batches, and the cost model predicts that placement."""
+    off it), with and without decode attention of an fp16 host cache share on
+    the host CPU; the shares are then rounded up to whole tiered layers and
+    whole host-resident GPU batches, and the cost model predicts that
+    placement."""
     from throughput_oriented_offloaded_amd import policy as P
     q4 = P.Q4G64
     wl = P.Workload(cfg["l"], cfg["h1"], cfg["h2"], cfg["s"], cfg["n"],
@@ -483,19 +485,21 @@ def plan_policy(cfg, gpu_gb: float, host_gb: float):
                          f"{host_gb} GB of host memory")
     gbs, nb = best["gbs"], best["num_gpu_batches"]
     r = P.realize(wl, best["shares"], nb)
-    est = P.estimate(wl, mc, gbs * nb, gbs, r["shares"])
+    cpu_attn = bool(best["cpu_attention"] and r["kv_host_batches"] > 0)
+    est = P.estimate(wl, mc, gbs * nb, gbs, r["shares"], cpu_attn)
     fits = est["peak"]["g"] * mc.alpha_g <= mc.cap_g and est["peak"]["c"] <= mc.cap_c
     block = {"gpu_mem_gb": gpu_gb, "host_mem_gb": host_gb, "search": "gbs {16,32,48,64} x nb 1..8",
              "gbs": gbs, "num_gpu_batches": nb, "bls": gbs * nb,
              "lp_shares": {k: round(v, 4) for k, v in best["shares"].items()},
              "realized_shares": {k: round(v, 4) for k, v in r["shares"].items()},
              "tiered_layers": r["n_tiered"], "kv_host_gpu_batches": r["kv_host_batches"],
+             "cpu_attention": cpu_attn,
              "realized_fits_budgets": bool(fits),
              "predicted_ms_per_step": round(est["T_gen"] * wl.l * 1e3, 2),
              "predicted_prefill_s": round(est["T_pre"] * wl.l, 3),
              "predicted_peak_gb": {k: round(v / 1e9, 2) for k, v in est["peak"].items()}}
     over = dict(gbs=gbs, nb=nb, tier_layers=r["tiered_layers"], tier=False,
-                kv_host_seqs=r["kv_host_batches"] * gbs)
+                kv_host_seqs=r["kv_host_batches"] * gbs, kv_host_attention=cpu_attn)
     return over, block
 
 

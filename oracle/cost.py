@@ -29,6 +29,17 @@ the same pattern (the readings are listed with the design notes):
     weight bytes at HBM bandwidth; decode attention is the cache bytes read
     at the GPU's attention bandwidth; prefill runs its projections and
     2 bls s^2 h1 causal attention flops at the prompt GEMM rate.
+
+CPU delegation of decode attention ([P2] "为什么有时应该在 CPU 上算注意力": for
+a cache already on the CPU side, computing its attention there moves the
+current token's activations instead of the cache), as a policy switch for
+fp16 caches: in decode, the CPU share of the cache (cc) no longer crosses
+CPU -> GPU nor comes back; instead each of its sequences sends its q, k, v
+rows down (3 h1 fp16) and its attention row up (h1 fp16), the CPU reads that
+share of the cache at its attention bandwidth (a sixth path, "cpu", which
+overlaps the others like them), and the GPU's attention reads only the
+other shares.  Parity unpinned for the CPU rate (a measured constant, as
+the GPU's rates are).
 """
 from __future__ import annotations
 
@@ -37,7 +48,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-PATHS = ("c2g", "g2c", "d2c", "c2d", "comp")
+PATHS = ("c2g", "g2c", "d2c", "c2d", "comp", "cpu")
 
 
 @dataclass(frozen=True)
@@ -67,6 +78,7 @@ class Hardware:
     alpha_g: float = 1.0      # peak memory is multiplied by these before the
     alpha_c: float = 1.0      # capacity test
     alpha_d: float = 1.0
+    cpu_attn_bw: float = 0.0  # bytes/s of cache read by decode attention on the CPU (0: none)
 
 
 def layer_weight_bytes(m: Model) -> float:
@@ -83,9 +95,10 @@ def act_bytes(m: Model, bls: int, tokens: float) -> float:
     return 2 * bls * tokens * m.h1
 
 
-def path_times(m: Model, hw: Hardware, bls: int, p: dict, phase: str) -> dict:
-    """Seconds per layer on each of the five paths for placement p (keys
-    wg wc wd hg hc hd cg cc cd) in phase "pre" or "gen"."""
+def path_times(m: Model, hw: Hardware, bls: int, p: dict, phase: str, cpu_attn: bool = False) -> dict:
+    """Seconds per layer on each of the six paths for placement p (keys
+    wg wc wd hg hc hd cg cc cd) in phase "pre" or "gen"; cpu_attn: decode
+    attention of the CPU-resident cache share on the CPU."""
     W = layer_weight_bytes(m)
     off_w = p["wc"] + p["wd"]
     off_c = p["cc"] + p["cd"]
@@ -102,12 +115,25 @@ def path_times(m: Model, hw: Hardware, bls: int, p: dict, phase: str) -> dict:
         cache_out = cache_bytes(m, bls, m.s)
         act = act_bytes(m, bls, m.s)
         comp = (bls * m.s * mats + 2 * bls * m.s * m.s * m.h1) / hw.prefill_flops
+    if cpu_attn and phase == "gen":
+        assert m.c_ratio == 1.0 and hw.cpu_attn_bw > 0, "CPU attention over an fp16 cache only"
+        qkv_down, attn_up = 3 * act, act             # fp16 rows of the CPU share's sequences
+        gpu_attn = cache_in * (1 - p["cc"]) / hw.attn_bw
+        return {
+            "c2g": (off_w * W + p["cd"] * cache_in + off_h * act + p["cc"] * attn_up) / hw.bw_c2g,
+            "g2c": (p["cd"] * cache_out + off_h * act + p["cc"] * qkv_down) / hw.bw_g2c,
+            "d2c": (p["wd"] * W + p["cd"] * cache_in + p["hd"] * act) / hw.bw_d2c,
+            "c2d": (p["cd"] * cache_out + p["hd"] * act) / hw.bw_c2d,
+            "comp": comp - cache_in / hw.attn_bw + gpu_attn,
+            "cpu": p["cc"] * cache_in / hw.cpu_attn_bw,
+        }
     return {
         "c2g": (off_w * W + off_c * cache_in + off_h * act) / hw.bw_c2g,
         "g2c": (off_c * cache_out + off_h * act) / hw.bw_g2c,
         "d2c": (p["wd"] * W + p["cd"] * cache_in + p["hd"] * act) / hw.bw_d2c,
         "c2d": (p["cd"] * cache_out + p["hd"] * act) / hw.bw_c2d,
         "comp": comp,
+        "cpu": 0.0,
     }
 
 
@@ -149,10 +175,10 @@ def peak_memory(m: Model, bls: int, gbs: int, p: dict) -> dict:
     return {t: max(pre[t], gen[t]) for t in "gcd"}
 
 
-def total_time(m: Model, hw: Hardware, bls: int, p: dict) -> float:
+def total_time(m: Model, hw: Hardware, bls: int, p: dict, cpu_attn: bool = False) -> float:
     """[P2]: T = l T_pre + l (n - 1) T_gen, each T the max over the paths."""
     t_pre = max(path_times(m, hw, bls, p, "pre").values())
-    t_gen = max(path_times(m, hw, bls, p, "gen").values())
+    t_gen = max(path_times(m, hw, bls, p, "gen", cpu_attn).values())
     return m.l * t_pre + m.l * (m.n - 1) * t_gen
 
 
@@ -168,12 +194,12 @@ def feasible(m: Model, hw: Hardware, bls: int, gbs: int, p: dict, tol: float = 1
         hw.alpha_d * pk["d"] <= hw.cap_d * (1 + tol) + tol
 
 
-def objective(m: Model, hw: Hardware, bls: int, p: dict) -> float:
+def objective(m: Model, hw: Hardware, bls: int, p: dict, cpu_attn: bool = False) -> float:
     """Seconds per sequence, T / bls (the quantity the search minimizes)."""
-    return total_time(m, hw, bls, p) / bls
+    return total_time(m, hw, bls, p, cpu_attn) / bls
 
 
-def grid_search(m: Model, hw: Hardware, bls: int, gbs: int, step: float):
+def grid_search(m: Model, hw: Hardware, bls: int, gbs: int, step: float, cpu_attn: bool = False):
     """Every placement whose fractions are multiples of `step`; returns the
     feasible one of least T / bls and its value (None, inf if none).  With no
     disk capacity only placements without a disk share are visited (any
@@ -190,7 +216,7 @@ def grid_search(m: Model, hw: Hardware, bls: int, gbs: int, step: float):
              "cg": cg, "cc": cc, "cd": max(0.0, 1 - cg - cc)}
         if not feasible(m, hw, bls, gbs, p):
             continue
-        v = objective(m, hw, bls, p)
+        v = objective(m, hw, bls, p, cpu_attn)
         if v < best_v:
             best, best_v = p, v
     return best, best_v

@@ -286,3 +286,110 @@ def test_executor_realization_rounds_up_and_stays_feasible(pol):
     wq = pol.Workload(48, 7168, 28672, 512, 32, w_ratio=pol.Q4G64, c_ratio=pol.Q4G64)
     bq = pol.search(wq, mc, gbs_list=(16,), nb_max=4, limits=pol.executor_limits(False))
     assert bq is not None and bq["shares"]["wc"] == pytest.approx(0.0)
+
+
+# ------------------------------------------------- CPU attention (decode)
+def _pin_cpu_attention_moves():
+    """[P2] "为什么有时应该在 CPU 上算注意力": bringing a CPU-resident cache to
+    the GPU for a one-query attention moves about 4 b s h1 bytes, while
+    attending on the CPU moves only about 4 b h1, a factor of about s apart.
+    With every link at 1 byte/s (times are bytes) and the whole cache on the
+    host: without delegation CPU -> GPU carries 4 b L h1 (L the mean decode
+    length standing for s); with it the two links together carry the new
+    cache entries, which go back in either case, plus exactly 4 b h1 (the
+    query going down and the attention row coming up)."""
+    m = oc.Model(l=4, h1=512, h2=2048, s=300, n=20)
+    hw = _hw(bw_c2g=1.0, bw_g2c=1.0, cpu_attn_bw=1e9)
+    p = dict(wg=1, wc=0, wd=0, hg=1, hc=0, hd=0, cg=0, cc=1, cd=0)
+    b, L = 24, m.s + m.n / 2
+    off = oc.path_times(m, hw, b, p, "gen")
+    on = oc.path_times(m, hw, b, p, "gen", cpu_attn=True)
+    kv_move = 4 * b * L * m.h1
+    act_move = 4 * b * m.h1
+    new_entries = 4 * b * m.h1
+    assert off["c2g"] == pytest.approx(kv_move, rel=1e-12)
+    assert off["g2c"] == pytest.approx(new_entries, rel=1e-12)
+    assert on["c2g"] + on["g2c"] - new_entries == pytest.approx(act_move, rel=1e-12)
+    assert off["c2g"] / (on["c2g"] + on["g2c"] - new_entries) == pytest.approx(L, rel=1e-12)
+    # the host reads the whole cache at its attention rate; the GPU none of it
+    assert on["cpu"] == pytest.approx(kv_move / hw.cpu_attn_bw, rel=1e-12)
+    free_attn = _hw(bw_c2g=1.0, bw_g2c=1.0, cpu_attn_bw=1e9, attn_bw=1e30)
+    assert on["comp"] == pytest.approx(oc.path_times(m, free_attn, b, p, "gen")["comp"], rel=1e-12)
+
+
+def test_pages_cpu_attention_moves():
+    _pin_cpu_attention_moves()
+
+
+def test_cpu_attention_without_a_host_share_changes_nothing():
+    """Delegation only touches the host-resident cache share: with cc = 0
+    every path time is the same either way and the CPU path is idle; the
+    prompt phase is never delegated."""
+    m = oc.Model(l=4, h1=512, h2=2048, s=128, n=16)
+    hw = _hw(cpu_attn_bw=40e9)
+    p = dict(wg=0.4, wc=0.5, wd=0.1, hg=0.7, hc=0.3, hd=0, cg=0.6, cc=0, cd=0.4)
+    assert oc.path_times(m, hw, 32, p, "gen", True) == oc.path_times(m, hw, 32, p, "gen")
+    q = dict(p, cg=0.2, cc=0.4)
+    assert oc.path_times(m, hw, 32, q, "pre", True) == oc.path_times(m, hw, 32, q, "pre")
+    assert oc.path_times(m, hw, 32, q, "gen")["cpu"] == 0.0
+
+
+def test_cpu_attention_fp16_cache_only(pol):
+    """The pages' authors turn delegation off with a 4-bit cache (the CPU's
+    quantize / dequantize costs eat the saving); both models refuse it, and
+    the search does not try it."""
+    m = oc.Model(l=4, h1=512, h2=2048, s=128, n=16, c_ratio=9 / 32)
+    hw = _hw(cpu_attn_bw=40e9)
+    p = dict(wg=1, wc=0, wd=0, hg=1, hc=0, hd=0, cg=0, cc=1, cd=0)
+    with pytest.raises(AssertionError):
+        oc.path_times(m, hw, 8, p, "gen", True)
+    _, _, wl, mc = _pair(pol, dict(l=4, h1=512, h2=2048, s=128, n=16, c_ratio=9 / 32), dict(cpu_attn_bw=40e9))
+    with pytest.raises(ValueError):
+        pol.estimate(wl, mc, 8, 8, p, cpu_attn=True)
+    best = pol.search(wl, mc, gbs_list=(8,), nb_max=2)
+    assert best is not None and best["cpu_attention"] is False
+
+
+CPU_CASES = [
+    # 30B fp16 on a 16 GB GPU: the cache lives on the host, PCIe-bound
+    (dict(l=48, h1=7168, h2=28672, s=512, n=32), dict(cpu_attn_bw=50e9), 144, 48, 0.1),
+    # 1.3B-shape, tight memories, a slow host
+    (dict(l=24, h1=2048, h2=8192, s=256, n=64), dict(cap_g=2e9, cap_c=20e9, cap_d=0.0, cpu_attn_bw=5e9),
+     256, 32, 0.05),
+]
+
+
+@pytest.mark.parametrize("wl_kw,hw_kw,bls,gbs,step", CPU_CASES)
+def test_cpu_attention_estimate_and_lp_match_oracle(pol, wl_kw, hw_kw, bls, gbs, step):
+    m, hw, wl, mc = _pair(pol, wl_kw, hw_kw)
+    rng = np.random.default_rng(2)
+    for _ in range(20):
+        f = [rng.dirichlet(np.ones(3)) for _ in range(3)]
+        p = dict(zip(pol.SHARES, np.concatenate(f).tolist()))
+        got = pol.estimate(wl, mc, bls, gbs, p, cpu_attn=True)
+        for ph in ("pre", "gen"):
+            want = oc.path_times(m, hw, bls, p, ph, cpu_attn=True)
+            for k in oc.PATHS:
+                assert got["paths_" + ph][k] == pytest.approx(want[k], rel=1e-12, abs=1e-18)
+        assert got["T"] == pytest.approx(oc.total_time(m, hw, bls, p, cpu_attn=True), rel=1e-12)
+    shares, v = pol.solve(wl, mc, bls, gbs, cpu_attn=True)
+    assert shares is not None
+    assert oc.feasible(m, hw, bls, gbs, shares, tol=1e-7)
+    assert oc.objective(m, hw, bls, shares, cpu_attn=True) == pytest.approx(v, rel=1e-6)
+    _, grid_v = oc.grid_search(m, hw, bls, gbs, step, cpu_attn=True)
+    assert v <= grid_v * (1 + 1e-9)
+
+
+def test_search_delegates_only_when_it_pays(pol):
+    """Where the host holds the cache and PCIe is the bottleneck, a host
+    with spare bandwidth makes delegation the better policy; a host with
+    almost none does not ("只在缓存本来就在 CPU、PCIe 搬运成为瓶颈、CPU 还有可用算力
+    时成立")."""
+    wl_kw = dict(l=48, h1=7168, h2=28672, s=512, n=32)
+    _, _, wl, fast = _pair(pol, wl_kw, dict(cpu_attn_bw=50e9))
+    _, _, _, slow = _pair(pol, wl_kw, dict(cpu_attn_bw=1e8))
+    on = pol.search(wl, fast, gbs_list=(16, 48), nb_max=4)
+    assert on["cpu_attention"] is True
+    off = pol.search(wl, fast, gbs_list=(16, 48), nb_max=4, cpu_attn=False)
+    assert on["seconds_per_sequence"] < off["seconds_per_sequence"]
+    assert pol.search(wl, slow, gbs_list=(16, 48), nb_max=4)["cpu_attention"] is False

@@ -25,6 +25,14 @@ bandwidth (small batches read weights faster than they multiply them);
 decode attention reads the cache at the attention kernel's bandwidth;
 prefill runs its flops (projections and causal attention) at the prompt
 GEMM rate.
+
+CPU attention ("为什么有时应该在 CPU 上算注意力"): for an fp16 cache the
+decode attention of the CPU-resident share can run on the host, which then
+reads that share at its own bandwidth (a sixth path, "cpu") while only the
+q, k, v rows of its sequences go down to the host (3 h1 fp16 each) and their
+attention rows come back (h1 fp16), instead of the cache crossing to the
+GPU; the GPU's attention reads the other shares only.  The search tries the
+policy both ways where the cache is fp16 and the machine has a CPU rate.
 """
 from __future__ import annotations
 
@@ -35,7 +43,7 @@ from dataclasses import asdict, dataclass
 import numpy as np
 
 SHARES = ("wg", "wc", "wd", "hg", "hc", "hd", "cg", "cc", "cd")
-PATHS = ("c2g", "g2c", "d2c", "c2d", "comp")
+PATHS = ("c2g", "g2c", "d2c", "c2d", "comp", "cpu")
 Q4G64 = 9.0 / 32.0          # 4-bit codes + fp16 (min, scale) per 64, over fp16
 
 
@@ -66,6 +74,7 @@ class Machine:
     alpha_g: float = 1.0     # peak-memory multipliers (fragmentation, runtime)
     alpha_c: float = 1.0
     alpha_d: float = 1.0
+    cpu_attn_bw: float = 0.0  # fp16 cache read by decode attention on the host, bytes/s (0: none)
 
 
 def mi355x(host_bytes: float = 1.0e12, disk_bytes: float = 0.0, disk_bw: float = 2.0e9) -> Machine:
@@ -74,11 +83,13 @@ def mi355x(host_bytes: float = 1.0e12, disk_bytes: float = 0.0, disk_bw: float =
     reverse direction assumed equal), 4-bit decode GEMM 961 TFLOP/s at
     M = 144, prompt-shaped GEMMs and attention 1.09 PFLOP/s effective (OPT-175B
     prefill), decode attention 5.63 TB/s, weight streaming at 5.6 TB/s of the
-    8 TB/s HBM.  288 GB of HBM with 10% held back (alpha_g 1.1).  Host memory
-    and disk are machine-specific arguments (no disk tier by default)."""
+    8 TB/s HBM.  288 GB of HBM with 10% held back (alpha_g 1.1).  Decode
+    attention on 16 host threads reads an fp16 cache at 260 GB/s or more
+    (the lower end measured).  Host memory and disk are machine-specific
+    arguments (no disk tier by default)."""
     return Machine(bw_c2g=55.9e9, bw_g2c=55.9e9, bw_d2c=disk_bw, bw_c2d=disk_bw / 2,
                    gemm_flops=961e12, prefill_flops=1.09e15, hbm_bw=5.6e12, attn_bw=5.63e12,
-                   cap_g=288e9, cap_c=host_bytes, cap_d=disk_bytes, alpha_g=1.1)
+                   cap_g=288e9, cap_c=host_bytes, cap_d=disk_bytes, alpha_g=1.1, cpu_attn_bw=260e9)
 
 
 MODELS = {   # OPT shapes: layers, h1, h2
@@ -87,10 +98,13 @@ MODELS = {   # OPT shapes: layers, h1, h2
 }
 
 
-def _affine(wl: Workload, mc: Machine, bls: int, gbs: int):
-    """Coefficients of the nine shares: path times T[phase] = A f + b (5 x 9,
-    5) for phase "pre" and "gen", and memory held M = P f + q (3 x 9, 3) for
-    tiers g, c, d in each phase ("mem_pre", "mem_gen")."""
+def _affine(wl: Workload, mc: Machine, bls: int, gbs: int, cpu_attn: bool = False):
+    """Coefficients of the nine shares: path times T[phase] = A f + b (6 x 9,
+    6) for phase "pre" and "gen", and memory held M = P f + q (3 x 9, 3) for
+    tiers g, c, d in each phase ("mem_pre", "mem_gen").  cpu_attn: decode
+    attention of the host cache share on the host (fp16 cache only)."""
+    if cpu_attn and not (wl.c_ratio == 1.0 and mc.cpu_attn_bw > 0):
+        raise ValueError("CPU attention needs an fp16 cache and a host attention rate")
     h1, h2 = wl.h1, wl.h2
     W = (8 * h1 * h1 + 4 * h1 * h2) * wl.w_ratio
     mats = 8 * h1 * h1 + 4 * h1 * h2
@@ -104,19 +118,26 @@ def _affine(wl: Workload, mc: Machine, bls: int, gbs: int):
         else:
             c_in, c_out, act = 0.0, 4 * bls * wl.s * h1 * wl.c_ratio, 2 * bls * wl.s * h1
             comp = (bls * wl.s * mats + 2 * bls * wl.s * wl.s * h1) / mc.prefill_flops
-        A = np.zeros((5, 9))
-        b = np.zeros(5)
-        # CPU -> GPU: every off-GPU share of the layer's inputs
-        for k, v in (("wc", W), ("wd", W), ("cc", c_in), ("cd", c_in), ("hc", act), ("hd", act)):
+        host_attn = cpu_attn and ph == "gen"
+        A = np.zeros((6, 9))
+        b = np.zeros(6)
+        # CPU -> GPU: every off-GPU share of the layer's inputs (host
+        # attention: the host share's attention rows instead of its cache)
+        for k, v in (("wc", W), ("wd", W), ("cc", act if host_attn else c_in), ("cd", c_in),
+                     ("hc", act), ("hd", act)):
             A[0, i[k]] += v / mc.bw_c2g
         # GPU -> CPU: new cache entries and outputs of the off-GPU shares
-        for k, v in (("cc", c_out), ("cd", c_out), ("hc", act), ("hd", act)):
+        # (host attention: the host share's q, k, v rows)
+        for k, v in (("cc", 3 * act if host_attn else c_out), ("cd", c_out), ("hc", act), ("hd", act)):
             A[1, i[k]] += v / mc.bw_g2c
         for k, v in (("wd", W), ("cd", c_in), ("hd", act)):
             A[2, i[k]] += v / mc.bw_d2c
         for k, v in (("cd", c_out), ("hd", act)):
             A[3, i[k]] += v / mc.bw_c2d
         b[4] = comp
+        if host_attn:                         # the host share leaves the GPU's attention
+            A[4, i["cc"]] -= c_in / mc.attn_bw
+            A[5, i["cc"]] += c_in / mc.cpu_attn_bw
         out[ph] = (A, b)
     # peak memory per phase: the prompt (cache at s, activations of s tokens
     # per sequence) and a decode step (cache at s + n, one token); each
@@ -140,10 +161,10 @@ def _affine(wl: Workload, mc: Machine, bls: int, gbs: int):
     return out
 
 
-def estimate(wl: Workload, mc: Machine, bls: int, gbs: int, shares: dict) -> dict:
+def estimate(wl: Workload, mc: Machine, bls: int, gbs: int, shares: dict, cpu_attn: bool = False) -> dict:
     """Times, throughput and peak memory of one policy."""
     f = np.array([shares[k] for k in SHARES], dtype=np.float64)
-    co = _affine(wl, mc, bls, gbs)
+    co = _affine(wl, mc, bls, gbs, cpu_attn)
     res = {}
     for ph in ("pre", "gen"):
         A, b = co[ph]
@@ -157,18 +178,19 @@ def estimate(wl: Workload, mc: Machine, bls: int, gbs: int, shares: dict) -> dic
     return res
 
 
-def solve(wl: Workload, mc: Machine, bls: int, gbs: int, limits: dict | None = None):
+def solve(wl: Workload, mc: Machine, bls: int, gbs: int, limits: dict | None = None,
+          cpu_attn: bool = False):
     """Best shares for fixed (bls, gbs): (shares, T / bls) or (None, inf).
     limits: optional {share: (low, high)} bounds, e.g. what an executor can
     realize (activations kept on the GPU, at most half of a layer's weights
-    off it)."""
+    off it).  cpu_attn: decode attention of the host cache share on the host."""
     from scipy.optimize import linprog
-    co = _affine(wl, mc, bls, gbs)
+    co = _affine(wl, mc, bls, gbs, cpu_attn)
     nv = 11                                   # nine shares, z_pre, z_gen
     rows, rhs = [], []
     for zi, ph in ((9, "pre"), (10, "gen")):
         A, b = co[ph]
-        for r in range(5):                    # A f + b <= z
+        for r in range(len(PATHS)):           # A f + b <= z
             row = np.zeros(nv)
             row[:9] = A[r]
             row[zi] = -1.0
@@ -202,19 +224,26 @@ def solve(wl: Workload, mc: Machine, bls: int, gbs: int, limits: dict | None = N
 
 
 def search(wl: Workload, mc: Machine, gbs_list=(8, 16, 24, 32, 48, 64, 96, 128, 192, 256),
-           nb_max: int = 64, limits: dict | None = None):
-    """The (gbs, nb, shares) of least T / bls over gbs_list x 1..nb_max."""
+           nb_max: int = 64, limits: dict | None = None, cpu_attn: bool | None = None):
+    """The (gbs, nb, shares, cpu attention) of least T / bls over gbs_list x
+    1..nb_max.  cpu_attn None: both ways where the cache is fp16 and the
+    machine has a host attention rate, else without."""
+    if cpu_attn is None:
+        modes = (False, True) if wl.c_ratio == 1.0 and mc.cpu_attn_bw > 0 else (False,)
+    else:
+        modes = (cpu_attn,)
     best = None
-    for gbs in gbs_list:
-        for nb in range(1, nb_max + 1):
-            shares, v = solve(wl, mc, gbs * nb, gbs, limits)
-            if shares is not None and (best is None or v < best[3]):
-                best = (gbs, nb, shares, v)
+    for ca in modes:
+        for gbs in gbs_list:
+            for nb in range(1, nb_max + 1):
+                shares, v = solve(wl, mc, gbs * nb, gbs, limits, ca)
+                if shares is not None and (best is None or v < best[3]):
+                    best = (gbs, nb, shares, v, ca)
     if best is None:
         return None
-    gbs, nb, shares, v = best
-    return {"gbs": gbs, "num_gpu_batches": nb, "bls": gbs * nb, "shares": shares,
-            "seconds_per_sequence": v, **estimate(wl, mc, gbs * nb, gbs, shares)}
+    gbs, nb, shares, v, ca = best
+    return {"gbs": gbs, "num_gpu_batches": nb, "bls": gbs * nb, "shares": shares, "cpu_attention": ca,
+            "seconds_per_sequence": v, **estimate(wl, mc, gbs * nb, gbs, shares, ca)}
 
 
 def executor_limits(fp16_weights: bool) -> dict:
@@ -254,6 +283,8 @@ def main(argv=None):
     ap.add_argument("--num-gpu-batches", type=int)
     ap.add_argument("--percent", type=float, nargs=6,
                     help="wg wc cg cc hg hc in percent (disk = the rest): estimate this policy")
+    ap.add_argument("--cpu-attention", choices=("auto", "on", "off"), default="auto",
+                    help="decode attention of the host cache share on the host (fp16 cache only)")
     a = ap.parse_args(argv)
     l, h1, h2 = MODELS[a.model]
     wl = Workload(l, h1, h2, a.prompt_len, a.gen_len,
@@ -265,10 +296,11 @@ def main(argv=None):
         sh = {"wg": wg, "wc": wc, "wd": 1 - wg - wc, "cg": cg, "cc": cc, "cd": 1 - cg - cc,
               "hg": hg, "hc": hc, "hd": 1 - hg - hc}
         gbs, nb = a.gpu_batch_size or 48, a.num_gpu_batches or 3
-        out = {"gbs": gbs, "num_gpu_batches": nb, "shares": sh,
-               **estimate(wl, mc, gbs * nb, gbs, sh)}
+        ca = a.cpu_attention == "on"
+        out = {"gbs": gbs, "num_gpu_batches": nb, "shares": sh, "cpu_attention": ca,
+               **estimate(wl, mc, gbs * nb, gbs, sh, ca)}
     else:
-        out = search(wl, mc)
+        out = search(wl, mc, cpu_attn=None if a.cpu_attention == "auto" else a.cpu_attention == "on")
     print(json.dumps({"workload": asdict(wl), "policy": out}, indent=1))
 
 
