@@ -469,37 +469,32 @@ def plan_policy(cfg, gpu_gb: float, host_gb: float):
     gbs in {16, 32, 48, 64} x 1..8 GPU batches, within what this executor
     realizes (activations on the GPU, at most half of an fp16 layer's weights
     off it), with and without decode attention of an fp16 host cache share on
-    the host CPU; the shares are then rounded up to whole tiered layers and
-    whole host-resident GPU batches, and the cost model predicts that
-    placement."""
+    the host CPU; each point's shares are rounded up to whole tiered layers
+    and whole host-resident GPU batches, and the cost model's best realized
+    placement is the one run."""
     from throughput_oriented_offloaded_amd import policy as P
     q4 = P.Q4G64
     wl = P.Workload(cfg["l"], cfg["h1"], cfg["h2"], cfg["s"], cfg["n"],
                     w_ratio=q4 if cfg["w"] == "q4" else 1.0, c_ratio=q4 if cfg["kv"] == "q4" else 1.0)
     base = P.mi355x(host_gb * 1e9)
     mc = P.Machine(**{**base.__dict__, "cap_g": gpu_gb * 1e9})
-    best = P.search(wl, mc, gbs_list=(16, 32, 48, 64), nb_max=8,
-                    limits=P.executor_limits(cfg["w"] == "f16"))
+    best = P.search_realized(wl, mc, gbs_list=(16, 32, 48, 64), nb_max=8,
+                             limits=P.executor_limits(cfg["w"] == "f16"))
     if best is None:
         raise SystemExit(f"policy: no placement of {cfg['workload']} fits {gpu_gb} GB of HBM and "
                          f"{host_gb} GB of host memory")
-    gbs, nb = best["gbs"], best["num_gpu_batches"]
-    r = P.realize(wl, best["shares"], nb)
-    cpu_attn = bool(best["cpu_attention"] and r["kv_host_batches"] > 0)
-    est = P.estimate(wl, mc, gbs * nb, gbs, r["shares"], cpu_attn)
-    fits = est["peak"]["g"] * mc.alpha_g <= mc.cap_g and est["peak"]["c"] <= mc.cap_c
+    gbs, nb, est = best["gbs"], best["num_gpu_batches"], best["estimate"]
     block = {"gpu_mem_gb": gpu_gb, "host_mem_gb": host_gb, "search": "gbs {16,32,48,64} x nb 1..8",
              "gbs": gbs, "num_gpu_batches": nb, "bls": gbs * nb,
-             "lp_shares": {k: round(v, 4) for k, v in best["shares"].items()},
-             "realized_shares": {k: round(v, 4) for k, v in r["shares"].items()},
-             "tiered_layers": r["n_tiered"], "kv_host_gpu_batches": r["kv_host_batches"],
-             "cpu_attention": cpu_attn,
-             "realized_fits_budgets": bool(fits),
+             "lp_shares": {k: round(v, 4) for k, v in best["lp_shares"].items()},
+             "realized_shares": {k: round(v, 4) for k, v in best["shares"].items()},
+             "tiered_layers": best["n_tiered"], "kv_host_gpu_batches": best["kv_host_batches"],
+             "cpu_attention": best["cpu_attention"],
              "predicted_ms_per_step": round(est["T_gen"] * wl.l * 1e3, 2),
              "predicted_prefill_s": round(est["T_pre"] * wl.l, 3),
              "predicted_peak_gb": {k: round(v / 1e9, 2) for k, v in est["peak"].items()}}
-    over = dict(gbs=gbs, nb=nb, tier_layers=r["tiered_layers"], tier=False,
-                kv_host_seqs=r["kv_host_batches"] * gbs, kv_host_attention=cpu_attn)
+    over = dict(gbs=gbs, nb=nb, tier_layers=best["tiered_layers"], tier=False,
+                kv_host_seqs=best["kv_host_batches"] * gbs, kv_host_attention=best["cpu_attention"])
     return over, block
 
 

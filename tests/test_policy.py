@@ -393,3 +393,31 @@ def test_search_delegates_only_when_it_pays(pol):
     off = pol.search(wl, fast, gbs_list=(16, 48), nb_max=4, cpu_attn=False)
     assert on["seconds_per_sequence"] < off["seconds_per_sequence"]
     assert pol.search(wl, slow, gbs_list=(16, 48), nb_max=4)["cpu_attention"] is False
+
+
+def test_realized_search_ranks_placements_as_realized(pol):
+    """OPT-1.3B fp16 with all of HBM: the continuous LP prefers a sliver of
+    host cache with CPU attention (the host attends in parallel with the
+    GPU), but whole GPU batches are the executor's unit, and one whole batch
+    on the host makes the CPU the slowest path; the realized search keeps
+    every cache on the GPU.  Its choice fits the capacities under the
+    oracle's own test and is no worse, as realized, than rounding either
+    mode's LP optimum."""
+    wl = pol.Workload(24, 2048, 8192, 512, 32)
+    mc = pol.mi355x(64e9)
+    lim = pol.executor_limits(True)
+    kw = dict(gbs_list=(16, 32, 48, 64), nb_max=8, limits=lim)
+    lp = pol.search(wl, mc, **kw)
+    assert lp["cpu_attention"] is True and 0 < lp["shares"]["cc"] < 0.5
+    best = pol.search_realized(wl, mc, **kw)
+    assert best["cpu_attention"] is False and best["kv_host_batches"] == 0
+    m = oc.Model(l=24, h1=2048, h2=8192, s=512, n=32)
+    hw = oc.Hardware(**{k: getattr(mc, k) for k in oc.Hardware.__dataclass_fields__})
+    assert oc.feasible(m, hw, best["bls"], best["gbs"], best["shares"], tol=1e-7)
+    assert oc.objective(m, hw, best["bls"], best["shares"], best["cpu_attention"]) == \
+        pytest.approx(best["seconds_per_sequence"], rel=1e-9)
+    for ca in (False, True):
+        b = pol.search(wl, mc, cpu_attn=ca, **kw)
+        r = pol.realize(wl, b["shares"], b["num_gpu_batches"])
+        v = oc.objective(m, hw, b["bls"], r["shares"], ca and r["kv_host_batches"] > 0)
+        assert best["seconds_per_sequence"] <= v * (1 + 1e-9)

@@ -270,6 +270,39 @@ def realize(wl: Workload, shares: dict, nb: int) -> dict:
     return {"n_tiered": n_tiered, "tiered_layers": layers, "kv_host_batches": nb_host, "shares": sh}
 
 
+def search_realized(wl: Workload, mc: Machine, gbs_list=(16, 32, 48, 64), nb_max: int = 8,
+                    limits: dict | None = None):
+    """The executor's best placement: every (gbs, nb, CPU attention) point's
+    LP optimum under `limits`, rounded by realize() and costed as realized
+    (CPU attention only where a whole GPU batch's cache ends up on the host);
+    the realized placement of least T / bls among those that fit the
+    capacities.  Rounding can reverse the LP's ranking: a small host cache
+    share with CPU attention wins the continuous program, and the whole GPU
+    batch it becomes may leave the host attending far more than it should."""
+    modes = (False, True) if wl.c_ratio == 1.0 and mc.cpu_attn_bw > 0 else (False,)
+    best = None
+    for ca in modes:
+        for gbs in gbs_list:
+            for nb in range(1, nb_max + 1):
+                bls = gbs * nb
+                shares, v_lp = solve(wl, mc, bls, gbs, limits, ca)
+                if shares is None:
+                    continue
+                r = realize(wl, shares, nb)
+                ca_r = ca and r["kv_host_batches"] > 0
+                est = estimate(wl, mc, bls, gbs, r["shares"], ca_r)
+                pk = est["peak"]
+                if pk["g"] * mc.alpha_g > mc.cap_g or pk["c"] * mc.alpha_c > mc.cap_c or \
+                        pk["d"] * mc.alpha_d > mc.cap_d + 1e-9:
+                    continue
+                v = est["T"] / bls
+                if best is None or v < best["seconds_per_sequence"]:
+                    best = {"gbs": gbs, "num_gpu_batches": nb, "bls": bls, "lp_shares": shares,
+                            "lp_seconds_per_sequence": v_lp, "cpu_attention": ca_r, **r,
+                            "seconds_per_sequence": v, "estimate": est}
+    return best
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description="offloading policy search / estimate on one MI355X")
     ap.add_argument("--model", default="opt-175b", choices=sorted(MODELS))
