@@ -230,3 +230,46 @@ def test_tiered_topk_decode_matches_oracle(L):
     err = np.abs(oracle.to_f16(got).astype(np.float32) - oracle.to_f16(ref_dense).astype(np.float32)).max()
     tol = 1e-2 * np.abs(oracle.to_f16(ref_dense).astype(np.float32)).max() + 1e-3
     assert err > tol, "the dense result also matches: Top-K was not exercised"
+
+
+def test_weight_tiering_with_host_attention(L):
+    """Weight tiering (host halves of layers 0 and 2), an fp16 cache with one
+    of two GPU batches in pinned host memory, and that batch's decode
+    attention on the host CPU, all in one model: the prefill's tokens and
+    logits equal the resident model's bit for bit (same kernels, the cache
+    through the slots); teacher-forced on the resident model's tokens, every
+    decode step's logits agree within the tolerance (the host computes its
+    batch's attention in its own order)."""
+    import torch
+    from throughput_oriented_offloaded_amd.model import DeviceLayer, Model, Shape, TierLayer
+    sh = Shape(n_layers=3, h1=768, h2=3072, n_heads=12, head_dim=64)
+    gbs, nb, s, n = 2, 2, 24, 5
+    bls = gbs * nb
+    f16 = L.FG_FMT_F16
+    Ws = [{k: v.cuda() for k, v in synth.layer_weights(sh.h1, sh.h2, j, seed=9).items()}
+          for j in range(sh.n_layers)]
+    emb = {k: v.cuda() for k, v in synth.embeddings(sh.h1, s + n, seed=9).items()}
+    ref = Model(sh, [DeviceLayer.from_fp16(W, f16) for W in Ws], emb, f16, bls, s + n)
+    layers, tier = [], []
+    for j, W in enumerate(Ws):
+        if j != 1:
+            dl, tl = TierLayer.split(W, f16)
+            layers.append(dl)
+            tier.append(tl)
+        else:
+            layers.append(DeviceLayer.from_fp16(W, f16))
+            tier.append(None)
+    both = Model(sh, layers, emb, f16, bls, s + n, tier=tier, kv_host_seqs=gbs, kv_host_attention=True,
+                 host_threads=4)
+    toks = synth.tokens(bls, s, seed=9).cuda()
+    lg_r, tok_r = ref.prefill(toks, gbs, nb)
+    lg_b, tok_b = both.prefill(toks, gbs, nb)
+    torch.cuda.synchronize()
+    assert torch.equal(lg_r, lg_b) and torch.equal(tok_r, tok_b)
+    tok = tok_r
+    for i in range(n - 1):
+        lg_r, nxt = ref.decode_step(tok, s + i, gbs, nb)
+        lg_b, _ = both.decode_step(tok, s + i, gbs, nb)
+        torch.cuda.synchronize()
+        assert_close(np16(lg_b), np16(lg_r), f"decode step {i} logits")
+        tok = nxt
