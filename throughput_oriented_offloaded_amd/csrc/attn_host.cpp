@@ -26,6 +26,7 @@
 #include <condition_variable>
 #include <cstring>
 #include <limits>
+#include <memory>
 #include <mutex>
 #include <new>
 #include <system_error>
@@ -288,24 +289,33 @@ int check_host_attn(const void* qkv, int64_t ld, const fg_kv* kv, int32_t seq0, 
     return FG_OK;
 }
 
-void host_attn_decode_f16(const uint16_t* qkv, int64_t ld, const fg_kv* kv, int32_t seq0, int32_t nseq,
-                          const fg_dims* d, int32_t pos, bool append, uint16_t* out, HostPool& pool) {
+int host_attn_decode_f16(const uint16_t* qkv, int64_t ld, const fg_kv* kv, int32_t seq0, int32_t nseq,
+                         const fg_dims* d, int32_t pos, bool append, uint16_t* out, HostPool& pool) {
     const int nh = d->n_heads, hd = d->head_dim;
     const int64_t h1 = d->h1, ml = kv->max_len;
     uint16_t* kc = static_cast<uint16_t*>(kv->k);
     uint16_t* vc = static_cast<uint16_t*>(kv->v);
     const bool avx = have_avx2();
+    // nothing may leave a worker by exception (it would end the process, or
+    // end run() while other threads still use f): a chunk whose score buffer
+    // cannot be allocated is skipped and reported after the loop
+    std::atomic<bool> no_mem{false};
     std::function<void(int64_t, int64_t)> f = [&](int64_t b, int64_t e) {
-        std::vector<float> s((size_t)((pos + 7) & ~7) + 8);
+        std::unique_ptr<float[]> buf(new (std::nothrow) float[(size_t)((pos + 7) & ~7) + 8]);
+        if (!buf) {
+            no_mem.store(true);
+            return;
+        }
+        float* s = buf.get();
         for (int64_t u = b; u < e; ++u) {
             const int64_t sq = u / nh;
             const int h = (int)(u - sq * nh);
             const int64_t row0 = ((seq0 + sq) * nh + h) * ml * hd;
             const uint16_t* r = qkv + sq * ld + (int64_t)h * hd;
             Item it{r, r + h1, r + 2 * h1, kc + row0, vc + row0, out + sq * h1 + (int64_t)h * hd};
-            if (avx && hd == 64) item_avx2<64>(it, pos, s.data());
-            else if (avx && hd == 128) item_avx2<128>(it, pos, s.data());
-            else item_scalar(it, hd, pos, s.data());
+            if (avx && hd == 64) item_avx2<64>(it, pos, s);
+            else if (avx && hd == 128) item_avx2<128>(it, pos, s);
+            else item_scalar(it, hd, pos, s);
             if (append) {
                 std::memcpy(it.K + (int64_t)pos * hd, it.kn, (size_t)hd * 2);
                 std::memcpy(it.V + (int64_t)pos * hd, it.vn, (size_t)hd * 2);
@@ -313,6 +323,8 @@ void host_attn_decode_f16(const uint16_t* qkv, int64_t ld, const fg_kv* kv, int3
         }
     };
     pool.run((int64_t)nseq * nh, f);
+    if (no_mem.load()) return set_error(FG_ERR_CAPACITY, "host attention: out of host memory");
+    return FG_OK;
 }
 
 }  // namespace fg
@@ -325,10 +337,9 @@ extern "C" int fg_attn_decode_host_f16(const void* qkv, int64_t ld, const fg_kv*
     if (st != FG_OK) return st;
     try {
         fg::HostPool pool(n_threads);
-        fg::host_attn_decode_f16(static_cast<const uint16_t*>(qkv), ld, kv, seq0, nseq, d, pos, append != 0,
-                                 static_cast<uint16_t*>(out), pool);
+        return fg::host_attn_decode_f16(static_cast<const uint16_t*>(qkv), ld, kv, seq0, nseq, d, pos,
+                                        append != 0, static_cast<uint16_t*>(out), pool);
     } catch (const std::bad_alloc&) {
         return fg::set_error(FG_ERR_CAPACITY, "host attention: out of host memory");
     }
-    return FG_OK;
 }

@@ -226,11 +226,7 @@ int kvtier_host_attend(const fg_kvtier* kt, const fg_kv* host, const fg_dims* d,
     const int64_t h1 = d->h1;
     const uint16_t* qkv = reinterpret_cast<const uint16_t*>(kt->hstage);
     uint16_t* o = reinterpret_cast<uint16_t*>(kt->hstage) + rows * 3 * h1;
-    try {
-        host_attn_decode_f16(qkv, 3 * h1, host, 0, (int32_t)rows, d, pos, true, o, *kt->pool);
-    } catch (const std::bad_alloc&) {
-        return set_error(FG_ERR_CAPACITY, "host attention: out of host memory");
-    }
+    FG_TRY(host_attn_decode_f16(qkv, 3 * h1, host, 0, (int32_t)rows, d, pos, true, o, *kt->pool));
     FG_HIP(hipMemcpyAsync(out, o, (size_t)rows * h1 * 2, hipMemcpyHostToDevice, st));
     return FG_OK;
 }
