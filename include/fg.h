@@ -304,7 +304,8 @@ int fg_kvtier_host_attention(fg_kvtier* kt, void* stage, size_t stage_bytes, int
  * rounding per output.  Runs on n_threads threads (<= 0: all hardware
  * threads) and returns when done.  FG_ERR_UNSUPPORTED for a 4-bit cache;
  * FG_ERR_INVALID for sequences or pos outside the cache, ld < 3*h1, null
- * pointers or bad dims.
+ * pointers or bad dims; FG_ERR_CAPACITY when host memory for the threads'
+ * score buffers runs out (out is then incomplete).
  */
 int fg_attn_decode_host_f16(const void* qkv, int64_t ld, const fg_kv* kv, int32_t seq0, int32_t nseq,
                             const fg_dims* d, int32_t pos, int32_t append, void* out,
