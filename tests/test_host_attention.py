@@ -10,6 +10,7 @@ from helpers import assert_close
 
 CASES = [  # bls, nh, hd, pos
     (1, 1, 64, 0), (2, 3, 64, 1), (2, 3, 64, 17), (3, 2, 128, 130), (4, 8, 64, 527), (2, 2, 128, 1000),
+    (1, 2, 128, 8191),   # the longest history a cache of 8192 rows holds
 ]
 
 
