@@ -232,12 +232,15 @@ def test_layer_decode_host_attention(L, nb_dev, P):
         assert torch.equal(hh[:, :, :P + 1], a[n_dev:, :, :P + 1].cpu())
 
 
-def test_model_decode_host_attention(L):
-    """2-layer OPT-125m-shape model, fp16 weights and cache, two of three GPU
-    batches' caches on the host: the prefill goes through the slots, the
-    decode steps' host attention runs on the CPU.  Teacher-forced on the
-    all-device model's tokens, every decode step's logits agree within the
-    tolerance and the host caches hold the same rows."""
+@pytest.mark.parametrize("host_batches", [1, 2, 3])
+def test_model_decode_host_attention(L, host_batches):
+    """2-layer OPT-125m-shape model, fp16 weights and cache, one, two or all
+    three GPU batches' caches on the host: the prefill goes through the slots,
+    the decode steps' host attention runs on the CPU, overlapped with the GPU's
+    work on the other rows (a device lane of the remaining batches, one or
+    two host lanes).  Teacher-forced on the all-device model's tokens, every
+    decode step's logits agree within the tolerance and the host caches hold
+    the same rows."""
     import torch
     from throughput_oriented_offloaded_amd.model import DeviceLayer, Model, Shape
     sh = Shape(n_layers=2, h1=768, h2=3072, n_heads=12, head_dim=64)
@@ -249,8 +252,8 @@ def test_model_decode_host_attention(L):
     layers = [DeviceLayer.from_fp16({k: v.cuda() for k, v in W.items()}, L.FG_FMT_F16) for W in Ws]
     embd = {k: v.cuda() for k, v in emb.items()}
     ref = Model(sh, layers, embd, L.FG_FMT_F16, bls, s + n)
-    ha = Model(sh, layers, embd, L.FG_FMT_F16, bls, s + n, kv_host_seqs=2 * gbs, kv_host_attention=True,
-               host_threads=4)
+    ha = Model(sh, layers, embd, L.FG_FMT_F16, bls, s + n, kv_host_seqs=host_batches * gbs,
+               kv_host_attention=True, host_threads=4)
     lg_r, tok_r = ref.prefill(toks, gbs, nb)
     lg_h, tok_h = ha.prefill(toks, gbs, nb)
     assert torch.equal(lg_r, lg_h)
@@ -261,7 +264,7 @@ def test_model_decode_host_attention(L):
         torch.cuda.synchronize()
         assert_close(np16(lg_h), np16(lg_r), f"decode step {i} logits")
         tok = nxt
-    n_dev = bls - 2 * gbs
+    n_dev = bls - host_batches * gbs
     for j in range(sh.n_layers):
         for a, hh in zip(_tensors(ref.kv[j]), _tensors(ha.kv_host[j])):
             assert torch.equal(hh[:, :, :s], a[n_dev:, :, :s].cpu())

@@ -108,15 +108,21 @@ int kvtier_check(const fg_kvtier* kt, const fg_dims* d, const fg_kv* dev, const 
 // Decode attention of the host-resident GPU batches on the host CPU
 // (kvtier.hip, attn_host.cpp), when the tier has a host stage: checks (fp16
 // host cache, dense attention, stage size for `rows` host sequences); send:
-// the rows' q, k, v to the stage and an event, on st; attend: wait for the
-// event on the host, compute the attention and append k, v at pos in the
-// host cache on the CPU, copy the attention rows to `out` on st.
+// the rows' q, k, v to the stage at byte offset `off` and the lane's event
+// (lane 0 or 1), on st; attend: wait for that event on the host, compute the
+// attention of host sequences seq0 .. seq0 + rows - 1 and append their k, v
+// at pos in the host cache on the CPU, copy the attention rows to `out` on
+// st.  A lane's stage region is host_stage_bytes(d, its rows).  lanes: the
+// tier's two lane compute streams and its start / lane-done events.
 bool kvtier_host_attention_on(const fg_kvtier* kt);
 size_t host_stage_bytes(const fg_dims* d, int64_t rows);
 int kvtier_host_check(const fg_kvtier* kt, const fg_kv* host, const fg_dims* d, int64_t rows, int32_t topk);
-int kvtier_host_send(const fg_kvtier* kt, const __half* qkv, int64_t rows, int64_t h1, hipStream_t st);
-int kvtier_host_attend(const fg_kvtier* kt, const fg_kv* host, const fg_dims* d, int64_t rows, int32_t pos,
-                       __half* out, hipStream_t st);
+int kvtier_host_send(const fg_kvtier* kt, int lane, size_t off, const __half* qkv, int64_t rows, int64_t h1,
+                     hipStream_t st);
+int kvtier_host_attend(const fg_kvtier* kt, int lane, size_t off, const fg_kv* host, int32_t seq0,
+                       const fg_dims* d, int64_t rows, int32_t pos, __half* out, hipStream_t st);
+size_t kvtier_host_stage_capacity(const fg_kvtier* kt);
+void kvtier_host_lanes(const fg_kvtier* kt, hipStream_t* lane_streams, hipEvent_t* events);
 // The host-resident GPU batches ("units") of one call, in execution order,
 // moved through the tier object's two slots.  begin(u): loads enqueued
 // through unit u + 1 (rows [0, load_rows) each), the compute stream made to
@@ -171,6 +177,12 @@ int layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, i
                   int32_t s, const fg_kv* kv, void* ws, size_t ws_bytes, hipStream_t st,
                   bool check_only, const KvTierCall* kvt);
 size_t layer_ws_bytes(const fg_dims* d, int64_t rows, int32_t fmt);
+// A whole decode step with the host batches' attention on the host CPU,
+// overlapped with the GPU's work on the other rows (layer.hip); *used false
+// (nothing enqueued) when it does not apply, see the definition.
+int model_decode_host_overlap(const fg_dims* d, int32_t n_layers, const fg_layer_w* w, const fg_kv* kv,
+                              void* x, int32_t gbs, int32_t nb, int32_t pos, void* ws, size_t ws_bytes,
+                              hipStream_t st, const fg_kv_tier* kvt, bool* used);
 
 int launch_layernorm(const __half* x, int64_t rows, int64_t h, const __half* g, const __half* b,
                      __half* y, hipStream_t st);

@@ -38,12 +38,16 @@ struct fg_kvtier {
     hipEvent_t stored[2];
     int device;
     // decode attention of the host batches on the host CPU (when hstage):
-    // pinned staging [rows, 3 h1] (q, k, v in) then [rows, h1] (attention
-    // out), the CPU threads, and the event that marks the rows' arrival
+    // pinned staging, per lane of host batches [rows, 3 h1] (q, k, v in) then
+    // [rows, h1] (attention out); the CPU threads; per lane the event that
+    // marks the rows' arrival; the lanes' compute streams and the events that
+    // order them against the caller's stream (start, lane 0 done, lane 1 done)
     unsigned char* hstage = nullptr;
     size_t hstage_bytes = 0;
     fg::HostPool* pool = nullptr;
-    hipEvent_t hready = nullptr;
+    hipEvent_t hready[2] = {nullptr, nullptr};
+    hipStream_t hs[2] = {nullptr, nullptr};
+    hipEvent_t hev[3] = {nullptr, nullptr, nullptr};
 };
 
 namespace fg {
@@ -210,25 +214,34 @@ int kvtier_host_check(const fg_kvtier* kt, const fg_kv* host, const fg_dims* d, 
     return FG_OK;
 }
 
-int kvtier_host_send(const fg_kvtier* kt, const __half* qkv, int64_t rows, int64_t h1, hipStream_t st) {
-    FG_HIP(hipMemcpyAsync(kt->hstage, qkv, (size_t)rows * 3 * h1 * 2, hipMemcpyDeviceToHost, st));
-    FG_HIP(hipEventRecord(kt->hready, st));
+int kvtier_host_send(const fg_kvtier* kt, int lane, size_t off, const __half* qkv, int64_t rows, int64_t h1,
+                     hipStream_t st) {
+    FG_HIP(hipMemcpyAsync(kt->hstage + off, qkv, (size_t)rows * 3 * h1 * 2, hipMemcpyDeviceToHost, st));
+    FG_HIP(hipEventRecord(kt->hready[lane], st));
     return FG_OK;
 }
 
-int kvtier_host_attend(const fg_kvtier* kt, const fg_kv* host, const fg_dims* d, int64_t rows, int32_t pos,
-                       __half* out, hipStream_t st) {
+int kvtier_host_attend(const fg_kvtier* kt, int lane, size_t off, const fg_kv* host, int32_t seq0,
+                       const fg_dims* d, int64_t rows, int32_t pos, __half* out, hipStream_t st) {
     // the host cache's rows stored by earlier calls (the prefill's) and this
     // layer's q, k, v rows must have landed before the CPU reads them
     FG_HIP(hipEventSynchronize(kt->stored[0]));
     FG_HIP(hipEventSynchronize(kt->stored[1]));
-    FG_HIP(hipEventSynchronize(kt->hready));
+    FG_HIP(hipEventSynchronize(kt->hready[lane]));
     const int64_t h1 = d->h1;
-    const uint16_t* qkv = reinterpret_cast<const uint16_t*>(kt->hstage);
-    uint16_t* o = reinterpret_cast<uint16_t*>(kt->hstage) + rows * 3 * h1;
-    FG_TRY(host_attn_decode_f16(qkv, 3 * h1, host, 0, (int32_t)rows, d, pos, true, o, *kt->pool));
+    const uint16_t* qkv = reinterpret_cast<const uint16_t*>(kt->hstage + off);
+    uint16_t* o = reinterpret_cast<uint16_t*>(kt->hstage + off) + rows * 3 * h1;
+    FG_TRY(host_attn_decode_f16(qkv, 3 * h1, host, seq0, (int32_t)rows, d, pos, true, o, *kt->pool));
     FG_HIP(hipMemcpyAsync(out, o, (size_t)rows * h1 * 2, hipMemcpyHostToDevice, st));
     return FG_OK;
+}
+
+size_t kvtier_host_stage_capacity(const fg_kvtier* kt) { return kt->hstage_bytes; }
+
+void kvtier_host_lanes(const fg_kvtier* kt, hipStream_t* lane_streams, hipEvent_t* events) {
+    lane_streams[0] = kt->hs[0];
+    lane_streams[1] = kt->hs[1];
+    for (int i = 0; i < 3; ++i) events[i] = kt->hev[i];
 }
 
 }  // namespace fg
@@ -304,7 +317,12 @@ extern "C" int fg_kvtier_host_attention(fg_kvtier* kt, void* stage, size_t stage
         (void)hipGetLastError();
         return fg::set_error(FG_ERR_INVALID, "host attention: the stage must be pinned host memory");
     }
-    if (!kt->hready) FG_HIP(hipEventCreateWithFlags(&kt->hready, hipEventDisableTiming));
+    for (int i = 0; i < 2; ++i) {
+        if (!kt->hready[i]) FG_HIP(hipEventCreateWithFlags(&kt->hready[i], hipEventDisableTiming));
+        if (!kt->hs[i]) FG_HIP(hipStreamCreateWithFlags(&kt->hs[i], hipStreamNonBlocking));
+    }
+    for (int i = 0; i < 3; ++i)
+        if (!kt->hev[i]) FG_HIP(hipEventCreateWithFlags(&kt->hev[i], hipEventDisableTiming));
     fg::HostPool* pool = nullptr;
     try {
         pool = new fg::HostPool(n_threads);
@@ -322,7 +340,15 @@ extern "C" int fg_kvtier_destroy(fg_kvtier* kt) {
     fg::clear_error();
     if (!kt) return FG_OK;
     delete kt->pool;
-    if (kt->hready) (void)hipEventDestroy(kt->hready);
+    for (int i = 0; i < 2; ++i) {
+        if (kt->hready[i]) (void)hipEventDestroy(kt->hready[i]);
+        if (kt->hs[i]) {
+            (void)hipStreamSynchronize(kt->hs[i]);
+            (void)hipStreamDestroy(kt->hs[i]);
+        }
+    }
+    for (int i = 0; i < 3; ++i)
+        if (kt->hev[i]) (void)hipEventDestroy(kt->hev[i]);
     (void)hipStreamSynchronize(kt->sp);
     (void)hipStreamDestroy(kt->sp);
     for (int i = 0; i < 2; ++i) {

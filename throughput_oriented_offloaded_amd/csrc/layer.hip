@@ -11,6 +11,10 @@
 // all bls = gbs * nb rows, so every weight byte is read once per layer per
 // step for the whole block.  The prefill walks the block's GPU batches one at
 // a time (workspace bounded by one GPU batch of gbs * s rows).
+#include <string>
+#include <system_error>
+#include <thread>
+
 #include "fg_internal.h"
 
 namespace fg {
@@ -123,6 +127,40 @@ int check_block(const fg_dims* d, const fg_kv* kv, int32_t gbs, int32_t nb, int3
     return FG_OK;
 }
 
+// The buffers of one decode call's workspace.
+struct DecWs {
+    __half *a, *qkv, *o, *f;
+    void* part;
+    size_t pb;
+};
+DecWs dec_ws(void* ws, const WsLayout& L) {
+    unsigned char* base = static_cast<unsigned char*>(ws);
+    return DecWs{(__half*)(base + L.a), (__half*)(base + L.qkv), (__half*)(base + L.o), (__half*)(base + L.f),
+                 base + L.part, L.wdq - L.part};
+}
+
+// A decode layer up to its attention: LN1 (unless the previous layer fused
+// it into the workspace) and the QKV projection of `rows` rows of x.
+int dec_pre(const fg_dims* d, const fg_layer_w* w, __half* xh, int64_t rows, const DecWs& b, hipStream_t st,
+            bool ln1_done) {
+    const int64_t h1 = d->h1;
+    if (!ln1_done)
+        FG_TRY(launch_layernorm(xh, rows, h1, (const __half*)w->ln1_g, (const __half*)w->ln1_b, b.a, st));
+    return lin(w, 0, b.a, rows, h1, 3 * h1, 0, nullptr, b.qkv, b.part, b.pb, st);
+}
+
+// A decode layer after its attention (rows in b.o): out-projection + residual
+// with LN2 fused, FC1 + ReLU, FC2 + residual (with the next layer's LN1
+// fused when `next`).
+int dec_post(const fg_dims* d, const fg_layer_w* w, __half* xh, int64_t rows, const DecWs& b, hipStream_t st,
+             const fg_layer_w* next) {
+    const int64_t h1 = d->h1, h2 = d->h2;
+    FG_TRY(lin(w, 1, b.o, rows, h1, h1, 0, xh, xh, b.part, b.pb, st, w->ln2_g, w->ln2_b, b.a));
+    FG_TRY(lin(w, 2, b.a, rows, h1, h2, 1, nullptr, b.f, b.part, b.pb, st));
+    if (next) return lin(w, 3, b.f, rows, h2, h1, 0, xh, xh, b.part, b.pb, st, next->ln1_g, next->ln1_b, b.a);
+    return lin(w, 3, b.f, rows, h2, h1, 0, xh, xh, b.part, b.pb, st);
+}
+
 }  // namespace
 
 // Positions whose V a sparse step reads: the fraction ppm / 1e6 of the
@@ -151,19 +189,13 @@ int layer_decode(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, in
     if (ws_bytes < L.total)
         return set_error(FG_ERR_CAPACITY, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
     if (check_only) return FG_OK;
-    unsigned char* base = static_cast<unsigned char*>(ws);
-    __half* a = (__half*)(base + L.a);
-    __half* qkv = (__half*)(base + L.qkv);
-    __half* o = (__half*)(base + L.o);
-    __half* f = (__half*)(base + L.f);
-    void* part = base + L.part;
-    const size_t pb = L.wdq - L.part;
+    const DecWs b = dec_ws(ws, L);
+    __half* qkv = b.qkv;
+    __half* o = b.o;
     __half* xh = (__half*)x;
-    const int64_t h1 = d->h1, h2 = d->h2;
+    const int64_t h1 = d->h1;
 
-    if (!ln1_done)
-        FG_TRY(launch_layernorm(xh, bls, h1, (const __half*)w->ln1_g, (const __half*)w->ln1_b, a, st));
-    FG_TRY(lin(w, 0, a, bls, h1, 3 * h1, 0, nullptr, qkv, part, pb, st));
+    FG_TRY(dec_pre(d, w, xh, bls, b, st, ln1_done));
     // GPU batches with a device-resident cache in one launch; the others one
     // by one on their slot of the KV tier (history loaded, row pos appended
     // there and stored back).  Attention reads rows < pos and takes the
@@ -176,13 +208,14 @@ int layer_decode(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, in
     // With host attention, the host batches' q, k, v rows go to the host
     // first, the device batches' attention runs while the CPU computes theirs,
     // and their attention rows come back before the out-projection.
-    if (host_attn) FG_TRY(kvtier_host_send(kvt->kt, qkv + (int64_t)nd * gbs * 3 * h1, (int64_t)(nb - nd) * gbs, h1, st));
+    if (host_attn)
+        FG_TRY(kvtier_host_send(kvt->kt, 0, 0, qkv + (int64_t)nd * gbs * 3 * h1, (int64_t)(nb - nd) * gbs, h1, st));
     FG_TRY(launch_attn_decode(qkv, qkv + h1, qkv + 2 * h1, 3 * h1, kv, nd * gbs, d, pos, 0, o, st,
                               topk));
     FG_TRY(launch_kv_store(qkv + h1, qkv + 2 * h1, 3 * h1, kv, 0, nd * gbs, pos, 1, d, st));
     if (host_attn)
-        FG_TRY(kvtier_host_attend(kvt->kt, kvt->host, d, (int64_t)(nb - nd) * gbs, pos, o + (int64_t)nd * gbs * h1,
-                                  st));
+        FG_TRY(kvtier_host_attend(kvt->kt, 0, 0, kvt->host, 0, d, (int64_t)(nb - nd) * gbs, pos,
+                                  o + (int64_t)nd * gbs * h1, st));
     for (int32_t k = host_attn ? nb : nd; k < nb; ++k) {
         const int32_t u = kvt->u0 + (k - nd);
         const __half* q = qkv + (int64_t)k * gbs * 3 * h1;
@@ -193,13 +226,121 @@ int layer_decode(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, in
         FG_TRY(launch_kv_store(q + h1, q + 2 * h1, 3 * h1, &slot, 0, gbs, pos, 1, d, st));
         FG_TRY(kvt->pipe->end(u, pos, pos + 1));
     }
-    FG_TRY(lin(w, 1, o, bls, h1, h1, 0, xh, xh, part, pb, st, w->ln2_g, w->ln2_b, a));
-    FG_TRY(lin(w, 2, a, bls, h1, h2, 1, nullptr, f, part, pb, st));
-    if (next)   // the next layer's first LayerNorm, fused with this residual sum
-        FG_TRY(lin(w, 3, f, bls, h2, h1, 0, xh, xh, part, pb, st, next->ln1_g, next->ln1_b, a));
-    else
-        FG_TRY(lin(w, 3, f, bls, h2, h1, 0, xh, xh, part, pb, st));
-    return FG_OK;
+    return dec_post(d, w, xh, bls, b, st, next);
+}
+
+// A decode step of the whole model whose host batches' attention runs on the
+// host CPU, overlapped with GPU work ("FlexGen 完全拆解": the CPU delegation of
+// section "为什么有时应该在 CPU 上算注意力", overlapped with compute as the
+// data paths of section "三条关键数据通路如何重叠" are).  With one fused block
+// GEMM per projection, a layer's out-projection needs every row's attention,
+// so the GPU would wait while the CPU attends.  Here the block's rows split
+// into lanes that share only the weights:
+//  * the device batches (cache in HBM): every layer enqueued at once on the
+//    caller's stream;
+//  * the host batches, in one lane or two of whole GPU batches, each on a
+//    stream of the tier's, driven layer by layer by the calling thread.
+//    While the CPU attends one lane's layer, the GPU runs the other lane's
+//    out-projection, MLP and next QKV projection, and the device lane.
+// Each lane multiplies its own rows, so each weight byte is read once per
+// lane per layer (the cost of the overlap).  *used: false, with nothing
+// enqueued, when the workspace cannot hold the lanes' buffers or the layers'
+// weight formats differ; the caller then takes the serialized path.
+int model_decode_host_overlap(const fg_dims* d, int32_t n_layers, const fg_layer_w* w, const fg_kv* kv,
+                              void* x, int32_t gbs, int32_t nb, int32_t pos, void* ws, size_t ws_bytes,
+                              hipStream_t st, const fg_kv_tier* kvt, bool* used) {
+    *used = false;
+    const int32_t nd = kvt->nb_dev, nh = nb - kvt->nb_dev;
+    const fg_kvtier* kt = kvt->pipe;
+    // every layer validated as the serialized path does (weights, block,
+    // caches, host stage for all host rows)
+    for (int32_t j = 0; j < n_layers; ++j) {
+        const KvTierCall kc{nullptr, kt, &kvt->host[j], nd, 0};
+        FG_TRY(layer_decode(d, &w[j], x, gbs, nb, pos, &kv[j], ws, ws_bytes, st, true, j > 0,
+                            j + 1 < n_layers ? &w[j + 1] : nullptr, 0, &kc));
+        if (w[j].fmt != w[0].fmt) return FG_OK;
+    }
+    const int nl = nh >= 2 ? 2 : 1;
+    const int64_t h1 = d->h1;
+    int64_t rows[2] = {(int64_t)((nh + 1) / 2) * gbs, (int64_t)(nh / 2) * gbs};
+    const int64_t seq0[2] = {0, rows[0]};
+    const size_t off[2] = {0, host_stage_bytes(d, rows[0])};
+    if (off[1] + host_stage_bytes(d, rows[1]) > kvtier_host_stage_capacity(kt)) return FG_OK;
+    // workspaces: the device lane's, then each host lane's
+    const size_t A = 256;
+    const WsLayout Ld = layout(d, (int64_t)nd * gbs, w[0].fmt);
+    WsLayout Ll[2];
+    size_t at = nd > 0 ? align_up(Ld.total, A) : 0, lane_at[2];
+    for (int l = 0; l < nl; ++l) {
+        Ll[l] = layout(d, rows[l], w[0].fmt);
+        lane_at[l] = at;
+        at += align_up(Ll[l].total, A);
+    }
+    if (at > ws_bytes) return FG_OK;
+    hipStream_t ls[2];
+    hipEvent_t ev[3];
+    kvtier_host_lanes(kt, ls, ev);
+    *used = true;
+
+    unsigned char* base = static_cast<unsigned char*>(ws);
+    __half* xh = (__half*)x;
+    FG_HIP(hipEventRecord(ev[0], st));   // the lanes start after the caller's work so far
+    for (int l = 0; l < nl; ++l) FG_HIP(hipStreamWaitEvent(ls[l], ev[0], 0));
+    // the device lane is enqueued by a thread of its own, so that its
+    // launches do not delay the host lanes' first attention
+    int dev_rc = FG_OK;
+    std::string dev_err;
+    auto device_lane = [&]() {
+        for (int32_t j = 0; nd > 0 && j < n_layers; ++j) {
+            dev_rc = layer_decode(d, &w[j], x, gbs, nd, pos, &kv[j], ws, Ld.total, st, false, j > 0,
+                                  j + 1 < n_layers ? &w[j + 1] : nullptr, 0, nullptr);
+            if (dev_rc != FG_OK) {
+                dev_err = fg_last_error();
+                return;
+            }
+        }
+    };
+    std::thread dev_thread;
+    try {
+        dev_thread = std::thread(device_lane);
+    } catch (const std::system_error&) {
+        device_lane();   // no thread to spare: enqueued here first
+    }
+    DecWs b[2];
+    __half* xl[2];
+    for (int l = 0; l < nl; ++l) {
+        b[l] = dec_ws(base + lane_at[l], Ll[l]);
+        xl[l] = xh + ((int64_t)nd * gbs + seq0[l]) * h1;
+    }
+    auto lanes = [&]() -> int {
+        for (int l = 0; l < nl; ++l) {
+            FG_TRY(dec_pre(d, &w[0], xl[l], rows[l], b[l], ls[l], false));
+            FG_TRY(kvtier_host_send(kt, l, off[l], b[l].qkv, rows[l], h1, ls[l]));
+        }
+        for (int32_t j = 0; j < n_layers; ++j) {
+            const fg_layer_w* next = j + 1 < n_layers ? &w[j + 1] : nullptr;
+            for (int l = 0; l < nl; ++l) {
+                FG_TRY(kvtier_host_attend(kt, l, off[l], &kvt->host[j], (int32_t)seq0[l], d, rows[l], pos, b[l].o,
+                                          ls[l]));
+                FG_TRY(dec_post(d, &w[j], xl[l], rows[l], b[l], ls[l], next));
+                if (next) {
+                    FG_TRY(dec_pre(d, next, xl[l], rows[l], b[l], ls[l], true));
+                    FG_TRY(kvtier_host_send(kt, l, off[l], b[l].qkv, rows[l], h1, ls[l]));
+                }
+            }
+        }
+        return FG_OK;
+    };
+    const int rc = lanes();
+    if (dev_thread.joinable()) dev_thread.join();
+    // the caller's stream continues after both lanes, also after an error
+    // (nothing enqueued on a lane is left unordered against later work)
+    for (int l = 0; l < nl; ++l) {
+        FG_HIP(hipEventRecord(ev[1 + l], ls[l]));
+        FG_HIP(hipStreamWaitEvent(st, ev[1 + l], 0));
+    }
+    if (dev_rc != FG_OK) return set_error(dev_rc, "%s", dev_err.c_str());
+    return rc;
 }
 
 int layer_prefill(const fg_dims* d, const fg_layer_w* w, void* x, int32_t gbs, int32_t nb,

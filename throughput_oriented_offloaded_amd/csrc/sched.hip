@@ -238,6 +238,14 @@ extern "C" int fg_model_decode_step(fg_sched* sc, const fg_dims* d, int32_t n_la
     FG_TRY(check_dims(d));
     FG_CHECK_ARG(n_layers >= 1 && w && kv, "need n_layers >= 1 and layer arrays");
     hipStream_t st = as_stream(stream);
+    // host batches attended by the host CPU, no weight tiering: the CPU's
+    // attention overlapped with the GPU's work on the other rows
+    if (!tier && kvt && kvt->host && kvt->nb_dev >= 0 && kvt->nb_dev < nb && kvtier_host_attention_on(kvt->pipe) &&
+        attn_topk_count(pos, attn_topk_ppm) < 0) {
+        bool used = false;
+        FG_TRY(model_decode_host_overlap(d, n_layers, w, kv, x, gbs, nb, pos, ws, ws_bytes, st, kvt, &used));
+        if (used) return FG_OK;
+    }
     KvPipe pipe(kvt ? kvt->pipe : nullptr, d, gbs, pos, st);
     FG_TRY(kv_units(kvt, n_layers, gbs, nb, pipe));
     return run_layers(sc, d, n_layers, w, tier, st, as_stream(copy_stream), flags,
