@@ -278,13 +278,25 @@ int fg_kvtier_destroy(fg_kvtier* kt);
  * After fg_kvtier_host_attention(kt, stage, stage_bytes, n_threads) with a
  * non-NULL stage, the decode calls of that tier (fg_layer_decode_block,
  * fg_model_decode_step) no longer move host batches' histories through the
- * slots.  Per layer they copy the host batches' q, k, v rows into `stage`
- * on the call's stream, wait on the host until they have arrived (the
- * device batches' attention is enqueued first and runs meanwhile), compute
- * the host batches' attention with n_threads CPU threads, append their k, v
- * at row pos of the host cache directly, and copy the attention rows back on
- * the stream; the calls therefore return only after the GPU has reached
- * each layer's attention.  Prefill calls keep using the slots.  stage:
+ * slots.  Per layer they copy the host batches' q, k, v rows into `stage`,
+ * wait on the host until they have arrived, compute the host batches'
+ * attention with n_threads CPU threads, append their k, v at row pos of the
+ * host cache directly, and copy the attention rows back; the calls
+ * therefore return only after the GPU has reached the last layer's
+ * attention.  fg_layer_decode_block does this on the call's stream (the
+ * device batches' attention is enqueued first and runs meanwhile).
+ * fg_model_decode_step without weight tiering overlaps the CPU's attention
+ * with GPU work: the device batches run every layer on the call's stream
+ * (enqueued from a second host thread) and the host batches run as one or
+ * two lanes of whole GPU batches on two streams the tier object creates, so
+ * that the GPU computes one lane while the CPU attends the other; each lane
+ * multiplies its own rows (each weight read once per lane per layer), and
+ * the call's stream waits for the lanes before the call returns.  It needs
+ * workspace for the lanes' buffers side by side (a little more than the
+ * whole block's: each lane has its own split-k partials); with less, or with
+ * weight tiering, it takes the serialized form above.  Results of the
+ * two forms agree within rounding (their GEMMs sum partials in different
+ * orders).  Prefill calls keep using the slots.  stage:
  * caller-owned pinned host memory of stage_bytes >=
  * fg_kvtier_host_stage_bytes(d, n_host_seq), n_host_seq the host-resident
  * sequences of a call ((nb - nb_dev) * gbs); it must not be touched while a

@@ -84,12 +84,12 @@ def mi355x(host_bytes: float = 1.0e12, disk_bytes: float = 0.0, disk_bw: float =
     M = 144, prompt-shaped GEMMs and attention 1.09 PFLOP/s effective (OPT-175B
     prefill), decode attention 5.63 TB/s, weight streaming at 5.6 TB/s of the
     8 TB/s HBM.  288 GB of HBM with 10% held back (alpha_g 1.1).  Decode
-    attention on 16 host threads reads an fp16 cache at 260 GB/s or more
-    (the lower end measured).  Host memory and disk are machine-specific
-    arguments (no disk tier by default)."""
+    attention on 16 host threads, overlapped with the GPU's work, reads an
+    fp16 cache at 300 GB/s (history bytes over the whole step).  Host memory
+    and disk are machine-specific arguments (no disk tier by default)."""
     return Machine(bw_c2g=55.9e9, bw_g2c=55.9e9, bw_d2c=disk_bw, bw_c2d=disk_bw / 2,
                    gemm_flops=961e12, prefill_flops=1.09e15, hbm_bw=5.6e12, attn_bw=5.63e12,
-                   cap_g=288e9, cap_c=host_bytes, cap_d=disk_bytes, alpha_g=1.1, cpu_attn_bw=260e9)
+                   cap_g=288e9, cap_c=host_bytes, cap_d=disk_bytes, alpha_g=1.1, cpu_attn_bw=300e9)
 
 
 MODELS = {   # OPT shapes: layers, h1, h2
