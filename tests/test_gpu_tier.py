@@ -232,14 +232,15 @@ def test_tiered_topk_decode_matches_oracle(L):
     assert err > tol, "the dense result also matches: Top-K was not exercised"
 
 
-def test_weight_tiering_with_host_attention(L):
+@pytest.mark.parametrize("host_batches", [1, 2])
+def test_weight_tiering_with_host_attention(L, host_batches):
     """Weight tiering (host halves of layers 0 and 2), an fp16 cache with one
-    of two GPU batches in pinned host memory, and that batch's decode
+    or both of two GPU batches in pinned host memory, and their decode
     attention on the host CPU, all in one model: the prefill's tokens and
     logits equal the resident model's bit for bit (same kernels, the cache
     through the slots); teacher-forced on the resident model's tokens, every
-    decode step's logits agree within the tolerance (the host computes its
-    batch's attention in its own order)."""
+    decode step's logits agree within the tolerance (the host computes the
+    attention in its own order)."""
     import torch
     from throughput_oriented_offloaded_amd.model import DeviceLayer, Model, Shape, TierLayer
     sh = Shape(n_layers=3, h1=768, h2=3072, n_heads=12, head_dim=64)
@@ -259,8 +260,8 @@ def test_weight_tiering_with_host_attention(L):
         else:
             layers.append(DeviceLayer.from_fp16(W, f16))
             tier.append(None)
-    both = Model(sh, layers, emb, f16, bls, s + n, tier=tier, kv_host_seqs=gbs, kv_host_attention=True,
-                 host_threads=4)
+    both = Model(sh, layers, emb, f16, bls, s + n, tier=tier, kv_host_seqs=host_batches * gbs,
+                 kv_host_attention=True, host_threads=4)
     toks = synth.tokens(bls, s, seed=9).cuda()
     lg_r, tok_r = ref.prefill(toks, gbs, nb)
     lg_b, tok_b = both.prefill(toks, gbs, nb)
