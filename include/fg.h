@@ -272,8 +272,11 @@ int fg_kvtier_destroy(fg_kvtier* kt);
  * the link is the bottleneck, the CPU computes that batch's attention, and
  * only the current token's q, k, v (3·h1 values per sequence) go down the
  * link and its attention row (h1 values) comes back, instead of the whole
- * history).  The pages turn this off with 4-bit compression; here it takes
- * fp16 caches only (FG_ERR_UNSUPPORTED for 4-bit ones at the layer calls).
+ * history).  The pages turn this off with 4-bit compression, since on their
+ * host the CPU's dequantization costs what the smaller transfer saves; here
+ * both formats are delegated: a 4-bit history is read compressed and
+ * dequantized in registers, and the new row is quantized on the CPU with the
+ * codec's exact arithmetic (the same bytes as the device quantizer).
  *
  * After fg_kvtier_host_attention(kt, stage, stage_bytes, n_threads) with a
  * non-NULL stage, the decode calls of that tier (fg_layer_decode_block,
@@ -308,13 +311,16 @@ int fg_kvtier_host_attention(fg_kvtier* kt, void* stage, size_t stage_bytes, int
 
 /*
  * The host-CPU attention itself, on host memory only (no GPU involved): for
- * sequences seq0 .. seq0+nseq-1 of the fp16 cache `kv` (host pointers) at
+ * sequences seq0 .. seq0+nseq-1 of the cache `kv` (host pointers; fp16 for
+ * the _f16 entry point, 4-bit for _q4, whose cached values are min + code *
+ * scale in fp32 and whose append quantizes k, v as fg_kv_append_q4 does) at
  * position pos, the history rows < pos from the cache and the current token
  * from its fresh k, v.  qkv: fp16 [nseq, ld] rows, q at column 0, k at h1, v
  * at 2*h1 (ld >= 3*h1).  out: fp16 [nseq, h1].  append != 0: also store k, v
  * at row pos of the cache.  Scores, softmax and the V sum in fp32, one fp16
  * rounding per output.  Runs on n_threads threads (<= 0: all hardware
- * threads) and returns when done.  FG_ERR_UNSUPPORTED for a 4-bit cache;
+ * threads) and returns when done.  FG_ERR_UNSUPPORTED for a cache of the
+ * other format;
  * FG_ERR_INVALID for sequences or pos outside the cache, ld < 3*h1, null
  * pointers or bad dims; FG_ERR_CAPACITY when host memory for the threads'
  * score buffers runs out (out is then incomplete).
@@ -322,6 +328,9 @@ int fg_kvtier_host_attention(fg_kvtier* kt, void* stage, size_t stage_bytes, int
 int fg_attn_decode_host_f16(const void* qkv, int64_t ld, const fg_kv* kv, int32_t seq0, int32_t nseq,
                             const fg_dims* d, int32_t pos, int32_t append, void* out,
                             int32_t n_threads);
+int fg_attn_decode_host_q4(const void* qkv, int64_t ld, const fg_kv* kv, int32_t seq0, int32_t nseq,
+                           const fg_dims* d, int32_t pos, int32_t append, void* out,
+                           int32_t n_threads);
 
 /* KV tier of one layer or model call.  host: one pinned host cache (layer
  * calls) or n_layers of them (model calls), each with n_seq >=

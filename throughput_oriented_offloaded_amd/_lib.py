@@ -116,6 +116,8 @@ _PROTOS = {
     "fg_kvtier_host_attention": (ctypes.c_int, [P, P, SZ, I32]),
     "fg_attn_decode_host_f16": (ctypes.c_int, [P, I64, ctypes.POINTER(KV), I32, I32, ctypes.POINTER(Dims),
                                                I32, I32, P, I32]),
+    "fg_attn_decode_host_q4": (ctypes.c_int, [P, I64, ctypes.POINTER(KV), I32, I32, ctypes.POINTER(Dims),
+                                              I32, I32, P, I32]),
     "fg_weight_bytes": (I64, [ctypes.POINTER(Dims), I32, I32]),
     "fg_kv_bytes": (I64, [ctypes.POINTER(Dims), I32, I32, I32, I32, I32]),
     "fg_plan_device_bytes": (I64, [ctypes.POINTER(Dims), ctypes.POINTER(Plan)]),
@@ -305,6 +307,12 @@ def fg_attn_decode_host_f16(qkv, ld, kv: KV, seq0, nseq, d: Dims, pos, append, o
     _check("fg_attn_decode_host_f16", _L.fg_attn_decode_host_f16(ptr(qkv), ld, ctypes.byref(kv), seq0, nseq,
                                                                  ctypes.byref(d), pos, int(append), ptr(out),
                                                                  n_threads))
+
+
+def fg_attn_decode_host_q4(qkv, ld, kv: KV, seq0, nseq, d: Dims, pos, append, out, n_threads=0):
+    _check("fg_attn_decode_host_q4", _L.fg_attn_decode_host_q4(ptr(qkv), ld, ctypes.byref(kv), seq0, nseq,
+                                                               ctypes.byref(d), pos, int(append), ptr(out),
+                                                               n_threads))
 
 
 def fg_stage_bytes(d: Dims) -> int:

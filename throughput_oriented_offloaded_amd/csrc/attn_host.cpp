@@ -6,8 +6,11 @@
 // bottleneck, computing that batch's single-query attention on the CPU moves
 // only the current token's activations across the link (about 4·b·h1 bytes)
 // instead of the cache (about 4·b·s·h1 bytes).  With 4-bit compression the
-// pages switch this delegation off (the CPU's dequantization costs what the
-// smaller transfer saves), and so does this library: fp16 caches only.
+// pages switch this delegation off (on their host the CPU's dequantization
+// costs what the smaller transfer saves); here both fp16 and 4-bit caches are
+// delegated, and the 4-bit history is read compressed, dequantized in
+// registers (fp32 min + code * scale), its new row quantized on the CPU with
+// the codec's exact arithmetic.
 //
 // Arithmetic (the attention the GPU kernels compute, with roundings of its
 // own): scores q·k / sqrt(head_dim) in fp32 from fp16 q and cache rows,
@@ -23,6 +26,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <cstdlib>
 #include <condition_variable>
 #include <cstring>
 #include <limits>
@@ -263,9 +267,213 @@ FG_AVX2 void item_avx2(const Item& it, int pos, float* s) {
     }
 }
 
+// ------------------------------------------------------ 4-bit cache rows
+// One (sequence, head) of a 4-bit cache: per position hd/2 bytes of codes
+// (byte i holds dims 2i, low nibble, and 2i + 1) and an fp16 (min, scale)
+// pair per 64-dim group.  A cached value is min + code * scale, evaluated in
+// fp32 (no fp16 rounding of the dequantized value), so per group
+//   q . x = min * sum(q) + scale * sum(q_d code_d)
+//   sum_p w_p x_pd = sum_p (w_p scale_p) code_pd + sum_p w_p min_p.
+struct ItemQ4 {
+    const uint16_t* q;
+    const uint16_t* kn;
+    const uint16_t* vn;
+    uint8_t* K;
+    uint8_t* V;
+    uint16_t* Km;
+    uint16_t* Vm;
+    uint16_t* out;
+};
+
+// The codec's quantization of one row of hd fp16 values (groups of 64): min
+// and max in binary32 with -0 made +0, inv = 15 / range by division, code =
+// rint((x - min) * inv) clamped to [0, 15], meta = (fp16(min), fp16(range /
+// 15)); one binary32 operation per step and no contraction, so the bytes are
+// those of the device quantizer.
+void quant_row(const uint16_t* x, int hd, uint8_t* codes, uint16_t* meta) {
+#pragma clang fp contract(off)
+    for (int g = 0; g < hd / 64; ++g) {
+        const uint16_t* xs = x + 64 * g;
+        float mn = h2f(xs[0]), mx = mn;
+        for (int i = 1; i < 64; ++i) {
+            const float v = h2f(xs[i]);
+            mn = v < mn ? v : mn;
+            mx = v > mx ? v : mx;
+        }
+        mn = mn + 0.0f;
+        mx = mx + 0.0f;
+        const float range = mx - mn;
+        const float inv = range > 0.0f ? 15.0f / range : 0.0f;
+        auto code = [&](uint16_t h) -> unsigned {
+            if (!(range > 0.0f)) return 0u;
+            const float d = h2f(h) - mn;
+            const float r = std::nearbyint(d * inv);
+            int q = (int)r;
+            q = q < 0 ? 0 : (q > 15 ? 15 : q);
+            return (unsigned)q;
+        };
+        for (int i = 0; i < 32; ++i) codes[32 * g + i] = (uint8_t)(code(xs[2 * i]) | (code(xs[2 * i + 1]) << 4));
+        meta[2 * g] = f2h(mn);
+        meta[2 * g + 1] = f2h(range / 15.0f);
+    }
+}
+
+void item_q4_scalar(const ItemQ4& it, int hd, int pos, float* s) {
+    const int G = hd / 64, hb = hd / 2;
+    float qf[256], sq[4] = {0.f, 0.f, 0.f, 0.f};
+    const float scale = 1.0f / std::sqrt((float)hd);
+    for (int d = 0; d < hd; ++d) {
+        qf[d] = h2f(it.q[d]) * scale;
+        sq[d / 64] += qf[d];
+    }
+    float snew = 0.f;
+    for (int d = 0; d < hd; ++d) snew += qf[d] * h2f(it.kn[d]);
+    float m = snew;
+    for (int p = 0; p < pos; ++p) {
+        const uint8_t* c = it.K + (int64_t)p * hb;
+        const uint16_t* mm = it.Km + (int64_t)p * 2 * G;
+        float a = 0.f;
+        for (int g = 0; g < G; ++g) {
+            float dg = 0.f;
+            for (int i = 0; i < 32; ++i) {
+                const unsigned b = c[32 * g + i];
+                dg += qf[64 * g + 2 * i] * (float)(b & 15u) + qf[64 * g + 2 * i + 1] * (float)(b >> 4);
+            }
+            a += h2f(mm[2 * g]) * sq[g] + h2f(mm[2 * g + 1]) * dg;
+        }
+        s[p] = a;
+        m = std::max(m, a);
+    }
+    float l = 0.f;
+    for (int p = 0; p < pos; ++p) {
+        s[p] = std::exp(s[p] - m);
+        l += s[p];
+    }
+    const float en = std::exp(snew - m);
+    float acc[256], bs[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < hd; ++d) acc[d] = 0.f;
+    for (int p = 0; p < pos; ++p) {
+        const uint8_t* c = it.V + (int64_t)p * hb;
+        const uint16_t* mm = it.Vm + (int64_t)p * 2 * G;
+        for (int g = 0; g < G; ++g) {
+            const float a = s[p] * h2f(mm[2 * g + 1]);
+            bs[g] += s[p] * h2f(mm[2 * g]);
+            for (int i = 0; i < 32; ++i) {
+                const unsigned b = c[32 * g + i];
+                acc[64 * g + 2 * i] += a * (float)(b & 15u);
+                acc[64 * g + 2 * i + 1] += a * (float)(b >> 4);
+            }
+        }
+    }
+    const float inv = 1.0f / (l + en);
+    for (int d = 0; d < hd; ++d) it.out[d] = f2h((acc[d] + bs[d / 64] + en * h2f(it.vn[d])) * inv);
+}
+
+// 8 code bytes as 8 int lanes: low nibbles (even dims), high nibbles (odd)
+FG_AVX2 inline void nib8(const uint8_t* p, __m256& lo, __m256& hi) {
+    const __m256i b = _mm256_cvtepu8_epi32(_mm_loadl_epi64(reinterpret_cast<const __m128i*>(p)));
+    lo = _mm256_cvtepi32_ps(_mm256_and_si256(b, _mm256_set1_epi32(15)));
+    hi = _mm256_cvtepi32_ps(_mm256_srli_epi32(b, 4));
+}
+
+template <int HD>
+FG_AVX2 void item_q4_avx2(const ItemQ4& it, int pos, float* s) {
+    constexpr int G = HD / 64, HB = HD / 2, NV = HD / 16;   // NV: 8-byte code chunks per row
+    const float scale = 1.0f / std::sqrt((float)HD);
+    // q in code order: chunk k lane j is byte 8k + j, i.e. dims 16k + 2j (even) and 16k + 2j + 1 (odd)
+    __m256 qe[NV], qo[NV];
+    float sq[G];
+    {
+        alignas(32) float e[HD / 2], o[HD / 2];
+        for (int i = 0; i < HD / 2; ++i) {
+            e[i] = h2f(it.q[2 * i]) * scale;
+            o[i] = h2f(it.q[2 * i + 1]) * scale;
+        }
+        for (int g = 0; g < G; ++g) {
+            float t = 0.f;
+            for (int i = 32 * g; i < 32 * g + 32; ++i) t += e[i] + o[i];
+            sq[g] = t;
+        }
+        for (int k = 0; k < NV; ++k) {
+            qe[k] = _mm256_load_ps(e + 8 * k);
+            qo[k] = _mm256_load_ps(o + 8 * k);
+        }
+    }
+    float snew = 0.f;
+    for (int d = 0; d < HD; ++d) snew += h2f(it.q[d]) * scale * h2f(it.kn[d]);
+    float m = snew;
+    for (int p = 0; p < pos; ++p) {
+        const uint8_t* c = it.K + (int64_t)p * HB;
+        const uint16_t* mm = it.Km + (int64_t)p * 2 * G;
+        __m256 tot = _mm256_setzero_ps();
+        float base = 0.f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            __m256 a0 = _mm256_setzero_ps(), a1 = _mm256_setzero_ps();
+#pragma unroll
+            for (int k = 4 * g; k < 4 * g + 4; ++k) {
+                __m256 lo, hi;
+                nib8(c + 8 * k, lo, hi);
+                a0 = _mm256_fmadd_ps(lo, qe[k], a0);
+                a1 = _mm256_fmadd_ps(hi, qo[k], a1);
+            }
+            tot = _mm256_fmadd_ps(_mm256_add_ps(a0, a1), _mm256_set1_ps(h2f(mm[2 * g + 1])), tot);
+            base += h2f(mm[2 * g]) * sq[g];
+        }
+        s[p] = base + hsum(tot);
+        m = std::max(m, s[p]);
+    }
+    const int pos8 = (pos + 7) & ~7;
+    for (int p = pos; p < pos8; ++p) s[p] = -std::numeric_limits<float>::infinity();
+    const __m256 mv = _mm256_set1_ps(m);
+    __m256 lv = _mm256_setzero_ps();
+    for (int p = 0; p < pos8; p += 8) {
+        const __m256 e = exp8(_mm256_sub_ps(_mm256_loadu_ps(s + p), mv));
+        _mm256_storeu_ps(s + p, e);
+        lv = _mm256_add_ps(lv, e);
+    }
+    const float en = _mm256_cvtss_f32(exp8(_mm256_set1_ps(snew - m)));
+    __m256 ae[NV], ao[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) ae[k] = ao[k] = _mm256_setzero_ps();
+    float bs[G];
+    for (int g = 0; g < G; ++g) bs[g] = 0.f;
+    for (int p = 0; p < pos; ++p) {
+        const uint8_t* c = it.V + (int64_t)p * HB;
+        const uint16_t* mm = it.Vm + (int64_t)p * 2 * G;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const __m256 a = _mm256_set1_ps(s[p] * h2f(mm[2 * g + 1]));
+            bs[g] += s[p] * h2f(mm[2 * g]);
+#pragma unroll
+            for (int k = 4 * g; k < 4 * g + 4; ++k) {
+                __m256 lo, hi;
+                nib8(c + 8 * k, lo, hi);
+                ae[k] = _mm256_fmadd_ps(lo, a, ae[k]);
+                ao[k] = _mm256_fmadd_ps(hi, a, ao[k]);
+            }
+        }
+    }
+    alignas(32) float e[HD / 2], o[HD / 2];
+    for (int k = 0; k < NV; ++k) {
+        _mm256_store_ps(e + 8 * k, ae[k]);
+        _mm256_store_ps(o + 8 * k, ao[k]);
+    }
+    const float inv = 1.0f / (hsum(lv) + en);
+    for (int i = 0; i < HD / 2; ++i) {
+        const float b = bs[i / 32];
+        it.out[2 * i] = f2h((e[i] + b + en * h2f(it.vn[2 * i])) * inv);
+        it.out[2 * i + 1] = f2h((o[i] + b + en * h2f(it.vn[2 * i + 1])) * inv);
+    }
+}
+
+// AVX2 + FMA + F16C present, and not switched off by FG_HOST_ATTN_SCALAR=1
+// (which runs the plain C++ items, e.g. to test them on a host that has the
+// extensions)
 bool have_avx2() {
     static const bool ok = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma") &&
-                           __builtin_cpu_supports("f16c");
+                           __builtin_cpu_supports("f16c") && !(getenv("FG_HOST_ATTN_SCALAR") &&
+                                                              strcmp(getenv("FG_HOST_ATTN_SCALAR"), "1") == 0);
     return ok;
 }
 
@@ -276,10 +484,10 @@ int check_host_attn(const void* qkv, int64_t ld, const fg_kv* kv, int32_t seq0, 
     int st = check_dims(d);
     if (st != FG_OK) return st;
     if (!qkv || !kv || !out) return set_error(FG_ERR_INVALID, "null pointer argument");
-    if (kv->fmt != FG_FMT_F16)
-        return set_error(FG_ERR_UNSUPPORTED,
-                         "host attention needs the fp16 cache (4-bit caches are not delegated)");
-    if (!kv->k || !kv->v) return set_error(FG_ERR_INVALID, "null cache tensors");
+    if (kv->fmt != FG_FMT_F16 && kv->fmt != FG_FMT_Q4G64)
+        return set_error(FG_ERR_UNSUPPORTED, "host attention: unknown cache format %d", kv->fmt);
+    if (!kv->k || !kv->v || (kv->fmt == FG_FMT_Q4G64 && (!kv->k_meta || !kv->v_meta)))
+        return set_error(FG_ERR_INVALID, "null cache tensors");
     if (seq0 < 0 || nseq < 0 || (int64_t)seq0 + nseq > kv->n_seq)
         return set_error(FG_ERR_INVALID, "sequences [%d, %d) outside the cache's %d", seq0, seq0 + nseq,
                          kv->n_seq);
@@ -289,12 +497,18 @@ int check_host_attn(const void* qkv, int64_t ld, const fg_kv* kv, int32_t seq0, 
     return FG_OK;
 }
 
-int host_attn_decode_f16(const uint16_t* qkv, int64_t ld, const fg_kv* kv, int32_t seq0, int32_t nseq,
-                         const fg_dims* d, int32_t pos, bool append, uint16_t* out, HostPool& pool) {
+int host_attn_decode(const uint16_t* qkv, int64_t ld, const fg_kv* kv, int32_t seq0, int32_t nseq,
+                     const fg_dims* d, int32_t pos, bool append, uint16_t* out, HostPool& pool) {
     const int nh = d->n_heads, hd = d->head_dim;
     const int64_t h1 = d->h1, ml = kv->max_len;
     uint16_t* kc = static_cast<uint16_t*>(kv->k);
     uint16_t* vc = static_cast<uint16_t*>(kv->v);
+    const bool q4 = kv->fmt == FG_FMT_Q4G64;
+    uint8_t* kq = static_cast<uint8_t*>(kv->k);
+    uint8_t* vq = static_cast<uint8_t*>(kv->v);
+    uint16_t* kmq = static_cast<uint16_t*>(kv->k_meta);
+    uint16_t* vmq = static_cast<uint16_t*>(kv->v_meta);
+    const int hb = hd / 2, mg = hd / 64 * 2;   // code bytes and meta values per cache row
     const bool avx = have_avx2();
     // nothing may leave a worker by exception (it would end the process, or
     // end run() while other threads still use f): a chunk whose score buffer
@@ -310,9 +524,22 @@ int host_attn_decode_f16(const uint16_t* qkv, int64_t ld, const fg_kv* kv, int32
         for (int64_t u = b; u < e; ++u) {
             const int64_t sq = u / nh;
             const int h = (int)(u - sq * nh);
-            const int64_t row0 = ((seq0 + sq) * nh + h) * ml * hd;
             const uint16_t* r = qkv + sq * ld + (int64_t)h * hd;
-            Item it{r, r + h1, r + 2 * h1, kc + row0, vc + row0, out + sq * h1 + (int64_t)h * hd};
+            uint16_t* o = out + sq * h1 + (int64_t)h * hd;
+            const int64_t rows0 = ((seq0 + sq) * nh + h) * ml;   // first cache row of this (sequence, head)
+            if (q4) {
+                ItemQ4 it{r, r + h1, r + 2 * h1, kq + rows0 * hb, vq + rows0 * hb, kmq + rows0 * mg, vmq + rows0 * mg, o};
+                if (avx && hd == 64) item_q4_avx2<64>(it, pos, s);
+                else if (avx && hd == 128) item_q4_avx2<128>(it, pos, s);
+                else item_q4_scalar(it, hd, pos, s);
+                if (append) {
+                    quant_row(it.kn, hd, it.K + (int64_t)pos * hb, it.Km + (int64_t)pos * mg);
+                    quant_row(it.vn, hd, it.V + (int64_t)pos * hb, it.Vm + (int64_t)pos * mg);
+                }
+                continue;
+            }
+            const int64_t row0 = rows0 * hd;
+            Item it{r, r + h1, r + 2 * h1, kc + row0, vc + row0, o};
             if (avx && hd == 64) item_avx2<64>(it, pos, s);
             else if (avx && hd == 128) item_avx2<128>(it, pos, s);
             else item_scalar(it, hd, pos, s);
@@ -329,17 +556,33 @@ int host_attn_decode_f16(const uint16_t* qkv, int64_t ld, const fg_kv* kv, int32
 
 }  // namespace fg
 
-extern "C" int fg_attn_decode_host_f16(const void* qkv, int64_t ld, const fg_kv* kv, int32_t seq0,
-                                       int32_t nseq, const fg_dims* d, int32_t pos, int32_t append,
-                                       void* out, int32_t n_threads) {
+namespace {
+int host_attn_entry(int32_t fmt, const void* qkv, int64_t ld, const fg_kv* kv, int32_t seq0, int32_t nseq,
+                    const fg_dims* d, int32_t pos, int32_t append, void* out, int32_t n_threads) {
     fg::clear_error();
+    if (kv && kv->fmt != fmt)
+        return fg::set_error(FG_ERR_UNSUPPORTED, "host attention: a cache of format %d given to the %s entry point",
+                             kv->fmt, fmt == FG_FMT_Q4G64 ? "4-bit" : "fp16");
     int st = fg::check_host_attn(qkv, ld, kv, seq0, nseq, d, pos, out);
     if (st != FG_OK) return st;
     try {
         fg::HostPool pool(n_threads);
-        return fg::host_attn_decode_f16(static_cast<const uint16_t*>(qkv), ld, kv, seq0, nseq, d, pos,
-                                        append != 0, static_cast<uint16_t*>(out), pool);
+        return fg::host_attn_decode(static_cast<const uint16_t*>(qkv), ld, kv, seq0, nseq, d, pos, append != 0,
+                                    static_cast<uint16_t*>(out), pool);
     } catch (const std::bad_alloc&) {
         return fg::set_error(FG_ERR_CAPACITY, "host attention: out of host memory");
     }
+}
+}  // namespace
+
+extern "C" int fg_attn_decode_host_f16(const void* qkv, int64_t ld, const fg_kv* kv, int32_t seq0,
+                                       int32_t nseq, const fg_dims* d, int32_t pos, int32_t append,
+                                       void* out, int32_t n_threads) {
+    return host_attn_entry(FG_FMT_F16, qkv, ld, kv, seq0, nseq, d, pos, append, out, n_threads);
+}
+
+extern "C" int fg_attn_decode_host_q4(const void* qkv, int64_t ld, const fg_kv* kv, int32_t seq0,
+                                      int32_t nseq, const fg_dims* d, int32_t pos, int32_t append,
+                                      void* out, int32_t n_threads) {
+    return host_attn_entry(FG_FMT_Q4G64, qkv, ld, kv, seq0, nseq, d, pos, append, out, n_threads);
 }

@@ -35,17 +35,18 @@ class HostPool {
     int nthreads_;
 };
 
-// Attention of sequences seq0 .. seq0 + nseq - 1 of an fp16 host cache at
-// position pos (rows < pos from the cache, the current token from its fresh
-// k, v), out fp16 [nseq, h1]; qkv: fp16 rows of ld elements, q at column 0,
-// k at h1, v at 2 h1.  append: also store k, v at row pos.  Arguments are
-// checked by the caller.  Returns FG_OK, or FG_ERR_CAPACITY (error text set)
-// when a thread's score buffer could not be allocated; that thread's items
-// are then not computed.
-int host_attn_decode_f16(const uint16_t* qkv, int64_t ld, const fg_kv* kv, int32_t seq0, int32_t nseq,
+// Attention of sequences seq0 .. seq0 + nseq - 1 of an fp16 or 4-bit host
+// cache at position pos (rows < pos from the cache, the current token from
+// its fresh k, v), out fp16 [nseq, h1]; qkv: fp16 rows of ld elements, q at
+// column 0, k at h1, v at 2 h1.  append: also store k, v at row pos (4-bit:
+// quantized as the device codec does).  Arguments are checked by the caller.
+// Returns FG_OK, or FG_ERR_CAPACITY (error text set) when a thread's score
+// buffer could not be allocated; that thread's items are then not computed.
+int host_attn_decode(const uint16_t* qkv, int64_t ld, const fg_kv* kv, int32_t seq0, int32_t nseq,
                          const fg_dims* d, int32_t pos, bool append, uint16_t* out, HostPool& pool);
 
-// Argument checks of fg_attn_decode_host_f16 (also used by the layer path).
+// Argument checks of the host attention entry points (also used by the layer
+// path): dims, pointers, either cache format, sequences, pos and ld.
 int check_host_attn(const void* qkv, int64_t ld, const fg_kv* kv, int32_t seq0, int32_t nseq,
                     const fg_dims* d, int32_t pos, const void* out);
 

@@ -204,8 +204,6 @@ size_t host_stage_bytes(const fg_dims* d, int64_t rows) {
 
 int kvtier_host_check(const fg_kvtier* kt, const fg_kv* host, const fg_dims* d, int64_t rows,
                       int32_t topk) {
-    FG_CHECK_SUP(host->fmt == FG_FMT_F16,
-                 "host attention: the host cache must be fp16 (4-bit caches are not delegated)");
     FG_CHECK_SUP(topk < 0, "host attention computes dense attention only (no Top-K sparse V)");
     const size_t need = host_stage_bytes(d, rows);
     if (kt->hstage_bytes < need)
@@ -231,7 +229,7 @@ int kvtier_host_attend(const fg_kvtier* kt, int lane, size_t off, const fg_kv* h
     const int64_t h1 = d->h1;
     const uint16_t* qkv = reinterpret_cast<const uint16_t*>(kt->hstage + off);
     uint16_t* o = reinterpret_cast<uint16_t*>(kt->hstage + off) + rows * 3 * h1;
-    FG_TRY(host_attn_decode_f16(qkv, 3 * h1, host, seq0, (int32_t)rows, d, pos, true, o, *kt->pool));
+    FG_TRY(host_attn_decode(qkv, 3 * h1, host, seq0, (int32_t)rows, d, pos, true, o, *kt->pool));
     FG_HIP(hipMemcpyAsync(out, o, (size_t)rows * h1 * 2, hipMemcpyHostToDevice, st));
     return FG_OK;
 }

@@ -150,9 +150,9 @@ class Model:
         kv_host_seqs: the last kv_host_seqs sequences keep their KV cache in
         pinned host memory (KV tiering; a whole number of GPU batches at every
         call), moved through two device slots by the library.
-        kv_host_attention: with an fp16 cache, the decode steps compute the
-        host-resident batches' attention on the host CPU (host_threads
-        threads, 0: all) instead of moving their history to the device."""
+        kv_host_attention: the decode steps compute the host-resident
+        batches' attention on the host CPU (host_threads threads, 0: all)
+        instead of moving their history to the device."""
         assert 0.0 <= attn_topk <= 1.0
         self.attn_topk_ppm = int(round(attn_topk * 1_000_000))
         self.shape, self.layers, self.emb = shape, layers, emb
@@ -160,8 +160,7 @@ class Model:
         self.n_seq, self.max_len = n_seq, max_len
         assert 0 <= kv_host_seqs <= n_seq
         self.kv_host_seqs = kv_host_seqs
-        assert not kv_host_attention or (kv_host_seqs and kv_fmt == L.FG_FMT_F16), \
-            "host attention needs host-resident sequences and the fp16 cache"
+        assert not kv_host_attention or kv_host_seqs, "host attention needs host-resident sequences"
         self.kv_host_attention, self.host_threads = kv_host_attention, host_threads
         n_dev = max(n_seq - kv_host_seqs, 1)   # the device cache is unused when every batch is on the host
         self.kv = [DeviceKV(kv_fmt, n_dev, shape.n_heads, shape.head_dim, max_len, device)
