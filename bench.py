@@ -61,6 +61,11 @@ CONFIGS = {
                      "pinned host memory, their attention on the host CPU",
             l=24, h1=2048, h2=8192, nh=32, hd=64, w="f16", kv="f16", gbs=32, nb=4, s=512, n=32,
             kv_host_seqs=64, kv_host_attention=True),
+    # config 6 with the host batches' attention on the host CPU over the
+    # 4-bit cache (read compressed), instead of moving the history over PCIe
+    10: dict(workload="opt-30b-shape 4-bit block decode, KV cache of every GPU batch in pinned "
+                      "host memory, attention on the host CPU", l=48, h1=7168, h2=28672, nh=56, hd=128,
+             w="q4", kv="q4", gbs=48, nb=3, s=512, n=32, kv_host_seqs=144, kv_host_attention=True),
 }
 # Workloads that are not run: an earlier version of the OPT-66B-shape tiered run
 # ended in a host segmentation fault after its timed decode, and the cause has
@@ -684,16 +689,17 @@ def main():
         # that cross the link (q, k, v down, the attention row back)
         step = t_dec / K
         p_mean = s + Wm + (K - 1) / 2
-        hist = cfg["kv_host_seqs"] * cfg["l"] * p_mean * cfg["h1"] * 2 * 2
+        per_elem = 9 / 16 if cfg["kv"] == "q4" else 2     # stored bytes per cached value
+        hist = cfg["kv_host_seqs"] * cfg["l"] * p_mean * cfg["h1"] * 2 * per_elem
         link = cfg["kv_host_seqs"] * cfg["l"] * 4 * cfg["h1"] * 2
         out["host_attention"] = {
-            "host_sequences": cfg["kv_host_seqs"], "cpu_threads": host_threads,
+            "host_sequences": cfg["kv_host_seqs"], "cpu_threads": host_threads, "cache": cfg["kv"],
             "history_bytes_per_step": round(hist), "link_bytes_per_step": round(link),
             "step_s": round(step, 4), "history_GBs_over_step": round(hist / step / 1e9, 2),
-            "definition": "the host batches' attention computed by the CPU over the fp16 host "
-                          "cache, only their q, k, v rows and attention rows crossing the link; "
-                          "history_GBs_over_step = history bytes read by the CPU per step / step "
-                          "time (a lower bound on the CPU's rate)"}
+            "definition": "the host batches' attention computed by the CPU over the host cache as "
+                          "stored (fp16, or 4-bit codes and metadata), only their q, k, v rows and "
+                          "attention rows crossing the link; history_GBs_over_step = stored history "
+                          "bytes read by the CPU per step / step time (a lower bound on the CPU's rate)"}
     if policy_block is not None:
         policy_block["measured_ms_per_step"] = out["ms_per_step"]
         policy_block["measured_prefill_s"] = round(t_prefill, 3)

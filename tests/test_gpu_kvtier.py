@@ -191,21 +191,23 @@ def _host_attn_tier(L, d, gbs, lmax, n_host_seq, threads=4):
     return kt, slots, cp, stage
 
 
+@pytest.mark.parametrize("fmt", ["f16", "q4"])
 @pytest.mark.parametrize("nb_dev,P", [(0, 17), (1, 17), (2, 40), (1, 0)])
-def test_layer_decode_host_attention(L, nb_dev, P):
+def test_layer_decode_host_attention(L, nb_dev, P, fmt):
     """fg_layer_decode_block with the host batches' attention on the CPU
-    ([P2] "为什么有时应该在 CPU 上算注意力"; fp16 cache): the layer output
-    against the oracle and against the all-device call (the CPU's roundings
-    differ, so within the tolerance), the device batches' rows bit for bit,
-    and the host cache: history untouched, row P the fresh k, v, bit for
-    bit equal to what the all-device call appended."""
+    ([P2] "为什么有时应该在 CPU 上算注意力"; fp16 and 4-bit caches): the layer
+    output against the oracle and against the all-device call (the CPU's
+    roundings differ, so within the tolerance), the device batches' rows bit
+    for bit, and the host cache: history untouched, row P the fresh k, v, bit
+    for bit equal to what the all-device call appended (for the 4-bit cache:
+    the CPU's quantizer gives the device quantizer's bytes)."""
     import torch
     from test_gpu_layer import _layer
     gbs, nb, lmax = 2, 3, 48
     bls = gbs * nb
     dl, Wn, od = _layer(L, OPT125, "q4", seed=71)
-    kv, d, kh, vh = _filled_cache(L, "f16", bls, P, lmax, seed=72)
-    dev, host = _split(L, kv, "f16", nb_dev * gbs, bls, lmax)
+    kv, d, kh, vh = _filled_cache(L, fmt, bls, P, lmax, seed=72)
+    dev, host = _split(L, kv, fmt, nb_dev * gbs, bls, lmax)
     x = synth.activations(bls, OPT125["h1"], seed=73)
     ws = torch.empty(L.fg_workspace_bytes(d, bls, dl.fmt), dtype=torch.uint8, device="cuda")
     x_ref = x.cuda()
@@ -219,7 +221,7 @@ def test_layer_decode_host_attention(L, nb_dev, P):
         torch.cuda.synchronize()
     finally:
         L.fg_kvtier_destroy(kt)
-    oc = oracle.KVCache("f16", bls, OPT125["nh"], OPT125["hd"], lmax)
+    oc = oracle.KVCache(fmt, bls, OPT125["nh"], OPT125["hd"], lmax)
     if P:
         oc.store(kh.numpy().view(np.uint16), vh.numpy().view(np.uint16), 0)
     ref, _, _ = oracle.layer_decode(od, Wn, x.numpy().view(np.uint16), P, oc)
@@ -232,10 +234,10 @@ def test_layer_decode_host_attention(L, nb_dev, P):
         assert torch.equal(hh[:, :, :P + 1], a[n_dev:, :, :P + 1].cpu())
 
 
-@pytest.mark.parametrize("host_batches", [1, 2, 3])
-def test_model_decode_host_attention(L, host_batches):
-    """2-layer OPT-125m-shape model, fp16 weights and cache, one, two or all
-    three GPU batches' caches on the host: the prefill goes through the slots,
+@pytest.mark.parametrize("host_batches,kv_fmt", [(1, "f16"), (2, "f16"), (3, "f16"), (2, "q4"), (3, "q4")])
+def test_model_decode_host_attention(L, host_batches, kv_fmt):
+    """2-layer OPT-125m-shape model, fp16 weights, an fp16 or 4-bit cache, one,
+    two or all three GPU batches' caches on the host: the prefill goes through the slots,
     the decode steps' host attention runs on the CPU, overlapped with the GPU's
     work on the other rows (a device lane of the remaining batches, one or
     two host lanes).  Teacher-forced on the all-device model's tokens, every
@@ -251,8 +253,9 @@ def test_model_decode_host_attention(L, host_batches):
     toks = synth.tokens(bls, s, seed=5).cuda()
     layers = [DeviceLayer.from_fp16({k: v.cuda() for k, v in W.items()}, L.FG_FMT_F16) for W in Ws]
     embd = {k: v.cuda() for k, v in emb.items()}
-    ref = Model(sh, layers, embd, L.FG_FMT_F16, bls, s + n)
-    ha = Model(sh, layers, embd, L.FG_FMT_F16, bls, s + n, kv_host_seqs=host_batches * gbs,
+    kf = L.FG_FMT_F16 if kv_fmt == "f16" else L.FG_FMT_Q4G64
+    ref = Model(sh, layers, embd, kf, bls, s + n)
+    ha = Model(sh, layers, embd, kf, bls, s + n, kv_host_seqs=host_batches * gbs,
                kv_host_attention=True, host_threads=4)
     lg_r, tok_r = ref.prefill(toks, gbs, nb)
     lg_h, tok_h = ha.prefill(toks, gbs, nb)
@@ -268,14 +271,16 @@ def test_model_decode_host_attention(L, host_batches):
     for j in range(sh.n_layers):
         for a, hh in zip(_tensors(ref.kv[j]), _tensors(ha.kv_host[j])):
             assert torch.equal(hh[:, :, :s], a[n_dev:, :, :s].cpu())
+            if kv_fmt == "q4":   # decode rows: codes of nearly equal k, v (rounding differs)
+                continue
             got = hh[:, :, s:s + n - 1].float()
             want = a[n_dev:, :, s:s + n - 1].float().cpu()
             assert (got - want).abs().max() <= 1e-2 * want.abs().max() + 1e-3
 
 
 def test_host_attention_refusals(L):
-    """4-bit host cache, Top-K sparse V, a small stage, an unpinned stage:
-    refused on the host before anything is enqueued."""
+    """Top-K sparse V (over either cache format), a small stage, an unpinned
+    stage: refused on the host before anything is enqueued."""
     import torch
     from test_gpu_layer import _layer
     gbs, nb, lmax, P = 2, 2, 24, 9
@@ -293,7 +298,7 @@ def test_host_attention_refusals(L):
     try:
         with pytest.raises(L.FgError) as e:
             L.fg_layer_decode_block(d, dl.struct, x, gbs, nb, P, devq.struct, ws, ws.numel(),
-                                    kvt=L.KvTier(kt, _ptr_kv(L, hostq), 1))
+                                    attn_topk_ppm=100000, kvt=L.KvTier(kt, _ptr_kv(L, hostq), 1))
         assert e.value.status == L.FG_ERR_UNSUPPORTED
         with pytest.raises(L.FgError) as e:
             L.fg_layer_decode_block(d, dl.struct, x, gbs, nb, P, dev16_.struct, ws, ws.numel(),
