@@ -146,18 +146,19 @@ def _q4_cache(L, kc16, vc16):
     return kv, (kt, kmt, vt, vmt), kdq, vdq
 
 
-@pytest.mark.parametrize("scalar", [False, True])
-@pytest.mark.parametrize("bls,nh,hd,pos", Q4_CASES)
-def test_host_attention_q4_matches_oracle(L, bls, nh, hd, pos, scalar):
+@pytest.mark.parametrize("bls,nh,hd,pos,mode", [c + ("native",) for c in Q4_CASES] +
+                         [c + (m,) for c in Q4_CASES[:4] for m in ("avx2", "scalar")])
+def test_host_attention_q4_matches_oracle(L, bls, nh, hd, pos, mode):
     """A 4-bit cache (the oracle's codec) attended on the host against the
-    oracle's attention over the dequantized fp16 history, in the AVX2 items
-    and in the plain C++ ones (a child process with FG_HOST_ATTN_SCALAR=1 for
-    the latter), and the appended row: the codec's bytes for the fresh k, v."""
-    if scalar:
+    oracle's attention over the dequantized fp16 history, in the widest items
+    the host has (AVX-512 or AVX2), in the AVX2 ones and in the plain C++ ones
+    (child processes with FG_HOST_ATTN_AVX2=1 or FG_HOST_ATTN_SCALAR=1), and
+    the appended row: the codec's bytes for the fresh k, v."""
+    if mode != "native":
         import subprocess
         import sys
-        env = dict(__import__("os").environ, FG_HOST_ATTN_SCALAR="1")
-        node = f"{__file__}::test_host_attention_q4_matches_oracle[{bls}-{nh}-{hd}-{pos}-False]"
+        env = dict(__import__("os").environ, **{"FG_HOST_ATTN_" + mode.upper(): "1"})
+        node = f"{__file__}::test_host_attention_q4_matches_oracle[{bls}-{nh}-{hd}-{pos}-native]"
         r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", node],
                            env=env, capture_output=True, text=True, timeout=600)
         assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]

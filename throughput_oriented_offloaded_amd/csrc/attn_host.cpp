@@ -467,13 +467,127 @@ FG_AVX2 void item_q4_avx2(const ItemQ4& it, int pos, float* s) {
     }
 }
 
-// AVX2 + FMA + F16C present, and not switched off by FG_HOST_ATTN_SCALAR=1
-// (which runs the plain C++ items, e.g. to test them on a host that has the
-// extensions)
+#define FG_AVX512 __attribute__((target("avx512f,avx512bw,avx512vl,avx2,fma,f16c")))
+
+// 16 code bytes as 16 int lanes: low nibbles (even dims), high nibbles (odd)
+FG_AVX512 inline void nib16(const uint8_t* p, __m512& lo, __m512& hi) {
+    const __m512i b = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(p)));
+    lo = _mm512_cvtepi32_ps(_mm512_and_si512(b, _mm512_set1_epi32(15)));
+    hi = _mm512_cvtepi32_ps(_mm512_srli_epi32(b, 4));
+}
+
+// The 4-bit item on 16-lane vectors (the same arithmetic as item_q4_avx2,
+// twice the values per instruction; the dequantization is what bounds the
+// 4-bit item, where the fp16 one is bound by memory).
+template <int HD>
+FG_AVX512 void item_q4_avx512(const ItemQ4& it, int pos, float* s) {
+    constexpr int G = HD / 64, HB = HD / 2, NV = HD / 32;   // NV: 16-byte code chunks per row
+    const float scale = 1.0f / std::sqrt((float)HD);
+    // chunk k lane j is byte 16k + j: dims 32k + 2j (even) and 32k + 2j + 1 (odd)
+    __m512 qe[NV], qo[NV];
+    float sq[G];
+    {
+        alignas(64) float e[HD / 2], o[HD / 2];
+        for (int i = 0; i < HD / 2; ++i) {
+            e[i] = h2f(it.q[2 * i]) * scale;
+            o[i] = h2f(it.q[2 * i + 1]) * scale;
+        }
+        for (int g = 0; g < G; ++g) {
+            float t = 0.f;
+            for (int i = 32 * g; i < 32 * g + 32; ++i) t += e[i] + o[i];
+            sq[g] = t;
+        }
+        for (int k = 0; k < NV; ++k) {
+            qe[k] = _mm512_load_ps(e + 16 * k);
+            qo[k] = _mm512_load_ps(o + 16 * k);
+        }
+    }
+    float snew = 0.f;
+    for (int d = 0; d < HD; ++d) snew += h2f(it.q[d]) * scale * h2f(it.kn[d]);
+    float m = snew;
+    for (int p = 0; p < pos; ++p) {
+        const uint8_t* c = it.K + (int64_t)p * HB;
+        const uint16_t* mm = it.Km + (int64_t)p * 2 * G;
+        __m512 tot = _mm512_setzero_ps();
+        float base = 0.f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            __m512 a0 = _mm512_setzero_ps(), a1 = _mm512_setzero_ps();
+#pragma unroll
+            for (int k = 2 * g; k < 2 * g + 2; ++k) {
+                __m512 lo, hi;
+                nib16(c + 16 * k, lo, hi);
+                a0 = _mm512_fmadd_ps(lo, qe[k], a0);
+                a1 = _mm512_fmadd_ps(hi, qo[k], a1);
+            }
+            tot = _mm512_fmadd_ps(_mm512_add_ps(a0, a1), _mm512_set1_ps(h2f(mm[2 * g + 1])), tot);
+            base += h2f(mm[2 * g]) * sq[g];
+        }
+        s[p] = base + _mm512_reduce_add_ps(tot);
+        m = std::max(m, s[p]);
+    }
+    const int pos8 = (pos + 7) & ~7;
+    for (int p = pos; p < pos8; ++p) s[p] = -std::numeric_limits<float>::infinity();
+    const __m256 mv = _mm256_set1_ps(m);
+    __m256 lv = _mm256_setzero_ps();
+    for (int p = 0; p < pos8; p += 8) {
+        const __m256 e = exp8(_mm256_sub_ps(_mm256_loadu_ps(s + p), mv));
+        _mm256_storeu_ps(s + p, e);
+        lv = _mm256_add_ps(lv, e);
+    }
+    const float en = _mm256_cvtss_f32(exp8(_mm256_set1_ps(snew - m)));
+    __m512 ae[NV], ao[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) ae[k] = ao[k] = _mm512_setzero_ps();
+    float bs[G];
+    for (int g = 0; g < G; ++g) bs[g] = 0.f;
+    for (int p = 0; p < pos; ++p) {
+        const uint8_t* c = it.V + (int64_t)p * HB;
+        const uint16_t* mm = it.Vm + (int64_t)p * 2 * G;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const __m512 a = _mm512_set1_ps(s[p] * h2f(mm[2 * g + 1]));
+            bs[g] += s[p] * h2f(mm[2 * g]);
+#pragma unroll
+            for (int k = 2 * g; k < 2 * g + 2; ++k) {
+                __m512 lo, hi;
+                nib16(c + 16 * k, lo, hi);
+                ae[k] = _mm512_fmadd_ps(lo, a, ae[k]);
+                ao[k] = _mm512_fmadd_ps(hi, a, ao[k]);
+            }
+        }
+    }
+    alignas(64) float e[HD / 2], o[HD / 2];
+    for (int k = 0; k < NV; ++k) {
+        _mm512_store_ps(e + 16 * k, ae[k]);
+        _mm512_store_ps(o + 16 * k, ao[k]);
+    }
+    const float inv = 1.0f / (hsum(lv) + en);
+    for (int i = 0; i < HD / 2; ++i) {
+        const float b = bs[i / 32];
+        it.out[2 * i] = f2h((e[i] + b + en * h2f(it.vn[2 * i])) * inv);
+        it.out[2 * i + 1] = f2h((o[i] + b + en * h2f(it.vn[2 * i + 1])) * inv);
+    }
+}
+
+// FG_HOST_ATTN_SCALAR=1 runs the plain C++ items and FG_HOST_ATTN_AVX2=1 the
+// AVX2 ones, e.g. to test them on a host that has wider extensions.
+bool env_on(const char* name) {
+    const char* v = getenv(name);
+    return v && strcmp(v, "1") == 0;
+}
+
+// AVX2 + FMA + F16C present and not switched off
 bool have_avx2() {
     static const bool ok = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma") &&
-                           __builtin_cpu_supports("f16c") && !(getenv("FG_HOST_ATTN_SCALAR") &&
-                                                              strcmp(getenv("FG_HOST_ATTN_SCALAR"), "1") == 0);
+                           __builtin_cpu_supports("f16c") && !env_on("FG_HOST_ATTN_SCALAR");
+    return ok;
+}
+
+// AVX-512 F + BW + VL as well, and not switched off
+bool have_avx512() {
+    static const bool ok = have_avx2() && __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
+                           __builtin_cpu_supports("avx512vl") && !env_on("FG_HOST_ATTN_AVX2");
     return ok;
 }
 
@@ -509,7 +623,7 @@ int host_attn_decode(const uint16_t* qkv, int64_t ld, const fg_kv* kv, int32_t s
     uint16_t* kmq = static_cast<uint16_t*>(kv->k_meta);
     uint16_t* vmq = static_cast<uint16_t*>(kv->v_meta);
     const int hb = hd / 2, mg = hd / 64 * 2;   // code bytes and meta values per cache row
-    const bool avx = have_avx2();
+    const bool avx = have_avx2(), avx512 = have_avx512();
     // nothing may leave a worker by exception (it would end the process, or
     // end run() while other threads still use f): a chunk whose score buffer
     // cannot be allocated is skipped and reported after the loop
@@ -529,7 +643,9 @@ int host_attn_decode(const uint16_t* qkv, int64_t ld, const fg_kv* kv, int32_t s
             const int64_t rows0 = ((seq0 + sq) * nh + h) * ml;   // first cache row of this (sequence, head)
             if (q4) {
                 ItemQ4 it{r, r + h1, r + 2 * h1, kq + rows0 * hb, vq + rows0 * hb, kmq + rows0 * mg, vmq + rows0 * mg, o};
-                if (avx && hd == 64) item_q4_avx2<64>(it, pos, s);
+                if (avx512 && hd == 64) item_q4_avx512<64>(it, pos, s);
+                else if (avx512 && hd == 128) item_q4_avx512<128>(it, pos, s);
+                else if (avx && hd == 64) item_q4_avx2<64>(it, pos, s);
                 else if (avx && hd == 128) item_q4_avx2<128>(it, pos, s);
                 else item_q4_scalar(it, hd, pos, s);
                 if (append) {
