@@ -32,14 +32,18 @@ the same pattern (the readings are listed with the design notes):
 
 CPU delegation of decode attention ([P2] "为什么有时应该在 CPU 上算注意力": for
 a cache already on the CPU side, computing its attention there moves the
-current token's activations instead of the cache), as a policy switch for
-fp16 caches: in decode, the CPU share of the cache (cc) no longer crosses
+current token's activations instead of the cache), as a policy switch: in
+decode, the CPU share of the cache (cc) no longer crosses
 CPU -> GPU nor comes back; instead each of its sequences sends its q, k, v
 rows down (3 h1 fp16) and its attention row up (h1 fp16), the CPU reads that
 share of the cache at its attention bandwidth (a sixth path, "cpu", which
 overlaps the others like them), and the GPU's attention reads only the
-other shares.  Parity unpinned for the CPU rate (a measured constant, as
-the GPU's rates are).
+other shares.  The pages' authors switch the delegation off with a
+compressed cache, because on their host the CPU's dequantization costs what
+the smaller transfer saves; here that is left to the rates: a compressed
+cache is read at a rate of its own (stored bytes per second), and without
+one the switch is refused.  Parity unpinned for the CPU rates (measured
+constants, as the GPU's rates are).
 """
 from __future__ import annotations
 
@@ -78,7 +82,8 @@ class Hardware:
     alpha_g: float = 1.0      # peak memory is multiplied by these before the
     alpha_c: float = 1.0      # capacity test
     alpha_d: float = 1.0
-    cpu_attn_bw: float = 0.0  # bytes/s of cache read by decode attention on the CPU (0: none)
+    cpu_attn_bw: float = 0.0  # bytes/s of fp16 cache read by decode attention on the CPU (0: none)
+    cpu_attn_bw_q4: float = 0.0  # the same for a compressed cache, stored bytes/s (0: none)
 
 
 def layer_weight_bytes(m: Model) -> float:
@@ -116,7 +121,8 @@ def path_times(m: Model, hw: Hardware, bls: int, p: dict, phase: str, cpu_attn: 
         act = act_bytes(m, bls, m.s)
         comp = (bls * m.s * mats + 2 * bls * m.s * m.s * m.h1) / hw.prefill_flops
     if cpu_attn and phase == "gen":
-        assert m.c_ratio == 1.0 and hw.cpu_attn_bw > 0, "CPU attention over an fp16 cache only"
+        rate = hw.cpu_attn_bw if m.c_ratio == 1.0 else hw.cpu_attn_bw_q4
+        assert rate > 0, "CPU attention needs the host's rate for this cache format"
         qkv_down, attn_up = 3 * act, act             # fp16 rows of the CPU share's sequences
         gpu_attn = cache_in * (1 - p["cc"]) / hw.attn_bw
         return {
@@ -125,7 +131,7 @@ def path_times(m: Model, hw: Hardware, bls: int, p: dict, phase: str, cpu_attn: 
             "d2c": (p["wd"] * W + p["cd"] * cache_in + p["hd"] * act) / hw.bw_d2c,
             "c2d": (p["cd"] * cache_out + p["hd"] * act) / hw.bw_c2d,
             "comp": comp - cache_in / hw.attn_bw + gpu_attn,
-            "cpu": p["cc"] * cache_in / hw.cpu_attn_bw,
+            "cpu": p["cc"] * cache_in / rate,
         }
     return {
         "c2g": (off_w * W + off_c * cache_in + off_h * act) / hw.bw_c2g,

@@ -334,20 +334,32 @@ def test_cpu_attention_without_a_host_share_changes_nothing():
     assert oc.path_times(m, hw, 32, q, "gen")["cpu"] == 0.0
 
 
-def test_cpu_attention_fp16_cache_only(pol):
-    """The pages' authors turn delegation off with a 4-bit cache (the CPU's
-    quantize / dequantize costs eat the saving); both models refuse it, and
-    the search does not try it."""
-    m = oc.Model(l=4, h1=512, h2=2048, s=128, n=16, c_ratio=9 / 32)
-    hw = _hw(cpu_attn_bw=40e9)
+def test_cpu_attention_compressed_cache_rate(pol):
+    """The pages' authors switch delegation off with a 4-bit cache (their
+    CPU's dequantization eats the saving); here a compressed cache is
+    delegated only at a rate of its own: without one both models refuse it
+    and the search does not try it; with one, the host path reads the share's
+    stored (compressed) bytes at that rate, and the links carry the same
+    fp16 rows as for an fp16 cache."""
+    kw = dict(l=4, h1=512, h2=2048, s=128, n=16, c_ratio=9 / 32)
+    m = oc.Model(**kw)
     p = dict(wg=1, wc=0, wd=0, hg=1, hc=0, hd=0, cg=0, cc=1, cd=0)
     with pytest.raises(AssertionError):
-        oc.path_times(m, hw, 8, p, "gen", True)
-    _, _, wl, mc = _pair(pol, dict(l=4, h1=512, h2=2048, s=128, n=16, c_ratio=9 / 32), dict(cpu_attn_bw=40e9))
+        oc.path_times(m, _hw(cpu_attn_bw=40e9), 8, p, "gen", True)
+    _, _, wl, mc = _pair(pol, kw, dict(cpu_attn_bw=40e9))
     with pytest.raises(ValueError):
         pol.estimate(wl, mc, 8, 8, p, cpu_attn=True)
     best = pol.search(wl, mc, gbs_list=(8,), nb_max=2)
     assert best is not None and best["cpu_attention"] is False
+    hw = _hw(cpu_attn_bw=40e9, cpu_attn_bw_q4=7e9, bw_c2g=1.0, bw_g2c=1.0)
+    b, L = 8, m.s + m.n / 2
+    on = oc.path_times(m, hw, b, p, "gen", True)
+    assert on["cpu"] == pytest.approx(4 * b * L * m.h1 * (9 / 32) / 7e9, rel=1e-12)
+    assert on["c2g"] + on["g2c"] == pytest.approx(8 * b * m.h1, rel=1e-12)   # q, k, v down, the row up
+    _, _, wl, mc = _pair(pol, kw, dict(cpu_attn_bw=40e9, cpu_attn_bw_q4=7e9, bw_c2g=1.0, bw_g2c=1.0))
+    got = pol.estimate(wl, mc, b, 8, p, cpu_attn=True)
+    for k in oc.PATHS:
+        assert got["paths_gen"][k] == pytest.approx(on[k], rel=1e-12, abs=1e-18)
 
 
 CPU_CASES = [

@@ -26,13 +26,16 @@ decode attention reads the cache at the attention kernel's bandwidth;
 prefill runs its flops (projections and causal attention) at the prompt
 GEMM rate.
 
-CPU attention ("为什么有时应该在 CPU 上算注意力"): for an fp16 cache the
-decode attention of the CPU-resident share can run on the host, which then
+CPU attention ("为什么有时应该在 CPU 上算注意力"): the decode attention of the
+CPU-resident cache share can run on the host, which then
 reads that share at its own bandwidth (a sixth path, "cpu") while only the
 q, k, v rows of its sequences go down to the host (3 h1 fp16 each) and their
 attention rows come back (h1 fp16), instead of the cache crossing to the
-GPU; the GPU's attention reads the other shares only.  The search tries the
-policy both ways where the cache is fp16 and the machine has a CPU rate.
+GPU; the GPU's attention reads the other shares only.  A compressed cache is
+read at a rate of its own (the pages' authors switch the delegation off with
+compression, their CPU's dequantization being too slow; here the measured
+rates decide).  The search tries the policy both ways where the machine has
+a CPU rate for the workload's cache format.
 """
 from __future__ import annotations
 
@@ -75,6 +78,7 @@ class Machine:
     alpha_c: float = 1.0
     alpha_d: float = 1.0
     cpu_attn_bw: float = 0.0  # fp16 cache read by decode attention on the host, bytes/s (0: none)
+    cpu_attn_bw_q4: float = 0.0  # 4-bit cache, stored bytes/s (0: none)
 
 
 def mi355x(host_bytes: float = 1.0e12, disk_bytes: float = 0.0, disk_bw: float = 2.0e9) -> Machine:
@@ -85,11 +89,13 @@ def mi355x(host_bytes: float = 1.0e12, disk_bytes: float = 0.0, disk_bw: float =
     prefill), decode attention 5.63 TB/s, weight streaming at 5.6 TB/s of the
     8 TB/s HBM.  288 GB of HBM with 10% held back (alpha_g 1.1).  Decode
     attention on 16 host threads, overlapped with the GPU's work, reads an
-    fp16 cache at 300 GB/s (history bytes over the whole step).  Host memory
-    and disk are machine-specific arguments (no disk tier by default)."""
+    fp16 cache at 300 GB/s and a 4-bit one at 165 GB/s of stored bytes
+    (history bytes over the whole step).  Host memory and disk are
+    machine-specific arguments (no disk tier by default)."""
     return Machine(bw_c2g=55.9e9, bw_g2c=55.9e9, bw_d2c=disk_bw, bw_c2d=disk_bw / 2,
                    gemm_flops=961e12, prefill_flops=1.09e15, hbm_bw=5.6e12, attn_bw=5.63e12,
-                   cap_g=288e9, cap_c=host_bytes, cap_d=disk_bytes, alpha_g=1.1, cpu_attn_bw=300e9)
+                   cap_g=288e9, cap_c=host_bytes, cap_d=disk_bytes, alpha_g=1.1, cpu_attn_bw=300e9,
+                   cpu_attn_bw_q4=165e9)
 
 
 MODELS = {   # OPT shapes: layers, h1, h2
@@ -98,13 +104,18 @@ MODELS = {   # OPT shapes: layers, h1, h2
 }
 
 
+def cpu_rate(wl: Workload, mc: Machine) -> float:
+    """Host attention rate for the workload's cache format (0: none)."""
+    return mc.cpu_attn_bw if wl.c_ratio == 1.0 else mc.cpu_attn_bw_q4
+
+
 def _affine(wl: Workload, mc: Machine, bls: int, gbs: int, cpu_attn: bool = False):
     """Coefficients of the nine shares: path times T[phase] = A f + b (6 x 9,
     6) for phase "pre" and "gen", and memory held M = P f + q (3 x 9, 3) for
     tiers g, c, d in each phase ("mem_pre", "mem_gen").  cpu_attn: decode
-    attention of the host cache share on the host (fp16 cache only)."""
-    if cpu_attn and not (wl.c_ratio == 1.0 and mc.cpu_attn_bw > 0):
-        raise ValueError("CPU attention needs an fp16 cache and a host attention rate")
+    attention of the host cache share on the host."""
+    if cpu_attn and not cpu_rate(wl, mc) > 0:
+        raise ValueError("CPU attention needs the host's attention rate for this cache format")
     h1, h2 = wl.h1, wl.h2
     W = (8 * h1 * h1 + 4 * h1 * h2) * wl.w_ratio
     mats = 8 * h1 * h1 + 4 * h1 * h2
@@ -137,7 +148,7 @@ def _affine(wl: Workload, mc: Machine, bls: int, gbs: int, cpu_attn: bool = Fals
         b[4] = comp
         if host_attn:                         # the host share leaves the GPU's attention
             A[4, i["cc"]] -= c_in / mc.attn_bw
-            A[5, i["cc"]] += c_in / mc.cpu_attn_bw
+            A[5, i["cc"]] += c_in / cpu_rate(wl, mc)
         out[ph] = (A, b)
     # peak memory per phase: the prompt (cache at s, activations of s tokens
     # per sequence) and a decode step (cache at s + n, one token); each
@@ -226,10 +237,10 @@ def solve(wl: Workload, mc: Machine, bls: int, gbs: int, limits: dict | None = N
 def search(wl: Workload, mc: Machine, gbs_list=(8, 16, 24, 32, 48, 64, 96, 128, 192, 256),
            nb_max: int = 64, limits: dict | None = None, cpu_attn: bool | None = None):
     """The (gbs, nb, shares, cpu attention) of least T / bls over gbs_list x
-    1..nb_max.  cpu_attn None: both ways where the cache is fp16 and the
-    machine has a host attention rate, else without."""
+    1..nb_max.  cpu_attn None: both ways where the machine has a host
+    attention rate for the cache format, else without."""
     if cpu_attn is None:
-        modes = (False, True) if wl.c_ratio == 1.0 and mc.cpu_attn_bw > 0 else (False,)
+        modes = (False, True) if cpu_rate(wl, mc) > 0 else (False,)
     else:
         modes = (cpu_attn,)
     best = None
@@ -279,7 +290,7 @@ def search_realized(wl: Workload, mc: Machine, gbs_list=(16, 32, 48, 64), nb_max
     capacities.  Rounding can reverse the LP's ranking: a small host cache
     share with CPU attention wins the continuous program, and the whole GPU
     batch it becomes may leave the host attending far more than it should."""
-    modes = (False, True) if wl.c_ratio == 1.0 and mc.cpu_attn_bw > 0 else (False,)
+    modes = (False, True) if cpu_rate(wl, mc) > 0 else (False,)
     best = None
     for ca in modes:
         for gbs in gbs_list:
@@ -317,7 +328,7 @@ def main(argv=None):
     ap.add_argument("--percent", type=float, nargs=6,
                     help="wg wc cg cc hg hc in percent (disk = the rest): estimate this policy")
     ap.add_argument("--cpu-attention", choices=("auto", "on", "off"), default="auto",
-                    help="decode attention of the host cache share on the host (fp16 cache only)")
+                    help="decode attention of the host cache share on the host")
     a = ap.parse_args(argv)
     l, h1, h2 = MODELS[a.model]
     wl = Workload(l, h1, h2, a.prompt_len, a.gen_len,
